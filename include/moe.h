@@ -1,0 +1,173 @@
+/*
+ * moe.h -- C ABI of the MI355X (gfx950) routed Mixture-of-Experts layer.
+ *
+ * One call of moe_forward runs the routed-MoE layer of an LLM decode/prefill step on
+ * one GPU, in five stream-ordered kernels:
+ *
+ *   1. router: key[t,e] = sum_h x[t,h] * Wr[e,h] (+ bias[e]), accumulated in fp64;
+ *      top-k by (key descending, expert id ascending); weights = sigmoid(key) of the
+ *      k picks renormalised to sum 1.
+ *      (sglang PR #29509 analysis, "GLM-4.7-Flash on NPU", section 2 "MoE TopK
+ *      scoring function": sigmoid scoring fused with the top-k.)
+ *   2. align: an expert-major token plan built from a histogram and a prefix scan,
+ *      padded to the GEMM block, with a block -> expert map.
+ *      (FlashInfer PR #6511 analysis, "AlphaMoE NVFP4 kernels", section 5
+ *      "moe_align_block_size_kernel synchronisation" and section 6 "self-routing up
+ *      kernels".)
+ *   3. grouped up-GEMM with SwiGLU: act = silu(x W13[e,0:I]^T) * (x W13[e,I:2I]^T).
+ *   4. grouped down-GEMM: y = act W2[e]^T, one row per (token, pick).
+ *      (AlphaMoE page, sections 1-4: up kernels, down kernels, token-tile gather.)
+ *   5. finalize: m = sum_j w[t,j] y[t*k+j]; z = m + residual; out = RMSNorm(z) * g.
+ *      (FlashInfer PR #5701 analysis, "Kimi K3 H7168/K16 MNNVL", intro and section 3:
+ *      MoE finalize followed by RMSNorm with RMS_EPS = 1e-5 and no weight offset;
+ *      FlashInfer PR #4690 analysis, "MiniMax-H3 BF16 pre-attention", section 1: the
+ *      RMSNorm is torch's rms_norm, eps inside the square root.)
+ *
+ * Conventions for every entry point:
+ *   - Tensor pointers are DEVICE pointers owned by the caller.  The library keeps no
+ *     reference to them after the call returns and allocates no device memory; all
+ *     scratch lives in a caller-provided workspace.
+ *   - bf16 values are passed as uint16_t bit patterns.  Layouts are row-major with the
+ *     last dimension contiguous.  Every device pointer must be 16-byte aligned.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL is the null stream).
+ *     No entry point synchronises the host, so a call can be captured in a graph.
+ *   - Arguments are validated on the host before anything is launched.  Errors are
+ *     returned as status codes (never abort); on error nothing has been launched,
+ *     except MOE_ERR_HIP, which reports a failed launch.
+ *   - Sizes: 1 <= top_k <= E <= 1024, H % 16 == 0 and 16 <= H <= 16384, I % 64 == 0,
+ *     M >= 0 (M == 0 is a successful no-op), M * top_k < 2^31.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* moe_stream_t; /* hipStream_t */
+typedef void* moe_event_t;  /* hipEvent_t  */
+
+enum {
+  MOE_OK = 0,
+  MOE_ERR_INVALID_ARG = -1, /* a size, pointer or scalar is outside its documented range */
+  MOE_ERR_UNSUPPORTED = -2, /* valid but not built (e.g. a block size with no kernel) */
+  MOE_ERR_WORKSPACE = -3,   /* workspace pointer NULL or smaller than required */
+  MOE_ERR_HIP = -4          /* a HIP launch or event call failed */
+};
+
+/* Human-readable text of a status code.  Never NULL; static storage. */
+const char* moe_strerror(int status);
+
+/* ABI version of this header (major * 100 + minor). */
+int moe_abi_version(void);
+
+/*
+ * Entries the align plan may need: M*top_k real entries plus at most block-1 padding
+ * slots for each touched expert (at most min(E, M*top_k) experts), rounded up to a
+ * whole block.  sorted_ids needs this many int32; block_expert needs capacity/block.
+ * Returns 0 for invalid sizes.
+ */
+size_t moe_align_capacity(int32_t M, int32_t top_k, int32_t E, int32_t block);
+
+/* Workspace bytes moe_route needs (fp64 keys [M, E]).  0 for invalid sizes. */
+size_t moe_route_workspace_bytes(int32_t M, int32_t E);
+
+/*
+ * Workspace bytes moe_forward needs for these sizes: routing ids/weights, the plan,
+ * the router keys, the bf16 SwiGLU activations [capacity, I] and the fp32 per-pick
+ * down-projection rows [M*top_k, H].  0 for invalid sizes.
+ */
+size_t moe_workspace_bytes(int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k,
+                           int32_t block);
+
+/*
+ * Router (step 1).
+ *   x          [M, H] bf16        hidden states
+ *   router_w   [E, H] bf16        gate weight
+ *   router_bias[E]    fp32 or NULL additive bias, used for selection and in the sigmoid
+ *   topk_ids   [M, top_k] int32   out: expert ids, key descending, ties to the lower id
+ *   topk_w     [M, top_k] fp32    out: sigmoid(key) renormalised over the k picks
+ *   workspace  >= moe_route_workspace_bytes(M, E) bytes of device memory
+ */
+int moe_route(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
+              int32_t M, int32_t H, int32_t E, int32_t top_k,
+              int32_t* topk_ids, float* topk_w,
+              void* workspace, size_t workspace_bytes, moe_stream_t stream);
+
+/*
+ * Align (step 2).  Flat index i = t * top_k + j of topk_ids [M, top_k].
+ *   sorted_ids  [moe_align_capacity] int32 out: expert-major plan; inside an expert the
+ *               flat indices ascend; each expert's run is padded with the sentinel
+ *               M*top_k up to a multiple of `block`.  Entries past num_padded are
+ *               left unwritten.
+ *   block_expert[capacity/block] int32 out: expert of each plan block (first
+ *               num_padded/block entries written).
+ *   num_padded  [1] int32 out: total plan length (a multiple of block).
+ * Ids outside [0, E) are skipped (never placed).  Any block >= 1 is accepted.
+ */
+int moe_align(const int32_t* topk_ids, int32_t M, int32_t top_k, int32_t E, int32_t block,
+              int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
+              moe_stream_t stream);
+
+/*
+ * Grouped up-GEMM with SwiGLU (step 3) over an align plan.
+ *   act [capacity, I] bf16 out: for every plan row r inside the 16-row groups that hold
+ *   at least one real entry, act[r] = silu(x[t] W13[e,0:I]^T) * (x[t] W13[e,I:2I]^T)
+ *   with t = sorted_ids[r] / top_k (rows holding the sentinel get 0).  Other rows are
+ *   left unwritten.  block must be 16, 32, 64 or 128.
+ */
+int moe_expert_up(const uint16_t* x, const uint16_t* w13, const int32_t* sorted_ids,
+                  const int32_t* block_expert, const int32_t* num_padded,
+                  int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k, int32_t block,
+                  int32_t capacity, uint16_t* act, moe_stream_t stream);
+
+/*
+ * Grouped down-GEMM (step 4).
+ *   y [M*top_k, H] fp32 out: y[i] = act[r] W2[e]^T for every plan row r holding a real
+ *   flat index i = sorted_ids[r].
+ */
+int moe_expert_down(const uint16_t* act, const uint16_t* w2, const int32_t* sorted_ids,
+                    const int32_t* block_expert, const int32_t* num_padded,
+                    int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k,
+                    int32_t block, int32_t capacity, float* y, moe_stream_t stream);
+
+/*
+ * Finalize (step 5).
+ *   y [M*top_k, H] fp32, topk_w [M, top_k] fp32, residual [M, H] bf16, norm_w [H] bf16.
+ *   z = sum_j topk_w[t,j] * y[t*top_k + j] (j ascending, fp32) + residual[t]
+ *   out[t] = bf16(z * (mean(z^2) + eps)^(-1/2) * norm_w); residual_out[t] = bf16(z)
+ *   when residual_out is not NULL.  eps > 0.
+ */
+int moe_finalize(const float* y, const float* topk_w, const uint16_t* residual,
+                 const uint16_t* norm_w, float eps, int32_t M, int32_t H, int32_t top_k,
+                 uint16_t* out, uint16_t* residual_out, moe_stream_t stream);
+
+/*
+ * The whole layer: steps 1-5 on one stream.
+ *   Required: x, router_w, w13 [E, 2I, H], w2 [E, H, I], residual, norm_w, out,
+ *   workspace.  Optional (NULL allowed): router_bias, residual_out, and the exported
+ *   intermediates topk_ids_out [M, top_k], topk_w_out [M, top_k], sorted_ids_out
+ *   [capacity], block_expert_out [capacity/block], num_padded_out [1]; when given,
+ *   the step writes there instead of the workspace.
+ *   block must be 16, 32, 64 or 128.
+ *   stage_events: NULL, or 6 hipEvent_t recorded on `stream` before step 1 and after
+ *   each of the five steps (for per-step timing).
+ */
+int moe_forward(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
+                const uint16_t* w13, const uint16_t* w2,
+                const uint16_t* residual, const uint16_t* norm_w, float eps,
+                int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k, int32_t block,
+                uint16_t* out, uint16_t* residual_out,
+                int32_t* topk_ids_out, float* topk_w_out,
+                int32_t* sorted_ids_out, int32_t* block_expert_out, int32_t* num_padded_out,
+                void* workspace, size_t workspace_bytes,
+                const moe_event_t* stage_events, moe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_MI355X_H */

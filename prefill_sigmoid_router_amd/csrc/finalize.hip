@@ -1,0 +1,116 @@
+// Finalize step of the routed-MoE layer: weighted top-k combine, residual add, RMSNorm.
+//
+// FlashInfer PR #5701 analysis ("Kimi K3 H7168/K16 MNNVL CuTe DSL"), intro and section 3:
+// the MoE finalize (combine of the top-k expert rows) is fused with the residual path
+// and RMSNorm, with RMS_EPS = 1e-5 and WEIGHT_BIAS = 0 (weight used as is); section 2: a
+// 7168-wide bf16 row is 896 packs of 16 bytes.  FlashInfer PR #4690 analysis
+// ("MiniMax-H3 BF16 pre-attention"), section 1: RMSNorm = torch rms_norm over the hidden
+// dim, eps inside the square root.  sglang PR #29509 analysis, "why it's good" 1:
+// RMSNorm is memory-bound, so it is fused with its producer's consumer here.
+//
+// One workgroup per token; each thread owns V groups of 4 hidden values, so z stays in
+// registers between the sum of squares and the scaling.  All arithmetic is fp32 with a
+// single bf16 rounding (RNE) at the store.
+#include "device_common.h"
+#include "launchers.h"
+
+namespace moe {
+
+template <int V>
+__global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ y,
+                                                       const float* __restrict__ topk_w,
+                                                       const uint16_t* __restrict__ residual,
+                                                       const uint16_t* __restrict__ norm_w,
+                                                       float eps, int H, int top_k,
+                                                       uint16_t* __restrict__ out,
+                                                       uint16_t* __restrict__ residual_out) {
+  __shared__ float part[4];
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int ngroups = H >> 2;
+
+  float4 m[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) m[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+
+  const float* yt = y + (size_t)t * top_k * H;
+  for (int j = 0; j < top_k; ++j) {  // j ascending
+    const float w = topk_w[(size_t)t * top_k + j];
+    const float4* yr = reinterpret_cast<const float4*>(yt + (size_t)j * H);
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const int c = tid + 256 * v;
+      if (c < ngroups) {
+        const float4 a = yr[c];
+        m[v].x = fmaf(w, a.x, m[v].x);
+        m[v].y = fmaf(w, a.y, m[v].y);
+        m[v].z = fmaf(w, a.z, m[v].z);
+        m[v].w = fmaf(w, a.w, m[v].w);
+      }
+    }
+  }
+
+  const uint2* rr = reinterpret_cast<const uint2*>(residual + (size_t)t * H);
+  float ss = 0.f;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int c = tid + 256 * v;
+    if (c < ngroups) {
+      const uint2 r = rr[c];
+      m[v].x += bf16lo(r.x);
+      m[v].y += bf16hi(r.x);
+      m[v].z += bf16lo(r.y);
+      m[v].w += bf16hi(r.y);
+      ss = fmaf(m[v].x, m[v].x, ss);
+      ss = fmaf(m[v].y, m[v].y, ss);
+      ss = fmaf(m[v].z, m[v].z, ss);
+      ss = fmaf(m[v].w, m[v].w, ss);
+    }
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
+  __syncthreads();
+  const float total = (part[0] + part[1]) + (part[2] + part[3]);
+  const float inv = 1.0f / sqrtf(total / (float)H + eps);
+
+  const uint2* gw = reinterpret_cast<const uint2*>(norm_w);
+  uint2* ot = reinterpret_cast<uint2*>(out + (size_t)t * H);
+  uint2* rt = residual_out ? reinterpret_cast<uint2*>(residual_out + (size_t)t * H) : nullptr;
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int c = tid + 256 * v;
+    if (c < ngroups) {
+      const uint2 g = gw[c];
+      uint2 o;
+      o.x = pack_bf16x2(m[v].x * inv * bf16lo(g.x), m[v].y * inv * bf16hi(g.x));
+      o.y = pack_bf16x2(m[v].z * inv * bf16lo(g.y), m[v].w * inv * bf16hi(g.y));
+      ot[c] = o;
+      if (rt) {
+        uint2 zr;
+        zr.x = pack_bf16x2(m[v].x, m[v].y);
+        zr.y = pack_bf16x2(m[v].z, m[v].w);
+        rt[c] = zr;
+      }
+    }
+  }
+}
+
+template <int V>
+static hipError_t launch_fin(const float* y, const float* w, const uint16_t* res, const uint16_t* g,
+                             float eps, int M, int H, int k, uint16_t* out, uint16_t* rout,
+                             hipStream_t s) {
+  hipLaunchKernelGGL((finalize_kernel<V>), dim3(M), dim3(256), 0, s, y, w, res, g, eps, H, k, out, rout);
+  return hipGetLastError();
+}
+
+hipError_t launch_finalize(const float* y, const float* topk_w, const uint16_t* residual,
+                           const uint16_t* norm_w, float eps, int M, int H, int top_k,
+                           uint16_t* out, uint16_t* residual_out, hipStream_t s) {
+  const int per_thread = (H / 4 + 255) / 256;
+  if (per_thread <= 1) return launch_fin<1>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
+  if (per_thread <= 2) return launch_fin<2>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
+  if (per_thread <= 4) return launch_fin<4>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
+  if (per_thread <= 8) return launch_fin<8>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
+  return launch_fin<16>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
+}
+
+}  // namespace moe

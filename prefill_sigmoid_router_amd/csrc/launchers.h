@@ -1,0 +1,35 @@
+// Internal launchers of the routed-MoE kernels (host side, C++ linkage).  The C ABI in
+// moe_api.hip validates arguments and then calls these; each returns the launch status.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+// Router keys (fp64, [M, E] in `keys`) then top-k ids / renormalised sigmoid weights.
+hipError_t launch_route(const uint16_t* x, const uint16_t* wr, const float* bias, int M, int H,
+                        int E, int top_k, int32_t* ids, float* w, double* keys, hipStream_t s);
+
+// Expert-major plan of the flat ids [n]; sentinel = n.
+hipError_t launch_align(const int32_t* ids, int n, int E, int block, int32_t* sorted_ids,
+                        int32_t* block_expert, int32_t* num_padded, hipStream_t s);
+
+// Grouped up-GEMM + SwiGLU over the plan: act [capacity, I] bf16.
+hipError_t launch_expert_up(const uint16_t* x, const uint16_t* w13, const int32_t* sorted_ids,
+                            const int32_t* block_expert, const int32_t* num_padded, int M, int H,
+                            int E, int I, int top_k, int block, int capacity, uint16_t* act,
+                            hipStream_t s);
+
+// Grouped down-GEMM over the plan: y [M*top_k, H] fp32.
+hipError_t launch_expert_down(const uint16_t* act, const uint16_t* w2, const int32_t* sorted_ids,
+                              const int32_t* block_expert, const int32_t* num_padded, int M,
+                              int H, int E, int I, int top_k, int block, int capacity, float* y,
+                              hipStream_t s);
+
+// Weighted top-k combine + residual add + RMSNorm.
+hipError_t launch_finalize(const float* y, const float* topk_w, const uint16_t* residual,
+                           const uint16_t* norm_w, float eps, int M, int H, int top_k,
+                           uint16_t* out, uint16_t* residual_out, hipStream_t s);
+
+}  // namespace moe

@@ -1,0 +1,236 @@
+// C ABI of the routed-MoE layer (declared in include/moe.h): host-side validation,
+// workspace carve-up and stream-ordered launches.  Nothing here allocates device memory
+// or synchronises the host.
+#include <math.h>
+#include <stdint.h>
+
+#include "../../include/moe.h"
+#include "launchers.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxE = 1024;
+constexpr int kMaxH = 16384;
+
+inline size_t round_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool sizes_ok(int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k) {
+  if (M < 0 || E < 1 || E > kMaxE || top_k < 1 || top_k > E) return false;
+  if (H < 16 || H > kMaxH || H % 16 != 0) return false;
+  if (I < 64 || I % 64 != 0) return false;
+  if ((int64_t)M * top_k >= ((int64_t)1 << 31)) return false;
+  return true;
+}
+
+bool gemm_block_ok(int32_t block) {
+  return block == 16 || block == 32 || block == 64 || block == 128;
+}
+
+size_t capacity_of(int32_t M, int32_t top_k, int32_t E, int32_t block) {
+  const int64_t n = (int64_t)M * top_k;
+  const int64_t touched = n < E ? n : E;
+  const int64_t cap = n + touched * (block - 1);
+  return (size_t)round_up((size_t)cap, (size_t)block);
+}
+
+// Workspace layout of moe_forward; every region starts on a 256-byte boundary.
+struct Layout {
+  size_t keys, ids, w, sorted, bexp, npad, act, y, total;
+};
+
+Layout layout_of(int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k, int32_t block) {
+  Layout L;
+  const size_t n = (size_t)M * top_k;
+  const size_t cap = capacity_of(M, top_k, E, block);
+  size_t off = 0;
+  L.keys = off;   off += round_up((size_t)M * E * sizeof(double), kAlign);
+  L.ids = off;    off += round_up(n * sizeof(int32_t), kAlign);
+  L.w = off;      off += round_up(n * sizeof(float), kAlign);
+  L.sorted = off; off += round_up(cap * sizeof(int32_t), kAlign);
+  L.bexp = off;   off += round_up((cap / block) * sizeof(int32_t), kAlign);
+  L.npad = off;   off += kAlign;
+  L.act = off;    off += round_up(cap * (size_t)I * sizeof(uint16_t), kAlign);
+  L.y = off;      off += round_up(n * (size_t)H * sizeof(float), kAlign);
+  L.total = off;
+  return L;
+}
+
+inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_strerror(int status) {
+  switch (status) {
+    case MOE_OK: return "ok";
+    case MOE_ERR_INVALID_ARG: return "invalid argument (size, pointer, alignment or scalar out of range)";
+    case MOE_ERR_UNSUPPORTED: return "unsupported configuration (no kernel built for it)";
+    case MOE_ERR_WORKSPACE: return "workspace missing or too small";
+    case MOE_ERR_HIP: return "HIP launch or event call failed";
+    default: return "unknown status";
+  }
+}
+
+int moe_abi_version(void) { return 100; }
+
+size_t moe_align_capacity(int32_t M, int32_t top_k, int32_t E, int32_t block) {
+  if (M < 0 || top_k < 1 || E < 1 || block < 1) return 0;
+  if ((int64_t)M * top_k >= ((int64_t)1 << 31)) return 0;
+  return capacity_of(M, top_k, E, block);
+}
+
+size_t moe_route_workspace_bytes(int32_t M, int32_t E) {
+  if (M < 0 || E < 1 || E > kMaxE) return 0;
+  return round_up((size_t)M * E * sizeof(double), kAlign) + kAlign;
+}
+
+size_t moe_workspace_bytes(int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k,
+                           int32_t block) {
+  if (!sizes_ok(M, H, E, I, top_k) || !gemm_block_ok(block)) return 0;
+  return layout_of(M, H, E, I, top_k, block).total;
+}
+
+int moe_route(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
+              int32_t M, int32_t H, int32_t E, int32_t top_k, int32_t* topk_ids, float* topk_w,
+              void* workspace, size_t workspace_bytes, moe_stream_t stream) {
+  if (M < 0 || E < 1 || E > kMaxE || top_k < 1 || top_k > E || H < 16 || H > kMaxH ||
+      H % 16 != 0 || (int64_t)M * top_k >= ((int64_t)1 << 31))
+    return MOE_ERR_INVALID_ARG;
+  if (M == 0) return MOE_OK;
+  if (!x || !router_w || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(topk_ids, 4) || !aligned(topk_w, 4) ||
+      (router_bias && !aligned(router_bias, 4)))
+    return MOE_ERR_INVALID_ARG;
+  if (!workspace || !aligned(workspace, 16) || workspace_bytes < moe_route_workspace_bytes(M, E))
+    return MOE_ERR_WORKSPACE;
+  return hip_status(moe::launch_route(x, router_w, router_bias, M, H, E, top_k, topk_ids, topk_w,
+                                      static_cast<double*>(workspace), (hipStream_t)stream));
+}
+
+int moe_align(const int32_t* topk_ids, int32_t M, int32_t top_k, int32_t E, int32_t block,
+              int32_t* sorted_ids, int32_t* block_expert, int32_t* num_padded,
+              moe_stream_t stream) {
+  if (M < 0 || top_k < 1 || E < 1 || E > kMaxE || block < 1 ||
+      (int64_t)M * top_k >= ((int64_t)1 << 31))
+    return MOE_ERR_INVALID_ARG;
+  if (!topk_ids || !sorted_ids || !block_expert || !num_padded) return MOE_ERR_INVALID_ARG;
+  if (!aligned(topk_ids, 4) || !aligned(sorted_ids, 4) || !aligned(block_expert, 4) ||
+      !aligned(num_padded, 4))
+    return MOE_ERR_INVALID_ARG;
+  if (capacity_of(M, top_k, E, block) >= ((size_t)1 << 31)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_align(topk_ids, M * top_k, E, block, sorted_ids, block_expert,
+                                      num_padded, (hipStream_t)stream));
+}
+
+int moe_expert_up(const uint16_t* x, const uint16_t* w13, const int32_t* sorted_ids,
+                  const int32_t* block_expert, const int32_t* num_padded, int32_t M, int32_t H,
+                  int32_t E, int32_t I, int32_t top_k, int32_t block, int32_t capacity,
+                  uint16_t* act, moe_stream_t stream) {
+  if (!sizes_ok(M, H, E, I, top_k)) return MOE_ERR_INVALID_ARG;
+  if (!gemm_block_ok(block)) return MOE_ERR_UNSUPPORTED;
+  if (capacity < 0 || capacity % block != 0 ||
+      (size_t)capacity < capacity_of(M, top_k, E, block))
+    return MOE_ERR_INVALID_ARG;
+  if (M == 0) return MOE_OK;
+  if (!x || !w13 || !sorted_ids || !block_expert || !num_padded || !act) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(w13, 16) || !aligned(act, 16)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_expert_up(x, w13, sorted_ids, block_expert, num_padded, M, H, E, I,
+                                          top_k, block, capacity, act, (hipStream_t)stream));
+}
+
+int moe_expert_down(const uint16_t* act, const uint16_t* w2, const int32_t* sorted_ids,
+                    const int32_t* block_expert, const int32_t* num_padded, int32_t M, int32_t H,
+                    int32_t E, int32_t I, int32_t top_k, int32_t block, int32_t capacity,
+                    float* y, moe_stream_t stream) {
+  if (!sizes_ok(M, H, E, I, top_k)) return MOE_ERR_INVALID_ARG;
+  if (!gemm_block_ok(block)) return MOE_ERR_UNSUPPORTED;
+  if (capacity < 0 || capacity % block != 0 ||
+      (size_t)capacity < capacity_of(M, top_k, E, block))
+    return MOE_ERR_INVALID_ARG;
+  if (M == 0) return MOE_OK;
+  if (!act || !w2 || !sorted_ids || !block_expert || !num_padded || !y) return MOE_ERR_INVALID_ARG;
+  if (!aligned(act, 16) || !aligned(w2, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_expert_down(act, w2, sorted_ids, block_expert, num_padded, M, H, E,
+                                            I, top_k, block, capacity, y, (hipStream_t)stream));
+}
+
+int moe_finalize(const float* y, const float* topk_w, const uint16_t* residual,
+                 const uint16_t* norm_w, float eps, int32_t M, int32_t H, int32_t top_k,
+                 uint16_t* out, uint16_t* residual_out, moe_stream_t stream) {
+  if (M < 0 || top_k < 1 || H < 16 || H > kMaxH || H % 16 != 0 || !(eps > 0.0f) || !isfinite(eps) ||
+      (int64_t)M * top_k >= ((int64_t)1 << 31))
+    return MOE_ERR_INVALID_ARG;
+  if (M == 0) return MOE_OK;
+  if (!y || !topk_w || !residual || !norm_w || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned(y, 16) || !aligned(residual, 16) || !aligned(norm_w, 16) || !aligned(out, 16) ||
+      (residual_out && !aligned(residual_out, 16)) || !aligned(topk_w, 4))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_finalize(y, topk_w, residual, norm_w, eps, M, H, top_k, out,
+                                         residual_out, (hipStream_t)stream));
+}
+
+int moe_forward(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
+                const uint16_t* w13, const uint16_t* w2, const uint16_t* residual,
+                const uint16_t* norm_w, float eps, int32_t M, int32_t H, int32_t E, int32_t I,
+                int32_t top_k, int32_t block, uint16_t* out, uint16_t* residual_out,
+                int32_t* topk_ids_out, float* topk_w_out, int32_t* sorted_ids_out,
+                int32_t* block_expert_out, int32_t* num_padded_out, void* workspace,
+                size_t workspace_bytes, const moe_event_t* stage_events, moe_stream_t stream) {
+  if (!sizes_ok(M, H, E, I, top_k) || !(eps > 0.0f) || !isfinite(eps)) return MOE_ERR_INVALID_ARG;
+  if (!gemm_block_ok(block)) return MOE_ERR_UNSUPPORTED;
+  if (M == 0) return MOE_OK;
+  if (!x || !router_w || !w13 || !w2 || !residual || !norm_w || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(w13, 16) || !aligned(w2, 16) ||
+      !aligned(residual, 16) || !aligned(norm_w, 16) || !aligned(out, 16) ||
+      (residual_out && !aligned(residual_out, 16)) || (router_bias && !aligned(router_bias, 4)) ||
+      (topk_ids_out && !aligned(topk_ids_out, 4)) || (topk_w_out && !aligned(topk_w_out, 4)) ||
+      (sorted_ids_out && !aligned(sorted_ids_out, 4)) ||
+      (block_expert_out && !aligned(block_expert_out, 4)) ||
+      (num_padded_out && !aligned(num_padded_out, 4)))
+    return MOE_ERR_INVALID_ARG;
+  const size_t cap = capacity_of(M, top_k, E, block);
+  if (cap >= ((size_t)1 << 31)) return MOE_ERR_INVALID_ARG;
+  const Layout L = layout_of(M, H, E, I, top_k, block);
+  if (!workspace || !aligned(workspace, kAlign) || workspace_bytes < L.total) return MOE_ERR_WORKSPACE;
+
+  char* ws = static_cast<char*>(workspace);
+  double* keys = reinterpret_cast<double*>(ws + L.keys);
+  int32_t* ids = topk_ids_out ? topk_ids_out : reinterpret_cast<int32_t*>(ws + L.ids);
+  float* w = topk_w_out ? topk_w_out : reinterpret_cast<float*>(ws + L.w);
+  int32_t* sorted = sorted_ids_out ? sorted_ids_out : reinterpret_cast<int32_t*>(ws + L.sorted);
+  int32_t* bexp = block_expert_out ? block_expert_out : reinterpret_cast<int32_t*>(ws + L.bexp);
+  int32_t* npad = num_padded_out ? num_padded_out : reinterpret_cast<int32_t*>(ws + L.npad);
+  uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
+  float* y = reinterpret_cast<float*>(ws + L.y);
+  hipStream_t s = (hipStream_t)stream;
+
+  auto mark = [&](int i) -> bool {
+    return !stage_events || hipEventRecord((hipEvent_t)stage_events[i], s) == hipSuccess;
+  };
+  if (!mark(0)) return MOE_ERR_HIP;
+  if (moe::launch_route(x, router_w, router_bias, M, H, E, top_k, ids, w, keys, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (!mark(1)) return MOE_ERR_HIP;
+  if (moe::launch_align(ids, M * top_k, E, block, sorted, bexp, npad, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (!mark(2)) return MOE_ERR_HIP;
+  if (moe::launch_expert_up(x, w13, sorted, bexp, npad, M, H, E, I, top_k, block, (int)cap, act, s) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  if (!mark(3)) return MOE_ERR_HIP;
+  if (moe::launch_expert_down(act, w2, sorted, bexp, npad, M, H, E, I, top_k, block, (int)cap, y, s) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  if (!mark(4)) return MOE_ERR_HIP;
+  if (moe::launch_finalize(y, w, residual, norm_w, eps, M, H, top_k, out, residual_out, s) !=
+      hipSuccess)
+    return MOE_ERR_HIP;
+  if (!mark(5)) return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,131 @@
+"""CPU checks of the C ABI: the library builds, loads, exports every function that
+include/moe.h declares, and rejects invalid arguments on the host before launching
+anything (no compute call runs here: these paths return before any HIP call)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from oracle import moe_oracle as orc
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+
+
+@pytest.fixture(scope="module")
+def B():
+    from prefill_sigmoid_router_amd import binding, build
+    if not os.path.exists(binding.library_path()):
+        build.build()
+    binding.load_library()
+    return binding
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\*?\s*(moe_[a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_header_declares_the_documented_entry_points():
+    names = _declared_functions()
+    for want in ("moe_route", "moe_align", "moe_forward", "moe_expert_up", "moe_expert_down",
+                 "moe_finalize", "moe_workspace_bytes", "moe_align_capacity", "moe_strerror",
+                 "moe_route_workspace_bytes", "moe_abi_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol(B):
+    out = subprocess.run(["nm", "-D", "--defined-only", B.library_path()], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    for name in _declared_functions():
+        assert name in exported, name
+        assert hasattr(B.load_library(), name)
+    assert set(B.EXPORTED_SYMBOLS) == set(_declared_functions())
+
+
+def test_library_links_no_torch(B):
+    out = subprocess.run(["ldd", B.library_path()], capture_output=True, text=True).stdout
+    assert "torch" not in out and "c10" not in out
+
+
+def test_strerror_and_version(B):
+    assert B.moe_abi_version() == 100
+    for s in (0, -1, -2, -3, -4, 17):
+        assert isinstance(B.moe_strerror(s), str) and B.moe_strerror(s)
+
+
+@pytest.mark.parametrize("M,k,E,block", [(4, 2, 8, 16), (8, 16, 256, 16), (128, 16, 256, 64),
+                                         (512, 16, 256, 64), (2048, 16, 256, 64), (1, 1, 1, 1),
+                                         (3, 5, 7, 3), (0, 4, 8, 16)])
+def test_align_capacity_agrees_with_oracle(B, M, k, E, block):
+    assert B.moe_align_capacity(M, k, E, block) == orc.align_capacity(M, k, E, block)
+
+
+def test_workspace_bytes_cover_the_buffers(B):
+    M, H, E, I, k, blk = 2048, 7168, 256, 2048, 16, 64
+    cap = B.moe_align_capacity(M, k, E, blk)
+    need = M * E * 8 + 2 * M * k * 4 + cap * 4 + cap // blk * 4 + 4 + cap * I * 2 + M * k * H * 4
+    got = B.moe_workspace_bytes(M, H, E, I, k, blk)
+    assert need <= got <= need + 8 * 256
+    assert B.moe_workspace_bytes(M, H, E, I, k, 48) == 0          # no kernel for block 48
+    assert B.moe_workspace_bytes(M, 7160, E, I, k, blk) == 0      # H % 16 != 0
+    assert B.moe_workspace_bytes(M, H, 2000, I, k, blk) == 0      # E > 1024
+    assert B.moe_route_workspace_bytes(M, E) >= M * E * 8
+
+
+def _fwd(lib, **kw):
+    args = dict(x=256, rw=256, bias=None, w13=256, w2=256, res=256, g=256, eps=1e-5, M=4, H=256,
+                E=8, I=512, k=2, block=16, out=256, rout=None, ids=None, w=None, sid=None, bexp=None, npad=None,
+                ws=256, wsb=1 << 40, ev=None)
+    args.update(kw)
+    p = lambda v: None if v is None else ctypes.c_void_p(v)  # noqa: E731
+    return lib.moe_forward(p(args["x"]), p(args["rw"]), p(args["bias"]), p(args["w13"]),
+                           p(args["w2"]), p(args["res"]), p(args["g"]), args["eps"], args["M"],
+                           args["H"], args["E"], args["I"], args["k"], args["block"], p(args["out"]),
+                           p(args["rout"]), p(args["ids"]), p(args["w"]), p(args["sid"]),
+                           p(args["bexp"]), p(args["npad"]), p(args["ws"]), args["wsb"], args["ev"],
+                           None)
+
+
+@pytest.mark.parametrize("bad,code", [
+    (dict(M=-1), -1), (dict(k=0), -1), (dict(k=9), -1), (dict(E=1025, k=2), -1),
+    (dict(H=250), -1), (dict(I=100), -1), (dict(eps=0.0), -1), (dict(eps=float("nan")), -1),
+    (dict(block=48), -2), (dict(block=8), -2), (dict(x=None), -1), (dict(out=None), -1),
+    (dict(w13=None), -1), (dict(x=9), -1), (dict(ws=None), -3), (dict(wsb=16), -3),
+    (dict(ws=64), -3),
+])
+def test_forward_rejects_invalid_arguments_on_the_host(B, bad, code):
+    assert _fwd(B.load_library(), **bad) == code
+
+
+def test_forward_zero_tokens_is_a_noop(B):
+    assert _fwd(B.load_library(), M=0, x=None, res=None, out=None, ws=None, wsb=0) == 0
+
+
+def test_route_align_finalize_validation(B):
+    lib = B.load_library()
+    p = ctypes.c_void_p
+    # route: top_k > E, H % 16, workspace too small
+    assert lib.moe_route(p(16), p(16), None, 4, 256, 8, 9, p(16), p(16), p(256), 1 << 30, None) == -1
+    assert lib.moe_route(p(16), p(16), None, 4, 200, 8, 2, p(16), p(16), p(256), 1 << 30, None) == -1
+    assert lib.moe_route(p(16), p(16), None, 4, 256, 8, 2, p(16), p(16), p(256), 8, None) == -3
+    assert lib.moe_route(None, p(16), None, 4, 256, 8, 2, p(16), p(16), p(256), 1 << 30, None) == -1
+    assert lib.moe_route(None, None, None, 0, 256, 8, 2, None, None, None, 0, None) == 0
+    # align: block 0, E too large, null output
+    assert lib.moe_align(p(16), 4, 2, 8, 0, p(16), p(16), p(16), None) == -1
+    assert lib.moe_align(p(16), 4, 2, 1025, 16, p(16), p(16), p(16), None) == -1
+    assert lib.moe_align(p(16), 4, 2, 8, 16, None, p(16), p(16), None) == -1
+    assert lib.moe_align(p(16), 4, 2, 8, 16, p(16), p(16), p(18), None) == -1   # misaligned
+    # finalize: eps <= 0, H % 16, null y
+    assert lib.moe_finalize(p(16), p(16), p(16), p(16), 0.0, 4, 256, 2, p(16), None, None) == -1
+    assert lib.moe_finalize(p(16), p(16), p(16), p(16), 1e-5, 4, 250, 2, p(16), None, None) == -1
+    assert lib.moe_finalize(None, p(16), p(16), p(16), 1e-5, 4, 256, 2, p(16), None, None) == -1
+    # expert GEMMs: capacity too small, unsupported block
+    assert lib.moe_expert_up(p(16), p(16), p(16), p(16), p(16), 4, 256, 8, 512, 2, 16, 16, p(16), None) == -1
+    assert lib.moe_expert_up(p(16), p(16), p(16), p(16), p(16), 4, 256, 8, 512, 2, 24, 240, p(16), None) == -2
+    assert lib.moe_expert_down(p(16), p(16), p(16), p(16), p(16), 4, 256, 8, 512, 2, 16, 16, p(16), None) == -1

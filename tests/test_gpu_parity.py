@@ -1,0 +1,377 @@
+"""GPU parity of the HIP path (through the C ABI) against the CPU oracle.
+
+Bar: routing ids, the plan (sorted ids, block -> expert map, num_padded) bit-exact;
+routing weights within 1e-6; bf16 layer outputs within max-abs 2e-2 and relative-L2
+1e-2 of the oracle.  Per-kernel tests use tighter bounds derived from the arithmetic.
+Every output buffer is poisoned before each run so stale values cannot pass.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+from oracle import moe_oracle as orc
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+REL_L2 = 1e-2
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def B(dev):
+    from prefill_sigmoid_router_amd import binding
+    binding.load_library()
+    return binding
+
+
+bits = mi.bf16_bits
+
+# Small layers the oracle finishes in seconds; they span several N and K tiles, ragged
+# token counts, K tails (H or I not a multiple of the 128-wide K step) and every block.
+SMALL = {
+    "tiny": mi.CONFIGS["tiny"],
+    "mid": mi.LayerConfig("mid", M=37, H=1024, E=32, top_k=4, I=256, block=16),
+    "ragged_ktail": mi.LayerConfig("ragged_ktail", M=13, H=208, E=10, top_k=3, I=192, block=32),
+    "block64_zipf": mi.LayerConfig("block64_zipf", M=50, H=512, E=16, top_k=6, I=128, block=64,
+                                   zipf_s=1.0),
+    "block128": mi.LayerConfig("block128", M=70, H=256, E=4, top_k=2, I=64, block=128),
+    "one_token": mi.LayerConfig("one_token", M=1, H=512, E=64, top_k=8, I=256, block=16),
+    "single_expert": mi.LayerConfig("single_expert", M=9, H=256, E=1, top_k=1, I=128, block=16),
+    "all_experts": mi.LayerConfig("all_experts", M=5, H=128, E=6, top_k=6, I=64, block=16),
+}
+FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048"]
+
+
+def _poisoned(shape, dtype, dev):
+    if dtype in (torch.int32,):
+        return torch.full(shape, -7, dtype=dtype, device=dev)
+    return torch.full(shape, float("nan"), dtype=dtype, device=dev)
+
+
+def _run_forward(B, L, dev, residual_out=True):
+    cfg = L["cfg"]
+    M, H, E, I, k, blk = L["M"], cfg.H, cfg.E, cfg.I, cfg.top_k, cfg.block
+    cap = B.moe_align_capacity(M, k, E, blk)
+    r = {
+        "out": _poisoned((M, H), torch.bfloat16, dev),
+        "rout": _poisoned((M, H), torch.bfloat16, dev) if residual_out else None,
+        "ids": _poisoned((M, k), torch.int32, dev),
+        "w": _poisoned((M, k), torch.float32, dev),
+        "sorted": _poisoned((cap,), torch.int32, dev),
+        "bexp": _poisoned((cap // blk,), torch.int32, dev),
+        "npad": _poisoned((1,), torch.int32, dev),
+    }
+    ws = torch.empty(B.moe_workspace_bytes(M, H, E, I, k, blk), dtype=torch.uint8, device=dev)
+    B.moe_forward(L["x"], L["router_w"], L["router_bias"], L["w13"], L["w2"], L["residual"],
+                  L["norm_w"], L["eps"], k, blk, r["out"], ws, residual_out=r["rout"],
+                  topk_ids_out=r["ids"], topk_w_out=r["w"], sorted_ids_out=r["sorted"],
+                  block_expert_out=r["bexp"], num_padded_out=r["npad"])
+    torch.cuda.synchronize()
+    return r
+
+
+def _bias_np(L):
+    return None if L["router_bias"] is None else L["router_bias"].cpu().numpy()
+
+
+def _check_close(got_bf16, ref, what):
+    g = got_bf16.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    err = np.abs(g - ref)
+    rel = np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-30)
+    assert err.max() <= MAX_ABS, f"{what}: max-abs {err.max():.4e} at {np.unravel_index(err.argmax(), err.shape)}"
+    assert rel <= REL_L2, f"{what}: rel-L2 {rel:.4e}"
+    return err.max(), rel
+
+
+def _check_plan(r, ref, blk, what):
+    n_pad = int(r["npad"].item())
+    assert n_pad == ref["num_padded"], what
+    assert np.array_equal(r["sorted"].cpu().numpy()[:n_pad], ref["sorted_ids"]), what
+    assert np.array_equal(r["bexp"].cpu().numpy()[:n_pad // blk], ref["block_expert"]), what
+
+
+# ---------------------------------------------------------------------------------------
+# Router
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name", list(SMALL) + FULL)
+def test_route_bit_exact(B, dev, name):
+    cfg = SMALL.get(name) or mi.CONFIGS[name]
+    print(f"route parity {name} M={cfg.M} E={cfg.E} k={cfg.top_k}", flush=True)
+    L = mi.make_layer(cfg, device=dev, seed=0, with_experts=False)
+    M, k = cfg.M, cfg.top_k
+    ids = _poisoned((M, k), torch.int32, dev)
+    w = _poisoned((M, k), torch.float32, dev)
+    ws = torch.empty(B.moe_route_workspace_bytes(M, cfg.E), dtype=torch.uint8, device=dev)
+    B.moe_route(L["x"], L["router_w"], L["router_bias"], k, ids, w, ws)
+    torch.cuda.synchronize()
+    ref_ids, ref_w, _ = orc.route(bits(L["x"]), bits(L["router_w"]), _bias_np(L), k)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=0, atol=1e-6)
+
+
+def test_route_exact_ties_go_to_the_lower_id(B, dev):
+    torch.manual_seed(0)
+    M, H, E, k = 40, 256, 64, 8
+    x = torch.randn(M, H, device=dev).to(torch.bfloat16)
+    wr = (torch.randn(E, H, device=dev) * 0.05).to(torch.bfloat16)
+    wr[33] = wr[5]
+    wr[60] = wr[5]
+    wr[7] = wr[2]
+    bias = torch.zeros(E, dtype=torch.float32, device=dev)
+    bias[[5, 33, 60]] = 3.0     # the tied triple always wins, in id order 5, 33, 60
+    ids = _poisoned((M, k), torch.int32, dev)
+    w = _poisoned((M, k), torch.float32, dev)
+    ws = torch.empty(B.moe_route_workspace_bytes(M, E), dtype=torch.uint8, device=dev)
+    B.moe_route(x, wr, bias, k, ids, w, ws)
+    torch.cuda.synchronize()
+    got = ids.cpu().numpy()
+    ref_ids, ref_w, _ = orc.route(bits(x), bits(wr), bias.cpu().numpy(), k)
+    assert np.array_equal(got, ref_ids)
+    for row in got.tolist():
+        i5 = row.index(5)
+        assert row[i5 + 1] == 33 and row[i5 + 2] == 60
+    # keys exactly equal (x = 0): bias decides, ties at the cut go to the lower id
+    xz = torch.zeros(1, H, dtype=torch.bfloat16, device=dev)
+    b2 = torch.tensor([0.5, 1.0, 0.5, 1.0, 0.25] + [-1.0] * (E - 5), dtype=torch.float32, device=dev)
+    ids1 = _poisoned((1, 3), torch.int32, dev)
+    w1 = _poisoned((1, 3), torch.float32, dev)
+    B.moe_route(xz, wr, b2, 3, ids1, w1, ws)
+    torch.cuda.synchronize()
+    assert ids1.cpu().tolist() == [[1, 3, 0]]
+
+
+# ---------------------------------------------------------------------------------------
+# Align
+# ---------------------------------------------------------------------------------------
+def _align_cases():
+    rng = np.random.default_rng(7)
+    cases = []
+    for (M, k, E, blk) in [(4, 2, 8, 16), (8, 16, 256, 16), (128, 16, 256, 64), (37, 4, 32, 16),
+                           (2048, 16, 256, 64), (512, 16, 256, 64), (33, 3, 5, 1), (700, 8, 1024, 128),
+                           (1, 1, 1, 16), (100, 7, 64, 3)]:
+        ids = np.stack([rng.permutation(E)[:k] for _ in range(M)])
+        cases.append((f"rand_{M}x{k}_E{E}_B{blk}", ids, E, blk))
+    E = 64
+    cases.append(("one_expert", np.full((300, 4), 9), E, 16))
+    cases.append(("out_of_range", rng.integers(-5, E + 5, size=(200, 8)), E, 16))
+    z = np.minimum(rng.zipf(1.2, size=(1024, 16)) - 1, 255)
+    cases.append(("zipf_dupes", z, 256, 64))
+    cases.append(("all_invalid", np.full((10, 2), 99), 8, 16))
+    return cases
+
+
+@pytest.mark.parametrize("case", _align_cases(), ids=lambda c: c[0])
+def test_align_bit_exact_and_repeatable(B, dev, case):
+    name, ids_np, E, blk = case
+    print(f"align parity {name}", flush=True)
+    M, k = ids_np.shape
+    ids = torch.from_numpy(ids_np.astype(np.int32)).to(dev)
+    cap = B.moe_align_capacity(M, k, E, blk)
+    ref_sorted, ref_bexp, ref_np, _, _ = orc.align(ids_np, E, blk)
+    for rep in range(20):       # repeated runs: a missing barrier shows up as a changing plan
+        s = _poisoned((cap,), torch.int32, dev)
+        b = _poisoned((max(cap // blk, 1),), torch.int32, dev)
+        npd = _poisoned((1,), torch.int32, dev)
+        B.moe_align(ids, E, blk, s, b, npd)
+        torch.cuda.synchronize()
+        n_pad = int(npd.item())
+        assert n_pad == ref_np, (name, rep)
+        assert np.array_equal(s.cpu().numpy()[:n_pad], ref_sorted), (name, rep)
+        assert np.array_equal(b.cpu().numpy()[:n_pad // blk], ref_bexp), (name, rep)
+
+
+# ---------------------------------------------------------------------------------------
+# Expert GEMMs and finalize, one kernel at a time
+# ---------------------------------------------------------------------------------------
+def _plan_on_gpu(B, L, dev):
+    cfg = L["cfg"]
+    M, E, k, blk = L["M"], cfg.E, cfg.top_k, cfg.block
+    ids = _poisoned((M, k), torch.int32, dev)
+    w = _poisoned((M, k), torch.float32, dev)
+    ws = torch.empty(B.moe_route_workspace_bytes(M, E), dtype=torch.uint8, device=dev)
+    B.moe_route(L["x"], L["router_w"], L["router_bias"], k, ids, w, ws)
+    cap = B.moe_align_capacity(M, k, E, blk)
+    s = _poisoned((cap,), torch.int32, dev)
+    b = _poisoned((cap // blk,), torch.int32, dev)
+    npd = _poisoned((1,), torch.int32, dev)
+    B.moe_align(ids, E, blk, s, b, npd)
+    torch.cuda.synchronize()
+    return ids, w, s, b, npd
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "ragged_ktail", "block64_zipf", "block128"])
+def test_expert_up_swiglu(B, dev, name):
+    cfg = SMALL[name]
+    print(f"expert_up parity {name}", flush=True)
+    L = mi.make_layer(cfg, device=dev, seed=1)
+    ids, w, s, b, npd = _plan_on_gpu(B, L, dev)
+    cap = s.numel()
+    act = _poisoned((cap, cfg.I), torch.bfloat16, dev)
+    B.moe_expert_up(L["x"], L["w13"], s, b, npd, cfg.top_k, cfg.block, act)
+    torch.cuda.synchronize()
+    n_pad = int(npd.item())
+    plan = s.cpu().numpy()[:n_pad]
+    bexp = b.cpu().numpy()[:n_pad // cfg.block]
+    a = act.float().cpu().numpy().astype(np.float64)
+    x64 = orc.bf16_to_f64(bits(L["x"]))
+    w13 = bits(L["w13"])
+    sentinel = L["M"] * cfg.top_k
+    for blk_i, e in enumerate(bexp):
+        rows = np.arange(blk_i * cfg.block, (blk_i + 1) * cfg.block)
+        live = rows[plan[rows] < sentinel]
+        if live.size == 0:
+            continue
+        ref = orc.expert_swiglu(x64[plan[live] // cfg.top_k], w13[e], cfg.I)
+        got = a[live]
+        # act is rounded to bf16 (relative half-ulp 2^-9); fp32 accumulation adds far less
+        tol = 2.0 ** -8 * np.abs(ref) + 1e-3 * (np.abs(ref).max() + 1e-30)
+        assert np.all(np.abs(got - ref) <= tol), (name, blk_i, e, np.abs(got - ref).max())
+        # sentinel rows inside a computed 16-row group are written as zeros
+        grp_end = min((blk_i + 1) * cfg.block, blk_i * cfg.block + ((live.size + 15) // 16) * 16)
+        pad_rows = np.arange(blk_i * cfg.block + live.size, grp_end)
+        assert np.all(a[pad_rows] == 0.0), (name, blk_i)
+
+
+@pytest.mark.parametrize("name", ["tiny", "mid", "ragged_ktail", "block64_zipf", "block128"])
+def test_expert_down(B, dev, name):
+    cfg = SMALL[name]
+    print(f"expert_down parity {name}", flush=True)
+    L = mi.make_layer(cfg, device=dev, seed=2)
+    ids, w, s, b, npd = _plan_on_gpu(B, L, dev)
+    cap = s.numel()
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    act = torch.randn((cap, cfg.I), generator=g, device=dev).to(torch.bfloat16)
+    M, k = L["M"], cfg.top_k
+    y = _poisoned((M * k, cfg.H), torch.float32, dev)
+    B.moe_expert_down(act, L["w2"], s, b, npd, M, k, cfg.block, y)
+    torch.cuda.synchronize()
+    n_pad = int(npd.item())
+    plan = s.cpu().numpy()[:n_pad]
+    bexp = b.cpu().numpy()[:n_pad // cfg.block]
+    a64 = orc.bf16_to_f64(bits(act))
+    w2 = bits(L["w2"])
+    got = y.cpu().numpy().astype(np.float64)
+    seen = np.zeros(M * k, dtype=bool)
+    for blk_i, e in enumerate(bexp):
+        rows = np.arange(blk_i * cfg.block, (blk_i + 1) * cfg.block)
+        live = rows[plan[rows] < M * k]
+        if live.size == 0:
+            continue
+        ref = orc.expert_down(a64[live], w2[e])
+        scale = np.abs(a64[live]) @ np.abs(orc.bf16_to_f64(w2[e])).T
+        # exact bf16 products, fp32 accumulation over I terms
+        assert np.all(np.abs(got[plan[live]] - ref) <= 2e-6 * scale + 1e-30), (name, blk_i, e)
+        seen[plan[live]] = True
+    assert seen.all()
+
+
+def test_finalize_closed_form_and_oracle(B, dev):
+    torch.manual_seed(3)
+    M, k, H, eps = 19, 5, 7168, 1e-5
+    y = torch.randn(M * k, H, device=dev)
+    wt = torch.rand(M, k, device=dev)
+    wt = wt / wt.sum(dim=1, keepdim=True)
+    res = torch.randn(M, H, device=dev).to(torch.bfloat16)
+    g = (1 + 0.05 * torch.randn(H, device=dev)).to(torch.bfloat16)
+    out = _poisoned((M, H), torch.bfloat16, dev)
+    rout = _poisoned((M, H), torch.bfloat16, dev)
+    B.moe_finalize(y, wt, res, g, eps, out, rout)
+    torch.cuda.synchronize()
+    ref, z = orc.finalize(y.cpu().numpy().astype(np.float64), wt.cpu().numpy().astype(np.float64),
+                          bits(res), bits(g), eps)
+    _check_close(out, ref, "finalize out")
+    _check_close(rout, z, "finalize residual_out")
+    # constant vector: z = 2 everywhere, g = 1 -> out = 2 / sqrt(4 + eps) -> bf16
+    y0 = torch.zeros(2 * 1, 256, device=dev)
+    w0 = torch.full((1, 2), 0.5, device=dev)
+    r2 = torch.full((1, 256), 2.0, dtype=torch.bfloat16, device=dev)
+    g1 = torch.ones(256, dtype=torch.bfloat16, device=dev)
+    o1 = _poisoned((1, 256), torch.bfloat16, dev)
+    B.moe_finalize(y0, w0, r2, g1, eps, o1)
+    torch.cuda.synchronize()
+    want = torch.tensor(2.0 / math.sqrt(4.0 + eps)).to(torch.bfloat16).item()
+    assert torch.all(o1.cpu() == want)
+
+
+# ---------------------------------------------------------------------------------------
+# Whole layer
+# ---------------------------------------------------------------------------------------
+@pytest.mark.parametrize("name", list(SMALL))
+def test_forward_small(B, dev, name):
+    cfg = SMALL[name]
+    print(f"forward parity {name}", flush=True)
+    L = mi.make_layer(cfg, device=dev, seed=3)
+    r = _run_forward(B, L, dev)
+    ref = orc.forward(bits(L["x"]), bits(L["router_w"]), _bias_np(L), bits(L["w13"]), bits(L["w2"]),
+                      bits(L["residual"]), bits(L["norm_w"]), L["eps"], cfg.top_k, cfg.block)
+    assert np.array_equal(r["ids"].cpu().numpy(), ref["topk_ids"])
+    np.testing.assert_allclose(r["w"].cpu().numpy(), ref["topk_w"], rtol=0, atol=1e-6)
+    _check_plan(r, ref, cfg.block, name)
+    _check_close(r["out"], ref["out"], name)
+    _check_close(r["rout"], ref["residual_out"], name + " residual_out")
+
+
+def test_forward_zero_tokens(B, dev):
+    cfg = SMALL["mid"]
+    L = mi.make_layer(cfg, device=dev, seed=0, M=0)
+    out = torch.empty((0, cfg.H), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(16, dtype=torch.uint8, device=dev)
+    B.moe_forward(L["x"], L["router_w"], None, L["w13"], L["w2"], L["residual"], L["norm_w"],
+                  L["eps"], cfg.top_k, cfg.block, out, ws)
+
+
+@pytest.fixture(scope="module")
+def full_weights(dev):
+    cfg = mi.CONFIGS["decode_m8"]
+    print("generating full-size expert weights", flush=True)
+    L = mi.make_layer(cfg, device=dev, seed=0)
+    torch.cuda.synchronize()
+    return {"w13": L["w13"], "w2": L["w2"], "router_w": L["router_w"], "norm_w": L["norm_w"]}
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_forward_full_size(B, dev, full_weights, name):
+    cfg = mi.CONFIGS[name]
+    print(f"forward full-size parity {name} M={cfg.M}", flush=True)
+    L = mi.make_layer(cfg, device=dev, seed=0, with_experts=False)
+    L.update(full_weights)
+    r = _run_forward(B, L, dev)
+    M, k = cfg.M, cfg.top_k
+    # routing and plan over every token, bit-exact
+    ref_ids, ref_w, _ = orc.route(bits(L["x"]), bits(L["router_w"]), _bias_np(L), k)
+    assert np.array_equal(r["ids"].cpu().numpy(), ref_ids)
+    np.testing.assert_allclose(r["w"].cpu().numpy(), ref_w, rtol=0, atol=1e-6)
+    sorted_ids, bexp, n_pad, counts, _ = orc.align(ref_ids, cfg.E, cfg.block)
+    _check_plan(r, {"sorted_ids": sorted_ids, "block_expert": bexp, "num_padded": n_pad}, cfg.block, name)
+    # properties of every token: finite, and out = RMSNorm(residual_out) * g within bf16 rounding
+    out = r["out"].float().cpu().numpy().astype(np.float64)
+    z = r["rout"].float().cpu().numpy().astype(np.float64)
+    g = orc.bf16_to_f64(bits(L["norm_w"]))
+    assert np.isfinite(out).all() and np.isfinite(z).all()
+    renorm = z / np.sqrt(np.mean(z * z, axis=1, keepdims=True) + L["eps"]) * g
+    assert np.abs(out - renorm).max() <= 4e-2
+    # sampled tokens against the oracle, one by one
+    rng = np.random.default_rng(cfg.M)
+    sample = sorted(set([0, M - 1] + rng.choice(M, size=min(M, 2), replace=False).tolist()))
+    if M > 8:
+        sample = sample[:3]
+    w13 = mi.DeviceExpertsAsBits(L["w13"])
+    w2 = mi.DeviceExpertsAsBits(L["w2"])
+    ref_out, ref_z, s_ids, _ = orc.forward_tokens(sample, bits(L["x"]), bits(L["router_w"]),
+                                                  _bias_np(L), w13, w2, bits(L["residual"]),
+                                                  bits(L["norm_w"]), L["eps"], k)
+    assert np.array_equal(s_ids, ref_ids[sample])
+    _check_close(r["out"][sample], ref_out, f"{name} sampled out")
+    _check_close(r["rout"][sample], ref_z, f"{name} sampled residual_out")

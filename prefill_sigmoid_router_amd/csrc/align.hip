@@ -19,6 +19,9 @@
 //      cursor + rank; the highest lane of each group advances the cursor;
 //   4. padding slots get the sentinel n; block b takes the expert found by a binary
 //      search of b * block in the prefix.
+// Optionally (for the grouped GEMMs of moe_forward) the kernel also lists the row tiles
+// of height T that hold real entries: tile = {first plan row, real rows in it}, tiles
+// never straddle two experts, listed expert by expert.
 #include "device_common.h"
 #include "launchers.h"
 
@@ -28,10 +31,31 @@ constexpr int kAlignWaves = 16;
 constexpr int kAlignThreads = kAlignWaves * kWave;
 constexpr int kAlignMaxE = 1024;
 
+__device__ __forceinline__ int block_exclusive_scan(int v, int* wave_total, int lane, int wave,
+                                                    int* total_out) {
+  int incl = v;
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int o = __shfl_up(incl, d, kWave);
+    if (lane >= d) incl += o;
+  }
+  if (lane == kWave - 1) wave_total[wave] = incl;
+  __syncthreads();
+  int base = 0, all = 0;
+  for (int w = 0; w < kAlignWaves; ++w) {
+    const int t = wave_total[w];
+    if (w < wave) base += t;
+    all += t;
+  }
+  *total_out = all;
+  return base + incl - v;
+}
+
 __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     const int32_t* __restrict__ ids, int n, int E, int block, int id_bits,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
-    int32_t* __restrict__ num_padded) {
+    int32_t* __restrict__ num_padded, int tile_rows, int2* __restrict__ tiles,
+    int32_t* __restrict__ num_tiles) {
   __shared__ int32_t cnt[kAlignWaves][kAlignMaxE];  // count, then cursor, per (wave, expert)
   __shared__ int32_t prefix[kAlignMaxE + 1];
   __shared__ int32_t wave_total[kAlignWaves];
@@ -59,17 +83,8 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     for (int w = 0; w < kAlignWaves; ++w) total += cnt[w][tid];
     padded = (total + block - 1) / block * block;
   }
-  int incl = padded;
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int o = __shfl_up(incl, d, kWave);
-    if (lane >= d) incl += o;
-  }
-  if (lane == kWave - 1) wave_total[wave] = incl;
-  __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += wave_total[w];
-  const int excl = base + incl - padded;
+  int all_padded;
+  const int excl = block_exclusive_scan(padded, wave_total, lane, wave, &all_padded);
   if (tid < E) {
     prefix[tid] = excl;
     int run = excl;
@@ -80,10 +95,10 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
       run += c;
     }
     for (int r = excl + total; r < excl + padded; ++r) sorted_ids[r] = n;  // sentinel
-    if (tid == E - 1) {
-      prefix[E] = excl + padded;
-      *num_padded = excl + padded;
-    }
+  }
+  if (tid == 0) {
+    prefix[E] = all_padded;
+    *num_padded = all_padded;
   }
   __syncthreads();  // prefix[] and the cursors are complete before they are read
 
@@ -118,14 +133,30 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     }
     block_expert[b] = l;
   }
+
+  // 5. optional list of row tiles holding real entries
+  if (tiles != nullptr) {
+    const int ntile_e = (tid < E) ? (total + tile_rows - 1) / tile_rows : 0;
+    __syncthreads();  // wave_total is reused by the scan
+    int all_tiles;
+    const int first = block_exclusive_scan(ntile_e, wave_total, lane, wave, &all_tiles);
+    if (tid < E) {
+      for (int j = 0; j < ntile_e; ++j) {
+        const int left = total - j * tile_rows;
+        tiles[first + j] = make_int2(excl + j * tile_rows, left < tile_rows ? left : tile_rows);
+      }
+    }
+    if (tid == 0) *num_tiles = all_tiles;
+  }
 }
 
 hipError_t launch_align(const int32_t* ids, int n, int E, int block, int32_t* sorted_ids,
-                        int32_t* block_expert, int32_t* num_padded, hipStream_t s) {
+                        int32_t* block_expert, int32_t* num_padded, int tile_rows, int2* tiles,
+                        int32_t* num_tiles, hipStream_t s) {
   int id_bits = 0;
   while ((1 << id_bits) < E) ++id_bits;
   hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, s, ids, n, E, block, id_bits,
-                     sorted_ids, block_expert, num_padded);
+                     sorted_ids, block_expert, num_padded, tile_rows, tiles, num_tiles);
   return hipGetLastError();
 }
 

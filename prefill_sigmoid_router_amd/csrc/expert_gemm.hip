@@ -1,20 +1,23 @@
-// Grouped expert GEMMs of the routed-MoE layer over the align plan.
+// Grouped expert GEMMs of the routed-MoE layer over the align plan: weight-streaming
+// kernels for 16-row token tiles.
 //
 // AlphaMoE page (FlashInfer PR #6511 analysis), sections 1-4: the up kernel gathers the
 // token tile of an expert and streams that expert's weights, the down kernel streams
-// W2 in deep K panels; the route chain is up -> down -> finalize.  Trainium2 megakernel
-// page, first paragraph, rule 2: split each weight stream over many programs so that
-// small-batch decode runs at memory bandwidth.
+// W2; the route chain is up -> down -> finalize.  Trainium2 megakernel page, first
+// paragraph, rule 2: split each weight stream over many programs so that small-batch
+// decode runs at memory bandwidth.
 //
-// MI355X layout: one workgroup = one plan block (block rows of one expert) x one N tile;
-// every wave owns 16-row weight tiles and streams them straight from HBM into MFMA
-// A-fragments (v_mfma_f32_16x16x32_bf16).  The token rows are the B operand, gathered by
-// plan row.  Each lane reads 16*P contiguous bytes of its weight row per K step: inside
-// one K step of 32*P values, lane group g = lane/16 covers [g*8P, (g+1)*8P) and MFMA p
-// takes values g*8P + 8p .. +8 -- a permutation of K applied identically to A and B,
-// so the sum is unchanged while every weight row is read in 64-byte runs.  Only the
-// 16-row groups of a block that hold at least one real entry are computed; the weight
-// fragments of a K step are loaded once and reused by every such group.
+// MI355X layout.  One workgroup = one 16-row tile of plan rows (one expert) x 16 output
+// columns (up: 16 gate + 16 up weight rows; down: 32 columns, two 16-row halves).  Its
+// 4 waves split the weight rows and the two halves of K; the partial sums meet through
+// LDS at the end, so every wave holds a single 16-row weight stream.  Every wave streams
+// its 16 weight rows straight from HBM into the A operand of v_mfma_f32_16x16x32_bf16 in
+// the instruction's natural layout -- lane l reads 16 bytes of row l%16 at K offset
+// 8*(l/16), so one load instruction covers 16 rows x 64 contiguous bytes -- with U = 4
+// K steps of 32 per batch and the next batch in flight while the MFMAs of this one run.
+// Token rows (x for up, act for down) are the B operand, gathered by plan row; rows past
+// the tile's real entries read as zero.  A K tail that is not a whole step is read with
+// per-lane predicates.
 //
 // D fragment of lane l: weight rows 4*(l/16)+q (q = 0..3) for token column l%16, so a
 // lane writes 4 consecutive outputs of one token row (8 bytes of act, 16 bytes of y).
@@ -23,229 +26,171 @@
 
 namespace moe {
 
-template <int NS, int NT, int P>
-__global__ __launch_bounds__(256) void expert_up_kernel(
+constexpr int kStreamU = 4;  // K steps of 32 per streamed batch
+
+// acc[j] += W_j(16 rows) . B(16 rows)^T over len K values.  wr[j] / br point at this
+// lane's first element (row start + K offset + 8 * (lane / 16)); br_live is false for
+// lanes whose B row is not a real entry (read as zero).
+template <int NW, int U>
+__device__ __forceinline__ void stream_k(const uint16_t* const (&wr)[NW], const uint16_t* br,
+                                         bool br_live, int len, int lg, f32x4 (&acc)[NW]) {
+  const u32x4 z4 = u32x4{0, 0, 0, 0};
+  const int full = len / (32 * U);
+  u32x4 wa[2][NW][U], xa[2][U];
+  if (full > 0) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+#pragma unroll
+      for (int j = 0; j < NW; ++j) wa[0][j][u] = ld16(wr[j] + 32 * u);
+      xa[0][u] = br_live ? ld16(br + 32 * u) : z4;
+    }
+  }
+  for (int m = 0; m < full; m += 2) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int mm = m + h;
+      if (mm < full) {
+        if (mm + 1 < full) {
+          const int kn = (mm + 1) * 32 * U;
+#pragma unroll
+          for (int u = 0; u < U; ++u) {
+#pragma unroll
+            for (int j = 0; j < NW; ++j) wa[h ^ 1][j][u] = ld16(wr[j] + kn + 32 * u);
+            xa[h ^ 1][u] = br_live ? ld16(br + kn + 32 * u) : z4;
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int j = 0; j < NW; ++j) acc[j] = mfma16x16x32(wa[h][j][u], xa[h][u], acc[j]);
+      }
+    }
+  }
+  for (int k = full * 32 * U; k < len; k += 32) {  // tail, 32 at a time
+    const bool in = k + 8 * lg + 8 <= len;
+    const u32x4 xb = (in && br_live) ? ld16(br + k) : z4;
+#pragma unroll
+    for (int j = 0; j < NW; ++j) {
+      const u32x4 wv = in ? ld16(wr[j] + k) : z4;
+      acc[j] = mfma16x16x32(wv, xb, acc[j]);
+    }
+  }
+}
+
+// Work item of a workgroup: a 16-row plan tile.  From the tile list when given, else the
+// blockIdx.y-th 16 rows of the plan (skipped when past the plan or without real rows).
+__device__ __forceinline__ bool tile_of(const int2* tiles, const int32_t* num_tiles,
+                                        const int32_t* sorted_ids, const int32_t* num_padded,
+                                        int sentinel, int& start, int& nlive) {
+  const int y = blockIdx.y;
+  if (tiles != nullptr) {
+    if (y >= *num_tiles) return false;
+    const int2 t = tiles[y];
+    start = t.x;
+    nlive = t.y;
+    return true;
+  }
+  start = y * 16;
+  if (start >= *num_padded) return false;
+  // real entries precede the sentinel padding inside an expert's run
+  const int lane = threadIdx.x & 63;
+  const bool live = lane < 16 && sorted_ids[start + lane] < sentinel;
+  nlive = __popcll(__ballot(live));
+  return nlive > 0;
+}
+
+// Up + SwiGLU: the four waves are {gate rows, up rows} x {low K half, high K half} of 16
+// act columns; the three partial sums meet wave 0 through LDS, which applies
+// silu(gate) * up and writes the bf16 act row fragment.
+template <int U>
+__global__ __launch_bounds__(256) void expert_up_stream_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ w13,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
-    const int32_t* __restrict__ num_padded, int H, int I, int top_k, int block, int sentinel,
+    const int32_t* __restrict__ num_padded, const int2* __restrict__ tiles,
+    const int32_t* __restrict__ num_tiles, int H, int I, int top_k, int block, int sentinel,
     uint16_t* __restrict__ act) {
-  const int b = blockIdx.y;
-  if (b * block >= *num_padded) return;  // workgroup-uniform
-  const int e = block_expert[b];
+  __shared__ f32x4 red[3][kWave];
+  int start, nlive;
+  if (!tile_of(tiles, num_tiles, sorted_ids, num_padded, sentinel, start, nlive)) return;
+  const int e = block_expert[start / block];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 15, lg = lane >> 4;
-
-  int tok[NS];
-  bool live[NS], active[NS];
+  const int gu = wave & 1, wk = wave >> 1;
+  const bool live = li < nlive;
+  const int tok = live ? sorted_ids[start + li] / top_k : 0;
+  const int n0 = blockIdx.x * 16;
+  const int khalf = H >> 1;
+  const int kb = wk * khalf + 8 * lg;
+  const uint16_t* wr[1] = {w13 + (size_t)e * 2 * I * H + (size_t)(gu * I + n0 + li) * H + kb};
+  f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+  stream_k<1, U>(wr, x + (size_t)tok * H + kb, live, khalf, lg, acc);
+  if (wave != 0) red[wave - 1][lane] = acc[0];   // wave 1: up low-K, 2: gate high-K, 3: up high-K
+  __syncthreads();
+  if (wave != 0) return;
+  const f32x4 g = acc[0] + red[1][lane];
+  const f32x4 u = red[0][lane] + red[2][lane];
+  float a[4];
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const int v = sorted_ids[b * block + 16 * s + li];
-    live[s] = v < sentinel;
-    tok[s] = live[s] ? v / top_k : 0;
-    active[s] = __ballot(live[s]) != 0ull;
-  }
-
-  const int nbase = blockIdx.x * (64 * NT) + wave * (16 * NT);
-  const uint16_t* wexp = w13 + (size_t)e * 2 * I * H;
-  const uint16_t* wg_row[NT];
-  const uint16_t* wu_row[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    const int n = nbase + 16 * nt + li;
-    wg_row[nt] = wexp + (size_t)n * H;
-    wu_row[nt] = wexp + (size_t)(I + n) * H;
-  }
-
-  f32x4 accg[NT][NS], accu[NT][NS];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int s = 0; s < NS; ++s) {
-      accg[nt][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-      accu[nt][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-
-  for (int k0 = 0; k0 < H; k0 += 32 * P) {
-    const int kl = k0 + lg * 8 * P;
-    u32x4 wg[NT][P], wu[NT][P], xf[NS][P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      const int kk = kl + 8 * p;
-      const bool in = kk < H;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        wg[nt][p] = in ? ld16(wg_row[nt] + kk) : u32x4{0, 0, 0, 0};
-        wu[nt][p] = in ? ld16(wu_row[nt] + kk) : u32x4{0, 0, 0, 0};
-      }
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-        xf[s][p] = (active[s] && live[s] && in) ? ld16(x + (size_t)tok[s] * H + kk)
-                                                : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int p = 0; p < P; ++p)
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        if (!active[s]) continue;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) {
-          accg[nt][s] = mfma16x16x32(wg[nt][p], xf[s][p], accg[nt][s]);
-          accu[nt][s] = mfma16x16x32(wu[nt][p], xf[s][p], accu[nt][s]);
-        }
-      }
-  }
-
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    if (!active[s]) continue;
-    const size_t r = (size_t)b * block + 16 * s + li;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      const int n = nbase + 16 * nt + 4 * lg;
-      float a[4];
-#pragma unroll
-      for (int q = 0; q < 4; ++q) a[q] = silu_f32(accg[nt][s][q]) * accu[nt][s][q];
-      uint2 v;
-      v.x = pack_bf16x2(a[0], a[1]);
-      v.y = pack_bf16x2(a[2], a[3]);
-      *reinterpret_cast<uint2*>(act + r * I + n) = v;
-    }
-  }
+  for (int q = 0; q < 4; ++q) a[q] = silu_f32(g[q]) * u[q];
+  uint2 v;
+  v.x = pack_bf16x2(a[0], a[1]);
+  v.y = pack_bf16x2(a[2], a[3]);
+  *reinterpret_cast<uint2*>(act + (size_t)(start + li) * I + n0 + 4 * lg) = v;
 }
 
-template <int NS, int NT, int P>
-__global__ __launch_bounds__(256) void expert_down_kernel(
+template <int U>
+__global__ __launch_bounds__(256) void expert_down_stream_kernel(
     const uint16_t* __restrict__ act, const uint16_t* __restrict__ w2,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
-    const int32_t* __restrict__ num_padded, int H, int I, int block, int sentinel,
+    const int32_t* __restrict__ num_padded, const int2* __restrict__ tiles,
+    const int32_t* __restrict__ num_tiles, int H, int I, int block, int sentinel,
     float* __restrict__ y) {
-  const int b = blockIdx.y;
-  if (b * block >= *num_padded) return;  // workgroup-uniform
-  const int e = block_expert[b];
+  __shared__ f32x4 red[2][kWave];
+  int start, nlive;
+  if (!tile_of(tiles, num_tiles, sorted_ids, num_padded, sentinel, start, nlive)) return;
+  const int e = block_expert[start / block];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 15, lg = lane >> 4;
+  const int wn = wave & 1, wk = wave >> 1;
 
-  int dst[NS];
-  bool live[NS], active[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const int v = sorted_ids[b * block + 16 * s + li];
-    live[s] = v < sentinel;
-    dst[s] = v;
-    active[s] = __ballot(live[s]) != 0ull;
-  }
+  const bool live = li < nlive;
+  const int n0 = blockIdx.x * 32 + wn * 16;
+  const bool n_in = n0 < H;  // H is a multiple of 16: a wave's 16 columns are all in or all out
+  const int khalf = I >> 1;
+  const int kb = wk * khalf + 8 * lg;
+  const uint16_t* wr[1] = {w2 + (size_t)e * H * I + (size_t)(n_in ? n0 + li : 0) * I + kb};
+  f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
+  if (n_in) stream_k<1, U>(wr, act + (size_t)(start + li) * I + kb, live, khalf, lg, acc);
 
-  const int nbase = blockIdx.x * (64 * NT) + wave * (16 * NT);
-  if (nbase >= H) return;  // wave-uniform (H is a multiple of 16); no barriers below
-  const uint16_t* wexp = w2 + (size_t)e * H * I;
-  const uint16_t* w_row[NT];
-  bool nt_in[NT];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt) {
-    nt_in[nt] = nbase + 16 * nt < H;
-    w_row[nt] = wexp + (size_t)(nt_in[nt] ? nbase + 16 * nt + li : 0) * I;
-  }
-  const uint16_t* a_row[NS];
-#pragma unroll
-  for (int s = 0; s < NS; ++s) a_row[s] = act + ((size_t)b * block + 16 * s + li) * I;
-
-  f32x4 acc[NT][NS];
-#pragma unroll
-  for (int nt = 0; nt < NT; ++nt)
-#pragma unroll
-    for (int s = 0; s < NS; ++s) acc[nt][s] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int k0 = 0; k0 < I; k0 += 32 * P) {
-    const int kl = k0 + lg * 8 * P;
-    u32x4 wf[NT][P], af[NS][P];
-#pragma unroll
-    for (int p = 0; p < P; ++p) {
-      const int kk = kl + 8 * p;
-      const bool in = kk < I;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        wf[nt][p] = (in && nt_in[nt]) ? ld16(w_row[nt] + kk) : u32x4{0, 0, 0, 0};
-#pragma unroll
-      for (int s = 0; s < NS; ++s)
-        af[s][p] = (active[s] && in) ? ld16(a_row[s] + kk) : u32x4{0, 0, 0, 0};
-    }
-#pragma unroll
-    for (int p = 0; p < P; ++p)
-#pragma unroll
-      for (int s = 0; s < NS; ++s) {
-        if (!active[s]) continue;
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt) acc[nt][s] = mfma16x16x32(wf[nt][p], af[s][p], acc[nt][s]);
-      }
-  }
-
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    if (!live[s]) continue;
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) {
-      if (!nt_in[nt]) continue;
-      const int n = nbase + 16 * nt + 4 * lg;
-      float4 v;
-      v.x = acc[nt][s][0];
-      v.y = acc[nt][s][1];
-      v.z = acc[nt][s][2];
-      v.w = acc[nt][s][3];
-      *reinterpret_cast<float4*>(y + (size_t)dst[s] * H + n) = v;
-    }
-  }
-}
-
-template <int NS>
-static hipError_t up_for_block(const uint16_t* x, const uint16_t* w13, const int32_t* sorted_ids,
-                               const int32_t* block_expert, const int32_t* num_padded, int M,
-                               int H, int I, int top_k, int block, int capacity, uint16_t* act,
-                               hipStream_t s) {
-  constexpr int NT = 1, P = NS <= 2 ? 4 : (NS == 4 ? 2 : 1);
-  dim3 grid(I / (64 * NT), capacity / block);
-  hipLaunchKernelGGL((expert_up_kernel<NS, NT, P>), grid, dim3(256), 0, s, x, w13, sorted_ids,
-                     block_expert, num_padded, H, I, top_k, block, M * top_k, act);
-  return hipGetLastError();
-}
-
-template <int NS>
-static hipError_t down_for_block(const uint16_t* act, const uint16_t* w2,
-                                 const int32_t* sorted_ids, const int32_t* block_expert,
-                                 const int32_t* num_padded, int M, int H, int I, int top_k,
-                                 int block, int capacity, float* y, hipStream_t s) {
-  constexpr int NT = 2, P = NS <= 2 ? 4 : (NS == 4 ? 2 : 1);
-  dim3 grid((H + 64 * NT - 1) / (64 * NT), capacity / block);
-  hipLaunchKernelGGL((expert_down_kernel<NS, NT, P>), grid, dim3(256), 0, s, act, w2, sorted_ids,
-                     block_expert, num_padded, H, I, block, M * top_k, y);
-  return hipGetLastError();
+  if (wk == 1) red[wn][lane] = acc[0];
+  __syncthreads();
+  if (wk == 1 || !n_in || !live) return;
+  acc[0] += red[wn][lane];
+  const int dst = sorted_ids[start + li];
+  *reinterpret_cast<float4*>(y + (size_t)dst * H + n0 + 4 * lg) =
+      make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
 }
 
 hipError_t launch_expert_up(const uint16_t* x, const uint16_t* w13, const int32_t* sorted_ids,
-                            const int32_t* block_expert, const int32_t* num_padded, int M, int H,
-                            int E, int I, int top_k, int block, int capacity, uint16_t* act,
-                            hipStream_t s) {
-  (void)E;
-  switch (block) {
-    case 16: return up_for_block<1>(x, w13, sorted_ids, block_expert, num_padded, M, H, I, top_k, block, capacity, act, s);
-    case 32: return up_for_block<2>(x, w13, sorted_ids, block_expert, num_padded, M, H, I, top_k, block, capacity, act, s);
-    case 64: return up_for_block<4>(x, w13, sorted_ids, block_expert, num_padded, M, H, I, top_k, block, capacity, act, s);
-    case 128: return up_for_block<8>(x, w13, sorted_ids, block_expert, num_padded, M, H, I, top_k, block, capacity, act, s);
-    default: return hipErrorInvalidValue;
-  }
+                            const int32_t* block_expert, const int32_t* num_padded,
+                            const int2* tiles, const int32_t* num_tiles, int max_tiles, int M,
+                            int H, int I, int top_k, int block, uint16_t* act, hipStream_t s) {
+  dim3 grid(I / 16, max_tiles);
+  hipLaunchKernelGGL((expert_up_stream_kernel<kStreamU>), grid, dim3(256), 0, s, x, w13, sorted_ids,
+                     block_expert, num_padded, tiles, num_tiles, H, I, top_k, block, M * top_k,
+                     act);
+  return hipGetLastError();
 }
 
 hipError_t launch_expert_down(const uint16_t* act, const uint16_t* w2, const int32_t* sorted_ids,
-                              const int32_t* block_expert, const int32_t* num_padded, int M,
-                              int H, int E, int I, int top_k, int block, int capacity, float* y,
-                              hipStream_t s) {
-  (void)E;
-  switch (block) {
-    case 16: return down_for_block<1>(act, w2, sorted_ids, block_expert, num_padded, M, H, I, top_k, block, capacity, y, s);
-    case 32: return down_for_block<2>(act, w2, sorted_ids, block_expert, num_padded, M, H, I, top_k, block, capacity, y, s);
-    case 64: return down_for_block<4>(act, w2, sorted_ids, block_expert, num_padded, M, H, I, top_k, block, capacity, y, s);
-    case 128: return down_for_block<8>(act, w2, sorted_ids, block_expert, num_padded, M, H, I, top_k, block, capacity, y, s);
-    default: return hipErrorInvalidValue;
-  }
+                              const int32_t* block_expert, const int32_t* num_padded,
+                              const int2* tiles, const int32_t* num_tiles, int max_tiles, int M,
+                              int H, int I, int top_k, int block, float* y, hipStream_t s) {
+  dim3 grid((H + 31) / 32, max_tiles);
+  hipLaunchKernelGGL((expert_down_stream_kernel<kStreamU>), grid, dim3(256), 0, s, act, w2,
+                     sorted_ids, block_expert, num_padded, tiles, num_tiles, H, I, block,
+                     M * top_k, y);
+  return hipGetLastError();
 }
 
 }  // namespace moe

@@ -8,23 +8,25 @@
 // dim, eps inside the square root.  sglang PR #29509 analysis, "why it's good" 1:
 // RMSNorm is memory-bound, so it is fused with its producer's consumer here.
 //
-// One workgroup per token; each thread owns V groups of 4 hidden values, so z stays in
-// registers between the sum of squares and the scaling.  All arithmetic is fp32 with a
-// single bf16 rounding (RNE) at the store.
+// One workgroup of 1024 threads per token; each thread owns V groups of 4 hidden values,
+// so z stays in registers between the sum of squares and the scaling.  The y rows of 8
+// picks are requested together (all V groups), so a token costs about k/8 memory round
+// trips rather than k.  All arithmetic is fp32 with a single bf16 rounding (RNE) at the
+// store; the combine adds the picks in ascending j.
 #include "device_common.h"
 #include "launchers.h"
 
 namespace moe {
 
+constexpr int kFinThreads = 1024;
+constexpr int kFinBatch = 8;
+
 template <int V>
-__global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__ y,
-                                                       const float* __restrict__ topk_w,
-                                                       const uint16_t* __restrict__ residual,
-                                                       const uint16_t* __restrict__ norm_w,
-                                                       float eps, int H, int top_k,
-                                                       uint16_t* __restrict__ out,
-                                                       uint16_t* __restrict__ residual_out) {
-  __shared__ float part[4];
+__global__ __launch_bounds__(kFinThreads) void finalize_kernel(
+    const float* __restrict__ y, const float* __restrict__ topk_w,
+    const uint16_t* __restrict__ residual, const uint16_t* __restrict__ norm_w, float eps, int H,
+    int top_k, uint16_t* __restrict__ out, uint16_t* __restrict__ residual_out) {
+  __shared__ float part[kFinThreads / kWave];
   const int t = blockIdx.x, tid = threadIdx.x;
   const int ngroups = H >> 2;
 
@@ -33,18 +35,29 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
   for (int v = 0; v < V; ++v) m[v] = make_float4(0.f, 0.f, 0.f, 0.f);
 
   const float* yt = y + (size_t)t * top_k * H;
-  for (int j = 0; j < top_k; ++j) {  // j ascending
-    const float w = topk_w[(size_t)t * top_k + j];
-    const float4* yr = reinterpret_cast<const float4*>(yt + (size_t)j * H);
+  const float* wt = topk_w + (size_t)t * top_k;
+  for (int j0 = 0; j0 < top_k; j0 += kFinBatch) {
+    float4 a[kFinBatch][V];
 #pragma unroll
-    for (int v = 0; v < V; ++v) {
-      const int c = tid + 256 * v;
-      if (c < ngroups) {
-        const float4 a = yr[c];
-        m[v].x = fmaf(w, a.x, m[v].x);
-        m[v].y = fmaf(w, a.y, m[v].y);
-        m[v].z = fmaf(w, a.z, m[v].z);
-        m[v].w = fmaf(w, a.w, m[v].w);
+    for (int u = 0; u < kFinBatch; ++u)
+#pragma unroll
+      for (int v = 0; v < V; ++v) {
+        const int c = tid + kFinThreads * v;
+        a[u][v] = (j0 + u < top_k && c < ngroups)
+                      ? reinterpret_cast<const float4*>(yt + (size_t)(j0 + u) * H)[c]
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+#pragma unroll
+    for (int u = 0; u < kFinBatch; ++u) {
+      if (j0 + u < top_k) {
+        const float w = wt[j0 + u];
+#pragma unroll
+        for (int v = 0; v < V; ++v) {
+          m[v].x = fmaf(w, a[u][v].x, m[v].x);
+          m[v].y = fmaf(w, a[u][v].y, m[v].y);
+          m[v].z = fmaf(w, a[u][v].z, m[v].z);
+          m[v].w = fmaf(w, a[u][v].w, m[v].w);
+        }
       }
     }
   }
@@ -53,7 +66,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
   float ss = 0.f;
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    const int c = tid + 256 * v;
+    const int c = tid + kFinThreads * v;
     if (c < ngroups) {
       const uint2 r = rr[c];
       m[v].x += bf16lo(r.x);
@@ -69,7 +82,9 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
   ss = wave_sum(ss);
   if ((tid & 63) == 0) part[tid >> 6] = ss;
   __syncthreads();
-  const float total = (part[0] + part[1]) + (part[2] + part[3]);
+  float total = 0.f;
+#pragma unroll
+  for (int w = 0; w < kFinThreads / kWave; ++w) total += part[w];
   const float inv = 1.0f / sqrtf(total / (float)H + eps);
 
   const uint2* gw = reinterpret_cast<const uint2*>(norm_w);
@@ -77,7 +92,7 @@ __global__ __launch_bounds__(256) void finalize_kernel(const float* __restrict__
   uint2* rt = residual_out ? reinterpret_cast<uint2*>(residual_out + (size_t)t * H) : nullptr;
 #pragma unroll
   for (int v = 0; v < V; ++v) {
-    const int c = tid + 256 * v;
+    const int c = tid + kFinThreads * v;
     if (c < ngroups) {
       const uint2 g = gw[c];
       uint2 o;
@@ -98,19 +113,18 @@ template <int V>
 static hipError_t launch_fin(const float* y, const float* w, const uint16_t* res, const uint16_t* g,
                              float eps, int M, int H, int k, uint16_t* out, uint16_t* rout,
                              hipStream_t s) {
-  hipLaunchKernelGGL((finalize_kernel<V>), dim3(M), dim3(256), 0, s, y, w, res, g, eps, H, k, out, rout);
+  hipLaunchKernelGGL((finalize_kernel<V>), dim3(M), dim3(kFinThreads), 0, s, y, w, res, g, eps, H, k,
+                     out, rout);
   return hipGetLastError();
 }
 
 hipError_t launch_finalize(const float* y, const float* topk_w, const uint16_t* residual,
                            const uint16_t* norm_w, float eps, int M, int H, int top_k,
                            uint16_t* out, uint16_t* residual_out, hipStream_t s) {
-  const int per_thread = (H / 4 + 255) / 256;
+  const int per_thread = (H / 4 + kFinThreads - 1) / kFinThreads;
   if (per_thread <= 1) return launch_fin<1>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
   if (per_thread <= 2) return launch_fin<2>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
-  if (per_thread <= 4) return launch_fin<4>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
-  if (per_thread <= 8) return launch_fin<8>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
-  return launch_fin<16>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
+  return launch_fin<4>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
 }
 
 }  // namespace moe

@@ -11,21 +11,30 @@ namespace moe {
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, const float* bias, int M, int H,
                         int E, int top_k, int32_t* ids, float* w, double* keys, hipStream_t s);
 
-// Expert-major plan of the flat ids [n]; sentinel = n.
+// Expert-major plan of the flat ids [n]; sentinel = n.  When `tiles` is not null the
+// kernel also lists the row tiles of height tile_rows holding real entries
+// ({first plan row, real rows}) and their count; at most tile_capacity(n, E, tile_rows).
 hipError_t launch_align(const int32_t* ids, int n, int E, int block, int32_t* sorted_ids,
-                        int32_t* block_expert, int32_t* num_padded, hipStream_t s);
+                        int32_t* block_expert, int32_t* num_padded, int tile_rows, int2* tiles,
+                        int32_t* num_tiles, hipStream_t s);
 
-// Grouped up-GEMM + SwiGLU over the plan: act [capacity, I] bf16.
+inline int tile_capacity(int n, int E, int tile_rows) {
+  return (n + tile_rows - 1) / tile_rows + (n < E ? n : E);
+}
+
+// Grouped up-GEMM + SwiGLU over the plan: act [capacity, I] bf16.  Work items are the
+// 16-row tiles of `tiles` (at most max_tiles of them), or, with tiles == nullptr, the
+// max_tiles consecutive 16-row slices of the plan.
 hipError_t launch_expert_up(const uint16_t* x, const uint16_t* w13, const int32_t* sorted_ids,
-                            const int32_t* block_expert, const int32_t* num_padded, int M, int H,
-                            int E, int I, int top_k, int block, int capacity, uint16_t* act,
-                            hipStream_t s);
+                            const int32_t* block_expert, const int32_t* num_padded,
+                            const int2* tiles, const int32_t* num_tiles, int max_tiles, int M,
+                            int H, int I, int top_k, int block, uint16_t* act, hipStream_t s);
 
-// Grouped down-GEMM over the plan: y [M*top_k, H] fp32.
+// Grouped down-GEMM over the plan: y [M*top_k, H] fp32.  Work items as for the up GEMM.
 hipError_t launch_expert_down(const uint16_t* act, const uint16_t* w2, const int32_t* sorted_ids,
-                              const int32_t* block_expert, const int32_t* num_padded, int M,
-                              int H, int E, int I, int top_k, int block, int capacity, float* y,
-                              hipStream_t s);
+                              const int32_t* block_expert, const int32_t* num_padded,
+                              const int2* tiles, const int32_t* num_tiles, int max_tiles, int M,
+                              int H, int I, int top_k, int block, float* y, hipStream_t s);
 
 // Weighted top-k combine + residual add + RMSNorm.
 hipError_t launch_finalize(const float* y, const float* topk_w, const uint16_t* residual,

@@ -38,7 +38,8 @@ size_t capacity_of(int32_t M, int32_t top_k, int32_t E, int32_t block) {
 
 // Workspace layout of moe_forward; every region starts on a 256-byte boundary.
 struct Layout {
-  size_t keys, ids, w, sorted, bexp, npad, act, y, total;
+  size_t keys, ids, w, sorted, bexp, npad, tiles, ntiles, act, y, total;
+  int max_tiles;
 };
 
 Layout layout_of(int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k, int32_t block) {
@@ -52,6 +53,9 @@ Layout layout_of(int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k, int3
   L.sorted = off; off += round_up(cap * sizeof(int32_t), kAlign);
   L.bexp = off;   off += round_up((cap / block) * sizeof(int32_t), kAlign);
   L.npad = off;   off += kAlign;
+  L.max_tiles = moe::tile_capacity((int)n, E, 16);
+  L.tiles = off;  off += round_up((size_t)L.max_tiles * sizeof(int2), kAlign);
+  L.ntiles = off; off += kAlign;
   L.act = off;    off += round_up(cap * (size_t)I * sizeof(uint16_t), kAlign);
   L.y = off;      off += round_up(n * (size_t)H * sizeof(float), kAlign);
   L.total = off;
@@ -123,7 +127,7 @@ int moe_align(const int32_t* topk_ids, int32_t M, int32_t top_k, int32_t E, int3
     return MOE_ERR_INVALID_ARG;
   if (capacity_of(M, top_k, E, block) >= ((size_t)1 << 31)) return MOE_ERR_INVALID_ARG;
   return hip_status(moe::launch_align(topk_ids, M * top_k, E, block, sorted_ids, block_expert,
-                                      num_padded, (hipStream_t)stream));
+                                      num_padded, 16, nullptr, nullptr, (hipStream_t)stream));
 }
 
 int moe_expert_up(const uint16_t* x, const uint16_t* w13, const int32_t* sorted_ids,
@@ -138,8 +142,9 @@ int moe_expert_up(const uint16_t* x, const uint16_t* w13, const int32_t* sorted_
   if (M == 0) return MOE_OK;
   if (!x || !w13 || !sorted_ids || !block_expert || !num_padded || !act) return MOE_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(w13, 16) || !aligned(act, 16)) return MOE_ERR_INVALID_ARG;
-  return hip_status(moe::launch_expert_up(x, w13, sorted_ids, block_expert, num_padded, M, H, E, I,
-                                          top_k, block, capacity, act, (hipStream_t)stream));
+  return hip_status(moe::launch_expert_up(x, w13, sorted_ids, block_expert, num_padded, nullptr,
+                                          nullptr, capacity / 16, M, H, I, top_k, block, act,
+                                          (hipStream_t)stream));
 }
 
 int moe_expert_down(const uint16_t* act, const uint16_t* w2, const int32_t* sorted_ids,
@@ -154,8 +159,9 @@ int moe_expert_down(const uint16_t* act, const uint16_t* w2, const int32_t* sort
   if (M == 0) return MOE_OK;
   if (!act || !w2 || !sorted_ids || !block_expert || !num_padded || !y) return MOE_ERR_INVALID_ARG;
   if (!aligned(act, 16) || !aligned(w2, 16) || !aligned(y, 16)) return MOE_ERR_INVALID_ARG;
-  return hip_status(moe::launch_expert_down(act, w2, sorted_ids, block_expert, num_padded, M, H, E,
-                                            I, top_k, block, capacity, y, (hipStream_t)stream));
+  return hip_status(moe::launch_expert_down(act, w2, sorted_ids, block_expert, num_padded, nullptr,
+                                            nullptr, capacity / 16, M, H, I, top_k, block, y,
+                                            (hipStream_t)stream));
 }
 
 int moe_finalize(const float* y, const float* topk_w, const uint16_t* residual,
@@ -204,6 +210,8 @@ int moe_forward(const uint16_t* x, const uint16_t* router_w, const float* router
   int32_t* sorted = sorted_ids_out ? sorted_ids_out : reinterpret_cast<int32_t*>(ws + L.sorted);
   int32_t* bexp = block_expert_out ? block_expert_out : reinterpret_cast<int32_t*>(ws + L.bexp);
   int32_t* npad = num_padded_out ? num_padded_out : reinterpret_cast<int32_t*>(ws + L.npad);
+  int2* tiles = reinterpret_cast<int2*>(ws + L.tiles);
+  int32_t* ntiles = reinterpret_cast<int32_t*>(ws + L.ntiles);
   uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
   float* y = reinterpret_cast<float*>(ws + L.y);
   hipStream_t s = (hipStream_t)stream;
@@ -215,15 +223,16 @@ int moe_forward(const uint16_t* x, const uint16_t* router_w, const float* router
   if (moe::launch_route(x, router_w, router_bias, M, H, E, top_k, ids, w, keys, s) != hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(1)) return MOE_ERR_HIP;
-  if (moe::launch_align(ids, M * top_k, E, block, sorted, bexp, npad, s) != hipSuccess)
+  if (moe::launch_align(ids, M * top_k, E, block, sorted, bexp, npad, 16, tiles, ntiles, s) !=
+      hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(2)) return MOE_ERR_HIP;
-  if (moe::launch_expert_up(x, w13, sorted, bexp, npad, M, H, E, I, top_k, block, (int)cap, act, s) !=
-      hipSuccess)
+  if (moe::launch_expert_up(x, w13, sorted, bexp, npad, tiles, ntiles, L.max_tiles, M, H, I, top_k,
+                            block, act, s) != hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(3)) return MOE_ERR_HIP;
-  if (moe::launch_expert_down(act, w2, sorted, bexp, npad, M, H, E, I, top_k, block, (int)cap, y, s) !=
-      hipSuccess)
+  if (moe::launch_expert_down(act, w2, sorted, bexp, npad, tiles, ntiles, L.max_tiles, M, H, I,
+                              top_k, block, y, s) != hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(4)) return MOE_ERR_HIP;
   if (moe::launch_finalize(y, w, residual, norm_w, eps, M, H, top_k, out, residual_out, s) !=

@@ -36,6 +36,19 @@ hipError_t launch_expert_down(const uint16_t* act, const uint16_t* w2, const int
                               const int2* tiles, const int32_t* num_tiles, int max_tiles, int M,
                               int H, int I, int top_k, int block, float* y, hipStream_t s);
 
+// LDS-tiled variants for plans whose experts carry many tokens: work items are the tiles
+// of height tile_rows (64 or 128) of `tiles`.
+hipError_t launch_expert_up_tiled(const uint16_t* x, const uint16_t* w13, const int32_t* sorted_ids,
+                                  const int32_t* block_expert, const int2* tiles,
+                                  const int32_t* num_tiles, int max_tiles, int tile_rows, int M,
+                                  int H, int I, int top_k, int block, uint16_t* act,
+                                  hipStream_t s);
+hipError_t launch_expert_down_tiled(const uint16_t* act, const uint16_t* w2,
+                                    const int32_t* sorted_ids, const int32_t* block_expert,
+                                    const int2* tiles, const int32_t* num_tiles, int max_tiles,
+                                    int tile_rows, int M, int H, int I, int top_k, int block,
+                                    float* y, hipStream_t s);
+
 // Weighted top-k combine + residual add + RMSNorm.
 hipError_t launch_finalize(const float* y, const float* topk_w, const uint16_t* residual,
                            const uint16_t* norm_w, float eps, int M, int H, int top_k,

@@ -64,6 +64,20 @@ Layout layout_of(int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k, int3
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Grouped-GEMM kernels by expected tokens per expert (M * top_k / E), the M-range
+// dispatch pattern of the FlashInfer MNNVL finalize presets: weight streaming over 16-row
+// tiles when experts see a few tokens, LDS-tiled MFMA over 64- or 128-row token tiles
+// when they see many.  Returns the tile height; 16 selects the streaming kernels.
+int gemm_tile_rows(int32_t M, int32_t E, int32_t top_k) {
+#if defined(MOE_FORCE_TILE_ROWS)
+  return MOE_FORCE_TILE_ROWS;
+#endif
+  const int64_t per_expert = (int64_t)M * top_k / E;
+  if (per_expert < 4) return 16;
+  if (per_expert < 32) return 64;
+  return 128;
+}
+
 }  // namespace
 
 extern "C" {
@@ -223,17 +237,25 @@ int moe_forward(const uint16_t* x, const uint16_t* router_w, const float* router
   if (moe::launch_route(x, router_w, router_bias, M, H, E, top_k, ids, w, keys, s) != hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(1)) return MOE_ERR_HIP;
-  if (moe::launch_align(ids, M * top_k, E, block, sorted, bexp, npad, 16, tiles, ntiles, s) !=
+  const int trows = gemm_tile_rows(M, E, top_k);
+  const int max_tiles = moe::tile_capacity(M * top_k, E, trows);
+  if (moe::launch_align(ids, M * top_k, E, block, sorted, bexp, npad, trows, tiles, ntiles, s) !=
       hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(2)) return MOE_ERR_HIP;
-  if (moe::launch_expert_up(x, w13, sorted, bexp, npad, tiles, ntiles, L.max_tiles, M, H, I, top_k,
-                            block, act, s) != hipSuccess)
-    return MOE_ERR_HIP;
+  const hipError_t up_err =
+      trows == 16 ? moe::launch_expert_up(x, w13, sorted, bexp, npad, tiles, ntiles, max_tiles, M, H,
+                                          I, top_k, block, act, s)
+                  : moe::launch_expert_up_tiled(x, w13, sorted, bexp, tiles, ntiles, max_tiles, trows,
+                                                M, H, I, top_k, block, act, s);
+  if (up_err != hipSuccess) return MOE_ERR_HIP;
   if (!mark(3)) return MOE_ERR_HIP;
-  if (moe::launch_expert_down(act, w2, sorted, bexp, npad, tiles, ntiles, L.max_tiles, M, H, I,
-                              top_k, block, y, s) != hipSuccess)
-    return MOE_ERR_HIP;
+  const hipError_t down_err =
+      trows == 16 ? moe::launch_expert_down(act, w2, sorted, bexp, npad, tiles, ntiles, max_tiles, M,
+                                            H, I, top_k, block, y, s)
+                  : moe::launch_expert_down_tiled(act, w2, sorted, bexp, tiles, ntiles, max_tiles,
+                                                  trows, M, H, I, top_k, block, y, s);
+  if (down_err != hipSuccess) return MOE_ERR_HIP;
   if (!mark(4)) return MOE_ERR_HIP;
   if (moe::launch_finalize(y, w, residual, norm_w, eps, M, H, top_k, out, residual_out, s) !=
       hipSuccess)

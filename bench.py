@@ -215,10 +215,11 @@ def main():
 
     traffic = load_traffic()
     roof = {
-        "bound": "hbm", "kernel": "expert_up_kernel (grouped up-GEMM + SwiGLU)",
+        "bound": "hbm", "kernel": "expert_up_stream_kernel (grouped up-GEMM + SwiGLU)",
         "achieved": round(res["up_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(res["up_gbs"] / HBM_PEAK_GBS, 4),
         "traffic": None if traffic is None else traffic.get("traffic_gbs"),
+        "traffic_bytes_per_launch": None if traffic is None else traffic.get("traffic_bytes_per_launch"),
         "algorithmic_bytes_per_launch": res["up_bytes"], "avg_launch_us": round(res["up_us"], 2),
     }
     cpu = None

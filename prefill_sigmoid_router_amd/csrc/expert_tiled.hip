@@ -1,22 +1,25 @@
 // Grouped expert GEMMs for plans whose experts carry many tokens (batched decode and
-// prefill): LDS-tiled MFMA kernels.
+// prefill): LDS-tiled MFMA kernels fed by direct global -> LDS copies.
 //
 // AlphaMoE page (FlashInfer PR #6511 analysis), section 4: the up kernel of the large
 // batch and prefill routes gathers a tile of tokens per expert; section 2: the down
 // kernel streams W2 in deep K panels.  Trainium2 megakernel page, first paragraph,
-// rule 1: keep the working set on chip -- the weight chunk in LDS is shared by all token
-// rows of the tile, and the M tiles of one expert run on one XCD at the same time so
-// they share the weight stream through that XCD's L2.
+// rule 1: keep the working set on chip -- the weight and token chunks in LDS are shared
+// by all waves of a workgroup, and the M tiles of one expert run on one XCD at the same
+// time so they share the weight stream through that XCD's L2.
 //
-// Workgroup tile: BM plan rows of one expert (a tile of the align kernel's list) x 128
-// weight rows (up: 64 gate + 64 up rows = 64 act columns; down: 128 output columns), K in
-// chunks of 64.  Both operands go global -> registers -> LDS in MFMA fragment order: a
-// fragment is 16 rows x 32 K values, 1 KiB, lane l holding row l%16, K values
-// 8*(l/16)..+8, so every global load instruction reads 16 rows x 64 contiguous bytes and
-// every LDS read of a fragment is one conflict-free 1 KiB ds_read_b128.  PF chunks are
-// in flight in registers while the current chunk is multiplied out of LDS (one barrier
-// per chunk).  Wave w owns weight row tiles {w, w+4} (up: the gate and up rows of the
-// same act columns) against every token row tile that holds real entries.
+// Workgroup tile: BM plan rows of one expert (a tile of the align kernel's list) x 256
+// weight rows (up: 128 gate + 128 up rows = 128 act columns; down: 256 output columns),
+// K in chunks of 64.  Both operands are copied global -> LDS with global_load_lds_dwordx4
+// in MFMA fragment order: a fragment is 16 rows x 32 K values (1 KiB), lane l copies row
+// l%16, K values 8*(l/16)..+8, and the instruction lands lane l's 16 bytes at LDS base +
+// 16 l -- so every global load reads 16 rows x 64 contiguous bytes, no registers stage
+// the data, and every fragment read is one conflict-free 1 KiB ds_read_b128.  An S-deep
+// ring keeps S-1 chunks in flight; each wave waits for its own copies of chunk c with
+// s_waitcnt vmcnt and a bare s_barrier publishes them (a fenced barrier would drain every
+// copy in flight).  Only a partial last K chunk goes through registers (zero-filled).
+// Waves form a WN x WM grid; each accumulates 4 weight tiles x BM/16/WM token tiles
+// (64 x 64 outputs for both configurations used) with v_mfma_f32_16x16x32_bf16.
 //
 // Work order: the hardware hands workgroup p to XCD p % 8.  Each XCD gets an equal,
 // contiguous share of the live (tile, N tile) items (the tile count is read on the
@@ -30,30 +33,40 @@ namespace moe {
 
 constexpr int kTileKC = 64;                     // K values per chunk
 constexpr int kTileKS = kTileKC / 32;           // MFMA K steps per chunk
-constexpr int kTileWT = 8;                      // 16-row weight tiles per workgroup
 constexpr int kXcds = 8;                        // MI355X: 8 XCDs, round-robin dispatch
-#ifndef MOE_TILE_PF
-#define MOE_TILE_PF 2
-#endif
-constexpr int kTilePF = MOE_TILE_PF;            // chunks in flight in registers
 
-template <int BM>
+// Workgroup of WN x WM waves.  Weight rows: 64 * WN (4 row tiles of 16 per wave along
+// WN); token rows: BM (BM / 16 / WM row tiles per wave along WM).  Each wave accumulates
+// 4 weight tiles x MTW token tiles.
+template <int BM, int WN, int WM>
 struct TiledCfg {
-  static constexpr int MT = BM / 16;                        // token row tiles
-  static constexpr int FRAGS = (kTileWT + MT) * kTileKS;    // fragments per chunk
-  static constexpr int FPW = FRAGS / 4;                     // fragments staged per wave
+  static constexpr int THREADS = 64 * WN * WM;
+  static constexpr int WT = 4 * WN;                          // weight row tiles per workgroup
+  static constexpr int MT = BM / 16;                         // token row tiles per workgroup
+  static constexpr int MTW = MT / WM;                        // token row tiles per wave
+  static constexpr int FRAGS = (WT + MT) * kTileKS;          // fragments per chunk
+  static constexpr int FPW = FRAGS / (WN * WM);              // fragments staged per wave
+  static_assert(FRAGS % (WN * WM) == 0, "fragments must split evenly over the waves");
+  static_assert(MT % WM == 0, "token tiles must split evenly over the waves");
 };
 
-// Fragment f of a chunk: f < kTileWT*kTileKS are weight fragments (row tile f / kTileKS,
-// K step f % kTileKS), the rest token fragments.
-template <int BM, bool UP>
-__global__ __launch_bounds__(256) void expert_tiled_kernel(
+typedef __attribute__((address_space(1))) void global_void;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Wait until at most N vector-memory operations of this wave are outstanding.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+template <int BM, int WN, int WM, int S, bool UP>
+__global__ __launch_bounds__(64 * WN * WM) void expert_tiled_kernel(
     const uint16_t* __restrict__ tok_src, const uint16_t* __restrict__ w,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
     const int2* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int n_ntiles, int K,
     int ncols, int I, int top_k, int block, uint16_t* __restrict__ act, float* __restrict__ y) {
-  using C = TiledCfg<BM>;
-  __shared__ __align__(16) unsigned char lds[2 * C::FRAGS * 1024];
+  using C = TiledCfg<BM, WN, WM>;
+  __shared__ __align__(16) unsigned char lds[S * C::FRAGS * 1024];
 
   const int ntiles_live = *num_tiles;
   const int live_items = ntiles_live * n_ntiles;
@@ -71,8 +84,11 @@ __global__ __launch_bounds__(256) void expert_tiled_kernel(
 
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 15, lg = lane >> 4;
+  const int wn = wave % WN, wm = wave / WN;
+  const int col0 = UP ? ntile * 32 * WN : ntile * 64 * WN;
 
-  // source row pointer (at K offset 8 * lg) of every fragment this wave stages
+  // source row pointer (at K offset 8 * lg) of every fragment this wave stages; rows that
+  // hold no data point at a valid row (their results are never stored)
   const uint16_t* src[C::FPW];
   bool src_on[C::FPW];
   int src_ks[C::FPW];
@@ -80,107 +96,116 @@ __global__ __launch_bounds__(256) void expert_tiled_kernel(
 #pragma unroll
   for (int i = 0; i < C::FPW; ++i) {
     const int f = wave * C::FPW + i;
-    if (f < kTileWT * kTileKS) {
+    if (f < C::WT * kTileKS) {
       const int rt = f / kTileKS;
       src_ks[i] = f % kTileKS;
       int row;
-      if (UP) row = (rt < 4) ? ntile * 64 + rt * 16 + li : I + ntile * 64 + (rt - 4) * 16 + li;
-      else row = ntile * 128 + rt * 16 + li;
+      if (UP) row = (rt < C::WT / 2) ? col0 + rt * 16 + li : I + col0 + (rt - C::WT / 2) * 16 + li;
+      else row = col0 + rt * 16 + li;
       src_on[i] = UP || row < ncols;
       src[i] = w + wexp + (size_t)(src_on[i] ? row : 0) * K + 8 * lg;
     } else {
-      const int g = f - kTileWT * kTileKS;
+      const int g = f - C::WT * kTileKS;
       const int mt = g / kTileKS;
       src_ks[i] = g % kTileKS;
       const int r = 16 * mt + li;
       src_on[i] = r < nlive;
       const int prow = start + (src_on[i] ? r : 0);
-      src[i] = UP ? tok_src + (size_t)(src_on[i] ? sorted_ids[prow] / top_k : 0) * K + 8 * lg
+      src[i] = UP ? tok_src + (size_t)(sorted_ids[prow] < 0 ? 0 : sorted_ids[prow] / top_k) * K + 8 * lg
                   : tok_src + (size_t)prow * K + 8 * lg;
+      if (UP && !src_on[i]) src[i] = tok_src + 8 * lg;
     }
   }
+  int wtile[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    wtile[j] = UP ? ((j < 2) ? 2 * wn + j : C::WT / 2 + 2 * wn + (j - 2)) : 4 * wn + j;
 
   const int nch = (K + kTileKC - 1) / kTileKC;
-  const u32x4 z4 = u32x4{0, 0, 0, 0};
-  u32x4 R[kTilePF][C::FPW];
-  auto issue = [&](int c, u32x4 (&dst)[C::FPW]) {
+  const int ndma = K / kTileKC;  // whole chunks
+  auto issue = [&](int c) {
+    unsigned char* base = lds + (size_t)(c % S) * C::FRAGS * 1024;
+    if (c < ndma) {
 #pragma unroll
-    for (int i = 0; i < C::FPW; ++i) {
-      const int k = c * kTileKC + src_ks[i] * 32;
-      dst[i] = (src_on[i] && k + 8 * lg + 8 <= K) ? ld16(src[i] + k) : z4;
+      for (int i = 0; i < C::FPW; ++i) {
+        const int f = wave * C::FPW + i;
+        __builtin_amdgcn_global_load_lds((global_void*)(src[i] + c * kTileKC + src_ks[i] * 32),
+                                         (lds_void*)(base + f * 1024), 16, 0, 0);
+      }
+    } else {  // partial chunk: zero-filled through registers
+#pragma unroll
+      for (int i = 0; i < C::FPW; ++i) {
+        const int f = wave * C::FPW + i;
+        const int k = c * kTileKC + src_ks[i] * 32;
+        const u32x4 v = (src_on[i] && k + 8 * lg + 8 <= K) ? ld16(src[i] + k) : u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(base + (size_t)f * 1024 + lane * 16) = v;
+      }
     }
   };
-  auto stash = [&](int buf, const u32x4 (&v)[C::FPW]) {
-#pragma unroll
-    for (int i = 0; i < C::FPW; ++i) {
-      const int f = wave * C::FPW + i;
-      *reinterpret_cast<u32x4*>(lds + ((size_t)(buf * C::FRAGS + f) * 64 + lane) * 16) = v[i];
-    }
-  };
-  auto frag = [&](int buf, int f) -> u32x4 {
-    return *reinterpret_cast<const u32x4*>(lds + ((size_t)(buf * C::FRAGS + f) * 64 + lane) * 16);
+  auto frag = [&](int c, int f) -> u32x4 {
+    return *reinterpret_cast<const u32x4*>(lds + ((size_t)((c % S) * C::FRAGS + f) * 64 + lane) * 16);
   };
 
-  f32x4 acc[2][C::MT];
+  f32x4 acc[4][C::MTW];
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+  for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int s = 0; s < C::MT; ++s) acc[j][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int s = 0; s < C::MTW; ++s) acc[j][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int my_active = mt_active - wm * C::MTW;
 
-  // chunk c lives in register stage c % PF until it is stashed into LDS buffer c % 2;
-  // the stage index is a compile-time constant so the stages stay in registers
-  auto body = [&](int c, auto stage_c) {
-    constexpr int st = decltype(stage_c)::value;   // = c % kTilePF
-    const int buf = c & 1;
-    if (c + kTilePF < nch) issue(c + kTilePF, R[st]);  // R[st] (chunk c) is already in LDS
 #pragma unroll
-    for (int ks = 0; ks < kTileKS; ++ks) {
-      const u32x4 wa0 = frag(buf, wave * kTileKS + ks);
-      const u32x4 wa1 = frag(buf, (wave + 4) * kTileKS + ks);
+  for (int p = 0; p < S - 1; ++p)
+    if (p < nch) issue(p);
+  for (int c = 0; c < nch; ++c) {
+    // this wave's whole chunks issued after c: min(S-2, ndma-1-c) (none once c reaches the
+    // register-staged tail chunk, whose loads are complete when it is stored)
+    const int after = c < ndma ? min(S - 2, ndma - 1 - c) : 0;
+    if (after >= S - 2) wait_vmcnt<(S - 2) * C::FPW>();
+    else if (S > 3 && after == 1) wait_vmcnt<C::FPW>();
+    else wait_vmcnt<0>();
+    // chunk c landed for every wave (each waited for its own copies above) and chunk c-1
+    // is fully consumed; a bare barrier, so the copies still in flight stay in flight
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (c + S - 1 < nch) issue(c + S - 1);
+    if (my_active > 0) {
 #pragma unroll
-      for (int s = 0; s < C::MT; ++s) {
-        if (s < mt_active) {
-          const u32x4 xb = frag(buf, (kTileWT + s) * kTileKS + ks);
-          acc[0][s] = mfma16x16x32(wa0, xb, acc[0][s]);
-          acc[1][s] = mfma16x16x32(wa1, xb, acc[1][s]);
+      for (int ks = 0; ks < kTileKS; ++ks) {
+        u32x4 wa[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) wa[j] = frag(c, wtile[j] * kTileKS + ks);
+#pragma unroll
+        for (int s = 0; s < C::MTW; ++s) {
+          if (s < my_active) {
+            const u32x4 xb = frag(c, (C::WT + wm * C::MTW + s) * kTileKS + ks);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j][s] = mfma16x16x32(wa[j], xb, acc[j][s]);
+          }
         }
       }
     }
-    if (c + 1 < nch) stash(buf ^ 1, R[(st + 1) % kTilePF]);
-    __syncthreads();
-  };
-
-#pragma unroll
-  for (int p = 0; p < kTilePF; ++p)
-    if (p < nch) issue(p, R[p]);
-  stash(0, R[0]);
-  __syncthreads();
-  for (int c = 0; c < nch; c += kTilePF) {
-    body(c, std::integral_constant<int, 0>{});
-    if (c + 1 < nch) body(c + 1, std::integral_constant<int, 1 % kTilePF>{});
-    if (kTilePF > 2 && c + 2 < nch) body(c + 2, std::integral_constant<int, 2 % kTilePF>{});
-    if (kTilePF > 3 && c + 3 < nch) body(c + 3, std::integral_constant<int, 3 % kTilePF>{});
   }
 
-  // epilogue: D rows 4*lg+q of weight tile, column li of token tile s
 #pragma unroll
-  for (int s = 0; s < C::MT; ++s) {
-    if (s >= mt_active) continue;
-    const int r = 16 * s + li;
+  for (int s = 0; s < C::MTW; ++s) {
+    if (s >= my_active) continue;
+    const int r = 16 * (wm * C::MTW + s) + li;
     if (UP) {
-      const int n = ntile * 64 + wave * 16 + 4 * lg;
-      float a[4];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) a[q] = silu_f32(acc[0][s][q]) * acc[1][s][q];
-      uint2 v;
-      v.x = pack_bf16x2(a[0], a[1]);
-      v.y = pack_bf16x2(a[2], a[3]);
-      *reinterpret_cast<uint2*>(act + (size_t)(start + r) * I + n) = v;
+      for (int h = 0; h < 2; ++h) {
+        const int n = col0 + wn * 32 + h * 16 + 4 * lg;
+        float a[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) a[q] = silu_f32(acc[h][s][q]) * acc[2 + h][s][q];
+        uint2 v;
+        v.x = pack_bf16x2(a[0], a[1]);
+        v.y = pack_bf16x2(a[2], a[3]);
+        *reinterpret_cast<uint2*>(act + (size_t)(start + r) * I + n) = v;
+      }
     } else if (r < nlive) {
       const int dst = sorted_ids[start + r];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int n = ntile * 128 + (wave + 4 * j) * 16 + 4 * lg;
+      for (int j = 0; j < 4; ++j) {
+        const int n = col0 + wn * 64 + j * 16 + 4 * lg;
         if (n < ncols)
           *reinterpret_cast<float4*>(y + (size_t)dst * ncols + n) =
               make_float4(acc[j][s][0], acc[j][s][1], acc[j][s][2], acc[j][s][3]);
@@ -189,19 +214,28 @@ __global__ __launch_bounds__(256) void expert_tiled_kernel(
   }
 }
 
-template <int BM, bool UP>
+template <int BM, int WN, int WM, int S, bool UP>
 static hipError_t launch_tiled(const uint16_t* src, const uint16_t* w, const int32_t* sorted_ids,
                                const int32_t* block_expert, const int2* tiles,
-                               const int32_t* num_tiles, int max_tiles, int n_ntiles, int K,
-                               int ncols, int I, int top_k, int block, uint16_t* act, float* y,
-                               hipStream_t s) {
+                               const int32_t* num_tiles, int max_tiles, int K, int ncols, int I,
+                               int top_k, int block, uint16_t* act, float* y, hipStream_t s) {
+  const int per_ntile = UP ? 32 * WN : 64 * WN;
+  if (UP && I % per_ntile != 0) return hipErrorInvalidValue;
+  const int n_ntiles = (ncols + per_ntile - 1) / per_ntile;
   const long total = (long)max_tiles * n_ntiles;
   const long grid = (total + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((expert_tiled_kernel<BM, UP>), dim3((unsigned)grid), dim3(256), 0, s, src, w,
-                     sorted_ids, block_expert, tiles, num_tiles, n_ntiles, K, ncols, I, top_k, block,
-                     act, y);
+  hipLaunchKernelGGL((expert_tiled_kernel<BM, WN, WM, S, UP>), dim3((unsigned)grid),
+                     dim3(TiledCfg<BM, WN, WM>::THREADS), 0, s, src, w, sorted_ids, block_expert,
+                     tiles, num_tiles, n_ntiles, K, ncols, I, top_k, block, act, y);
   return hipGetLastError();
 }
+
+// 64-row token tiles: 4 waves x 256 weight rows, 2-chunk ring (80 KiB LDS, two
+// workgroups per CU).  128-row token tiles: 8 waves x 256 weight rows, 3-chunk ring
+// (144 KiB LDS, one workgroup per CU).
+constexpr int kTileWN = 4;
+
+int tiled_up_columns() { return 32 * kTileWN; }
 
 hipError_t launch_expert_up_tiled(const uint16_t* x, const uint16_t* w13, const int32_t* sorted_ids,
                                   const int32_t* block_expert, const int2* tiles,
@@ -209,13 +243,14 @@ hipError_t launch_expert_up_tiled(const uint16_t* x, const uint16_t* w13, const 
                                   int H, int I, int top_k, int block, uint16_t* act,
                                   hipStream_t s) {
   (void)M;
-  const int nt = I / 64;
   if (tile_rows == 64)
-    return launch_tiled<64, true>(x, w13, sorted_ids, block_expert, tiles, num_tiles, max_tiles, nt,
-                                  H, I, I, top_k, block, act, nullptr, s);
+    return launch_tiled<64, kTileWN, 1, 2, true>(x, w13, sorted_ids, block_expert, tiles,
+                                                 num_tiles, max_tiles, H, I, I, top_k, block, act,
+                                                 nullptr, s);
   if (tile_rows == 128)
-    return launch_tiled<128, true>(x, w13, sorted_ids, block_expert, tiles, num_tiles, max_tiles, nt,
-                                   H, I, I, top_k, block, act, nullptr, s);
+    return launch_tiled<128, kTileWN, 2, 3, true>(x, w13, sorted_ids, block_expert, tiles,
+                                                  num_tiles, max_tiles, H, I, I, top_k, block, act,
+                                                  nullptr, s);
   return hipErrorInvalidValue;
 }
 
@@ -225,13 +260,14 @@ hipError_t launch_expert_down_tiled(const uint16_t* act, const uint16_t* w2,
                                     int tile_rows, int M, int H, int I, int top_k, int block,
                                     float* y, hipStream_t s) {
   (void)M;
-  const int nt = (H + 127) / 128;
   if (tile_rows == 64)
-    return launch_tiled<64, false>(act, w2, sorted_ids, block_expert, tiles, num_tiles, max_tiles,
-                                   nt, I, H, I, top_k, block, nullptr, y, s);
+    return launch_tiled<64, kTileWN, 1, 2, false>(act, w2, sorted_ids, block_expert, tiles,
+                                                  num_tiles, max_tiles, I, H, I, top_k, block,
+                                                  nullptr, y, s);
   if (tile_rows == 128)
-    return launch_tiled<128, false>(act, w2, sorted_ids, block_expert, tiles, num_tiles, max_tiles,
-                                    nt, I, H, I, top_k, block, nullptr, y, s);
+    return launch_tiled<128, kTileWN, 2, 3, false>(act, w2, sorted_ids, block_expert, tiles,
+                                                   num_tiles, max_tiles, I, H, I, top_k, block,
+                                                   nullptr, y, s);
   return hipErrorInvalidValue;
 }
 

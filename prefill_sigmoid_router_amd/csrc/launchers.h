@@ -37,7 +37,9 @@ hipError_t launch_expert_down(const uint16_t* act, const uint16_t* w2, const int
                               int H, int I, int top_k, int block, float* y, hipStream_t s);
 
 // LDS-tiled variants for plans whose experts carry many tokens: work items are the tiles
-// of height tile_rows (64 or 128) of `tiles`.
+// of height tile_rows (64 or 128) of `tiles`.  The up variant needs I to be a multiple of
+// tiled_up_columns().
+int tiled_up_columns();
 hipError_t launch_expert_up_tiled(const uint16_t* x, const uint16_t* w13, const int32_t* sorted_ids,
                                   const int32_t* block_expert, const int2* tiles,
                                   const int32_t* num_tiles, int max_tiles, int tile_rows, int M,

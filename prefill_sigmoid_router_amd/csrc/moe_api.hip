@@ -67,11 +67,10 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 // Grouped-GEMM kernels by expected tokens per expert (M * top_k / E), the M-range
 // dispatch pattern of the FlashInfer MNNVL finalize presets: weight streaming over 16-row
 // tiles when experts see a few tokens, LDS-tiled MFMA over 64- or 128-row token tiles
-// when they see many.  Returns the tile height; 16 selects the streaming kernels.
-int gemm_tile_rows(int32_t M, int32_t E, int32_t top_k) {
-#if defined(MOE_FORCE_TILE_ROWS)
-  return MOE_FORCE_TILE_ROWS;
-#endif
+// when they see many (thresholds measured on MI355X at H=7168, I=2048, E=256).  Returns
+// the tile height; 16 selects the streaming kernels.
+int gemm_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I) {
+  if (I % moe::tiled_up_columns() != 0) return 16;
   const int64_t per_expert = (int64_t)M * top_k / E;
   if (per_expert < 4) return 16;
   if (per_expert < 32) return 64;
@@ -237,7 +236,7 @@ int moe_forward(const uint16_t* x, const uint16_t* router_w, const float* router
   if (moe::launch_route(x, router_w, router_bias, M, H, E, top_k, ids, w, keys, s) != hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(1)) return MOE_ERR_HIP;
-  const int trows = gemm_tile_rows(M, E, top_k);
+  const int trows = gemm_tile_rows(M, E, top_k, I);
   const int max_tiles = moe::tile_capacity(M * top_k, E, trows);
   if (moe::launch_align(ids, M * top_k, E, block, sorted, bexp, npad, trows, tiles, ntiles, s) !=
       hipSuccess)

@@ -89,6 +89,39 @@ __global__ __launch_bounds__(256) void router_keys_kernel(const uint16_t* __rest
 
 constexpr int kTopkMaxE = 1024;
 constexpr int kTopkThreads = 256;
+// Tokens from which the certified path (below) replaces the all-fp64 keys: from about
+// 256 tokens its fp32 MFMA logits plus a few fp64 recomputes per token cost less than
+// fp64 dot products for every (token, expert) pair.
+#ifndef MOE_ROUTE_CERTIFIED_MIN
+#define MOE_ROUTE_CERTIFIED_MIN 256
+#endif
+constexpr int kRouteCertifiedMinTokens = MOE_ROUTE_CERTIFIED_MIN;
+constexpr int kSelectMaxH = 16384;  // largest H whose x row the select kernel stages in LDS
+constexpr int kSelChunks = 16;      // 16-byte chunks per lane in flight per candidate batch
+
+// Number of entries of vals[0..n) ahead of (v, id): larger, or equal with a lower index.
+// Eight LDS values are requested per step so the loop is not bound by LDS latency.
+template <int SL>
+__device__ __forceinline__ void count_ahead(const double* vals, int n, const double (&v)[SL],
+                                            const int (&id)[SL], int (&rank)[SL]) {
+#pragma unroll
+  for (int s = 0; s < SL; ++s) rank[s] = 0;
+  int j = 0;
+  for (; j + 8 <= n; j += 8) {
+    double b[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) b[u] = vals[j + u];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+#pragma unroll
+      for (int s = 0; s < SL; ++s) rank[s] += (b[u] > v[s] || (b[u] == v[s] && j + u < id[s])) ? 1 : 0;
+  }
+  for (; j < n; ++j) {
+    const double b = vals[j];
+#pragma unroll
+    for (int s = 0; s < SL; ++s) rank[s] += (b > v[s] || (b == v[s] && j < id[s])) ? 1 : 0;
+  }
+}
 
 // One workgroup per token.  Thread i owns experts i, i + 256, ... (SL of them).  The
 // token's keys (logit + bias) sit in LDS; each owned expert's rank is the number of
@@ -116,17 +149,10 @@ __global__ __launch_bounds__(kTopkThreads) void router_topk_kernel(const double*
     }
   }
   __syncthreads();
-  int rank[SL];
+  int rank[SL], myid[SL];
 #pragma unroll
-  for (int s = 0; s < SL; ++s) rank[s] = 0;
-  for (int j = 0; j < E; ++j) {
-    const double kj = sk[j];
-#pragma unroll
-    for (int s = 0; s < SL; ++s) {
-      const int e = tid + kTopkThreads * s;
-      rank[s] += (kj > mine[s] || (kj == mine[s] && j < e)) ? 1 : 0;
-    }
-  }
+  for (int s = 0; s < SL; ++s) myid[s] = tid + kTopkThreads * s;
+  count_ahead<SL>(sk, E, mine, myid, rank);
 #pragma unroll
   for (int s = 0; s < SL; ++s) {
     const int e = tid + kTopkThreads * s;
@@ -142,6 +168,218 @@ __global__ __launch_bounds__(kTopkThreads) void router_topk_kernel(const double*
     const double total = wave_sum(part);
     for (int r = tid; r < top_k; r += kWave)
       weights[(size_t)t * top_k + r] = (float)(ssig[r] / total);
+  }
+}
+
+// ---------------------------------------------------------------------------------------
+// Certified fast path for many tokens.
+//
+// 1. router_logits_mfma_kernel: fp32 logits L = x . Wr^T on bf16 MFMA, together with
+//    A = sum_h |x_h| |w_h| from the same fragments with the sign bits cleared.  Products
+//    of two bf16 values are exact in fp32, so the only error is the fp32 summation.  A
+//    product passes at most 31 roundings inside its MFMA, one per later K step of its
+//    wave (at most H / 128 <= 128 for H <= 16384) and the 3 adds that join the waves:
+//    at most 162 roundings, so |L - exact| <= 162 * 2u * A even if the hardware truncates
+//    (u = 2^-24).  The selection uses d = 2^-14 A = 1024 u A, above that with margin,
+//    plus an absolute floor for flushed subnormal products.
+// 2. router_select_kernel, one workgroup per token: with lo = L + b - d and hi = L + b + d,
+//    T = the k-th largest lo.  An expert with hi < T has an exact key below at least k
+//    other exact keys, so it cannot be picked; every other expert is a candidate.  The
+//    candidates' keys are recomputed as fp64 dot products and ranked exactly as the fp64
+//    path ranks them (key descending, ties to the lower id).
+// ---------------------------------------------------------------------------------------
+constexpr int kLogitU = 4;
+
+// One workgroup per 16 experts x 16 tokens; its four waves take four contiguous quarters
+// of the 32-wide K steps and meet in LDS in a fixed order.
+__global__ __launch_bounds__(256) void router_logits_mfma_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int M, int H, int E,
+    float* __restrict__ logits, float* __restrict__ absdot) {
+  __shared__ f32x4 part[3][2][kWave];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int li = lane & 15, lg = lane >> 4;
+  const int e0 = blockIdx.x * 16;
+  const int t0 = blockIdx.y * 16;
+  const bool e_in = e0 + li < E;
+  const bool t_in = t0 + li < M;
+  const int nsteps = (H + 31) / 32;
+  const int s_lo = wave * nsteps / 4, s_hi = (wave + 1) * nsteps / 4;
+  const uint16_t* wrow = wr + (size_t)(e_in ? e0 + li : 0) * H + 8 * lg;
+  const uint16_t* xrow = x + (size_t)(t_in ? t0 + li : 0) * H + 8 * lg;
+  const u32x4 z4 = u32x4{0, 0, 0, 0};
+  const u32x4 absmask = u32x4{0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu};
+  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}, aab = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int st = s_lo; st < s_hi; st += kLogitU) {
+    u32x4 wv[kLogitU], xv[kLogitU];
+#pragma unroll
+    for (int u = 0; u < kLogitU; ++u) {
+      const int k = (st + u) * 32;
+      const bool in = st + u < s_hi && k + 8 * lg + 8 <= H;
+      wv[u] = (in && e_in) ? ld16(wrow + k) : z4;
+      xv[u] = (in && t_in) ? ld16(xrow + k) : z4;
+    }
+#pragma unroll
+    for (int u = 0; u < kLogitU; ++u) {
+      acc = mfma16x16x32(wv[u], xv[u], acc);
+      aab = mfma16x16x32(wv[u] & absmask, xv[u] & absmask, aab);
+    }
+  }
+  if (wave > 0) {
+    part[wave - 1][0][lane] = acc;
+    part[wave - 1][1][lane] = aab;
+  }
+  __syncthreads();
+  if (wave > 0) return;
+  acc = ((acc + part[0][0][lane]) + part[1][0][lane]) + part[2][0][lane];
+  aab = ((aab + part[0][1][lane]) + part[1][1][lane]) + part[2][1][lane];
+  // D rows 4*lg+q = experts, column li = token
+  if (t_in) {
+    const int e = e0 + 4 * lg;
+    float* lrow = logits + (size_t)(t0 + li) * E;
+    float* arow = absdot + (size_t)(t0 + li) * E;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      if (e + q < E) {
+        lrow[e + q] = acc[q];
+        arow[e + q] = aab[q];
+      }
+    }
+  }
+}
+
+template <int SL>
+__global__ __launch_bounds__(kTopkThreads) void router_select_kernel(
+    const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias,
+    const float* __restrict__ logits, const float* __restrict__ absdot, int M, int H, int E,
+    int top_k, int32_t* __restrict__ ids, float* __restrict__ weights) {
+  __shared__ double s_lo[kTopkMaxE];
+  __shared__ double s_key[kTopkMaxE];     // fp64 keys of the candidates, by candidate slot
+  __shared__ int s_cand[kTopkMaxE];       // expert id of each candidate slot
+  __shared__ double s_sig[kTopkMaxE];
+  __shared__ int s_wave_cnt[kTopkThreads / kWave];
+  __shared__ double s_T;
+  __shared__ u32x4 s_x[kSelectMaxH / 8];  // the token's x row
+  const int t = blockIdx.x, tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  for (int ch = tid; ch < (H >> 3); ch += kTopkThreads) s_x[ch] = ld16(x + (size_t)t * H + (size_t)ch * 8);
+
+  double lo[SL], hi[SL];
+#pragma unroll
+  for (int s = 0; s < SL; ++s) {
+    const int e = tid + kTopkThreads * s;
+    lo[s] = hi[s] = 0.0;
+    if (e < E) {
+      const double key = (double)logits[(size_t)t * E + e] + (bias ? (double)bias[e] : 0.0);
+      const double d = (double)absdot[(size_t)t * E + e] * 0x1p-14 * (1.0 + 0x1p-20) +
+                       fabs(key) * 0x1p-50 + (double)H * 0x1p-126 + 1e-300;
+      lo[s] = key - d;
+      hi[s] = key + d;
+      s_lo[e] = lo[s];
+    }
+  }
+  __syncthreads();
+  // T = the top_k-th largest lower bound (rank top_k - 1 by (lo desc, id asc))
+  int rank[SL], myid[SL];
+#pragma unroll
+  for (int s = 0; s < SL; ++s) myid[s] = tid + kTopkThreads * s;
+  count_ahead<SL>(s_lo, E, lo, myid, rank);
+#pragma unroll
+  for (int s = 0; s < SL; ++s)
+    if (tid + kTopkThreads * s < E && rank[s] == top_k - 1) s_T = lo[s];
+  __syncthreads();
+  const double T = s_T;
+
+  // compact the candidates (hi >= T) in ascending expert order
+  int ncand = 0;
+#pragma unroll
+  for (int s = 0; s < SL; ++s) {
+    const int e = tid + kTopkThreads * s;
+    const bool cand = e < E && hi[s] >= T;
+    const uint64_t m = __ballot(cand);
+    if (lane == 0) s_wave_cnt[wave] = __popcll(m);
+    __syncthreads();
+    int before = ncand;
+    for (int w = 0; w < kTopkThreads / kWave; ++w) {
+      if (w < wave) before += s_wave_cnt[w];
+      ncand += s_wave_cnt[w];
+    }
+    if (cand) s_cand[before + __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))))] = e;
+    __syncthreads();
+  }
+
+  // fp64 keys of the candidates: wave w takes candidates w, w+4, ...; lane l takes the
+  // 16-byte chunks l, l+64, ... of H (x from LDS).  A candidate's chunks are requested
+  // together (kSelChunks per lane at a time) and the next candidate's first batch is in
+  // flight while this one is summed; xor-butterfly reduction per candidate.
+  const int nchunk = H >> 3;
+  const int nwaves = kTopkThreads / kWave;
+  u32x4 wv[2][kSelChunks];
+  auto fetch = [&](int c, u32x4 (&dst)[kSelChunks], int base) {
+    const uint16_t* wrow = wr + (size_t)s_cand[c] * H;
+#pragma unroll
+    for (int u = 0; u < kSelChunks; ++u) {
+      const int ch = base + lane + u * kWave;
+      dst[u] = ch < nchunk ? ld16(wrow + (size_t)ch * 8) : u32x4{0, 0, 0, 0};
+    }
+  };
+  auto dot = [&](const u32x4 (&src)[kSelChunks], int base, double acc) {
+#pragma unroll
+    for (int u = 0; u < kSelChunks; ++u) {
+      const int ch = base + lane + u * kWave;
+      if (ch < nchunk) {
+        const u32x4 xv = s_x[ch];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          acc = fma((double)bf16lo(xv[q]), (double)bf16lo(src[u][q]), acc);
+          acc = fma((double)bf16hi(xv[q]), (double)bf16hi(src[u][q]), acc);
+        }
+      }
+    }
+    return acc;
+  };
+  if (wave < ncand) fetch(wave, wv[0], 0);
+  for (int c = wave, it = 0; c < ncand; c += nwaves, ++it) {
+    double acc = 0.0;
+    for (int base = 0; base < nchunk; base += kSelChunks * kWave) {
+      // batch (c, base) sits in wv[it & 1] ... keep the stage index static by branching
+      const bool last_batch = base + kSelChunks * kWave >= nchunk;
+      const int next_c = last_batch ? c + nwaves : c;
+      const int next_base = last_batch ? 0 : base + kSelChunks * kWave;
+      if ((it & 1) == 0) {
+        if (next_c < ncand) fetch(next_c, wv[1], next_base);
+        acc = dot(wv[0], base, acc);
+      } else {
+        if (next_c < ncand) fetch(next_c, wv[0], next_base);
+        acc = dot(wv[1], base, acc);
+      }
+      it += last_batch ? 0 : 1;
+    }
+    acc = wave_sum(acc);
+    if (lane == 0) s_key[c] = acc + (bias ? (double)bias[s_cand[c]] : 0.0);
+  }
+  __syncthreads();
+
+  // rank the candidates exactly: key descending, ties to the lower id
+  for (int c = tid; c < ncand; c += kTopkThreads) {
+    const double kc = s_key[c];
+    const int ec = s_cand[c];
+    int r = 0;
+    for (int j = 0; j < ncand; ++j) {
+      const double kj = s_key[j];
+      r += (kj > kc || (kj == kc && s_cand[j] < ec)) ? 1 : 0;
+    }
+    if (r < top_k) {
+      ids[(size_t)t * top_k + r] = ec;
+      s_sig[r] = 1.0 / (1.0 + exp(-kc));
+    }
+  }
+  __syncthreads();
+  if (tid < kWave) {
+    double part = 0.0;
+    for (int r = tid; r < top_k; r += kWave) part += s_sig[r];
+    const double total = wave_sum(part);
+    for (int r = tid; r < top_k; r += kWave)
+      weights[(size_t)t * top_k + r] = (float)(s_sig[r] / total);
   }
 }
 
@@ -164,11 +402,26 @@ static hipError_t launch_topk(const double* keys, const float* bias, int M, int 
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, const float* bias, int M, int H,
                         int E, int top_k, int32_t* ids, float* w, double* keys, hipStream_t s) {
   hipError_t err;
-  if (M <= 16) err = launch_keys<2, 4, 4>(x, wr, M, H, E, keys, s);
-  else if (M <= 256) err = launch_keys<4, 4, 2>(x, wr, M, H, E, keys, s);
-  else err = launch_keys<4, 8, 1>(x, wr, M, H, E, keys, s);
-  if (err != hipSuccess) return err;
   const int per_thread = (E + kTopkThreads - 1) / kTopkThreads;
+  if (M >= kRouteCertifiedMinTokens) {
+    // the fp64 key buffer [M, E] doubles as the fp32 logits and |x|.|w| buffers
+    float* logits = reinterpret_cast<float*>(keys);
+    float* absdot = logits + (size_t)M * E;
+    hipLaunchKernelGGL(router_logits_mfma_kernel, dim3((E + 15) / 16, (M + 15) / 16), dim3(256), 0,
+                       s, x, wr, M, H, E, logits, absdot);
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+#define MOE_SELECT(SLV)                                                                          \
+  hipLaunchKernelGGL((router_select_kernel<SLV>), dim3(M), dim3(kTopkThreads), 0, s, x, wr, bias, \
+                     logits, absdot, M, H, E, top_k, ids, w)
+    if (per_thread <= 1) MOE_SELECT(1);
+    else if (per_thread <= 2) MOE_SELECT(2);
+    else MOE_SELECT(4);
+#undef MOE_SELECT
+    return hipGetLastError();
+  }
+  if (M <= 16) err = launch_keys<2, 4, 4>(x, wr, M, H, E, keys, s);
+  else err = launch_keys<4, 4, 2>(x, wr, M, H, E, keys, s);
+  if (err != hipSuccess) return err;
   if (per_thread <= 1) return launch_topk<1>(keys, bias, M, E, top_k, ids, w, s);
   if (per_thread <= 2) return launch_topk<2>(keys, bias, M, E, top_k, ids, w, s);
   return launch_topk<4>(keys, bias, M, E, top_k, ids, w, s);

@@ -120,6 +120,33 @@ def test_route_bit_exact(B, dev, name):
     np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=0, atol=1e-6)
 
 
+# Shapes on the many-token router path (fp32 MFMA logits with an error bound, fp64
+# recompute of the candidates): ragged token, expert and K tiles, the largest H (the
+# x row staged in LDS) and the largest E (four experts per thread).
+ROUTE_MANY = {
+    "ragged": mi.LayerConfig("route_ragged", M=261, H=208, E=37, top_k=5, I=64, block=16),
+    "max_h": mi.LayerConfig("route_max_h", M=256, H=16384, E=8, top_k=2, I=64, block=16),
+    "max_e": mi.LayerConfig("route_max_e", M=300, H=128, E=1024, top_k=8, I=64, block=16,
+                            zipf_s=1.1),
+}
+
+
+@pytest.mark.parametrize("name", list(ROUTE_MANY))
+def test_route_many_tokens_bit_exact(B, dev, name):
+    cfg = ROUTE_MANY[name]
+    print(f"route parity {cfg.name} M={cfg.M} H={cfg.H} E={cfg.E} k={cfg.top_k}", flush=True)
+    L = mi.make_layer(cfg, device=dev, seed=3, with_experts=False)
+    M, k = cfg.M, cfg.top_k
+    ids = _poisoned((M, k), torch.int32, dev)
+    w = _poisoned((M, k), torch.float32, dev)
+    ws = torch.empty(B.moe_route_workspace_bytes(M, cfg.E), dtype=torch.uint8, device=dev)
+    B.moe_route(L["x"], L["router_w"], L["router_bias"], k, ids, w, ws)
+    torch.cuda.synchronize()
+    ref_ids, ref_w, _ = orc.route(bits(L["x"]), bits(L["router_w"]), _bias_np(L), k)
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=0, atol=1e-6)
+
+
 def test_route_exact_ties_go_to_the_lower_id(B, dev):
     torch.manual_seed(0)
     M, H, E, k = 40, 256, 64, 8
@@ -149,6 +176,40 @@ def test_route_exact_ties_go_to_the_lower_id(B, dev):
     B.moe_route(xz, wr, b2, 3, ids1, w1, ws)
     torch.cuda.synchronize()
     assert ids1.cpu().tolist() == [[1, 3, 0]]
+
+
+@pytest.mark.parametrize("M", [16, 300])
+def test_route_near_ties_resolved_like_fp64(B, dev, M):
+    """Router rows that fp32 logits cannot tell apart but fp64 keys can: rows 10/11 equal
+    except one element one bf16 step apart, where every token's x is 2^-20 (a key gap of
+    about 1e-10); rows 20/21 identical (an exact tie).  Both pairs get a +12 bias so they
+    are picked.  M=300 runs the many-token path (MFMA logits, fp64 recompute), M=16 the
+    all-fp64 path."""
+    g = torch.Generator(device="cpu").manual_seed(9)
+    H, E, k = 512, 64, 6
+    x = torch.randn(M, H, generator=g)
+    x[:, 100] = 2.0 ** -20
+    wr = torch.randn(E, H, generator=g) * 0.05
+    wr[11] = wr[10]
+    wr[21] = wr[20]
+    xb = x.to(torch.bfloat16)
+    wb = wr.to(torch.bfloat16)
+    bits11 = wb[11, 100].view(torch.int16).item()
+    wb[11, 100] = torch.tensor([bits11 + (1 if bits11 >= 0 else -1)], dtype=torch.int16).view(torch.bfloat16)[0]
+    bias = torch.zeros(E, dtype=torch.float32)
+    bias[[10, 11, 20, 21]] = 12.0
+    xb, wb, bias = xb.to(dev), wb.to(dev), bias.to(dev)
+    ids = _poisoned((M, k), torch.int32, dev)
+    w = _poisoned((M, k), torch.float32, dev)
+    ws = torch.empty(B.moe_route_workspace_bytes(M, E), dtype=torch.uint8, device=dev)
+    B.moe_route(xb, wb, bias, k, ids, w, ws)
+    torch.cuda.synchronize()
+    ref_ids, ref_w, keys = orc.route(bits(xb), bits(wb), bias.cpu().numpy(), k)
+    assert np.all(keys[:, 10] != keys[:, 11])            # the pair is separated in fp64
+    assert np.array_equal(ids.cpu().numpy(), ref_ids)
+    np.testing.assert_allclose(w.cpu().numpy(), ref_w, rtol=0, atol=1e-6)
+    for row in ids.cpu().tolist():
+        assert row.index(21) == row.index(20) + 1
 
 
 # ---------------------------------------------------------------------------------------

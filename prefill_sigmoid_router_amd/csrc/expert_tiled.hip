@@ -8,18 +8,19 @@
 // by all waves of a workgroup, and the M tiles of one expert run on one XCD at the same
 // time so they share the weight stream through that XCD's L2.
 //
-// Workgroup tile: BM plan rows of one expert (a tile of the align kernel's list) x 256
-// weight rows (up: 128 gate + 128 up rows = 128 act columns; down: 256 output columns),
-// K in chunks of 64.  Both operands are copied global -> LDS with global_load_lds_dwordx4
-// in MFMA fragment order: a fragment is 16 rows x 32 K values (1 KiB), lane l copies row
-// l%16, K values 8*(l/16)..+8, and the instruction lands lane l's 16 bytes at LDS base +
-// 16 l -- so every global load reads 16 rows x 64 contiguous bytes, no registers stage
-// the data, and every fragment read is one conflict-free 1 KiB ds_read_b128.  An S-deep
-// ring keeps S-1 chunks in flight; each wave waits for its own copies of chunk c with
-// s_waitcnt vmcnt and a bare s_barrier publishes them (a fenced barrier would drain every
-// copy in flight).  Only a partial last K chunk goes through registers (zero-filled).
-// Waves form a WN x WM grid; each accumulates 4 weight tiles x BM/16/WM token tiles
-// (64 x 64 outputs for both configurations used) with v_mfma_f32_16x16x32_bf16.
+// Workgroup tile: BM plan rows of one expert (a tile of the align kernel's list) x 64 WN
+// weight rows (up: gate and up rows of 32 WN act columns; down: 64 WN output columns), K
+// in chunks of 64.  Both operands are copied global -> LDS with global_load_lds_dwordx4,
+// which lands lane l's 16 bytes at LDS base + 16 l.  One copy covers 8 rows x one whole
+// 128-byte line each (a 16 rows x 64-byte pattern, two half lines per row, streams at a
+// third of the rate when the lines come from L2), and inside a row the 16-byte K chunks
+// are XOR-swizzled so that an MFMA fragment (16 rows x 32 K values) is one conflict-free
+// ds_read_b128 per lane.  No registers stage the data.  An S-deep ring keeps S-1 chunks
+// in flight; each wave waits for its own copies of chunk c with s_waitcnt vmcnt and a
+// bare s_barrier publishes them (a fenced barrier would drain every copy in flight).
+// Only a partial last K chunk goes through registers (zero-filled).  Waves form a
+// WN x WM grid; each accumulates 4 weight tiles x BM/16/WM token tiles with
+// v_mfma_f32_16x16x32_bf16.
 //
 // Work order: the hardware hands workgroup p to XCD p % 8.  Each XCD gets an equal,
 // contiguous share of the live (tile, N tile) items (the tile count is read on the
@@ -31,7 +32,7 @@
 
 namespace moe {
 
-constexpr int kTileKC = 64;                     // K values per chunk
+constexpr int kTileKC = 64;                     // K values per chunk: one 128-byte line per row
 constexpr int kTileKS = kTileKC / 32;           // MFMA K steps per chunk
 constexpr int kXcds = 8;                        // MI355X: 8 XCDs, round-robin dispatch
 
@@ -44,9 +45,9 @@ struct TiledCfg {
   static constexpr int WT = 4 * WN;                          // weight row tiles per workgroup
   static constexpr int MT = BM / 16;                         // token row tiles per workgroup
   static constexpr int MTW = MT / WM;                        // token row tiles per wave
-  static constexpr int FRAGS = (WT + MT) * kTileKS;          // fragments per chunk
-  static constexpr int FPW = FRAGS / (WN * WM);              // fragments staged per wave
-  static_assert(FRAGS % (WN * WM) == 0, "fragments must split evenly over the waves");
+  static constexpr int FRAGS = (WT + MT) * 2;                // 1 KiB copies per chunk (8 rows each)
+  static constexpr int FPW = FRAGS / (WN * WM);              // copies issued per wave
+  static_assert(FRAGS % (WN * WM) == 0, "copies must split evenly over the waves");
   static_assert(MT % WM == 0, "token tiles must split evenly over the waves");
 };
 
@@ -59,6 +60,18 @@ __device__ __forceinline__ void wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
+// Wait until only this wave's copies of the `after` chunks issued after the one needed
+// are outstanding (FPW copies per chunk; after <= A).
+template <int FPW, int A>
+__device__ __forceinline__ void wait_chunks_after(int after) {
+  if constexpr (A <= 0) {
+    wait_vmcnt<0>();
+  } else {
+    if (after >= A) wait_vmcnt<A * FPW>();
+    else wait_chunks_after<FPW, A - 1>(after);
+  }
+}
+
 template <int BM, int WN, int WM, int S, bool UP>
 __global__ __launch_bounds__(64 * WN * WM) void expert_tiled_kernel(
     const uint16_t* __restrict__ tok_src, const uint16_t* __restrict__ w,
@@ -66,6 +79,8 @@ __global__ __launch_bounds__(64 * WN * WM) void expert_tiled_kernel(
     const int2* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int n_ntiles, int K,
     int ncols, int I, int top_k, int block, uint16_t* __restrict__ act, float* __restrict__ y) {
   using C = TiledCfg<BM, WN, WM>;
+  static_assert(S >= 2 && (S - 2) * C::FPW <= 63, "the copies in flight must fit the vmcnt counter");
+  static_assert(S * C::FRAGS * 1024 <= 160 * 1024, "the ring must fit the LDS");
   __shared__ __align__(16) unsigned char lds[S * C::FRAGS * 1024];
 
   const int ntiles_live = *num_tiles;
@@ -87,33 +102,39 @@ __global__ __launch_bounds__(64 * WN * WM) void expert_tiled_kernel(
   const int wn = wave % WN, wm = wave / WN;
   const int col0 = UP ? ntile * 32 * WN : ntile * 64 * WN;
 
-  // source row pointer (at K offset 8 * lg) of every fragment this wave stages; rows that
-  // hold no data point at a valid row (their results are never stored)
+  // Copy f of a chunk covers rows 8h..8h+7 (h = f % 2) of row tile f / 2 (weight tiles
+  // first, then token tiles), one 128-byte line per row: lane l copies row 8h + l / 8, and
+  // its 16 bytes land at LDS slot l % 8 of that row.  The slot holds K chunk
+  // q = (l % 8) ^ (row % 8) ^ h of the row, an XOR swizzle that keeps the fragment reads
+  // below free of bank conflicts.  Rows that hold no data point at a valid row (their
+  // results are never stored).
   const uint16_t* src[C::FPW];
   bool src_on[C::FPW];
-  int src_ks[C::FPW];
+  int src_q[C::FPW];
   const size_t wexp = UP ? (size_t)e * 2 * I * K : (size_t)e * ncols * K;
 #pragma unroll
   for (int i = 0; i < C::FPW; ++i) {
     const int f = wave * C::FPW + i;
-    if (f < C::WT * kTileKS) {
-      const int rt = f / kTileKS;
-      src_ks[i] = f % kTileKS;
+    const int rt = f >> 1, h = f & 1;
+    const int rr = 8 * h + (lane >> 3);           // row inside the 16-row tile
+    src_q[i] = (lane & 7) ^ (lane >> 3) ^ h;
+    const int koff = 8 * src_q[i];
+    if (rt < C::WT) {
       int row;
-      if (UP) row = (rt < C::WT / 2) ? col0 + rt * 16 + li : I + col0 + (rt - C::WT / 2) * 16 + li;
-      else row = col0 + rt * 16 + li;
+      if (UP) row = (rt < C::WT / 2) ? col0 + rt * 16 + rr : I + col0 + (rt - C::WT / 2) * 16 + rr;
+      else row = col0 + rt * 16 + rr;
       src_on[i] = UP || row < ncols;
-      src[i] = w + wexp + (size_t)(src_on[i] ? row : 0) * K + 8 * lg;
+      src[i] = w + wexp + (size_t)(src_on[i] ? row : 0) * K + koff;
     } else {
-      const int g = f - C::WT * kTileKS;
-      const int mt = g / kTileKS;
-      src_ks[i] = g % kTileKS;
-      const int r = 16 * mt + li;
+      const int r = 16 * (rt - C::WT) + rr;
       src_on[i] = r < nlive;
       const int prow = start + (src_on[i] ? r : 0);
-      src[i] = UP ? tok_src + (size_t)(sorted_ids[prow] < 0 ? 0 : sorted_ids[prow] / top_k) * K + 8 * lg
-                  : tok_src + (size_t)prow * K + 8 * lg;
-      if (UP && !src_on[i]) src[i] = tok_src + 8 * lg;
+      if (UP) {
+        const int sid = src_on[i] ? sorted_ids[prow] : 0;
+        src[i] = tok_src + (size_t)(sid < 0 ? 0 : sid / top_k) * K + koff;
+      } else {
+        src[i] = tok_src + (size_t)prow * K + koff;
+      }
     }
   }
   int wtile[4];
@@ -129,21 +150,26 @@ __global__ __launch_bounds__(64 * WN * WM) void expert_tiled_kernel(
 #pragma unroll
       for (int i = 0; i < C::FPW; ++i) {
         const int f = wave * C::FPW + i;
-        __builtin_amdgcn_global_load_lds((global_void*)(src[i] + c * kTileKC + src_ks[i] * 32),
+        __builtin_amdgcn_global_load_lds((global_void*)(src[i] + c * kTileKC),
                                          (lds_void*)(base + f * 1024), 16, 0, 0);
       }
     } else {  // partial chunk: zero-filled through registers
 #pragma unroll
       for (int i = 0; i < C::FPW; ++i) {
         const int f = wave * C::FPW + i;
-        const int k = c * kTileKC + src_ks[i] * 32;
-        const u32x4 v = (src_on[i] && k + 8 * lg + 8 <= K) ? ld16(src[i] + k) : u32x4{0, 0, 0, 0};
+        const int k = c * kTileKC + 8 * src_q[i];
+        const u32x4 v = (src_on[i] && k + 8 <= K) ? ld16(src[i] + c * kTileKC) : u32x4{0, 0, 0, 0};
         *reinterpret_cast<u32x4*>(base + (size_t)f * 1024 + lane * 16) = v;
       }
     }
   };
-  auto frag = [&](int c, int f) -> u32x4 {
-    return *reinterpret_cast<const u32x4*>(lds + ((size_t)((c % S) * C::FRAGS + f) * 64 + lane) * 16);
+  // MFMA fragment (16 rows x 32 K values) ks of row tile t: lane (li, lg) reads row li,
+  // K chunk lg + 4 ks, from its swizzled slot
+  const int frag_off = (li >> 3) * 1024 + (li & 7) * 128;
+  auto frag = [&](int c, int t, int ks) -> u32x4 {
+    const int q = (lg + 4 * ks) ^ (li & 7) ^ (li >> 3);
+    return *reinterpret_cast<const u32x4*>(lds + (size_t)(c % S) * C::FRAGS * 1024 + t * 2048 +
+                                           frag_off + q * 16);
   };
 
   f32x4 acc[4][C::MTW];
@@ -153,6 +179,24 @@ __global__ __launch_bounds__(64 * WN * WM) void expert_tiled_kernel(
     for (int s = 0; s < C::MTW; ++s) acc[j][s] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int my_active = mt_active - wm * C::MTW;
 
+  auto compute = [&](int c) {
+    if (my_active <= 0) return;
+#pragma unroll
+    for (int ks = 0; ks < kTileKS; ++ks) {
+      u32x4 wa[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wa[j] = frag(c, wtile[j], ks);
+#pragma unroll
+      for (int s = 0; s < C::MTW; ++s) {
+        if (s < my_active) {
+          const u32x4 xb = frag(c, C::WT + wm * C::MTW + s, ks);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[j][s] = mfma16x16x32(wa[j], xb, acc[j][s]);
+        }
+      }
+    }
+  };
+
 #pragma unroll
   for (int p = 0; p < S - 1; ++p)
     if (p < nch) issue(p);
@@ -160,29 +204,12 @@ __global__ __launch_bounds__(64 * WN * WM) void expert_tiled_kernel(
     // this wave's whole chunks issued after c: min(S-2, ndma-1-c) (none once c reaches the
     // register-staged tail chunk, whose loads are complete when it is stored)
     const int after = c < ndma ? min(S - 2, ndma - 1 - c) : 0;
-    if (after >= S - 2) wait_vmcnt<(S - 2) * C::FPW>();
-    else if (S > 3 && after == 1) wait_vmcnt<C::FPW>();
-    else wait_vmcnt<0>();
+    wait_chunks_after<C::FPW, S - 2>(after);
     // chunk c landed for every wave (each waited for its own copies above) and chunk c-1
     // is fully consumed; a bare barrier, so the copies still in flight stay in flight
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
     if (c + S - 1 < nch) issue(c + S - 1);
-    if (my_active > 0) {
-#pragma unroll
-      for (int ks = 0; ks < kTileKS; ++ks) {
-        u32x4 wa[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) wa[j] = frag(c, wtile[j] * kTileKS + ks);
-#pragma unroll
-        for (int s = 0; s < C::MTW; ++s) {
-          if (s < my_active) {
-            const u32x4 xb = frag(c, (C::WT + wm * C::MTW + s) * kTileKS + ks);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[j][s] = mfma16x16x32(wa[j], xb, acc[j][s]);
-          }
-        }
-      }
-    }
+    compute(c);
   }
 
 #pragma unroll
@@ -230,10 +257,12 @@ static hipError_t launch_tiled(const uint16_t* src, const uint16_t* w, const int
   return hipGetLastError();
 }
 
-// 64-row token tiles: 4 waves x 256 weight rows, 2-chunk ring (80 KiB LDS, two
-// workgroups per CU).  128-row token tiles: 8 waves x 256 weight rows, 3-chunk ring
-// (144 KiB LDS, one workgroup per CU).
-constexpr int kTileWN = 4;
+// Both token-tile heights run 8 waves x 512 weight rows (up: 256 act columns) with a
+// 2-chunk ring: 72 KiB (64 rows) or 80 KiB (128 rows) per chunk, one workgroup per CU.
+// Measured on MI355X at H=7168, I=2048: the 256-row tile with a 3-chunk ring re-reads
+// the token rows twice as often, which costs more than the shallower ring.
+constexpr int kTileWN = 8;
+constexpr int kTileStages = 2;
 
 int tiled_up_columns() { return 32 * kTileWN; }
 
@@ -244,11 +273,11 @@ hipError_t launch_expert_up_tiled(const uint16_t* x, const uint16_t* w13, const 
                                   hipStream_t s) {
   (void)M;
   if (tile_rows == 64)
-    return launch_tiled<64, kTileWN, 1, 2, true>(x, w13, sorted_ids, block_expert, tiles,
+    return launch_tiled<64, kTileWN, 1, kTileStages, true>(x, w13, sorted_ids, block_expert, tiles,
                                                  num_tiles, max_tiles, H, I, I, top_k, block, act,
                                                  nullptr, s);
   if (tile_rows == 128)
-    return launch_tiled<128, kTileWN, 2, 3, true>(x, w13, sorted_ids, block_expert, tiles,
+    return launch_tiled<128, kTileWN, 1, kTileStages, true>(x, w13, sorted_ids, block_expert, tiles,
                                                   num_tiles, max_tiles, H, I, I, top_k, block, act,
                                                   nullptr, s);
   return hipErrorInvalidValue;
@@ -261,11 +290,11 @@ hipError_t launch_expert_down_tiled(const uint16_t* act, const uint16_t* w2,
                                     float* y, hipStream_t s) {
   (void)M;
   if (tile_rows == 64)
-    return launch_tiled<64, kTileWN, 1, 2, false>(act, w2, sorted_ids, block_expert, tiles,
+    return launch_tiled<64, kTileWN, 1, kTileStages, false>(act, w2, sorted_ids, block_expert, tiles,
                                                   num_tiles, max_tiles, I, H, I, top_k, block,
                                                   nullptr, y, s);
   if (tile_rows == 128)
-    return launch_tiled<128, kTileWN, 2, 3, false>(act, w2, sorted_ids, block_expert, tiles,
+    return launch_tiled<128, kTileWN, 1, kTileStages, false>(act, w2, sorted_ids, block_expert, tiles,
                                                    num_tiles, max_tiles, I, H, I, top_k, block,
                                                    nullptr, y, s);
   return hipErrorInvalidValue;

@@ -214,8 +214,13 @@ def main():
             sweep[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
 
     traffic = load_traffic()
+    rows = B.moe_gemm_tile_rows(head.M, head.E, head.top_k, head.I)
+    up_kernel = ("expert_up_stream_kernel<4>" if rows == 16
+                 else f"expert_tiled_kernel<{rows}, 8, 1, 2, true>")
+    if traffic is not None and traffic.get("workload") != head.name:
+        traffic = None  # counters were taken on another workload
     roof = {
-        "bound": "hbm", "kernel": "expert_up_stream_kernel (grouped up-GEMM + SwiGLU)",
+        "bound": "hbm", "kernel": f"{up_kernel} (grouped up-GEMM + SwiGLU)",
         "achieved": round(res["up_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(res["up_gbs"] / HBM_PEAK_GBS, 4),
         "traffic": None if traffic is None else traffic.get("traffic_gbs"),

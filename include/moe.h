@@ -61,7 +61,7 @@ enum {
 /* Human-readable text of a status code.  Never NULL; static storage. */
 const char* moe_strerror(int status);
 
-/* ABI version of this header (major * 100 + minor). */
+/* ABI version of this header (major * 100 + minor): 101. */
 int moe_abi_version(void);
 
 /*
@@ -82,6 +82,14 @@ size_t moe_route_workspace_bytes(int32_t M, int32_t E);
  */
 size_t moe_workspace_bytes(int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k,
                            int32_t block);
+
+/*
+ * Token-tile height moe_forward uses for its grouped GEMMs at these sizes: 16 selects the
+ * weight-streaming kernels (few tokens per expert), 64 or 128 the LDS-tiled MFMA
+ * kernels.  Chosen by the expected tokens per expert, M * top_k / E, and whether I is a
+ * multiple of the tiled kernels' 256 act columns.  Host-only; 0 for invalid sizes.
+ */
+int32_t moe_gemm_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I);
 
 /*
  * Router (step 1).

@@ -36,6 +36,7 @@ _PROTOS = {
     "moe_align_capacity": (_sz, [_i32, _i32, _i32, _i32]),
     "moe_route_workspace_bytes": (_sz, [_i32, _i32]),
     "moe_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
+    "moe_gemm_tile_rows": (_i32, [_i32, _i32, _i32, _i32]),
     "moe_route": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p, _sz, _p]),
     "moe_align": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _p, _p, _p, _p]),
     "moe_expert_up": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -128,6 +129,10 @@ def moe_route_workspace_bytes(M: int, E: int) -> int:
 
 def moe_workspace_bytes(M: int, H: int, E: int, I: int, top_k: int, block: int) -> int:
     return int(load_library().moe_workspace_bytes(M, H, E, I, top_k, block))
+
+
+def moe_gemm_tile_rows(M: int, E: int, top_k: int, I: int) -> int:
+    return int(load_library().moe_gemm_tile_rows(M, E, top_k, I))
 
 
 def moe_route(x, router_w, router_bias, top_k: int, topk_ids, topk_w, workspace, stream=None):

@@ -92,7 +92,7 @@ const char* moe_strerror(int status) {
   }
 }
 
-int moe_abi_version(void) { return 100; }
+int moe_abi_version(void) { return 101; }
 
 size_t moe_align_capacity(int32_t M, int32_t top_k, int32_t E, int32_t block) {
   if (M < 0 || top_k < 1 || E < 1 || block < 1) return 0;
@@ -103,6 +103,11 @@ size_t moe_align_capacity(int32_t M, int32_t top_k, int32_t E, int32_t block) {
 size_t moe_route_workspace_bytes(int32_t M, int32_t E) {
   if (M < 0 || E < 1 || E > kMaxE) return 0;
   return round_up((size_t)M * E * sizeof(double), kAlign) + kAlign;
+}
+
+int32_t moe_gemm_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I) {
+  if (M < 0 || E < 1 || E > kMaxE || top_k < 1 || top_k > E || I < 64 || I % 64 != 0) return 0;
+  return gemm_tile_rows(M, E, top_k, I);
 }
 
 size_t moe_workspace_bytes(int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k,

@@ -54,7 +54,7 @@ def test_library_links_no_torch(B):
 
 
 def test_strerror_and_version(B):
-    assert B.moe_abi_version() == 100
+    assert B.moe_abi_version() == 101
     for s in (0, -1, -2, -3, -4, 17):
         assert isinstance(B.moe_strerror(s), str) and B.moe_strerror(s)
 
@@ -131,3 +131,18 @@ def test_route_align_finalize_validation(B):
     assert lib.moe_expert_up(p(16), p(16), p(16), p(16), p(16), 4, 256, 8, 512, 2, 16, 16, p(16), None) == -1
     assert lib.moe_expert_up(p(16), p(16), p(16), p(16), p(16), 4, 256, 8, 512, 2, 24, 240, p(16), None) == -2
     assert lib.moe_expert_down(p(16), p(16), p(16), p(16), p(16), 4, 256, 8, 512, 2, 16, 16, p(16), None) == -1
+
+
+def test_gemm_tile_rows_follows_tokens_per_expert(B):
+    # expected tokens per expert M * top_k / E: < 4 -> 16-row streaming kernels,
+    # < 32 -> 64-row tiles, else 128-row tiles; I must be a multiple of 256 for tiles
+    assert B.moe_gemm_tile_rows(8, 256, 16, 2048) == 16
+    assert B.moe_gemm_tile_rows(63, 256, 16, 2048) == 16
+    assert B.moe_gemm_tile_rows(64, 256, 16, 2048) == 64
+    assert B.moe_gemm_tile_rows(128, 256, 16, 2048) == 64
+    assert B.moe_gemm_tile_rows(512, 256, 16, 2048) == 128
+    assert B.moe_gemm_tile_rows(2048, 256, 16, 2048) == 128
+    assert B.moe_gemm_tile_rows(2048, 256, 16, 192) == 16
+    assert B.moe_gemm_tile_rows(2048, 256, 16, 100) == 0
+    assert B.moe_gemm_tile_rows(8, 0, 1, 2048) == 0
+    assert B.moe_gemm_tile_rows(-1, 256, 16, 2048) == 0

@@ -11,8 +11,10 @@ six HIP events per step around the five kernels for the per-kernel durations (an
 between two kernels adds a few microseconds of idle, so that pass is not the headline).  `value` is tokens/s
 of the headline workload (decode, M=8); `sweep` holds the same measurement at M=128,
 512 and 2048 on the same weights.  `roofline` is for the dominant kernel (the grouped
-up-GEMM + SwiGLU, which streams W13) against the 8 TB/s HBM peak; `cpu_baseline` is the
-CPU oracle timed on a bounded sample of the decode workload.
+up-GEMM + SwiGLU, which streams W13) against the 8 TB/s HBM peak, and against the read
+rate this device reaches with a plain streaming read (`measured_read_peak`, from the
+probe library built next to the layer's); `cpu_baseline` is the CPU oracle timed on a
+bounded sample of the decode workload.
 """
 from __future__ import annotations
 
@@ -146,6 +148,41 @@ def cpu_baseline(mi, torch):
     }
 
 
+def read_probe_gbs(torch, dev, gib=4, reps=5):
+    """Achievable HBM read rate on this device: best of `reps` timed passes of the read
+    probe (prefill_sigmoid_router_amd/probe/read_bw.hip) over a `gib` GiB buffer."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "prefill_sigmoid_router_amd", "libmoe_probe.so"))
+    lib.moe_probe_read.restype = ctypes.c_int
+    lib.moe_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
+                                   ctypes.c_void_p]
+    lib.moe_probe_read_grid.restype = ctypes.c_int
+    n = gib << 30
+    buf = torch.ones(n // 4, dtype=torch.int32, device=dev)
+    sink = torch.empty(lib.moe_probe_read_grid(), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def once():
+        st = lib.moe_probe_read(ctypes.c_void_p(buf.data_ptr()), n,
+                                ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"moe_probe_read failed with status {st}")
+
+    once()
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(reps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        once()
+        b.record(stream)
+        b.synchronize()
+        best = min(best, a.elapsed_time(b))
+    del buf, sink
+    return n / (best * 1e-3) / 1e9
+
+
 def load_traffic():
     try:
         with open(TRAFFIC_FILE) as f:
@@ -213,6 +250,8 @@ def main():
                              max(1, args.warmup // 2), dev)
             sweep[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
 
+    print("bench: timing the HBM read probe", file=sys.stderr, flush=True)
+    read_gbs = read_probe_gbs(torch, dev)
     traffic = load_traffic()
     rows = B.moe_gemm_tile_rows(head.M, head.E, head.top_k, head.I)
     up_kernel = ("expert_up_stream_kernel<4>" if rows == 16
@@ -226,6 +265,8 @@ def main():
         "traffic": None if traffic is None else traffic.get("traffic_gbs"),
         "traffic_bytes_per_launch": None if traffic is None else traffic.get("traffic_bytes_per_launch"),
         "algorithmic_bytes_per_launch": res["up_bytes"], "avg_launch_us": round(res["up_us"], 2),
+        "measured_read_peak": round(read_gbs, 1),
+        "frac_of_measured_read": round(res["up_gbs"] / read_gbs, 4),
     }
     cpu = None
     if not args.no_cpu_baseline:
@@ -254,6 +295,7 @@ def main():
         "stages_us": res["stages_us"],
         "layer_hbm_frac": round(res["layer_hbm_frac"], 4),
         "layer_gbs": round(res["layer_gbs"], 1),
+        "layer_frac_of_measured_read": round(res["layer_gbs"] / read_gbs, 4),
         "roofline": roof,
         "cpu_baseline": cpu,
         "sweep": sweep,

@@ -3,7 +3,8 @@
     python -m prefill_sigmoid_router_amd.build
 
 compiles every .hip file under csrc/ with hipcc into csrc objects and links them into
-prefill_sigmoid_router_amd/libmoe_mi355x.so (in-tree, next to the Python binding).  It
+prefill_sigmoid_router_amd/libmoe_mi355x.so (in-tree, next to the Python binding), and
+probe/ into libmoe_probe.so (the read-bandwidth probe the benchmark loads).  It
 cross-compiles without a GPU.
 """
 from __future__ import annotations
@@ -20,6 +21,8 @@ CSRC = os.path.join(PKG_DIR, "csrc")
 BUILD_DIR = os.path.join(REPO_DIR, "_build")
 LIB_NAME = "libmoe_mi355x.so"
 LIB_PATH = os.path.join(PKG_DIR, LIB_NAME)
+PROBE_DIR = os.path.join(PKG_DIR, "probe")
+PROBE_PATH = os.path.join(PKG_DIR, "libmoe_probe.so")
 ARCH = "gfx950"
 
 HIPCC_FLAGS = [
@@ -38,15 +41,21 @@ def _hipcc() -> str:
     raise RuntimeError("hipcc not found; the ROCm toolchain is required to build the library")
 
 
-def sources():
-    return sorted(os.path.join(CSRC, f) for f in os.listdir(CSRC) if f.endswith(".hip"))
+def sources(folder: str = CSRC):
+    return sorted(os.path.join(folder, f) for f in os.listdir(folder) if f.endswith(".hip"))
 
 
 def build(verbose: bool = False, jobs: int = 4) -> str:
+    lib = _build_one(sources(CSRC), LIB_PATH, "lib", verbose, jobs)
+    _build_one(sources(PROBE_DIR), PROBE_PATH, "probe", verbose, jobs)
+    return lib
+
+
+def _build_one(srcs, out_path: str, tag: str, verbose: bool, jobs: int) -> str:
     hipcc = _hipcc()
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    srcs = sources()
-    objs = [os.path.join(BUILD_DIR, os.path.basename(s)[:-4] + ".o") for s in srcs]
+    obj_dir = os.path.join(BUILD_DIR, tag)
+    os.makedirs(obj_dir, exist_ok=True)
+    objs = [os.path.join(obj_dir, os.path.basename(s)[:-4] + ".o") for s in srcs]
 
     def compile_one(pair):
         src, obj = pair
@@ -64,15 +73,15 @@ def build(verbose: bool = False, jobs: int = 4) -> str:
 
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
         list(ex.map(compile_one, zip(srcs, objs)))
-    tmp = LIB_PATH + ".tmp"
+    tmp = out_path + ".tmp"
     cmd = [hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", tmp]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed:\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
-    return LIB_PATH
+    os.replace(tmp, out_path)
+    return out_path
 
 
 if __name__ == "__main__":

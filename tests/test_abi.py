@@ -146,3 +146,14 @@ def test_gemm_tile_rows_follows_tokens_per_expert(B):
     assert B.moe_gemm_tile_rows(2048, 256, 16, 100) == 0
     assert B.moe_gemm_tile_rows(8, 0, 1, 2048) == 0
     assert B.moe_gemm_tile_rows(-1, 256, 16, 2048) == 0
+
+
+def test_read_probe_library_is_built_apart_from_the_layer(B):
+    probe = os.path.join(os.path.dirname(B.library_path()), "libmoe_probe.so")
+    out = subprocess.run(["nm", "-D", "--defined-only", probe], capture_output=True, text=True,
+                         check=True).stdout
+    names = set(line.split()[-1] for line in out.splitlines() if line.strip())
+    assert {"moe_probe_read", "moe_probe_read_grid"} <= names
+    layer = subprocess.run(["nm", "-D", "--defined-only", B.library_path()], capture_output=True,
+                           text=True, check=True).stdout
+    assert "moe_probe_read" not in layer

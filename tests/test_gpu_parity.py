@@ -48,6 +48,13 @@ SMALL = {
     "one_token": mi.LayerConfig("one_token", M=1, H=512, E=64, top_k=8, I=256, block=16),
     "single_expert": mi.LayerConfig("single_expert", M=9, H=256, E=1, top_k=1, I=128, block=16),
     "all_experts": mi.LayerConfig("all_experts", M=5, H=128, E=6, top_k=6, I=64, block=16),
+    # many tokens per expert: moe_forward runs the LDS-tiled GEMMs (moe_gemm_tile_rows 128 /
+    # 64) with a partial last K chunk (H % 64 = 16), a partial last N tile of the down GEMM
+    # (H < 512 columns per tile) and hot experts spanning several token tiles
+    "tiled128_zipf": mi.LayerConfig("tiled128_zipf", M=300, H=720, E=8, top_k=4, I=256,
+                                    block=64, zipf_s=1.0),
+    "tiled64_zipf": mi.LayerConfig("tiled64_zipf", M=40, H=336, E=16, top_k=4, I=512, block=16,
+                                   zipf_s=1.0),
 }
 FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048"]
 
@@ -372,7 +379,10 @@ def test_finalize_closed_form_and_oracle(B, dev):
 @pytest.mark.parametrize("name", list(SMALL))
 def test_forward_small(B, dev, name):
     cfg = SMALL[name]
-    print(f"forward parity {name}", flush=True)
+    rows = B.moe_gemm_tile_rows(cfg.M, cfg.E, cfg.top_k, cfg.I)
+    print(f"forward parity {name} (GEMM token tile {rows})", flush=True)
+    if name.startswith("tiled"):
+        assert rows == int(name[5:name.index("_")])
     L = mi.make_layer(cfg, device=dev, seed=3)
     r = _run_forward(B, L, dev)
     ref = orc.forward(bits(L["x"]), bits(L["router_w"]), _bias_np(L), bits(L["w13"]), bits(L["w2"]),

@@ -72,7 +72,10 @@ int moe_abi_version(void);
  */
 size_t moe_align_capacity(int32_t M, int32_t top_k, int32_t E, int32_t block);
 
-/* Workspace bytes moe_route needs (fp64 keys [M, E]).  0 for invalid sizes. */
+/*
+ * Workspace bytes moe_route needs: router scratch of 32 bytes per (token, expert) (fp64
+ * keys, or fp32 partial logits and |x|.|w| sums for many tokens).  0 for invalid sizes.
+ */
 size_t moe_route_workspace_bytes(int32_t M, int32_t E);
 
 /*

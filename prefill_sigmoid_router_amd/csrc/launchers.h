@@ -7,7 +7,10 @@
 
 namespace moe {
 
-// Router keys (fp64, [M, E] in `keys`) then top-k ids / renormalised sigmoid weights.
+// Router: top-k ids / renormalised sigmoid weights.  `keys` is scratch of
+// kRouteScratchPerPair bytes per (token, expert): fp64 keys below the many-token
+// threshold, fp32 partial logits and |x|.|w| sums above it.
+constexpr int kRouteScratchPerPair = 32;
 hipError_t launch_route(const uint16_t* x, const uint16_t* wr, const float* bias, int M, int H,
                         int E, int top_k, int32_t* ids, float* w, double* keys, hipStream_t s);
 

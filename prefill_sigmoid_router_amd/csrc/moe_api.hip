@@ -47,7 +47,7 @@ Layout layout_of(int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k, int3
   const size_t n = (size_t)M * top_k;
   const size_t cap = capacity_of(M, top_k, E, block);
   size_t off = 0;
-  L.keys = off;   off += round_up((size_t)M * E * sizeof(double), kAlign);
+  L.keys = off;   off += round_up((size_t)M * E * moe::kRouteScratchPerPair, kAlign);
   L.ids = off;    off += round_up(n * sizeof(int32_t), kAlign);
   L.w = off;      off += round_up(n * sizeof(float), kAlign);
   L.sorted = off; off += round_up(cap * sizeof(int32_t), kAlign);
@@ -102,7 +102,7 @@ size_t moe_align_capacity(int32_t M, int32_t top_k, int32_t E, int32_t block) {
 
 size_t moe_route_workspace_bytes(int32_t M, int32_t E) {
   if (M < 0 || E < 1 || E > kMaxE) return 0;
-  return round_up((size_t)M * E * sizeof(double), kAlign) + kAlign;
+  return round_up((size_t)M * E * moe::kRouteScratchPerPair, kAlign) + kAlign;
 }
 
 int32_t moe_gemm_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I) {

@@ -14,6 +14,8 @@
 //                          token's keys (key descending, ties to the lower id) by
 //                          counting, picks = ranks below k; sigmoid and
 //                          renormalisation in fp64.
+#include <algorithm>
+
 #include "device_common.h"
 #include "launchers.h"
 
@@ -96,8 +98,7 @@ constexpr int kTopkThreads = 256;
 #define MOE_ROUTE_CERTIFIED_MIN 256
 #endif
 constexpr int kRouteCertifiedMinTokens = MOE_ROUTE_CERTIFIED_MIN;
-constexpr int kSelectMaxH = 16384;  // largest H whose x row the select kernel stages in LDS
-constexpr int kSelChunks = 16;      // 16-byte chunks per lane in flight per candidate batch
+constexpr int kSelChunks = 8;       // 16-byte chunks per lane in flight per candidate batch
 
 // Number of entries of vals[0..n) ahead of (v, id): larger, or equal with a lower index.
 // Eight LDS values are requested per step so the loop is not bound by LDS latency.
@@ -175,73 +176,142 @@ __global__ __launch_bounds__(kTopkThreads) void router_topk_kernel(const double*
 // Certified fast path for many tokens.
 //
 // 1. router_logits_mfma_kernel: fp32 logits L = x . Wr^T on bf16 MFMA, together with
-//    A = sum_h |x_h| |w_h| from the same fragments with the sign bits cleared.  Products
-//    of two bf16 values are exact in fp32, so the only error is the fp32 summation.  A
-//    product passes at most 31 roundings inside its MFMA, one per later K step of its
-//    wave (at most H / 128 <= 128 for H <= 16384) and the 3 adds that join the waves:
-//    at most 162 roundings, so |L - exact| <= 162 * 2u * A even if the hardware truncates
-//    (u = 2^-24).  The selection uses d = 2^-14 A = 1024 u A, above that with margin,
-//    plus an absolute floor for flushed subnormal products.
-// 2. router_select_kernel, one workgroup per token: with lo = L + b - d and hi = L + b + d,
-//    T = the k-th largest lo.  An expert with hi < T has an exact key below at least k
-//    other exact keys, so it cannot be picked; every other expert is a candidate.  The
-//    candidates' keys are recomputed as fp64 dot products and ranked exactly as the fp64
-//    path ranks them (key descending, ties to the lower id).
+//    A = sum_h |x_h| |w_h| from the same fragments with the sign bits cleared, over P
+//    contiguous parts of K (one partial result per part).  Products of two bf16 values
+//    are exact in fp32, so the only error is the fp32 summation: a product passes at most
+//    31 roundings inside its MFMA and one per later 32-wide K step of its part, n =
+//    32 + ceil(Kpart / 32) in all.  With each rounding off by at most 2u (u = 2^-24, even
+//    if the hardware truncates), |L_p - exact_p| <= n 2u A_p (1 + 2^-10) for n <= 1024,
+//    and the computed A_p is within a factor (1 + 2^-10) of A_p.  The parts are added in
+//    fp64.
+// 2. router_select_kernel, one workgroup per token: with d = n 2^-23 A (1 + 2^-9) plus an
+//    absolute floor for flushed subnormal products and the fp64 key rounding, lo = L + b
+//    - d and hi = L + b + d, T = the k-th largest lo.  An expert with hi < T has an exact
+//    key below at least k other exact keys, so it cannot be picked; every other expert is
+//    a candidate.  The candidates' keys are recomputed as fp64 dot products and ranked
+//    exactly as the fp64 path ranks them (key descending, ties to the lower id).
 // ---------------------------------------------------------------------------------------
-constexpr int kLogitU = 4;
+constexpr int kLgTokens = 32;               // tokens per workgroup
+constexpr int kLgExperts = 64;              // experts per workgroup
+constexpr int kLgKC = 64;                   // K values per chunk: one 128-byte line per row
+constexpr int kLgStages = 4;
+constexpr int kLgCopies = (kLgTokens + kLgExperts) / 8;   // 1 KiB copies per chunk
+constexpr int kLgCPW = kLgCopies / 4;                     // per wave
+constexpr int kLgMaxParts = 4;
+static_assert(2 * kLgMaxParts * sizeof(float) <= kRouteScratchPerPair &&
+              sizeof(double) <= kRouteScratchPerPair, "router scratch per (token, expert)");
 
-// One workgroup per 16 experts x 16 tokens; its four waves take four contiguous quarters
-// of the 32-wide K steps and meet in LDS in a fixed order.
+template <int N>
+__device__ __forceinline__ void lg_wait_vmcnt() {
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// One workgroup per 64 experts x 32 tokens x one part of K.  The 96 rows of a 64-wide K
+// chunk (experts first, then tokens) are copied global -> LDS with global_load_lds_dwordx4,
+// 8 rows x one 128-byte line per copy, the 16-byte K chunks of a row XOR-swizzled
+// (slot = chunk ^ row % 8 ^ (row / 8) % 2) so every MFMA fragment is one conflict-free
+// ds_read_b128; a 4-chunk ring keeps 3 chunks in flight.  Wave w computes 16 tokens
+// (half w % 2) x 32 experts (half w / 2).
 __global__ __launch_bounds__(256) void router_logits_mfma_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, int M, int H, int E,
-    float* __restrict__ logits, float* __restrict__ absdot) {
-  __shared__ f32x4 part[3][2][kWave];
+    int kpart, float* __restrict__ logits, float* __restrict__ absdot) {
+  __shared__ __align__(16) unsigned char lds[kLgStages * kLgCopies * 1024];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 15, lg = lane >> 4;
-  const int e0 = blockIdx.x * 16;
-  const int t0 = blockIdx.y * 16;
-  const bool e_in = e0 + li < E;
-  const bool t_in = t0 + li < M;
-  const int nsteps = (H + 31) / 32;
-  const int s_lo = wave * nsteps / 4, s_hi = (wave + 1) * nsteps / 4;
-  const uint16_t* wrow = wr + (size_t)(e_in ? e0 + li : 0) * H + 8 * lg;
-  const uint16_t* xrow = x + (size_t)(t_in ? t0 + li : 0) * H + 8 * lg;
-  const u32x4 z4 = u32x4{0, 0, 0, 0};
+  const int e0 = blockIdx.x * kLgExperts;
+  const int t0 = blockIdx.y * kLgTokens;
+  const int part = blockIdx.z;
+  const int kbeg = min(H, part * kpart), kend = min(H, kbeg + kpart);
+  const int klen = kend - kbeg;
+
+  const uint16_t* src[kLgCPW];
+  bool on[kLgCPW];
+  int qk[kLgCPW];
+#pragma unroll
+  for (int i = 0; i < kLgCPW; ++i) {
+    const int f = wave * kLgCPW + i;
+    const int r = 8 * f + (lane >> 3);
+    qk[i] = (lane & 7) ^ (lane >> 3) ^ (f & 1);
+    const uint16_t* row;
+    if (r < kLgExperts) {
+      on[i] = e0 + r < E;
+      row = wr + (size_t)(on[i] ? e0 + r : 0) * H;
+    } else {
+      on[i] = t0 + r - kLgExperts < M;
+      row = x + (size_t)(on[i] ? t0 + r - kLgExperts : 0) * H;
+    }
+    src[i] = row + kbeg + 8 * qk[i];
+  }
+  const int nch = (klen + kLgKC - 1) / kLgKC;
+  const int ndma = klen / kLgKC;
+  auto issue = [&](int c) {
+    unsigned char* base = lds + (size_t)(c % kLgStages) * kLgCopies * 1024;
+    if (c < ndma) {
+#pragma unroll
+      for (int i = 0; i < kLgCPW; ++i)
+        __builtin_amdgcn_global_load_lds(
+            (__attribute__((address_space(1))) void*)(src[i] + c * kLgKC),
+            (__attribute__((address_space(3))) void*)(base + (wave * kLgCPW + i) * 1024), 16, 0, 0);
+    } else {  // partial chunk: zero-filled through registers
+#pragma unroll
+      for (int i = 0; i < kLgCPW; ++i) {
+        const int k = kbeg + c * kLgKC + 8 * qk[i];
+        const u32x4 v = (on[i] && k + 8 <= kend) ? ld16(src[i] + c * kLgKC) : u32x4{0, 0, 0, 0};
+        *reinterpret_cast<u32x4*>(base + (size_t)(wave * kLgCPW + i) * 1024 + lane * 16) = v;
+      }
+    }
+  };
+  const int frag_off = (li >> 3) * 1024 + (li & 7) * 128;
+  auto frag = [&](int c, int t, int ks) -> u32x4 {
+    const int q = (lg + 4 * ks) ^ (li & 7) ^ (li >> 3);
+    return *reinterpret_cast<const u32x4*>(lds + (size_t)(c % kLgStages) * kLgCopies * 1024 +
+                                           t * 2048 + frag_off + q * 16);
+  };
+
   const u32x4 absmask = u32x4{0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu, 0x7fff7fffu};
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f}, aab = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int st = s_lo; st < s_hi; st += kLogitU) {
-    u32x4 wv[kLogitU], xv[kLogitU];
+  const int ttile = kLgExperts / 16 + (wave & 1);   // token row tile in the stage
+  const int etile = 2 * (wave >> 1);                // first of two expert row tiles
+  f32x4 acc[2], aab[2];
 #pragma unroll
-    for (int u = 0; u < kLogitU; ++u) {
-      const int k = (st + u) * 32;
-      const bool in = st + u < s_hi && k + 8 * lg + 8 <= H;
-      wv[u] = (in && e_in) ? ld16(wrow + k) : z4;
-      xv[u] = (in && t_in) ? ld16(xrow + k) : z4;
-    }
+  for (int j = 0; j < 2; ++j) acc[j] = aab[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
 #pragma unroll
-    for (int u = 0; u < kLogitU; ++u) {
-      acc = mfma16x16x32(wv[u], xv[u], acc);
-      aab = mfma16x16x32(wv[u] & absmask, xv[u] & absmask, aab);
+  for (int p = 0; p < kLgStages - 1; ++p)
+    if (p < nch) issue(p);
+  for (int c = 0; c < nch; ++c) {
+    // this wave's whole chunks issued after c: min(2, ndma-1-c)
+    const int after = c < ndma ? min(kLgStages - 2, ndma - 1 - c) : 0;
+    if (after >= 2) lg_wait_vmcnt<2 * kLgCPW>();
+    else if (after == 1) lg_wait_vmcnt<kLgCPW>();
+    else lg_wait_vmcnt<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (c + kLgStages - 1 < nch) issue(c + kLgStages - 1);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const u32x4 xb = frag(c, ttile, ks);
+      const u32x4 xa = xb & absmask;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const u32x4 wa = frag(c, etile + j, ks);
+        acc[j] = mfma16x16x32(wa, xb, acc[j]);
+        aab[j] = mfma16x16x32(wa & absmask, xa, aab[j]);
+      }
     }
   }
-  if (wave > 0) {
-    part[wave - 1][0][lane] = acc;
-    part[wave - 1][1][lane] = aab;
-  }
-  __syncthreads();
-  if (wave > 0) return;
-  acc = ((acc + part[0][0][lane]) + part[1][0][lane]) + part[2][0][lane];
-  aab = ((aab + part[0][1][lane]) + part[1][1][lane]) + part[2][1][lane];
-  // D rows 4*lg+q = experts, column li = token
-  if (t_in) {
-    const int e = e0 + 4 * lg;
-    float* lrow = logits + (size_t)(t0 + li) * E;
-    float* arow = absdot + (size_t)(t0 + li) * E;
+  // D rows 4*lg+q = experts of tile etile+j, column li = token
+  const int t = t0 + 16 * (wave & 1) + li;
+  if (t < M) {
+    float* lrow = logits + ((size_t)part * M + t) * E;
+    float* arow = absdot + ((size_t)part * M + t) * E;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if (e + q < E) {
-        lrow[e + q] = acc[q];
-        arow[e + q] = aab[q];
+    for (int j = 0; j < 2; ++j) {
+      const int e = e0 + 16 * (etile + j) + 4 * lg;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (e + q < E) {
+          lrow[e + q] = acc[j][q];
+          arow[e + q] = aab[j][q];
+        }
       }
     }
   }
@@ -250,28 +320,36 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(
 template <int SL>
 __global__ __launch_bounds__(kTopkThreads) void router_select_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias,
-    const float* __restrict__ logits, const float* __restrict__ absdot, int M, int H, int E,
-    int top_k, int32_t* __restrict__ ids, float* __restrict__ weights) {
-  __shared__ double s_lo[kTopkMaxE];
-  __shared__ double s_key[kTopkMaxE];     // fp64 keys of the candidates, by candidate slot
-  __shared__ int s_cand[kTopkMaxE];       // expert id of each candidate slot
-  __shared__ double s_sig[kTopkMaxE];
+    const float* __restrict__ logits, const float* __restrict__ absdot, int parts, int nround,
+    int M, int H, int E, int top_k, int32_t* __restrict__ ids, float* __restrict__ weights) {
+  // LDS sized by the launch: the token's x row, then per expert the lower bound, the
+  // candidates' fp64 keys and ids, and the picks' sigmoids
+  extern __shared__ __align__(16) unsigned char sel_lds[];
+  u32x4* s_x = reinterpret_cast<u32x4*>(sel_lds);
+  double* s_lo = reinterpret_cast<double*>(sel_lds + (size_t)H * 2);
+  double* s_key = s_lo + E;     // fp64 keys of the candidates, by candidate slot
+  double* s_sig = s_key + E;
+  int* s_cand = reinterpret_cast<int*>(s_sig + E);   // expert id of each candidate slot
   __shared__ int s_wave_cnt[kTopkThreads / kWave];
   __shared__ double s_T;
-  __shared__ u32x4 s_x[kSelectMaxH / 8];  // the token's x row
   const int t = blockIdx.x, tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   for (int ch = tid; ch < (H >> 3); ch += kTopkThreads) s_x[ch] = ld16(x + (size_t)t * H + (size_t)ch * 8);
 
+  const double rel = (double)nround * 0x1p-23 * (1.0 + 0x1p-9);
   double lo[SL], hi[SL];
 #pragma unroll
   for (int s = 0; s < SL; ++s) {
     const int e = tid + kTopkThreads * s;
     lo[s] = hi[s] = 0.0;
     if (e < E) {
-      const double key = (double)logits[(size_t)t * E + e] + (bias ? (double)bias[e] : 0.0);
-      const double d = (double)absdot[(size_t)t * E + e] * 0x1p-14 * (1.0 + 0x1p-20) +
-                       fabs(key) * 0x1p-50 + (double)H * 0x1p-126 + 1e-300;
+      double l = 0.0, a = 0.0;
+      for (int p = 0; p < parts; ++p) {
+        l += (double)logits[((size_t)p * M + t) * E + e];
+        a += (double)absdot[((size_t)p * M + t) * E + e];
+      }
+      const double key = l + (bias ? (double)bias[e] : 0.0);
+      const double d = a * rel + fabs(key) * 0x1p-50 + (double)H * 0x1p-126 + 1e-300;
       lo[s] = key - d;
       hi[s] = key + d;
       s_lo[e] = lo[s];
@@ -404,15 +482,23 @@ hipError_t launch_route(const uint16_t* x, const uint16_t* wr, const float* bias
   hipError_t err;
   const int per_thread = (E + kTopkThreads - 1) / kTopkThreads;
   if (M >= kRouteCertifiedMinTokens) {
-    // the fp64 key buffer [M, E] doubles as the fp32 logits and |x|.|w| buffers
+    // K is cut into parts (whole 64-wide chunks) so that about 512 workgroups run; the
+    // workspace holds parts x [M, E] fp32 logits, then parts x [M, E] fp32 |x|.|w|
+    const int base = ((E + kLgExperts - 1) / kLgExperts) * ((M + kLgTokens - 1) / kLgTokens);
+    const int parts = std::min(kLgMaxParts, std::max(1, (512 + base - 1) / base));
+    const int chunks = (H + kLgKC - 1) / kLgKC;
+    const int kpart = ((chunks + parts - 1) / parts) * kLgKC;
+    const int nround = 32 + (kpart + 31) / 32;
     float* logits = reinterpret_cast<float*>(keys);
-    float* absdot = logits + (size_t)M * E;
-    hipLaunchKernelGGL(router_logits_mfma_kernel, dim3((E + 15) / 16, (M + 15) / 16), dim3(256), 0,
-                       s, x, wr, M, H, E, logits, absdot);
+    float* absdot = logits + (size_t)parts * M * E;
+    hipLaunchKernelGGL(router_logits_mfma_kernel,
+                       dim3((E + kLgExperts - 1) / kLgExperts, (M + kLgTokens - 1) / kLgTokens, parts),
+                       dim3(256), 0, s, x, wr, M, H, E, kpart, logits, absdot);
     if ((err = hipGetLastError()) != hipSuccess) return err;
-#define MOE_SELECT(SLV)                                                                          \
-  hipLaunchKernelGGL((router_select_kernel<SLV>), dim3(M), dim3(kTopkThreads), 0, s, x, wr, bias, \
-                     logits, absdot, M, H, E, top_k, ids, w)
+    const size_t lds = (size_t)H * 2 + (size_t)E * (3 * sizeof(double) + sizeof(int));
+#define MOE_SELECT(SLV)                                                                     \
+  hipLaunchKernelGGL((router_select_kernel<SLV>), dim3(M), dim3(kTopkThreads), lds, s, x, wr, \
+                     bias, logits, absdot, parts, nround, M, H, E, top_k, ids, w)
     if (per_thread <= 1) MOE_SELECT(1);
     else if (per_thread <= 2) MOE_SELECT(2);
     else MOE_SELECT(4);

@@ -2,7 +2,7 @@
 one MI355X, through the C ABI.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--workload decode_m8]
-                    [--no-sweep] [--no-cpu-baseline]
+                    [--no-sweep] [--no-cpu-baseline] [--no-mx]
 
 Prints ONE JSON line.  A step is one moe_forward call (all five kernels) over resident
 inputs of the workload; K steps are timed between two synchronisations (wall clock and
@@ -14,7 +14,9 @@ of the headline workload (decode, M=8); `sweep` holds the same measurement at M=
 up-GEMM + SwiGLU, which streams W13) against the 8 TB/s HBM peak, and against the read
 rate this device reaches with a plain streaming read (`measured_read_peak`, from the
 probe library built next to the layer's); `cpu_baseline` is the CPU oracle timed on a
-bounded sample of the decode workload.
+bounded sample of the decode workload.  `mxfp8_decode` times the same decode layer with
+the expert weights quantized to MXFP8 (moe_forward_mx); it is a separate measurement, not
+the headline, whose weights are bf16.
 """
 from __future__ import annotations
 
@@ -42,24 +44,32 @@ def source_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def layer_bytes(cfg, M, touched):
+def weight_bytes_per_value(mx):
+    """bf16: 2 bytes; MXFP8: one E4M3 byte plus one scale byte per 32 values."""
+    return 1 + 1 / 32 if mx else 2
+
+
+def layer_bytes(cfg, M, touched, mx=False):
     """Algorithmic HBM bytes of one layer: touched experts' W13+W2, the router weight,
     x, residual and out rows, and the norm weight."""
-    per_expert = 2 * cfg.I * cfg.H * 2 + cfg.H * cfg.I * 2
-    return touched * per_expert + cfg.E * cfg.H * 2 + 3 * M * cfg.H * 2 + cfg.H * 2
+    per_expert = 3 * cfg.I * cfg.H * weight_bytes_per_value(mx)
+    return int(touched * per_expert) + cfg.E * cfg.H * 2 + 3 * M * cfg.H * 2 + cfg.H * 2
 
 
-def up_bytes(cfg, M, touched):
+def up_bytes(cfg, M, touched, mx=False):
     """Algorithmic bytes of the up kernel: W13 of every touched expert, each token's x
     row once, and one bf16 act row per (token, pick)."""
-    return touched * 2 * cfg.I * cfg.H * 2 + M * cfg.H * 2 + M * cfg.top_k * cfg.I * 2
+    return (int(touched * 2 * cfg.I * cfg.H * weight_bytes_per_value(mx)) + M * cfg.H * 2
+            + M * cfg.top_k * cfg.I * 2)
 
 
 def layer_flops(cfg, M):
     return 2 * M * cfg.E * cfg.H + 6 * M * cfg.top_k * cfg.H * cfg.I
 
 
-def run_workload(B, mi, torch, cfg, weights, steps, warmup, dev):
+def run_workload(B, mi, torch, cfg, weights, steps, warmup, dev, mx=None):
+    """Times moe_forward (bf16 experts), or moe_forward_mx when `mx` holds the MXFP8
+    (w13 codes, w13 scales, w2 codes, w2 scales)."""
     L = mi.make_layer(cfg, device=dev, seed=0, with_experts=False)
     L.update(weights)
     M, H, E, I, k, blk = cfg.M, cfg.H, cfg.E, cfg.I, cfg.top_k, cfg.block
@@ -70,9 +80,14 @@ def run_workload(B, mi, torch, cfg, weights, steps, warmup, dev):
     stream = torch.cuda.current_stream()
 
     def step(events=None):
-        B.moe_forward(L["x"], L["router_w"], L["router_bias"], L["w13"], L["w2"], L["residual"],
-                      L["norm_w"], L["eps"], k, blk, out, ws, topk_ids_out=ids,
-                      stage_events=events, stream=stream)
+        if mx is None:
+            B.moe_forward(L["x"], L["router_w"], L["router_bias"], L["w13"], L["w2"],
+                          L["residual"], L["norm_w"], L["eps"], k, blk, out, ws,
+                          topk_ids_out=ids, stage_events=events, stream=stream)
+        else:
+            B.moe_forward_mx(L["x"], L["router_w"], L["router_bias"], *mx, L["residual"],
+                             L["norm_w"], L["eps"], k, blk, out, ws, topk_ids_out=ids,
+                             stage_events=events, stream=stream)
 
     for _ in range(warmup):
         step()
@@ -99,8 +114,8 @@ def run_workload(B, mi, torch, cfg, weights, steps, warmup, dev):
     ms = max(wall_ms, span_ms)
     touched = int(torch.unique(ids).numel())
     counts = torch.bincount(ids.flatten().long(), minlength=E)
-    lb = layer_bytes(cfg, M, touched)
-    ub = up_bytes(cfg, M, touched)
+    lb = layer_bytes(cfg, M, touched, mx is not None)
+    ub = up_bytes(cfg, M, touched, mx is not None)
     return {
         "M": M, "ms_per_step": ms, "us_per_layer": ms * 1e3, "tokens_per_s": M / (ms / 1e3),
         "wall_ms": wall_ms, "event_span_ms": span_ms,
@@ -202,6 +217,8 @@ def main():
     ap.add_argument("--workload", default="decode_m8")
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mx", action="store_true",
+                    help="skip the decode leg with MXFP8 expert weights")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -249,6 +266,29 @@ def main():
             r = run_workload(B, mi, torch, mi.CONFIGS[name], weights, max(3, args.steps // 2),
                              max(1, args.warmup // 2), dev)
             sweep[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+
+    mx_line = None
+    if not args.no_mx:
+        # the same decode layer with MXFP8 expert weights (quantized on the device)
+        print("bench: quantizing the experts to MXFP8 and timing decode_m8", file=sys.stderr,
+              flush=True)
+        mx = []
+        for name in ("w13", "w2"):
+            w = weights[name]
+            c = torch.empty(tuple(w.shape), dtype=torch.uint8, device=dev)
+            sc = torch.empty(tuple(w.shape[:-1]) + (w.shape[-1] // 32,), dtype=torch.uint8,
+                             device=dev)
+            B.moe_mx_quantize(w, c, sc)
+            mx += [c, sc]
+        torch.cuda.synchronize()
+        r = run_workload(B, mi, torch, mi.CONFIGS["decode_m8"], weights, args.steps, args.warmup,
+                         dev, mx=mx)
+        mx_line = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+        mx_line["weights"] = "MXFP8 (E4M3 + E8M0 per 32 values along K), activations bf16"
+        mx_line["up_kernel"] = "expert_up_mx_kernel<4>"
+        mx_line["up_hbm_frac"] = round(r["up_gbs"] / HBM_PEAK_GBS, 4)
+        del mx
+        torch.cuda.empty_cache()
 
     print("bench: timing the HBM read probe", file=sys.stderr, flush=True)
     read_gbs = read_probe_gbs(torch, dev)
@@ -299,6 +339,7 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "sweep": sweep,
+        "mxfp8_decode": mx_line,
     }
     print(json.dumps(line), flush=True)
 

@@ -61,7 +61,7 @@ enum {
 /* Human-readable text of a status code.  Never NULL; static storage. */
 const char* moe_strerror(int status);
 
-/* ABI version of this header (major * 100 + minor): 101. */
+/* ABI version of this header (major * 100 + minor): 102. */
 int moe_abi_version(void);
 
 /*
@@ -176,6 +176,49 @@ int moe_forward(const uint16_t* x, const uint16_t* router_w, const float* router
                 int32_t* sorted_ids_out, int32_t* block_expert_out, int32_t* num_padded_out,
                 void* workspace, size_t workspace_bytes,
                 const moe_event_t* stage_events, moe_stream_t stream);
+
+/*
+ * MXFP8 expert weights.  The AlphaMoE page (FlashInfer PR #6511 analysis, section 1)
+ * streams block-scaled narrow expert weights to cut the bytes of a decode step and gives
+ * no recipe; the one here is the OCP Microscaling (MX) v1.0 conversion with FP8 E4M3
+ * elements: each run of 32 consecutive values of a row (along K) gets one E8M0 scale
+ * byte b = s + 127 with s = floor(log2(max |v|)) - 8 (a run of zeros gets b = 0), and
+ * each value becomes the E4M3 code of v / 2^s, rounded to nearest even and clamped to
+ * +-448.  Dequantized values code * 2^s are exact bf16 numbers.  Only the expert weights
+ * are quantized; activations stay bf16.
+ *
+ * moe_mx_quantize:   w [rows, K] bf16 -> codes [rows, K] uint8 and scales
+ *                    [rows, K / 32] uint8.  K a multiple of 32; w and codes 16-byte
+ *                    aligned.  Values must be finite.  W13 [E, 2I, H] is rows = E * 2I,
+ *                    K = H; W2 [E, H, I] is rows = E * H, K = I.
+ * moe_mx_dequantize: the inverse map back to bf16 [rows, K], with the same conversion
+ *                    the MXFP8 GEMMs use.
+ * Both return MOE_ERR_INVALID_ARG for bad sizes or pointers; rows = 0 is a no-op.
+ */
+int moe_mx_quantize(const uint16_t* w, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                    moe_stream_t stream);
+int moe_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t K,
+                      uint16_t* w, moe_stream_t stream);
+
+/*
+ * moe_forward with MXFP8 expert weights: w13_codes [E, 2I, H] + w13_scales [E, 2I, H/32],
+ * w2_codes [E, H, I] + w2_scales [E, H, I/32] (as written by moe_mx_quantize) in place of
+ * w13 and w2; every other argument, the workspace and the outputs are those of
+ * moe_forward.  The result is the layer on the dequantized weights.  H must be a multiple
+ * of 256 and I of 128 (MOE_ERR_UNSUPPORTED otherwise).  The GEMMs are the weight-streaming
+ * kernels at every size: they fit decode (few tokens per expert); there are no LDS-tiled
+ * MXFP8 kernels for large batches.
+ */
+int moe_forward_mx(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
+                   const uint8_t* w13_codes, const uint8_t* w13_scales,
+                   const uint8_t* w2_codes, const uint8_t* w2_scales,
+                   const uint16_t* residual, const uint16_t* norm_w, float eps,
+                   int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k, int32_t block,
+                   uint16_t* out, uint16_t* residual_out,
+                   int32_t* topk_ids_out, float* topk_w_out,
+                   int32_t* sorted_ids_out, int32_t* block_expert_out, int32_t* num_padded_out,
+                   void* workspace, size_t workspace_bytes,
+                   const moe_event_t* stage_events, moe_stream_t stream);
 
 #ifdef __cplusplus
 }

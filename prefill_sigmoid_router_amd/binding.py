@@ -17,7 +17,8 @@ __all__ = [
     "MoeError", "load_library", "library_path", "EXPORTED_SYMBOLS",
     "moe_strerror", "moe_abi_version", "moe_align_capacity", "moe_route_workspace_bytes",
     "moe_workspace_bytes", "moe_route", "moe_align", "moe_expert_up", "moe_expert_down",
-    "moe_finalize", "moe_forward", "HipEvent",
+    "moe_finalize", "moe_forward", "moe_mx_quantize", "moe_mx_dequantize", "moe_forward_mx",
+    "HipEvent",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -47,6 +48,11 @@ _PROTOS = {
     "moe_forward": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, ctypes.c_float,
                                    _i32, _i32, _i32, _i32, _i32, _i32,
                                    _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
+    "moe_mx_quantize": (ctypes.c_int, [_p, ctypes.c_int64, _i32, _p, _p, _p]),
+    "moe_mx_dequantize": (ctypes.c_int, [_p, _p, ctypes.c_int64, _i32, _p, _p]),
+    "moe_forward_mx": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float,
+                                      _i32, _i32, _i32, _i32, _i32, _i32,
+                                      _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
 }
 EXPORTED_SYMBOLS = tuple(_PROTOS)
 
@@ -252,6 +258,78 @@ def moe_forward(x, router_w, router_bias, w13, w2, residual, norm_w, eps: float,
         _ptr(norm_w), float(eps), M, H, E, I, top_k, block, _ptr(out), _ptr(residual_out),
         _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(sorted_ids_out), _ptr(block_expert_out),
         _ptr(num_padded_out), _ptr(workspace), workspace.numel(), ev, _stream(stream)))
+
+
+def moe_mx_quantize(w, codes, scales, stream=None):
+    """w [..., K] bf16 -> codes [..., K] uint8, scales [..., K / 32] uint8 (MXFP8)."""
+    _need(w, "w", torch.bfloat16)
+    K = w.shape[-1]
+    rows = w.numel() // K if K else 0
+    _need(codes, "codes", torch.uint8, tuple(w.shape))
+    _need(scales, "scales", torch.uint8, tuple(w.shape[:-1]) + (K // 32,))
+    _check("moe_mx_quantize", load_library().moe_mx_quantize(
+        _ptr(w), rows, K, _ptr(codes), _ptr(scales), _stream(stream)))
+
+
+def moe_mx_dequantize(codes, scales, w, stream=None):
+    """codes [..., K] uint8 + scales [..., K / 32] uint8 -> w [..., K] bf16."""
+    _need(codes, "codes", torch.uint8)
+    K = codes.shape[-1]
+    rows = codes.numel() // K if K else 0
+    _need(scales, "scales", torch.uint8, tuple(codes.shape[:-1]) + (K // 32,))
+    _need(w, "w", torch.bfloat16, tuple(codes.shape))
+    _check("moe_mx_dequantize", load_library().moe_mx_dequantize(
+        _ptr(codes), _ptr(scales), rows, K, _ptr(w), _stream(stream)))
+
+
+def moe_forward_mx(x, router_w, router_bias, w13_codes, w13_scales, w2_codes, w2_scales,
+                   residual, norm_w, eps: float, top_k: int, block: int, out, workspace,
+                   residual_out=None, topk_ids_out=None, topk_w_out=None, sorted_ids_out=None,
+                   block_expert_out=None, num_padded_out=None,
+                   stage_events: Optional[Sequence["HipEvent"]] = None, stream=None):
+    M, H = x.shape
+    E, two_i, _ = w13_codes.shape
+    I = two_i // 2
+    _need(x, "x", torch.bfloat16)
+    _need(router_w, "router_w", torch.bfloat16, (E, H))
+    if router_bias is not None:
+        _need(router_bias, "router_bias", torch.float32, (E,))
+    _need(w13_codes, "w13_codes", torch.uint8, (E, 2 * I, H))
+    _need(w13_scales, "w13_scales", torch.uint8, (E, 2 * I, H // 32))
+    _need(w2_codes, "w2_codes", torch.uint8, (E, H, I))
+    _need(w2_scales, "w2_scales", torch.uint8, (E, H, I // 32))
+    _need(residual, "residual", torch.bfloat16, (M, H))
+    _need(norm_w, "norm_w", torch.bfloat16, (H,))
+    _need(out, "out", torch.bfloat16, (M, H))
+    _need(workspace, "workspace", torch.uint8)
+    if residual_out is not None:
+        _need(residual_out, "residual_out", torch.bfloat16, (M, H))
+    cap = moe_align_capacity(M, top_k, E, block)
+    if topk_ids_out is not None:
+        _need(topk_ids_out, "topk_ids_out", torch.int32, (M, top_k))
+    if topk_w_out is not None:
+        _need(topk_w_out, "topk_w_out", torch.float32, (M, top_k))
+    if sorted_ids_out is not None:
+        _need(sorted_ids_out, "sorted_ids_out", torch.int32)
+        if sorted_ids_out.numel() < cap:
+            raise ValueError("sorted_ids_out smaller than the plan capacity")
+    if block_expert_out is not None:
+        _need(block_expert_out, "block_expert_out", torch.int32)
+        if block_expert_out.numel() < cap // block:
+            raise ValueError("block_expert_out smaller than capacity / block")
+    if num_padded_out is not None:
+        _need(num_padded_out, "num_padded_out", torch.int32)
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != 6:
+            raise ValueError("stage_events must hold 6 events")
+        ev = (ctypes.c_void_p * 6)(*[e.handle for e in stage_events])
+    _check("moe_forward_mx", load_library().moe_forward_mx(
+        _ptr(x), _ptr(router_w), _ptr(router_bias), _ptr(w13_codes), _ptr(w13_scales),
+        _ptr(w2_codes), _ptr(w2_scales), _ptr(residual), _ptr(norm_w), float(eps), M, H, E, I,
+        top_k, block, _ptr(out), _ptr(residual_out), _ptr(topk_ids_out), _ptr(topk_w_out),
+        _ptr(sorted_ids_out), _ptr(block_expert_out), _ptr(num_padded_out), _ptr(workspace),
+        workspace.numel(), ev, _stream(stream)))
 
 
 # ---------------------------------------------------------------------------------------

@@ -47,6 +47,21 @@ __device__ __forceinline__ f32x4 mfma16x16x32(u32x4 a, u32x4 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
+// MXFP8 weights: 16 E4M3 codes (K values k..k+15 of one row, all in one 32-value scale
+// block) and the block's E8M0 scale byte -> the two bf16 MFMA fragments of K values
+// k..k+7 (lo) and k+8..k+15 (hi).  The products code * 2^(byte - 127) are exact in bf16.
+__device__ __forceinline__ void mx_dequant16(u32x4 codes, uint32_t scale_byte, u32x4& lo,
+                                             u32x4& hi) {
+  const float scale = __uint_as_float(scale_byte ? scale_byte << 23 : 0x00400000u);
+#define MOE_CVT(word, high) \
+  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(word, scale, high))
+  lo = u32x4{MOE_CVT(codes[0], false), MOE_CVT(codes[0], true), MOE_CVT(codes[1], false),
+             MOE_CVT(codes[1], true)};
+  hi = u32x4{MOE_CVT(codes[2], false), MOE_CVT(codes[2], true), MOE_CVT(codes[3], false),
+             MOE_CVT(codes[3], true)};
+#undef MOE_CVT
+}
+
 template <typename T>
 __device__ __forceinline__ T wave_sum(T v) {
 #pragma unroll

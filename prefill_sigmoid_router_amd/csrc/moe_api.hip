@@ -92,7 +92,7 @@ const char* moe_strerror(int status) {
   }
 }
 
-int moe_abi_version(void) { return 101; }
+int moe_abi_version(void) { return 102; }
 
 size_t moe_align_capacity(int32_t M, int32_t top_k, int32_t E, int32_t block) {
   if (M < 0 || top_k < 1 || E < 1 || block < 1) return 0;
@@ -197,19 +197,38 @@ int moe_finalize(const float* y, const float* topk_w, const uint16_t* residual,
                                          residual_out, (hipStream_t)stream));
 }
 
-int moe_forward(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
-                const uint16_t* w13, const uint16_t* w2, const uint16_t* residual,
-                const uint16_t* norm_w, float eps, int32_t M, int32_t H, int32_t E, int32_t I,
-                int32_t top_k, int32_t block, uint16_t* out, uint16_t* residual_out,
-                int32_t* topk_ids_out, float* topk_w_out, int32_t* sorted_ids_out,
-                int32_t* block_expert_out, int32_t* num_padded_out, void* workspace,
-                size_t workspace_bytes, const moe_event_t* stage_events, moe_stream_t stream) {
+}  // extern "C"
+
+namespace {
+
+// Expert weights of one call: bf16 (w13, w2) or MXFP8 (codes and scale bytes).
+struct ExpertWeights {
+  const uint16_t* w13 = nullptr;
+  const uint16_t* w2 = nullptr;
+  const uint8_t* w13c = nullptr;
+  const uint8_t* w13s = nullptr;
+  const uint8_t* w2c = nullptr;
+  const uint8_t* w2s = nullptr;
+  bool mx() const { return w13c != nullptr; }
+};
+
+int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
+                 const ExpertWeights& W, const uint16_t* residual, const uint16_t* norm_w,
+                 float eps, int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k,
+                 int32_t block, uint16_t* out, uint16_t* residual_out, int32_t* topk_ids_out,
+                 float* topk_w_out, int32_t* sorted_ids_out, int32_t* block_expert_out,
+                 int32_t* num_padded_out, void* workspace, size_t workspace_bytes,
+                 const moe_event_t* stage_events, moe_stream_t stream) {
   if (!sizes_ok(M, H, E, I, top_k) || !(eps > 0.0f) || !isfinite(eps)) return MOE_ERR_INVALID_ARG;
   if (!gemm_block_ok(block)) return MOE_ERR_UNSUPPORTED;
+  if (W.mx() && (H % 256 != 0 || I % 128 != 0)) return MOE_ERR_UNSUPPORTED;
   if (M == 0) return MOE_OK;
-  if (!x || !router_w || !w13 || !w2 || !residual || !norm_w || !out) return MOE_ERR_INVALID_ARG;
-  if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(w13, 16) || !aligned(w2, 16) ||
-      !aligned(residual, 16) || !aligned(norm_w, 16) || !aligned(out, 16) ||
+  const bool w_ok = W.mx() ? (W.w13c && W.w13s && W.w2c && W.w2s && aligned(W.w13c, 16) &&
+                              aligned(W.w2c, 16))
+                           : (W.w13 && W.w2 && aligned(W.w13, 16) && aligned(W.w2, 16));
+  if (!x || !router_w || !w_ok || !residual || !norm_w || !out) return MOE_ERR_INVALID_ARG;
+  if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(residual, 16) ||
+      !aligned(norm_w, 16) || !aligned(out, 16) ||
       (residual_out && !aligned(residual_out, 16)) || (router_bias && !aligned(router_bias, 4)) ||
       (topk_ids_out && !aligned(topk_ids_out, 4)) || (topk_w_out && !aligned(topk_w_out, 4)) ||
       (sorted_ids_out && !aligned(sorted_ids_out, 4)) ||
@@ -241,24 +260,35 @@ int moe_forward(const uint16_t* x, const uint16_t* router_w, const float* router
   if (moe::launch_route(x, router_w, router_bias, M, H, E, top_k, ids, w, keys, s) != hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(1)) return MOE_ERR_HIP;
-  const int trows = gemm_tile_rows(M, E, top_k, I);
+  // MXFP8 weights run the streaming kernels at every size (no tiled MXFP8 kernels)
+  const int trows = W.mx() ? 16 : gemm_tile_rows(M, E, top_k, I);
   const int max_tiles = moe::tile_capacity(M * top_k, E, trows);
   if (moe::launch_align(ids, M * top_k, E, block, sorted, bexp, npad, trows, tiles, ntiles, s) !=
       hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(2)) return MOE_ERR_HIP;
-  const hipError_t up_err =
-      trows == 16 ? moe::launch_expert_up(x, w13, sorted, bexp, npad, tiles, ntiles, max_tiles, M, H,
-                                          I, top_k, block, act, s)
-                  : moe::launch_expert_up_tiled(x, w13, sorted, bexp, tiles, ntiles, max_tiles, trows,
-                                                M, H, I, top_k, block, act, s);
+  hipError_t up_err;
+  if (W.mx())
+    up_err = moe::launch_expert_up_mx(x, W.w13c, W.w13s, sorted, bexp, npad, tiles, ntiles,
+                                      max_tiles, M, H, I, top_k, block, act, s);
+  else if (trows == 16)
+    up_err = moe::launch_expert_up(x, W.w13, sorted, bexp, npad, tiles, ntiles, max_tiles, M, H, I,
+                                   top_k, block, act, s);
+  else
+    up_err = moe::launch_expert_up_tiled(x, W.w13, sorted, bexp, tiles, ntiles, max_tiles, trows,
+                                         M, H, I, top_k, block, act, s);
   if (up_err != hipSuccess) return MOE_ERR_HIP;
   if (!mark(3)) return MOE_ERR_HIP;
-  const hipError_t down_err =
-      trows == 16 ? moe::launch_expert_down(act, w2, sorted, bexp, npad, tiles, ntiles, max_tiles, M,
-                                            H, I, top_k, block, y, s)
-                  : moe::launch_expert_down_tiled(act, w2, sorted, bexp, tiles, ntiles, max_tiles,
-                                                  trows, M, H, I, top_k, block, y, s);
+  hipError_t down_err;
+  if (W.mx())
+    down_err = moe::launch_expert_down_mx(act, W.w2c, W.w2s, sorted, bexp, npad, tiles, ntiles,
+                                          max_tiles, M, H, I, top_k, block, y, s);
+  else if (trows == 16)
+    down_err = moe::launch_expert_down(act, W.w2, sorted, bexp, npad, tiles, ntiles, max_tiles, M,
+                                       H, I, top_k, block, y, s);
+  else
+    down_err = moe::launch_expert_down_tiled(act, W.w2, sorted, bexp, tiles, ntiles, max_tiles,
+                                             trows, M, H, I, top_k, block, y, s);
   if (down_err != hipSuccess) return MOE_ERR_HIP;
   if (!mark(4)) return MOE_ERR_HIP;
   if (moe::launch_finalize(y, w, residual, norm_w, eps, M, H, top_k, out, residual_out, s) !=
@@ -266,6 +296,62 @@ int moe_forward(const uint16_t* x, const uint16_t* router_w, const float* router
     return MOE_ERR_HIP;
   if (!mark(5)) return MOE_ERR_HIP;
   return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_forward(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
+                const uint16_t* w13, const uint16_t* w2, const uint16_t* residual,
+                const uint16_t* norm_w, float eps, int32_t M, int32_t H, int32_t E, int32_t I,
+                int32_t top_k, int32_t block, uint16_t* out, uint16_t* residual_out,
+                int32_t* topk_ids_out, float* topk_w_out, int32_t* sorted_ids_out,
+                int32_t* block_expert_out, int32_t* num_padded_out, void* workspace,
+                size_t workspace_bytes, const moe_event_t* stage_events, moe_stream_t stream) {
+  ExpertWeights W;
+  W.w13 = w13;
+  W.w2 = w2;
+  return forward_impl(x, router_w, router_bias, W, residual, norm_w, eps, M, H, E, I, top_k, block,
+                      out, residual_out, topk_ids_out, topk_w_out, sorted_ids_out,
+                      block_expert_out, num_padded_out, workspace, workspace_bytes, stage_events,
+                      stream);
+}
+
+int moe_forward_mx(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
+                   const uint8_t* w13_codes, const uint8_t* w13_scales, const uint8_t* w2_codes,
+                   const uint8_t* w2_scales, const uint16_t* residual, const uint16_t* norm_w,
+                   float eps, int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k,
+                   int32_t block, uint16_t* out, uint16_t* residual_out, int32_t* topk_ids_out,
+                   float* topk_w_out, int32_t* sorted_ids_out, int32_t* block_expert_out,
+                   int32_t* num_padded_out, void* workspace, size_t workspace_bytes,
+                   const moe_event_t* stage_events, moe_stream_t stream) {
+  ExpertWeights W;
+  W.w13c = w13_codes;
+  W.w13s = w13_scales;
+  W.w2c = w2_codes;
+  W.w2s = w2_scales;
+  if (!w13_codes) return MOE_ERR_INVALID_ARG;
+  return forward_impl(x, router_w, router_bias, W, residual, norm_w, eps, M, H, E, I, top_k, block,
+                      out, residual_out, topk_ids_out, topk_w_out, sorted_ids_out,
+                      block_expert_out, num_padded_out, workspace, workspace_bytes, stage_events,
+                      stream);
+}
+
+int moe_mx_quantize(const uint16_t* w, int64_t rows, int32_t K, uint8_t* codes, uint8_t* scales,
+                    moe_stream_t stream) {
+  if (rows < 0 || K < 32 || K % 32 != 0 || rows > ((int64_t)1 << 40) / K) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!w || !codes || !scales || !aligned(w, 16) || !aligned(codes, 16)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_mx_quantize(w, rows, K, codes, scales, (hipStream_t)stream));
+}
+
+int moe_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int32_t K,
+                      uint16_t* w, moe_stream_t stream) {
+  if (rows < 0 || K < 32 || K % 32 != 0 || rows > ((int64_t)1 << 40) / K) return MOE_ERR_INVALID_ARG;
+  if (rows == 0) return MOE_OK;
+  if (!w || !codes || !scales || !aligned(w, 16) || !aligned(codes, 16)) return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_mx_dequantize(codes, scales, rows, K, w, (hipStream_t)stream));
 }
 
 }  // extern "C"

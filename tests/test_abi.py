@@ -54,7 +54,7 @@ def test_library_links_no_torch(B):
 
 
 def test_strerror_and_version(B):
-    assert B.moe_abi_version() == 101
+    assert B.moe_abi_version() == 102
     for s in (0, -1, -2, -3, -4, 17):
         assert isinstance(B.moe_strerror(s), str) and B.moe_strerror(s)
 
@@ -157,3 +157,27 @@ def test_read_probe_library_is_built_apart_from_the_layer(B):
     layer = subprocess.run(["nm", "-D", "--defined-only", B.library_path()], capture_output=True,
                            text=True, check=True).stdout
     assert "moe_probe_read" not in layer
+
+
+def test_mx_entry_points_validate_on_the_host(B):
+    lib = B.load_library()
+    p = ctypes.c_void_p
+    # quantize / dequantize: K not a multiple of 32, null or misaligned pointers, rows 0
+    assert lib.moe_mx_quantize(p(256), 4, 48, p(256), p(256), None) == -1
+    assert lib.moe_mx_quantize(None, 4, 64, p(256), p(256), None) == -1
+    assert lib.moe_mx_quantize(p(258), 4, 64, p(256), p(256), None) == -1
+    assert lib.moe_mx_quantize(p(256), -1, 64, p(256), p(256), None) == -1
+    assert lib.moe_mx_quantize(None, 0, 64, None, None, None) == 0
+    assert lib.moe_mx_dequantize(p(256), p(256), 4, 16, p(256), None) == -1
+    assert lib.moe_mx_dequantize(p(256), None, 4, 64, p(256), None) == -1
+    assert lib.moe_mx_dequantize(None, None, 0, 64, None, None) == 0
+
+    def fwd_mx(H=256, I=512, w13c=256, M=4):
+        return lib.moe_forward_mx(p(256), p(256), None, None if w13c is None else p(w13c), p(256),
+                                  p(256), p(256), p(256), p(256), 1e-5, M, H, 8, I, 2, 16, p(256),
+                                  None, None, None, None, None, None, p(256), 1 << 40, None, None)
+    assert fwd_mx(H=208) == -2             # H % 256 != 0
+    assert fwd_mx(H=384) == -2             # H % 256 != 0
+    assert fwd_mx(I=192) == -2             # I % 128 != 0
+    assert fwd_mx(w13c=None) == -1
+    assert fwd_mx(H=250) == -1             # H % 16 != 0 fails the shared size checks first

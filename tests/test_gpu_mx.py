@@ -1,0 +1,220 @@
+"""GPU parity of the MXFP8 expert weights (through the C ABI) against the CPU oracle.
+
+Bar: the device's E4M3 codes and E8M0 scale bytes equal the oracle's bit for bit; its
+dequantization to bf16 equals the oracle's exact values bit for bit; moe_forward_mx
+equals the oracle layer run on the oracle's own dequantized weights to the bf16 bar
+(routing and plan bit-exact, outputs max-abs 2e-2 and relative-L2 1e-2).
+"""
+import numpy as np
+import pytest
+import torch
+
+import moe_inputs as mi
+from oracle import moe_oracle as orc
+from oracle import mx_oracle as mxo
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+REL_L2 = 1e-2
+bits = mi.bf16_bits
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+@pytest.fixture(scope="module")
+def B(dev):
+    from prefill_sigmoid_router_amd import binding
+    binding.load_library()
+    return binding
+
+
+def _quantize(B, w, dev):
+    K = w.shape[-1]
+    codes = torch.full(tuple(w.shape), 0x5A, dtype=torch.uint8, device=dev)
+    scales = torch.full(tuple(w.shape[:-1]) + (K // 32,), 0xA5, dtype=torch.uint8, device=dev)
+    B.moe_mx_quantize(w, codes, scales)
+    torch.cuda.synchronize()
+    return codes, scales
+
+
+def test_dequantize_every_code_at_several_scales(B, dev):
+    """The conversion the MXFP8 GEMMs use, for all 254 finite codes, against the format."""
+    finite = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], dtype=np.uint8)
+    codes_np = np.resize(finite, (6, 256)).astype(np.uint8)      # 254 codes + 2 repeats per row
+    scales_np = np.array([[10] * 8, [60] * 8, [119] * 8, [127] * 8, [150] * 8, [246] * 8],
+                         dtype=np.uint8)
+    codes = torch.from_numpy(codes_np).to(dev)
+    scales = torch.from_numpy(scales_np).to(dev)
+    w = torch.full((6, 256), float("nan"), dtype=torch.bfloat16, device=dev)
+    B.moe_mx_dequantize(codes, scales, w)
+    torch.cuda.synchronize()
+    want = mxo.mx_dequantize_bf16_bits(codes_np, scales_np)
+    assert np.array_equal(bits(w), want)
+
+
+@pytest.mark.parametrize("case", ["normal", "wide", "ties_and_zeros", "full_row"])
+def test_quantize_bit_exact(B, dev, case):
+    rng = np.random.default_rng(7)
+    if case == "normal":
+        v = rng.normal(0, 0.02, (64, 512))
+    elif case == "wide":      # blocks whose magnitudes span many binades
+        v = rng.normal(0, 1, (32, 256)) * np.exp2(rng.integers(-20, 20, (32, 256)))
+    elif case == "ties_and_zeros":
+        # values that land exactly between E4M3 neighbours after scaling, zero blocks,
+        # negative zeros and block maxima that clamp to 448
+        pos = mxo.e4m3_decode(np.arange(0x00, 0x7F, dtype=np.uint8))
+        mids = (pos[1:] + pos[:-1]) / 2
+        v = np.zeros((8, 256))
+        v[0, :125] = mids[:125] / 256.0
+        v[0, 200] = 1.0                                   # sets s = -8 for its block
+        v[1, :125] = -mids[:125] / 256.0 * 8
+        v[2, 32:64] = -0.0
+        v[3, 5] = 1.875
+        v[4] = rng.normal(0, 1e-30, 256)
+        v[5, ::7] = 3.0
+    else:                     # a whole W13 row of the decode shape
+        v = rng.normal(0, 0.02, (4, 7168))
+    w_bits = (v.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    w = torch.from_numpy(w_bits.view(np.int16)).view(torch.bfloat16).to(dev)
+    codes, scales = _quantize(B, w, dev)
+    ref_codes, ref_scales = mxo.mx_quantize(w_bits)
+    assert np.array_equal(scales.cpu().numpy(), ref_scales), case
+    assert np.array_equal(codes.cpu().numpy(), ref_codes), case
+
+
+def _mx_weights(B, L, dev):
+    w13c, w13s = _quantize(B, L["w13"], dev)
+    w2c, w2s = _quantize(B, L["w2"], dev)
+    return w13c, w13s, w2c, w2s
+
+
+def _run_forward_mx(B, L, dev, mx):
+    cfg = L["cfg"]
+    M, H, E, I, k, blk = L["M"], cfg.H, cfg.E, cfg.I, cfg.top_k, cfg.block
+    cap = B.moe_align_capacity(M, k, E, blk)
+    r = {
+        "out": torch.full((M, H), float("nan"), dtype=torch.bfloat16, device=dev),
+        "rout": torch.full((M, H), float("nan"), dtype=torch.bfloat16, device=dev),
+        "ids": torch.full((M, k), -7, dtype=torch.int32, device=dev),
+        "w": torch.full((M, k), float("nan"), dtype=torch.float32, device=dev),
+        "sorted": torch.full((cap,), -7, dtype=torch.int32, device=dev),
+        "bexp": torch.full((cap // blk,), -7, dtype=torch.int32, device=dev),
+        "npad": torch.full((1,), -7, dtype=torch.int32, device=dev),
+    }
+    ws = torch.empty(B.moe_workspace_bytes(M, H, E, I, k, blk), dtype=torch.uint8, device=dev)
+    B.moe_forward_mx(L["x"], L["router_w"], L["router_bias"], *mx, L["residual"], L["norm_w"],
+                     L["eps"], k, blk, r["out"], ws, residual_out=r["rout"], topk_ids_out=r["ids"],
+                     topk_w_out=r["w"], sorted_ids_out=r["sorted"], block_expert_out=r["bexp"],
+                     num_padded_out=r["npad"])
+    torch.cuda.synchronize()
+    return r
+
+
+def _check_close(got_bf16, ref, what):
+    g = got_bf16.float().cpu().numpy().astype(np.float64)
+    assert np.isfinite(g).all(), f"{what}: non-finite output"
+    err = np.abs(g - ref)
+    rel = np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-30)
+    assert err.max() <= MAX_ABS, f"{what}: max-abs {err.max():.3e}"
+    assert rel <= REL_L2, f"{what}: rel-L2 {rel:.3e}"
+
+
+def _bias_np(L):
+    return None if L["router_bias"] is None else L["router_bias"].cpu().numpy()
+
+
+class _OracleMxExperts:
+    """Expert e of a device bf16 stack, quantized and dequantized by the oracle."""
+
+    def __init__(self, stack):
+        self.stack = stack
+
+    def __len__(self):
+        return self.stack.shape[0]
+
+    def __getitem__(self, e):
+        c, s = mxo.mx_quantize(bits(self.stack[int(e)]))
+        return mxo.mx_dequantize_bf16_bits(c, s)
+
+
+SMALL_MX = {
+    "mx_tiny": mi.LayerConfig("mx_tiny", M=4, H=256, E=8, top_k=2, I=512, block=16),
+    "mx_mid": mi.LayerConfig("mx_mid", M=37, H=1024, E=32, top_k=4, I=256, block=16),
+    "mx_many": mi.LayerConfig("mx_many", M=300, H=768, E=8, top_k=4, I=384, block=64,
+                              zipf_s=1.0),
+    "mx_one_token": mi.LayerConfig("mx_one_token", M=1, H=512, E=64, top_k=8, I=128, block=16),
+}
+
+
+@pytest.mark.parametrize("name", list(SMALL_MX))
+def test_forward_mx_small(B, dev, name):
+    cfg = SMALL_MX[name]
+    print(f"forward_mx parity {name}", flush=True)
+    L = mi.make_layer(cfg, device=dev, seed=5)
+    mx = _mx_weights(B, L, dev)
+    r = _run_forward_mx(B, L, dev, mx)
+    ref_w13c, ref_w13s = mxo.mx_quantize(bits(L["w13"]))
+    ref_w2c, ref_w2s = mxo.mx_quantize(bits(L["w2"]))
+    assert np.array_equal(mx[0].cpu().numpy(), ref_w13c) and np.array_equal(mx[1].cpu().numpy(), ref_w13s)
+    assert np.array_equal(mx[2].cpu().numpy(), ref_w2c) and np.array_equal(mx[3].cpu().numpy(), ref_w2s)
+    ref = orc.forward(bits(L["x"]), bits(L["router_w"]), _bias_np(L),
+                      mxo.mx_dequantize_bf16_bits(ref_w13c, ref_w13s),
+                      mxo.mx_dequantize_bf16_bits(ref_w2c, ref_w2s),
+                      bits(L["residual"]), bits(L["norm_w"]), L["eps"], cfg.top_k, cfg.block)
+    assert np.array_equal(r["ids"].cpu().numpy(), ref["topk_ids"])
+    n_pad = int(r["npad"].item())
+    assert n_pad == ref["num_padded"]
+    assert np.array_equal(r["sorted"].cpu().numpy()[:n_pad], ref["sorted_ids"])
+    _check_close(r["out"], ref["out"], name)
+    _check_close(r["rout"], ref["residual_out"], name + " residual_out")
+
+
+def test_forward_mx_rejects_unsupported_widths(B, dev):
+    cfg = mi.LayerConfig("mx_bad", M=4, H=208, E=8, top_k=2, I=256, block=16)
+    L = mi.make_layer(cfg, device=dev, seed=5)
+    w13c = torch.zeros((8, 512, 208), dtype=torch.uint8, device=dev)
+    w13s = torch.zeros((8, 512, 6), dtype=torch.uint8, device=dev)
+    w2c = torch.zeros((8, 208, 256), dtype=torch.uint8, device=dev)
+    w2s = torch.zeros((8, 208, 8), dtype=torch.uint8, device=dev)
+    out = torch.empty((4, 208), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(B.moe_workspace_bytes(4, 208, 8, 256, 2, 16), dtype=torch.uint8, device=dev)
+    with pytest.raises(B.MoeError) as ei:
+        B.moe_forward_mx(L["x"], L["router_w"], None, w13c, w13s, w2c, w2s, L["residual"],
+                         L["norm_w"], L["eps"], 2, 16, out, ws)
+    assert ei.value.status == -2
+
+
+def test_forward_mx_full_decode(B, dev):
+    """The decode workload (M=8, H=7168, E=256, k=16, I=2048) with MXFP8 weights: routing and
+    plan bit-exact for every token; codes of the experts a sampled token uses bit-exact;
+    that token's output against the oracle on the oracle's own dequantized weights."""
+    cfg = mi.CONFIGS["decode_m8"]
+    print("forward_mx full-size decode", flush=True)
+    L = mi.make_layer(cfg, device=dev, seed=0)
+    mx = _mx_weights(B, L, dev)
+    r = _run_forward_mx(B, L, dev, mx)
+    k = cfg.top_k
+    ref_ids, ref_w, _ = orc.route(bits(L["x"]), bits(L["router_w"]), _bias_np(L), k)
+    assert np.array_equal(r["ids"].cpu().numpy(), ref_ids)
+    sorted_ids, bexp, n_pad, _, _ = orc.align(ref_ids, cfg.E, cfg.block)
+    assert int(r["npad"].item()) == n_pad
+    assert np.array_equal(r["sorted"].cpu().numpy()[:n_pad], sorted_ids)
+    out = r["out"].float().cpu().numpy()
+    assert np.isfinite(out).all()
+    t = 3
+    for e in ref_ids[t][:2]:   # two of its experts' codes, bit for bit
+        c, s = mxo.mx_quantize(bits(L["w13"][int(e)]))
+        assert np.array_equal(mx[0][int(e)].cpu().numpy(), c) and np.array_equal(mx[1][int(e)].cpu().numpy(), s)
+    ref_out, ref_z, s_ids, _ = orc.forward_tokens([t], bits(L["x"]), bits(L["router_w"]),
+                                                  _bias_np(L), _OracleMxExperts(L["w13"]),
+                                                  _OracleMxExperts(L["w2"]), bits(L["residual"]),
+                                                  bits(L["norm_w"]), L["eps"], k)
+    assert np.array_equal(s_ids, ref_ids[[t]])
+    _check_close(r["out"][[t]], ref_out, "decode mx sampled out")
+    _check_close(r["rout"][[t]], ref_z, "decode mx sampled residual_out")

@@ -239,18 +239,19 @@ __global__ __launch_bounds__(256) void expert_down_stream_kernel(
       make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
 }
 
-// Up + SwiGLU on MXFP8 W13 (codes [E, 2I, H], scale bytes [E, 2I, H/32]), 16 act columns
-// per workgroup.  GU = 1: the waves of expert_up_stream_kernel ({gate, up} x K halves).
-// GU = 2: each wave streams the gate and the up rows over one quarter of K, so one B
-// fragment of x serves both.  H is a multiple of 256.
-template <int U, int GU>
+// Up + SwiGLU on MXFP8 W13 (codes [E, 2I, H], scale bytes [E, 2I, H/32]): 16 CG act
+// columns per workgroup.  Each of the four waves streams the gate and the up rows of all
+// CG column groups over one quarter of K, so one fragment of x feeds 2 CG MFMAs; the
+// quarters meet wave 0 through LDS in a fixed order.  H is a multiple of 256.
+template <int U, int CG>
 __global__ __launch_bounds__(256) void expert_up_mx_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13c,
     const uint8_t* __restrict__ w13s, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
     const int2* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int H, int I,
     int top_k, int block, int sentinel, uint16_t* __restrict__ act) {
-  __shared__ f32x4 red[3][GU][kWave];
+  constexpr int NS = 2 * CG;  // weight streams per wave: gate and up of each group
+  __shared__ f32x4 red[3][NS][kWave];
   int start, nlive;
   if (!tile_of(tiles, num_tiles, sorted_ids, num_padded, sentinel, start, nlive)) return;
   const int e = block_expert[start / block];
@@ -258,56 +259,52 @@ __global__ __launch_bounds__(256) void expert_up_mx_kernel(
   const int li = lane & 15, lg = lane >> 4;
   const bool live = li < nlive;
   const int tok = live ? sorted_ids[start + li] / top_k : 0;
-  const int n0 = blockIdx.x * 16;
-  const int nk = GU == 1 ? 2 : 4;                 // parts of K
-  const int wk = GU == 1 ? wave >> 1 : wave;
-  const int kpart = H / nk;
-  const int koff = wk * kpart + 16 * lg;
-  const uint8_t* wr[GU];
-  const uint8_t* sr[GU];
+  const int n0 = blockIdx.x * 16 * CG;
+  const int kpart = H / 4;
+  const int koff = wave * kpart + 16 * lg;
+  const uint8_t* wr[NS];
+  const uint8_t* sr[NS];
 #pragma unroll
-  for (int j = 0; j < GU; ++j) {
-    const int gu = GU == 1 ? (wave & 1) : j;
-    const size_t row = (size_t)e * 2 * I + gu * I + n0 + li;
+  for (int j = 0; j < NS; ++j) {   // stream j: group j / 2, gate (j even) or up (j odd)
+    const size_t row = (size_t)e * 2 * I + (j & 1) * I + n0 + 16 * (j >> 1) + li;
     wr[j] = w13c + row * H + koff;
     sr[j] = w13s + row * (H / 32) + koff / 32;
   }
-  f32x4 acc[GU];
+  f32x4 acc[NS];
 #pragma unroll
-  for (int j = 0; j < GU; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stream_mx<GU, U>(wr, sr, x + (size_t)tok * H + koff, live, kpart / 64, acc);
+  for (int j = 0; j < NS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  stream_mx<NS, U>(wr, sr, x + (size_t)tok * H + koff, live, kpart / 64, acc);
   if (wave != 0)
 #pragma unroll
-    for (int j = 0; j < GU; ++j) red[wave - 1][j][lane] = acc[j];
+    for (int j = 0; j < NS; ++j) red[wave - 1][j][lane] = acc[j];
   __syncthreads();
   if (wave != 0) return;
-  f32x4 g, u;
-  if (GU == 1) {
-    g = acc[0] + red[1][0][lane];                 // gate: waves 0 and 2
-    u = red[0][0][lane] + red[2][0][lane];        // up: waves 1 and 3
-  } else {
-    g = ((acc[0] + red[0][0][lane]) + red[1][0][lane]) + red[2][0][lane];
-    u = ((acc[GU - 1] + red[0][GU - 1][lane]) + red[1][GU - 1][lane]) + red[2][GU - 1][lane];
-  }
-  float a[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) a[q] = silu_f32(g[q]) * u[q];
-  uint2 v;
-  v.x = pack_bf16x2(a[0], a[1]);
-  v.y = pack_bf16x2(a[2], a[3]);
-  *reinterpret_cast<uint2*>(act + (size_t)(start + li) * I + n0 + 4 * lg) = v;
+  for (int c = 0; c < CG; ++c) {
+    const f32x4 g = ((acc[2 * c] + red[0][2 * c][lane]) + red[1][2 * c][lane]) + red[2][2 * c][lane];
+    const f32x4 u =
+        ((acc[2 * c + 1] + red[0][2 * c + 1][lane]) + red[1][2 * c + 1][lane]) + red[2][2 * c + 1][lane];
+    float a[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) a[q] = silu_f32(g[q]) * u[q];
+    uint2 v;
+    v.x = pack_bf16x2(a[0], a[1]);
+    v.y = pack_bf16x2(a[2], a[3]);
+    *reinterpret_cast<uint2*>(act + (size_t)(start + li) * I + n0 + 16 * c + 4 * lg) = v;
+  }
 }
 
-// Down on MXFP8 W2 (codes [E, H, I], scale bytes [E, H, I/32]): the layout of
-// expert_down_stream_kernel; I is a multiple of 128.
-template <int U>
+// Down on MXFP8 W2 (codes [E, H, I], scale bytes [E, H, I/32]): 32 NC output columns per
+// workgroup; waves = 2 column groups x 2 halves of K, each streaming NC 16-row tiles of W2
+// against one act fragment; I is a multiple of 128.
+template <int U, int NC>
 __global__ __launch_bounds__(256) void expert_down_mx_kernel(
     const uint16_t* __restrict__ act, const uint8_t* __restrict__ w2c,
     const uint8_t* __restrict__ w2s, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int32_t* __restrict__ num_padded,
     const int2* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int H, int I,
     int block, int sentinel, float* __restrict__ y) {
-  __shared__ f32x4 red[2][kWave];
+  __shared__ f32x4 red[2][NC][kWave];
   int start, nlive;
   if (!tile_of(tiles, num_tiles, sorted_ids, num_padded, sentinel, start, nlive)) return;
   const int e = block_expert[start / block];
@@ -315,21 +312,36 @@ __global__ __launch_bounds__(256) void expert_down_mx_kernel(
   const int li = lane & 15, lg = lane >> 4;
   const int wn = wave & 1, wk = wave >> 1;
   const bool live = li < nlive;
-  const int n0 = blockIdx.x * 32 + wn * 16;
-  const bool n_in = n0 < H;
+  const int n0 = blockIdx.x * 32 * NC + wn * 16 * NC;
   const int khalf = I >> 1;
   const int koff = wk * khalf + 16 * lg;
-  const size_t row = (size_t)e * H + (n_in ? n0 + li : 0);
-  f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
-  const uint8_t* wr[1] = {w2c + row * I + koff};
-  const uint8_t* sr[1] = {w2s + row * (I / 32) + koff / 32};
-  if (n_in) stream_mx<1, U>(wr, sr, act + (size_t)(start + li) * I + koff, live, khalf / 64, acc);
-  if (wk == 1) red[wn][lane] = acc[0];
+  const uint8_t* wr[NC];
+  const uint8_t* sr[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int n = n0 + 16 * j;
+    const size_t row = (size_t)e * H + (n < H ? n + li : 0);   // H % 16 == 0
+    wr[j] = w2c + row * I + koff;
+    sr[j] = w2s + row * (I / 32) + koff / 32;
+  }
+  f32x4 acc[NC];
+#pragma unroll
+  for (int j = 0; j < NC; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  if (n0 < H) stream_mx<NC, U>(wr, sr, act + (size_t)(start + li) * I + koff, live, khalf / 64, acc);
+  if (wk == 1)
+#pragma unroll
+    for (int j = 0; j < NC; ++j) red[wn][j][lane] = acc[j];
   __syncthreads();
-  if (wk == 1 || !n_in || !live) return;
-  const f32x4 d = acc[0] + red[wn][lane];
+  if (wk == 1 || !live) return;
   const int dst = sorted_ids[start + li];
-  *reinterpret_cast<float4*>(y + (size_t)dst * H + n0 + 4 * lg) = make_float4(d[0], d[1], d[2], d[3]);
+#pragma unroll
+  for (int j = 0; j < NC; ++j) {
+    const int n = n0 + 16 * j;
+    if (n < H) {
+      const f32x4 d = acc[j] + red[wn][j][lane];
+      *reinterpret_cast<float4*>(y + (size_t)dst * H + n + 4 * lg) = make_float4(d[0], d[1], d[2], d[3]);
+    }
+  }
 }
 
 hipError_t launch_expert_up(const uint16_t* x, const uint16_t* w13, const int32_t* sorted_ids,
@@ -354,20 +366,22 @@ hipError_t launch_expert_down(const uint16_t* act, const uint16_t* w2, const int
   return hipGetLastError();
 }
 
-// Chunks of 64 K values per streamed batch.  Measured at M=8, H=7168, I=2048: the up
-// kernel with gate and up rows in every wave (one x fragment for both) and 4 chunks is
-// 7 % faster than the {gate, up} x K-halves split.
+// Chunks of 64 K values per streamed batch, act column groups per up workgroup and W2 tiles
+// per down wave.  Measured at M=8 (interleaved runs): one column group is fastest for up
+// (two: +11 %, the 298 registers leave one wave per SIMD); two W2 tiles per wave take down
+// from 425 to 393 us (four spill).
 constexpr int kMxStreamU = 4;
-constexpr int kMxUpGU = 2;
+constexpr int kMxUpCG = 1;
+constexpr int kMxDownNC = 2;
 
 hipError_t launch_expert_up_mx(const uint16_t* x, const uint8_t* w13c, const uint8_t* w13s,
                                const int32_t* sorted_ids, const int32_t* block_expert,
                                const int32_t* num_padded, const int2* tiles,
                                const int32_t* num_tiles, int max_tiles, int M, int H, int I,
                                int top_k, int block, uint16_t* act, hipStream_t s) {
-  if (H % (kMxUpGU == 2 ? 256 : 128) != 0) return hipErrorInvalidValue;
-  dim3 grid(I / 16, max_tiles);
-  hipLaunchKernelGGL((expert_up_mx_kernel<kMxStreamU, kMxUpGU>), grid, dim3(256), 0, s, x, w13c, w13s,
+  if (H % 256 != 0 || I % (16 * kMxUpCG) != 0) return hipErrorInvalidValue;
+  dim3 grid(I / (16 * kMxUpCG), max_tiles);
+  hipLaunchKernelGGL((expert_up_mx_kernel<kMxStreamU, kMxUpCG>), grid, dim3(256), 0, s, x, w13c, w13s,
                      sorted_ids, block_expert, num_padded, tiles, num_tiles, H, I, top_k, block,
                      M * top_k, act);
   return hipGetLastError();
@@ -379,8 +393,8 @@ hipError_t launch_expert_down_mx(const uint16_t* act, const uint8_t* w2c, const 
                                  const int32_t* num_tiles, int max_tiles, int M, int H, int I,
                                  int top_k, int block, float* y, hipStream_t s) {
   if (I % 128 != 0) return hipErrorInvalidValue;
-  dim3 grid((H + 31) / 32, max_tiles);
-  hipLaunchKernelGGL((expert_down_mx_kernel<kMxStreamU>), grid, dim3(256), 0, s, act, w2c, w2s,
+  dim3 grid((H + 32 * kMxDownNC - 1) / (32 * kMxDownNC), max_tiles);
+  hipLaunchKernelGGL((expert_down_mx_kernel<kMxStreamU, kMxDownNC>), grid, dim3(256), 0, s, act, w2c, w2s,
                      sorted_ids, block_expert, num_padded, tiles, num_tiles, H, I, block,
                      M * top_k, y);
   return hipGetLastError();

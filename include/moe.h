@@ -204,8 +204,9 @@ int moe_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
  * moe_forward with MXFP8 expert weights: w13_codes [E, 2I, H] + w13_scales [E, 2I, H/32],
  * w2_codes [E, H, I] + w2_scales [E, H, I/32] (as written by moe_mx_quantize) in place of
  * w13 and w2; every other argument, the workspace and the outputs are those of
- * moe_forward.  The result is the layer on the dequantized weights.  H must be a multiple
- * of 256 and I of 128 (MOE_ERR_UNSUPPORTED otherwise).  The GEMMs are the weight-streaming
+ * moe_forward.  The result is the layer on the dequantized weights.  H and I must be
+ * multiples of 256 (MOE_ERR_UNSUPPORTED otherwise); codes 16-byte and scales 8-byte
+ * aligned (MOE_ERR_INVALID_ARG otherwise).  The GEMMs are the weight-streaming
  * kernels at every size: they fit decode (few tokens per expert); there are no LDS-tiled
  * MXFP8 kernels for large batches.
  */

@@ -81,66 +81,59 @@ __device__ __forceinline__ void stream_k(const uint16_t* const (&wr)[NW], const 
   }
 }
 
-// MXFP8 weights: acc += W(16 rows) . B(16 rows)^T over nch chunks of 64 K values.  wr
-// points at this lane's 16 E4M3 codes of the first chunk (row start + K offset + 16 *
-// (lane / 16)), sr at the scale byte of that block, br at the lane's B row + the same K
-// offset.  A chunk's 16 codes dequantize (exactly, to bf16) into two MFMA fragments: K
-// values 16*lg..+8 and 16*lg+8..+16 of the chunk, paired with the same K values of B --
-// the MFMA sums over its K group whatever the order, so this only permutes K.
-template <int NW, int U>
+// MXFP8 weights: acc += W(16 rows) . B(16 rows)^T over ng groups of 256 K values (4
+// chunks of 64, 8 scale bytes).  wr points at this lane's 16 E4M3 codes of the first chunk
+// (row start + K offset + 16 * (lane / 16)), sr at the row's scale bytes of the first group
+// (8-byte aligned), br at the lane's B row + the same K offset as wr.  A chunk's 16 codes
+// dequantize (exactly, to bf16) into two MFMA fragments: K values 16*lg..+8 and
+// 16*lg+8..+16 of the chunk, paired with the same K values of B -- the MFMA sums over its
+// K group whatever the order, so this only permutes K.  One 8-byte load per row and group
+// brings the scales of all four chunks (chunk u of the lane uses byte 2u + lg / 2): a byte
+// load per chunk costs as many cache-line requests as the codes themselves.
+template <int NW>
 __device__ __forceinline__ void stream_mx(const uint8_t* const (&wr)[NW],
                                           const uint8_t* const (&sr)[NW], const uint16_t* br,
-                                          bool br_live, int nch, f32x4 (&acc)[NW]) {
+                                          bool br_live, int ng, f32x4 (&acc)[NW]) {
+  constexpr int U = 4;
   const u32x4 z4 = u32x4{0, 0, 0, 0};
-  const int full = nch / U;
+  const int sshift = 8 * ((threadIdx.x & 63) >> 5);   // byte lg / 2 of each 16-bit pair
   u32x4 wc[2][NW][U], xa[2][U], xb[2][U];
-  uint32_t sc[2][NW][U];
-  auto fetch = [&](int c0, u32x4 (&cw)[NW][U], uint32_t (&sv)[NW][U], u32x4 (&a)[U],
-                   u32x4 (&b)[U]) {
+  uint2 sc[2][NW];
+  auto fetch = [&](int g, u32x4 (&cw)[NW][U], uint2 (&sv)[NW], u32x4 (&a)[U], u32x4 (&b)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const int c = c0 + u;
+      const int c = g * U + u;
 #pragma unroll
-      for (int j = 0; j < NW; ++j) {
-        cw[j][u] = ld16(wr[j] + 64 * c);
-        sv[j][u] = sr[j][2 * c];
-      }
+      for (int j = 0; j < NW; ++j) cw[j][u] = ld16(wr[j] + 64 * c);
       a[u] = br_live ? ld16(br + 64 * c) : z4;
       b[u] = br_live ? ld16(br + 64 * c + 8) : z4;
     }
+#pragma unroll
+    for (int j = 0; j < NW; ++j) sv[j] = *reinterpret_cast<const uint2*>(sr[j] + 8 * g);
   };
-  auto mma = [&](const u32x4 (&cw)[NW][U], const uint32_t (&sv)[NW][U], const u32x4 (&a)[U],
+  auto mma = [&](const u32x4 (&cw)[NW][U], const uint2 (&sv)[NW], const u32x4 (&a)[U],
                  const u32x4 (&b)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int j = 0; j < NW; ++j) {
+        const uint32_t word = u < 2 ? sv[j].x : sv[j].y;
+        const uint32_t sbyte = (word >> (16 * (u & 1) + sshift)) & 0xFFu;
         u32x4 lo, hi;
-        mx_dequant16(cw[j][u], sv[j][u], lo, hi);
+        mx_dequant16(cw[j][u], sbyte, lo, hi);
         acc[j] = mfma16x16x32(lo, a[u], acc[j]);
         acc[j] = mfma16x16x32(hi, b[u], acc[j]);
       }
   };
-  if (full > 0) fetch(0, wc[0], sc[0], xa[0], xb[0]);
-  for (int m = 0; m < full; m += 2) {
+  if (ng > 0) fetch(0, wc[0], sc[0], xa[0], xb[0]);
+  for (int m = 0; m < ng; m += 2) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int mm = m + h;
-      if (mm < full) {
-        if (mm + 1 < full) fetch((mm + 1) * U, wc[h ^ 1], sc[h ^ 1], xa[h ^ 1], xb[h ^ 1]);
+      if (mm < ng) {
+        if (mm + 1 < ng) fetch(mm + 1, wc[h ^ 1], sc[h ^ 1], xa[h ^ 1], xb[h ^ 1]);
         mma(wc[h], sc[h], xa[h], xb[h]);
       }
-    }
-  }
-  for (int c = full * U; c < nch; ++c) {  // remaining chunks, one at a time
-    const u32x4 a1 = br_live ? ld16(br + 64 * c) : z4;
-    const u32x4 b1 = br_live ? ld16(br + 64 * c + 8) : z4;
-#pragma unroll
-    for (int j = 0; j < NW; ++j) {
-      u32x4 lo, hi;
-      mx_dequant16(ld16(wr[j] + 64 * c), sr[j][2 * c], lo, hi);
-      acc[j] = mfma16x16x32(lo, a1, acc[j]);
-      acc[j] = mfma16x16x32(hi, b1, acc[j]);
     }
   }
 }
@@ -241,9 +234,10 @@ __global__ __launch_bounds__(256) void expert_down_stream_kernel(
 
 // Up + SwiGLU on MXFP8 W13 (codes [E, 2I, H], scale bytes [E, 2I, H/32]): 16 CG act
 // columns per workgroup.  Each of the four waves streams the gate and the up rows of all
-// CG column groups over one quarter of K, so one fragment of x feeds 2 CG MFMAs; the
-// quarters meet wave 0 through LDS in a fixed order.  H is a multiple of 256.
-template <int U, int CG>
+// CG column groups over a quarter of K (whole 256-value groups), so one fragment of x
+// feeds 2 CG MFMAs; the quarters meet wave 0 through LDS in a fixed order.  H is a
+// multiple of 256, the scale rows 8-byte aligned.
+template <int CG>
 __global__ __launch_bounds__(256) void expert_up_mx_kernel(
     const uint16_t* __restrict__ x, const uint8_t* __restrict__ w13c,
     const uint8_t* __restrict__ w13s, const int32_t* __restrict__ sorted_ids,
@@ -260,20 +254,21 @@ __global__ __launch_bounds__(256) void expert_up_mx_kernel(
   const bool live = li < nlive;
   const int tok = live ? sorted_ids[start + li] / top_k : 0;
   const int n0 = blockIdx.x * 16 * CG;
-  const int kpart = H / 4;
-  const int koff = wave * kpart + 16 * lg;
+  const int ng = H / 256;                                  // groups of 256 K values
+  const int g0 = wave * ng / 4, g1 = (wave + 1) * ng / 4;  // this wave's share of K
+  const int kb = 256 * g0;
   const uint8_t* wr[NS];
   const uint8_t* sr[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) {   // stream j: group j / 2, gate (j even) or up (j odd)
     const size_t row = (size_t)e * 2 * I + (j & 1) * I + n0 + 16 * (j >> 1) + li;
-    wr[j] = w13c + row * H + koff;
-    sr[j] = w13s + row * (H / 32) + koff / 32;
+    wr[j] = w13c + row * H + kb + 16 * lg;
+    sr[j] = w13s + row * (H / 32) + kb / 32;
   }
   f32x4 acc[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stream_mx<NS, U>(wr, sr, x + (size_t)tok * H + koff, live, kpart / 64, acc);
+  stream_mx<NS>(wr, sr, x + (size_t)tok * H + kb + 16 * lg, live, g1 - g0, acc);
   if (wave != 0)
 #pragma unroll
     for (int j = 0; j < NS; ++j) red[wave - 1][j][lane] = acc[j];
@@ -295,9 +290,9 @@ __global__ __launch_bounds__(256) void expert_up_mx_kernel(
 }
 
 // Down on MXFP8 W2 (codes [E, H, I], scale bytes [E, H, I/32]): 32 NC output columns per
-// workgroup; waves = 2 column groups x 2 halves of K, each streaming NC 16-row tiles of W2
-// against one act fragment; I is a multiple of 128.
-template <int U, int NC>
+// workgroup; waves = 2 column groups x 2 halves of K (whole 256-value groups), each
+// streaming NC 16-row tiles of W2 against one act fragment; I is a multiple of 256.
+template <int NC>
 __global__ __launch_bounds__(256) void expert_down_mx_kernel(
     const uint16_t* __restrict__ act, const uint8_t* __restrict__ w2c,
     const uint8_t* __restrict__ w2s, const int32_t* __restrict__ sorted_ids,
@@ -313,21 +308,22 @@ __global__ __launch_bounds__(256) void expert_down_mx_kernel(
   const int wn = wave & 1, wk = wave >> 1;
   const bool live = li < nlive;
   const int n0 = blockIdx.x * 32 * NC + wn * 16 * NC;
-  const int khalf = I >> 1;
-  const int koff = wk * khalf + 16 * lg;
+  const int ng = I / 256;                                  // groups of 256 K values
+  const int g0 = wk * ng / 2, g1 = (wk + 1) * ng / 2;      // this wave's half of K
+  const int kb = 256 * g0;
   const uint8_t* wr[NC];
   const uint8_t* sr[NC];
 #pragma unroll
   for (int j = 0; j < NC; ++j) {
     const int n = n0 + 16 * j;
     const size_t row = (size_t)e * H + (n < H ? n + li : 0);   // H % 16 == 0
-    wr[j] = w2c + row * I + koff;
-    sr[j] = w2s + row * (I / 32) + koff / 32;
+    wr[j] = w2c + row * I + kb + 16 * lg;
+    sr[j] = w2s + row * (I / 32) + kb / 32;
   }
   f32x4 acc[NC];
 #pragma unroll
   for (int j = 0; j < NC; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (n0 < H) stream_mx<NC, U>(wr, sr, act + (size_t)(start + li) * I + koff, live, khalf / 64, acc);
+  if (n0 < H) stream_mx<NC>(wr, sr, act + (size_t)(start + li) * I + kb + 16 * lg, live, g1 - g0, acc);
   if (wk == 1)
 #pragma unroll
     for (int j = 0; j < NC; ++j) red[wn][j][lane] = acc[j];
@@ -366,11 +362,9 @@ hipError_t launch_expert_down(const uint16_t* act, const uint16_t* w2, const int
   return hipGetLastError();
 }
 
-// Chunks of 64 K values per streamed batch, act column groups per up workgroup and W2 tiles
-// per down wave.  Measured at M=8 (interleaved runs): one column group is fastest for up
-// (two: +11 %, the 298 registers leave one wave per SIMD); two W2 tiles per wave take down
-// from 425 to 393 us (four spill).
-constexpr int kMxStreamU = 4;
+// Act column groups per up workgroup and W2 tiles per down wave.  Measured at M=8
+// (interleaved runs): one column group is fastest for up (two: +11 %, the 298 registers
+// leave one wave per SIMD); two W2 tiles per wave take down from 425 to 393 us (four spill).
 constexpr int kMxUpCG = 1;
 constexpr int kMxDownNC = 2;
 
@@ -379,9 +373,10 @@ hipError_t launch_expert_up_mx(const uint16_t* x, const uint8_t* w13c, const uin
                                const int32_t* num_padded, const int2* tiles,
                                const int32_t* num_tiles, int max_tiles, int M, int H, int I,
                                int top_k, int block, uint16_t* act, hipStream_t s) {
-  if (H % 256 != 0 || I % (16 * kMxUpCG) != 0) return hipErrorInvalidValue;
+  if (H % 256 != 0 || I % (16 * kMxUpCG) != 0 || (uintptr_t)w13s % 8 != 0)
+    return hipErrorInvalidValue;
   dim3 grid(I / (16 * kMxUpCG), max_tiles);
-  hipLaunchKernelGGL((expert_up_mx_kernel<kMxStreamU, kMxUpCG>), grid, dim3(256), 0, s, x, w13c, w13s,
+  hipLaunchKernelGGL((expert_up_mx_kernel<kMxUpCG>), grid, dim3(256), 0, s, x, w13c, w13s,
                      sorted_ids, block_expert, num_padded, tiles, num_tiles, H, I, top_k, block,
                      M * top_k, act);
   return hipGetLastError();
@@ -392,9 +387,9 @@ hipError_t launch_expert_down_mx(const uint16_t* act, const uint8_t* w2c, const 
                                  const int32_t* num_padded, const int2* tiles,
                                  const int32_t* num_tiles, int max_tiles, int M, int H, int I,
                                  int top_k, int block, float* y, hipStream_t s) {
-  if (I % 128 != 0) return hipErrorInvalidValue;
+  if (I % 256 != 0 || (uintptr_t)w2s % 8 != 0) return hipErrorInvalidValue;
   dim3 grid((H + 32 * kMxDownNC - 1) / (32 * kMxDownNC), max_tiles);
-  hipLaunchKernelGGL((expert_down_mx_kernel<kMxStreamU, kMxDownNC>), grid, dim3(256), 0, s, act, w2c, w2s,
+  hipLaunchKernelGGL((expert_down_mx_kernel<kMxDownNC>), grid, dim3(256), 0, s, act, w2c, w2s,
                      sorted_ids, block_expert, num_padded, tiles, num_tiles, H, I, block,
                      M * top_k, y);
   return hipGetLastError();

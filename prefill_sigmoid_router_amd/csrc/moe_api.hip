@@ -221,10 +221,10 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
                  const moe_event_t* stage_events, moe_stream_t stream) {
   if (!sizes_ok(M, H, E, I, top_k) || !(eps > 0.0f) || !isfinite(eps)) return MOE_ERR_INVALID_ARG;
   if (!gemm_block_ok(block)) return MOE_ERR_UNSUPPORTED;
-  if (W.mx() && (H % 256 != 0 || I % 128 != 0)) return MOE_ERR_UNSUPPORTED;
+  if (W.mx() && (H % 256 != 0 || I % 256 != 0)) return MOE_ERR_UNSUPPORTED;
   if (M == 0) return MOE_OK;
   const bool w_ok = W.mx() ? (W.w13c && W.w13s && W.w2c && W.w2s && aligned(W.w13c, 16) &&
-                              aligned(W.w2c, 16))
+                              aligned(W.w2c, 16) && aligned(W.w13s, 8) && aligned(W.w2s, 8))
                            : (W.w13 && W.w2 && aligned(W.w13, 16) && aligned(W.w2, 16));
   if (!x || !router_w || !w_ok || !residual || !norm_w || !out) return MOE_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(residual, 16) ||

@@ -172,12 +172,16 @@ def test_mx_entry_points_validate_on_the_host(B):
     assert lib.moe_mx_dequantize(p(256), None, 4, 64, p(256), None) == -1
     assert lib.moe_mx_dequantize(None, None, 0, 64, None, None) == 0
 
-    def fwd_mx(H=256, I=512, w13c=256, M=4):
-        return lib.moe_forward_mx(p(256), p(256), None, None if w13c is None else p(w13c), p(256),
-                                  p(256), p(256), p(256), p(256), 1e-5, M, H, 8, I, 2, 16, p(256),
-                                  None, None, None, None, None, None, p(256), 1 << 40, None, None)
+    def fwd_mx(H=256, I=512, w13c=256, w13s=256, w2s=256, M=4):
+        return lib.moe_forward_mx(p(256), p(256), None, None if w13c is None else p(w13c),
+                                  p(w13s), p(256), p(w2s), p(256), p(256), 1e-5, M, H, 8, I, 2, 16,
+                                  p(256), None, None, None, None, None, None, p(256), 1 << 40, None,
+                                  None)
     assert fwd_mx(H=208) == -2             # H % 256 != 0
     assert fwd_mx(H=384) == -2             # H % 256 != 0
-    assert fwd_mx(I=192) == -2             # I % 128 != 0
+    assert fwd_mx(I=192) == -2             # I % 256 != 0
+    assert fwd_mx(I=384) == -2             # I % 256 != 0
     assert fwd_mx(w13c=None) == -1
+    assert fwd_mx(w13s=260) == -1          # scales must be 8-byte aligned
+    assert fwd_mx(w2s=252) == -1
     assert fwd_mx(H=250) == -1             # H % 16 != 0 fails the shared size checks first

@@ -146,9 +146,11 @@ class _OracleMxExperts:
 SMALL_MX = {
     "mx_tiny": mi.LayerConfig("mx_tiny", M=4, H=256, E=8, top_k=2, I=512, block=16),
     "mx_mid": mi.LayerConfig("mx_mid", M=37, H=1024, E=32, top_k=4, I=256, block=16),
-    "mx_many": mi.LayerConfig("mx_many", M=300, H=768, E=8, top_k=4, I=384, block=64,
+    # H=768: three 256-value K groups over four waves (one wave streams none)
+    "mx_many": mi.LayerConfig("mx_many", M=300, H=768, E=8, top_k=4, I=512, block=64,
                               zipf_s=1.0),
-    "mx_one_token": mi.LayerConfig("mx_one_token", M=1, H=512, E=64, top_k=8, I=128, block=16),
+    # I=256: one K group, so one down K half is empty
+    "mx_one_token": mi.LayerConfig("mx_one_token", M=1, H=512, E=64, top_k=8, I=256, block=16),
 }
 
 

@@ -33,9 +33,13 @@ constexpr int kUpStreamU = 8;
 constexpr int kDownStreamU = 4;
 
 // acc[j] += W_j(16 rows) . B(16 rows)^T over len K values.  wr[j] / br point at this
-// lane's first element (row start + K offset + 8 * (lane / 16)); br_live is false for
-// lanes whose B row is not a real entry (read as zero).
-template <int NW, int U>
+// lane's first element (row start + K offset + 8 * (lane / 16)).  MASKED: lanes with
+// br_live false read B as zero (their loads are skipped).  Otherwise every lane loads its B
+// row -- the caller points a lane without a real entry at lane 0's row, so it adds no cache
+// lines and its unused output column stays finite -- and the compiler, which drains the
+// next batch's loads before the MFMAs when loads sit under a lane mask, keeps them in
+// flight (measured at M=8: up 1,057 -> 1,000 us unmasked; down 494 masked, 512 unmasked).
+template <int NW, int U, bool MASKED>
 __device__ __forceinline__ void stream_k(const uint16_t* const (&wr)[NW], const uint16_t* br,
                                          bool br_live, int len, int lg, f32x4 (&acc)[NW]) {
   const u32x4 z4 = u32x4{0, 0, 0, 0};
@@ -46,7 +50,7 @@ __device__ __forceinline__ void stream_k(const uint16_t* const (&wr)[NW], const 
     for (int u = 0; u < U; ++u) {
 #pragma unroll
       for (int j = 0; j < NW; ++j) wa[0][j][u] = ld16(wr[j] + 32 * u);
-      xa[0][u] = br_live ? ld16(br + 32 * u) : z4;
+      xa[0][u] = (!MASKED || br_live) ? ld16(br + 32 * u) : z4;
     }
   }
   for (int m = 0; m < full; m += 2) {
@@ -60,7 +64,7 @@ __device__ __forceinline__ void stream_k(const uint16_t* const (&wr)[NW], const 
           for (int u = 0; u < U; ++u) {
 #pragma unroll
             for (int j = 0; j < NW; ++j) wa[h ^ 1][j][u] = ld16(wr[j] + kn + 32 * u);
-            xa[h ^ 1][u] = br_live ? ld16(br + kn + 32 * u) : z4;
+            xa[h ^ 1][u] = (!MASKED || br_live) ? ld16(br + kn + 32 * u) : z4;
           }
         }
 #pragma unroll
@@ -72,7 +76,7 @@ __device__ __forceinline__ void stream_k(const uint16_t* const (&wr)[NW], const 
   }
   for (int k = full * 32 * U; k < len; k += 32) {  // tail, 32 at a time
     const bool in = k + 8 * lg + 8 <= len;
-    const u32x4 xb = (in && br_live) ? ld16(br + k) : z4;
+    const u32x4 xb = (in && (!MASKED || br_live)) ? ld16(br + k) : z4;
 #pragma unroll
     for (int j = 0; j < NW; ++j) {
       const u32x4 wv = in ? ld16(wr[j] + k) : z4;
@@ -87,29 +91,33 @@ __device__ __forceinline__ void stream_k(const uint16_t* const (&wr)[NW], const 
 // (8-byte aligned), br at the lane's B row + the same K offset as wr.  A chunk's 16 codes
 // dequantize (exactly, to bf16) into two MFMA fragments: K values 16*lg..+8 and
 // 16*lg+8..+16 of the chunk, paired with the same K values of B -- the MFMA sums over its
-// K group whatever the order, so this only permutes K.  One 8-byte load per row and group
-// brings the scales of all four chunks (chunk u of the lane uses byte 2u + lg / 2): a byte
-// load per chunk costs as many cache-line requests as the codes themselves.
+// K group whatever the order, so this only permutes K.  Scales: a byte load per chunk costs
+// as many cache-line requests as the codes, so one 8-byte load per row brings two groups'
+// scales -- lanes 0-31 load the even group, lanes 32-63 the odd one, and a lane-half swap
+// (v_permlane32_swap) gives every lane both; chunk u of a group uses byte 2u + lg / 2.
 template <int NW>
 __device__ __forceinline__ void stream_mx(const uint8_t* const (&wr)[NW],
                                           const uint8_t* const (&sr)[NW], const uint16_t* br,
-                                          bool br_live, int ng, f32x4 (&acc)[NW]) {
+                                          int ng, f32x4 (&acc)[NW]) {
   constexpr int U = 4;
-  const u32x4 z4 = u32x4{0, 0, 0, 0};
-  const int sshift = 8 * ((threadIdx.x & 63) >> 5);   // byte lg / 2 of each 16-bit pair
+  const int upper = (threadIdx.x & 63) >> 5;   // also lg / 2
+  const int sshift = 8 * upper;
   u32x4 wc[2][NW][U], xa[2][U], xb[2][U];
-  uint2 sc[2][NW];
-  auto fetch = [&](int g, u32x4 (&cw)[NW][U], uint2 (&sv)[NW], u32x4 (&a)[U], u32x4 (&b)[U]) {
+  uint2 sp[NW];                                // pair load in flight: group 2p + upper
+  auto fetch = [&](int g, u32x4 (&cw)[NW][U], u32x4 (&a)[U], u32x4 (&b)[U]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int c = g * U + u;
 #pragma unroll
       for (int j = 0; j < NW; ++j) cw[j][u] = ld16(wr[j] + 64 * c);
-      a[u] = br_live ? ld16(br + 64 * c) : z4;
-      b[u] = br_live ? ld16(br + 64 * c + 8) : z4;
+      a[u] = ld16(br + 64 * c);
+      b[u] = ld16(br + 64 * c + 8);
     }
+  };
+  auto fetch_scales = [&](int g) {             // g even: groups g and g + 1 (if any)
+    const int gg = min(g + upper, ng - 1);
 #pragma unroll
-    for (int j = 0; j < NW; ++j) sv[j] = *reinterpret_cast<const uint2*>(sr[j] + 8 * g);
+    for (int j = 0; j < NW; ++j) sp[j] = *reinterpret_cast<const uint2*>(sr[j] + 8 * gg);
   };
   auto mma = [&](const u32x4 (&cw)[NW][U], const uint2 (&sv)[NW], const u32x4 (&a)[U],
                  const u32x4 (&b)[U]) {
@@ -125,16 +133,25 @@ __device__ __forceinline__ void stream_mx(const uint8_t* const (&wr)[NW],
         acc[j] = mfma16x16x32(hi, b[u], acc[j]);
       }
   };
-  if (ng > 0) fetch(0, wc[0], sc[0], xa[0], xb[0]);
+  if (ng <= 0) return;
+  fetch_scales(0);
+  fetch(0, wc[0], xa[0], xb[0]);
   for (int m = 0; m < ng; m += 2) {
+    if (m + 1 < ng) fetch(m + 1, wc[1], xa[1], xb[1]);
+    uint2 s_even[NW], s_odd[NW];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int mm = m + h;
-      if (mm < ng) {
-        if (mm + 1 < ng) fetch(mm + 1, wc[h ^ 1], sc[h ^ 1], xa[h ^ 1], xb[h ^ 1]);
-        mma(wc[h], sc[h], xa[h], xb[h]);
-      }
+    for (int j = 0; j < NW; ++j) {
+      const auto rx = __builtin_amdgcn_permlane32_swap(sp[j].x, sp[j].x, false, false);
+      const auto ry = __builtin_amdgcn_permlane32_swap(sp[j].y, sp[j].y, false, false);
+      s_even[j] = uint2{rx[0], ry[0]};
+      s_odd[j] = uint2{rx[1], ry[1]};
     }
+    mma(wc[0], s_even, xa[0], xb[0]);
+    if (m + 2 < ng) {
+      fetch_scales(m + 2);
+      fetch(m + 2, wc[0], xa[0], xb[0]);
+    }
+    if (m + 1 < ng) mma(wc[1], s_odd, xa[1], xb[1]);
   }
 }
 
@@ -178,13 +195,13 @@ __global__ __launch_bounds__(256) void expert_up_stream_kernel(
   const int li = lane & 15, lg = lane >> 4;
   const int gu = wave & 1, wk = wave >> 1;
   const bool live = li < nlive;
-  const int tok = live ? sorted_ids[start + li] / top_k : 0;
+  const int tok = sorted_ids[start + (live ? li : 0)] / top_k;  // dead lanes: lane 0's row
   const int n0 = blockIdx.x * 16;
   const int khalf = H >> 1;
   const int kb = wk * khalf + 8 * lg;
   const uint16_t* wr[1] = {w13 + (size_t)e * 2 * I * H + (size_t)(gu * I + n0 + li) * H + kb};
   f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
-  stream_k<1, U>(wr, x + (size_t)tok * H + kb, live, khalf, lg, acc);
+  stream_k<1, U, false>(wr, x + (size_t)tok * H + kb, live, khalf, lg, acc);
   if (wave != 0) red[wave - 1][lane] = acc[0];   // wave 1: up low-K, 2: gate high-K, 3: up high-K
   __syncthreads();
   if (wave != 0) return;
@@ -192,7 +209,7 @@ __global__ __launch_bounds__(256) void expert_up_stream_kernel(
   const f32x4 u = red[0][lane] + red[2][lane];
   float a[4];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) a[q] = silu_f32(g[q]) * u[q];
+  for (int q = 0; q < 4; ++q) a[q] = live ? silu_f32(g[q]) * u[q] : 0.0f;  // sentinel rows: 0
   uint2 v;
   v.x = pack_bf16x2(a[0], a[1]);
   v.y = pack_bf16x2(a[2], a[3]);
@@ -221,7 +238,7 @@ __global__ __launch_bounds__(256) void expert_down_stream_kernel(
   const int kb = wk * khalf + 8 * lg;
   const uint16_t* wr[1] = {w2 + (size_t)e * H * I + (size_t)(n_in ? n0 + li : 0) * I + kb};
   f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
-  if (n_in) stream_k<1, U>(wr, act + (size_t)(start + li) * I + kb, live, khalf, lg, acc);
+  if (n_in) stream_k<1, U, true>(wr, act + (size_t)(start + li) * I + kb, live, khalf, lg, acc);
 
   if (wk == 1) red[wn][lane] = acc[0];
   __syncthreads();
@@ -252,7 +269,7 @@ __global__ __launch_bounds__(256) void expert_up_mx_kernel(
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 15, lg = lane >> 4;
   const bool live = li < nlive;
-  const int tok = live ? sorted_ids[start + li] / top_k : 0;
+  const int tok = sorted_ids[start + (live ? li : 0)] / top_k;  // dead lanes: lane 0's row
   const int n0 = blockIdx.x * 16 * CG;
   const int ng = H / 256;                                  // groups of 256 K values
   const int g0 = wave * ng / 4, g1 = (wave + 1) * ng / 4;  // this wave's share of K
@@ -268,7 +285,7 @@ __global__ __launch_bounds__(256) void expert_up_mx_kernel(
   f32x4 acc[NS];
 #pragma unroll
   for (int j = 0; j < NS; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  stream_mx<NS>(wr, sr, x + (size_t)tok * H + kb + 16 * lg, live, g1 - g0, acc);
+  stream_mx<NS>(wr, sr, x + (size_t)tok * H + kb + 16 * lg, g1 - g0, acc);
   if (wave != 0)
 #pragma unroll
     for (int j = 0; j < NS; ++j) red[wave - 1][j][lane] = acc[j];
@@ -281,7 +298,7 @@ __global__ __launch_bounds__(256) void expert_up_mx_kernel(
         ((acc[2 * c + 1] + red[0][2 * c + 1][lane]) + red[1][2 * c + 1][lane]) + red[2][2 * c + 1][lane];
     float a[4];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) a[q] = silu_f32(g[q]) * u[q];
+    for (int q = 0; q < 4; ++q) a[q] = live ? silu_f32(g[q]) * u[q] : 0.0f;  // sentinel rows: 0
     uint2 v;
     v.x = pack_bf16x2(a[0], a[1]);
     v.y = pack_bf16x2(a[2], a[3]);
@@ -323,7 +340,8 @@ __global__ __launch_bounds__(256) void expert_down_mx_kernel(
   f32x4 acc[NC];
 #pragma unroll
   for (int j = 0; j < NC; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-  if (n0 < H) stream_mx<NC>(wr, sr, act + (size_t)(start + li) * I + kb + 16 * lg, live, g1 - g0, acc);
+  const int arow = start + (live ? li : 0);  // dead lanes read lane 0's row
+  if (n0 < H) stream_mx<NC>(wr, sr, act + (size_t)arow * I + kb + 16 * lg, g1 - g0, acc);
   if (wk == 1)
 #pragma unroll
     for (int j = 0; j < NC; ++j) red[wn][j][lane] = acc[j];

@@ -50,7 +50,9 @@ def test_library_exports_every_declared_symbol(B):
 
 def test_library_links_no_torch(B):
     out = subprocess.run(["ldd", B.library_path()], capture_output=True, text=True).stdout
-    assert "torch" not in out and "c10" not in out
+    # library names only: the load addresses ldd prints are hex and can spell "c10"
+    names = [line.split()[0] for line in out.splitlines() if line.strip()]
+    assert names and not any("torch" in n or n.startswith("libc10") for n in names), names
 
 
 def test_strerror_and_version(B):

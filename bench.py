@@ -285,7 +285,7 @@ def main():
                          dev, mx=mx)
         mx_line = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
         mx_line["weights"] = "MXFP8 (E4M3 + E8M0 per 32 values along K), activations bf16"
-        mx_line["up_kernel"] = "expert_up_mx_kernel<4>"
+        mx_line["up_kernel"] = "expert_up_mx_kernel"
         mx_line["up_hbm_frac"] = round(r["up_gbs"] / HBM_PEAK_GBS, 4)
         del mx
         torch.cuda.empty_cache()
@@ -294,8 +294,8 @@ def main():
     read_gbs = read_probe_gbs(torch, dev)
     traffic = load_traffic()
     rows = B.moe_gemm_tile_rows(head.M, head.E, head.top_k, head.I)
-    up_kernel = ("expert_up_stream_kernel<4>" if rows == 16
-                 else f"expert_tiled_kernel<{rows}, 8, 1, 2, true>")
+    up_kernel = ("expert_up_stream_kernel" if rows == 16
+                 else f"expert_tiled_kernel<{rows}, ..., true>")
     if traffic is not None and traffic.get("workload") != head.name:
         traffic = None  # counters were taken on another workload
     roof = {

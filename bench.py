@@ -287,6 +287,17 @@ def main():
         mx_line["weights"] = "MXFP8 (E4M3 + E8M0 per 32 values along K), activations bf16"
         mx_line["up_kernel"] = "expert_up_mx_kernel"
         mx_line["up_hbm_frac"] = round(r["up_gbs"] / HBM_PEAK_GBS, 4)
+        if not args.no_sweep:
+            mx_sweep = {}
+            for name in ("batch_m128", "batch_m512", "prefill_m2048"):
+                print(f"bench: timing {name} with MXFP8 experts", file=sys.stderr, flush=True)
+                rs = run_workload(B, mi, torch, mi.CONFIGS[name], weights, max(3, args.steps // 2),
+                                  max(1, args.warmup // 2), dev, mx=mx)
+                mx_sweep[name] = {k: (round(v, 4) if isinstance(v, float) else v)
+                                  for k, v in rs.items()}
+                mx_sweep[name]["tile_rows"] = B.moe_gemm_tile_rows_mx(
+                    rs["M"], head.E, head.top_k, head.I)
+            mx_line["sweep"] = mx_sweep
         del mx
         torch.cuda.empty_cache()
 

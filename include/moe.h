@@ -61,7 +61,7 @@ enum {
 /* Human-readable text of a status code.  Never NULL; static storage. */
 const char* moe_strerror(int status);
 
-/* ABI version of this header (major * 100 + minor): 102. */
+/* ABI version of this header (major * 100 + minor): 103. */
 int moe_abi_version(void);
 
 /*
@@ -93,6 +93,8 @@ size_t moe_workspace_bytes(int32_t M, int32_t H, int32_t E, int32_t I, int32_t t
  * multiple of the tiled kernels' 256 act columns.  Host-only; 0 for invalid sizes.
  */
 int32_t moe_gemm_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I);
+/* The same for moe_forward_mx (MXFP8 weights; I a multiple of 256, else 0). */
+int32_t moe_gemm_tile_rows_mx(int32_t M, int32_t E, int32_t top_k, int32_t I);
 
 /*
  * Router (step 1).
@@ -206,9 +208,9 @@ int moe_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
  * w13 and w2; every other argument, the workspace and the outputs are those of
  * moe_forward.  The result is the layer on the dequantized weights.  H and I must be
  * multiples of 256 (MOE_ERR_UNSUPPORTED otherwise); codes 16-byte and scales 8-byte
- * aligned (MOE_ERR_INVALID_ARG otherwise).  The GEMMs are the weight-streaming
- * kernels at every size: they fit decode (few tokens per expert); there are no LDS-tiled
- * MXFP8 kernels for large batches.
+ * aligned (MOE_ERR_INVALID_ARG otherwise).  The GEMMs stream the codes straight into the
+ * MFMA operands when experts see few tokens and dequantize them into the LDS tiles of the
+ * tiled kernels when they see many (moe_gemm_tile_rows_mx).
  */
 int moe_forward_mx(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
                    const uint8_t* w13_codes, const uint8_t* w13_scales,

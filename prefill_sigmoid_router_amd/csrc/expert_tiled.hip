@@ -241,6 +241,215 @@ __global__ __launch_bounds__(64 * WN * WM) void expert_tiled_kernel(
   }
 }
 
+// MXFP8 weights (E4M3 codes, one E8M0 scale byte per 32 values along K) in the tiled
+// kernels.  Same workgroup tile, work order, LDS ring layout and MFMA loop as
+// expert_tiled_kernel; the weight part of a ring stage is filled from the codes instead of
+// by copies: each thread loads PIECES pieces of 16 codes (4 lanes cover a row's 64 codes
+// of a chunk: 16 rows x 64 bytes per wave load), dequantizes them exactly to bf16 with
+// the block's scale (v_cvt_scalef32_pk_bf16_fp8) and writes them into the swizzled slots
+// with ds_write_b128.  The scales of 4 chunks of a row come with one 8-byte load.  Token
+// rows still arrive by global_load_lds.  Per chunk c: wait for the token copies of c and
+// barrier, then dequantize the codes of c + 1 (loaded while c - 1 was computed) into the
+// other stage, copy the token rows of c + 1 there, load the codes of c + 2, and compute c.
+template <int BM, int WN, int WM, bool UP>
+__global__ __launch_bounds__(64 * WN * WM) void expert_tiled_mx_kernel(
+    const uint16_t* __restrict__ tok_src, const uint8_t* __restrict__ wc,
+    const uint8_t* __restrict__ ws, const int32_t* __restrict__ sorted_ids,
+    const int32_t* __restrict__ block_expert, const int2* __restrict__ tiles,
+    const int32_t* __restrict__ num_tiles, int n_ntiles, int K, int ncols, int I, int top_k,
+    int block, uint16_t* __restrict__ act, float* __restrict__ y) {
+  using C = TiledCfg<BM, WN, WM>;
+  constexpr int S = 2;
+  constexpr int TCOPIES = 2 * C::MT;                    // 1 KiB token copies per chunk
+  static_assert(TCOPIES % (WN * WM) == 0, "token copies must split evenly over the waves");
+  constexpr int TPW = TCOPIES / (WN * WM);
+  constexpr int PIECES = 16 * C::WT * 4 / C::THREADS;   // 16-code pieces per thread per chunk
+  static_assert(PIECES * C::THREADS == 16 * C::WT * 4, "code pieces must split evenly");
+  static_assert(S * C::FRAGS * 1024 <= 160 * 1024, "the ring must fit the LDS");
+  __shared__ __align__(16) unsigned char lds[S * C::FRAGS * 1024];
+
+  const int ntiles_live = *num_tiles;
+  const int live_items = ntiles_live * n_ntiles;
+  const int per_xcd = (live_items + kXcds - 1) / kXcds;
+  const int slot = blockIdx.x / kXcds;
+  if (slot >= per_xcd) return;
+  const int logical = (blockIdx.x % kXcds) * per_xcd + slot;
+  if (logical >= live_items) return;
+  const int ntile = logical / ntiles_live;
+  const int ti = logical % ntiles_live;
+  const int2 tile = tiles[ti];
+  const int start = tile.x, nlive = tile.y;
+  const int mt_active = (nlive + 15) >> 4;
+  const int e = block_expert[start / block];
+
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int li = lane & 15, lg = lane >> 4;
+  const int wn = wave % WN, wm = wave / WN;
+  const int col0 = UP ? ntile * 32 * WN : ntile * 64 * WN;
+  const int rows_e = UP ? 2 * I : ncols;                // weight rows per expert
+
+  // code pieces: piece id = tid + THREADS * i is row R = id / 4 of the workgroup's weight
+  // rows (row tile R / 16, weight tiles as in expert_tiled_kernel), K values 16 (id % 4)
+  // .. + 16 of the chunk = the two 8-value slots q = 2 (id % 4) and q + 1
+  const uint8_t* wsrc[PIECES];
+  const uint8_t* ssrc[PIECES];
+  int wdst[PIECES][2];
+  int sbyte[PIECES];                                     // scale byte of a chunk: 2 (c % 4) + this
+#pragma unroll
+  for (int i = 0; i < PIECES; ++i) {
+    const int id = tid + C::THREADS * i;
+    const int R = id >> 2, p = id & 3;
+    const int t = R >> 4, rr = R & 15;
+    int row;
+    if (UP) row = (t < C::WT / 2) ? col0 + t * 16 + rr : I + col0 + (t - C::WT / 2) * 16 + rr;
+    else row = col0 + t * 16 + rr;
+    if (!UP && row >= ncols) row = 0;                    // rows past H: never stored
+    const size_t grow = (size_t)e * rows_e + row;
+    wsrc[i] = wc + grow * K + 16 * p;
+    ssrc[i] = ws + grow * (K / 32);
+    sbyte[i] = p >> 1;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int q = 2 * p + h;
+      wdst[i][h] = t * 2048 + (rr >> 3) * 1024 + (rr & 7) * 128 + ((q ^ (rr & 7) ^ (rr >> 3)) * 16);
+    }
+  }
+  // token copies: copy f = 2 WT + wave * TPW + i as in expert_tiled_kernel
+  const uint16_t* tsrc[TPW];
+#pragma unroll
+  for (int i = 0; i < TPW; ++i) {
+    const int f = 2 * C::WT + wave * TPW + i;
+    const int rt = f >> 1, h = f & 1;
+    const int rr = 8 * h + (lane >> 3);
+    const int koff = 8 * ((lane & 7) ^ (lane >> 3) ^ h);
+    const int r = 16 * (rt - C::WT) + rr;
+    const bool on = r < nlive;
+    const int prow = start + (on ? r : 0);
+    if (UP) {
+      const int sid = on ? sorted_ids[prow] : 0;
+      tsrc[i] = tok_src + (size_t)(sid < 0 ? 0 : sid / top_k) * K + koff;
+    } else {
+      tsrc[i] = tok_src + (size_t)prow * K + koff;
+    }
+  }
+  int wtile[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+    wtile[j] = UP ? ((j < 2) ? 2 * wn + j : C::WT / 2 + 2 * wn + (j - 2)) : 4 * wn + j;
+
+  const int nch = K / kTileKC;                           // K is a multiple of 256
+  u32x4 codes[PIECES];
+  uint2 scl[PIECES];
+  auto load = [&](int c) {                               // codes of chunk c (+ scales of its 4)
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) codes[i] = ld16(wsrc[i] + c * kTileKC);
+    if ((c & 3) == 0) {
+#pragma unroll
+      for (int i = 0; i < PIECES; ++i) scl[i] = *reinterpret_cast<const uint2*>(ssrc[i] + 2 * c);
+    }
+  };
+  auto put = [&](int c, int stage) {                     // dequantized codes of chunk c
+    unsigned char* base = lds + (size_t)stage * C::FRAGS * 1024;
+#pragma unroll
+    for (int i = 0; i < PIECES; ++i) {
+      const int b = 2 * (c & 3) + sbyte[i];
+      const uint32_t word = b < 4 ? scl[i].x : scl[i].y;
+      u32x4 lo, hi;
+      mx_dequant16(codes[i], (word >> (8 * (b & 3))) & 0xFFu, lo, hi);
+      *reinterpret_cast<u32x4*>(base + wdst[i][0]) = lo;
+      *reinterpret_cast<u32x4*>(base + wdst[i][1]) = hi;
+    }
+  };
+  auto copy_tokens = [&](int c, int stage) {
+    unsigned char* base = lds + (size_t)stage * C::FRAGS * 1024;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i)
+      __builtin_amdgcn_global_load_lds((global_void*)(tsrc[i] + c * kTileKC),
+                                       (lds_void*)(base + (2 * C::WT + wave * TPW + i) * 1024),
+                                       16, 0, 0);
+  };
+  const int frag_off = (li >> 3) * 1024 + (li & 7) * 128;
+  auto frag = [&](int stage, int t, int ks) -> u32x4 {
+    const int q = (lg + 4 * ks) ^ (li & 7) ^ (li >> 3);
+    return *reinterpret_cast<const u32x4*>(lds + (size_t)stage * C::FRAGS * 1024 + t * 2048 +
+                                           frag_off + q * 16);
+  };
+
+  f32x4 acc[4][C::MTW];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int s = 0; s < C::MTW; ++s) acc[j][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int my_active = mt_active - wm * C::MTW;
+
+  auto compute = [&](int stage) {
+    if (my_active <= 0) return;
+#pragma unroll
+    for (int ks = 0; ks < kTileKS; ++ks) {
+      u32x4 wa[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wa[j] = frag(stage, wtile[j], ks);
+#pragma unroll
+      for (int s = 0; s < C::MTW; ++s) {
+        if (s < my_active) {
+          const u32x4 xb = frag(stage, C::WT + wm * C::MTW + s, ks);
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[j][s] = mfma16x16x32(wa[j], xb, acc[j][s]);
+        }
+      }
+    }
+  };
+
+  // The codes of a chunk are dequantized before the token copies of the same chunk are
+  // issued, so waiting for the codes never waits for those copies.
+  load(0);
+  put(0, 0);
+  copy_tokens(0, 0);
+  if (nch > 1) load(1);
+  for (int c = 0; c < nch; ++c) {
+    // this wave's token copies of chunk c and the codes of c + 1 (needed right after the
+    // barrier) have landed; after the barrier chunk c is in LDS for every wave and chunk
+    // c - 1 is fully consumed
+    wait_vmcnt<0>();
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    if (c + 1 < nch) {
+      put(c + 1, (c + 1) & 1);
+      copy_tokens(c + 1, (c + 1) & 1);
+      if (c + 2 < nch) load(c + 2);
+    }
+    compute(c & 1);
+  }
+
+#pragma unroll
+  for (int s = 0; s < C::MTW; ++s) {
+    if (s >= my_active) continue;
+    const int r = 16 * (wm * C::MTW + s) + li;
+    if (UP) {
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int n = col0 + wn * 32 + h * 16 + 4 * lg;
+        float a[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) a[q] = silu_f32(acc[h][s][q]) * acc[2 + h][s][q];
+        uint2 v;
+        v.x = pack_bf16x2(a[0], a[1]);
+        v.y = pack_bf16x2(a[2], a[3]);
+        *reinterpret_cast<uint2*>(act + (size_t)(start + r) * I + n) = v;
+      }
+    } else if (r < nlive) {
+      const int dst = sorted_ids[start + r];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = col0 + wn * 64 + j * 16 + 4 * lg;
+        if (n < ncols)
+          *reinterpret_cast<float4*>(y + (size_t)dst * ncols + n) =
+              make_float4(acc[j][s][0], acc[j][s][1], acc[j][s][2], acc[j][s][3]);
+      }
+    }
+  }
+}
+
 template <int BM, int WN, int WM, int S, bool UP>
 static hipError_t launch_tiled(const uint16_t* src, const uint16_t* w, const int32_t* sorted_ids,
                                const int32_t* block_expert, const int2* tiles,
@@ -297,6 +506,55 @@ hipError_t launch_expert_down_tiled(const uint16_t* act, const uint16_t* w2,
     return launch_tiled<128, kTileWN, 1, kTileStages, false>(act, w2, sorted_ids, block_expert, tiles,
                                                    num_tiles, max_tiles, I, H, I, top_k, block,
                                                    nullptr, y, s);
+  return hipErrorInvalidValue;
+}
+
+
+template <int BM, bool UP>
+static hipError_t launch_tiled_mx(const uint16_t* src, const uint8_t* wc, const uint8_t* ws,
+                                  const int32_t* sorted_ids, const int32_t* block_expert,
+                                  const int2* tiles, const int32_t* num_tiles, int max_tiles, int K,
+                                  int ncols, int I, int top_k, int block, uint16_t* act, float* y,
+                                  hipStream_t s) {
+  const int per_ntile = UP ? 32 * kTileWN : 64 * kTileWN;
+  if (K % 256 != 0 || (UP && I % per_ntile != 0) || (uintptr_t)ws % 8 != 0)
+    return hipErrorInvalidValue;
+  const int n_ntiles = (ncols + per_ntile - 1) / per_ntile;
+  const long total = (long)max_tiles * n_ntiles;
+  const long grid = (total + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL((expert_tiled_mx_kernel<BM, kTileWN, 1, UP>), dim3((unsigned)grid),
+                     dim3(TiledCfg<BM, kTileWN, 1>::THREADS), 0, s, src, wc, ws, sorted_ids,
+                     block_expert, tiles, num_tiles, n_ntiles, K, ncols, I, top_k, block, act, y);
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_up_tiled_mx(const uint16_t* x, const uint8_t* w13c, const uint8_t* w13s,
+                                     const int32_t* sorted_ids, const int32_t* block_expert,
+                                     const int2* tiles, const int32_t* num_tiles, int max_tiles,
+                                     int tile_rows, int M, int H, int I, int top_k, int block,
+                                     uint16_t* act, hipStream_t s) {
+  (void)M;
+  if (tile_rows == 64)
+    return launch_tiled_mx<64, true>(x, w13c, w13s, sorted_ids, block_expert, tiles, num_tiles,
+                                     max_tiles, H, I, I, top_k, block, act, nullptr, s);
+  if (tile_rows == 128)
+    return launch_tiled_mx<128, true>(x, w13c, w13s, sorted_ids, block_expert, tiles, num_tiles,
+                                      max_tiles, H, I, I, top_k, block, act, nullptr, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_expert_down_tiled_mx(const uint16_t* act, const uint8_t* w2c, const uint8_t* w2s,
+                                       const int32_t* sorted_ids, const int32_t* block_expert,
+                                       const int2* tiles, const int32_t* num_tiles, int max_tiles,
+                                       int tile_rows, int M, int H, int I, int top_k, int block,
+                                       float* y, hipStream_t s) {
+  (void)M;
+  if (tile_rows == 64)
+    return launch_tiled_mx<64, false>(act, w2c, w2s, sorted_ids, block_expert, tiles, num_tiles,
+                                      max_tiles, I, H, I, top_k, block, nullptr, y, s);
+  if (tile_rows == 128)
+    return launch_tiled_mx<128, false>(act, w2c, w2s, sorted_ids, block_expert, tiles, num_tiles,
+                                       max_tiles, I, H, I, top_k, block, nullptr, y, s);
   return hipErrorInvalidValue;
 }
 

@@ -54,6 +54,19 @@ hipError_t launch_expert_down_tiled(const uint16_t* act, const uint16_t* w2,
                                     int tile_rows, int M, int H, int I, int top_k, int block,
                                     float* y, hipStream_t s);
 
+// The same LDS-tiled kernels on MXFP8 weights (codes dequantized into the LDS tiles); K
+// (H for up, I for down) a multiple of 256, scales 8-byte aligned.
+hipError_t launch_expert_up_tiled_mx(const uint16_t* x, const uint8_t* w13c, const uint8_t* w13s,
+                                     const int32_t* sorted_ids, const int32_t* block_expert,
+                                     const int2* tiles, const int32_t* num_tiles, int max_tiles,
+                                     int tile_rows, int M, int H, int I, int top_k, int block,
+                                     uint16_t* act, hipStream_t s);
+hipError_t launch_expert_down_tiled_mx(const uint16_t* act, const uint8_t* w2c, const uint8_t* w2s,
+                                       const int32_t* sorted_ids, const int32_t* block_expert,
+                                       const int2* tiles, const int32_t* num_tiles, int max_tiles,
+                                       int tile_rows, int M, int H, int I, int top_k, int block,
+                                       float* y, hipStream_t s);
+
 // MXFP8 weights (E4M3 codes, one E8M0 scale byte per 32 values along K): quantize bf16
 // [rows, K] (K % 32 == 0), dequantize back to bf16, and the streaming GEMMs on them
 // (same work items as launch_expert_up / launch_expert_down; H resp. I % 128 == 0).

@@ -69,10 +69,12 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 // tiles when experts see a few tokens, LDS-tiled MFMA over 64- or 128-row token tiles
 // when they see many (thresholds measured on MI355X at H=7168, I=2048, E=256).  Returns
 // the tile height; 16 selects the streaming kernels.
-int gemm_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I) {
+// MXFP8 weights stay on the streaming kernels longer: their tiled kernels dequantize every
+// weight once per token tile (streaming faster up to 12 tokens per expert, tiled from 16).
+int gemm_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I, bool mx) {
   if (I % moe::tiled_up_columns() != 0) return 16;
   const int64_t per_expert = (int64_t)M * top_k / E;
-  if (per_expert < 4) return 16;
+  if (per_expert < (mx ? 16 : 4)) return 16;
   if (per_expert < 32) return 64;
   return 128;
 }
@@ -92,7 +94,7 @@ const char* moe_strerror(int status) {
   }
 }
 
-int moe_abi_version(void) { return 102; }
+int moe_abi_version(void) { return 103; }
 
 size_t moe_align_capacity(int32_t M, int32_t top_k, int32_t E, int32_t block) {
   if (M < 0 || top_k < 1 || E < 1 || block < 1) return 0;
@@ -107,7 +109,12 @@ size_t moe_route_workspace_bytes(int32_t M, int32_t E) {
 
 int32_t moe_gemm_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I) {
   if (M < 0 || E < 1 || E > kMaxE || top_k < 1 || top_k > E || I < 64 || I % 64 != 0) return 0;
-  return gemm_tile_rows(M, E, top_k, I);
+  return gemm_tile_rows(M, E, top_k, I, false);
+}
+
+int32_t moe_gemm_tile_rows_mx(int32_t M, int32_t E, int32_t top_k, int32_t I) {
+  if (M < 0 || E < 1 || E > kMaxE || top_k < 1 || top_k > E || I < 256 || I % 256 != 0) return 0;
+  return gemm_tile_rows(M, E, top_k, I, true);
 }
 
 size_t moe_workspace_bytes(int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k,
@@ -260,17 +267,19 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   if (moe::launch_route(x, router_w, router_bias, M, H, E, top_k, ids, w, keys, s) != hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(1)) return MOE_ERR_HIP;
-  // MXFP8 weights run the streaming kernels at every size (no tiled MXFP8 kernels)
-  const int trows = W.mx() ? 16 : gemm_tile_rows(M, E, top_k, I);
+  const int trows = gemm_tile_rows(M, E, top_k, I, W.mx());
   const int max_tiles = moe::tile_capacity(M * top_k, E, trows);
   if (moe::launch_align(ids, M * top_k, E, block, sorted, bexp, npad, trows, tiles, ntiles, s) !=
       hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(2)) return MOE_ERR_HIP;
   hipError_t up_err;
-  if (W.mx())
+  if (W.mx() && trows == 16)
     up_err = moe::launch_expert_up_mx(x, W.w13c, W.w13s, sorted, bexp, npad, tiles, ntiles,
                                       max_tiles, M, H, I, top_k, block, act, s);
+  else if (W.mx())
+    up_err = moe::launch_expert_up_tiled_mx(x, W.w13c, W.w13s, sorted, bexp, tiles, ntiles,
+                                            max_tiles, trows, M, H, I, top_k, block, act, s);
   else if (trows == 16)
     up_err = moe::launch_expert_up(x, W.w13, sorted, bexp, npad, tiles, ntiles, max_tiles, M, H, I,
                                    top_k, block, act, s);
@@ -280,9 +289,12 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   if (up_err != hipSuccess) return MOE_ERR_HIP;
   if (!mark(3)) return MOE_ERR_HIP;
   hipError_t down_err;
-  if (W.mx())
+  if (W.mx() && trows == 16)
     down_err = moe::launch_expert_down_mx(act, W.w2c, W.w2s, sorted, bexp, npad, tiles, ntiles,
                                           max_tiles, M, H, I, top_k, block, y, s);
+  else if (W.mx())
+    down_err = moe::launch_expert_down_tiled_mx(act, W.w2c, W.w2s, sorted, bexp, tiles, ntiles,
+                                                max_tiles, trows, M, H, I, top_k, block, y, s);
   else if (trows == 16)
     down_err = moe::launch_expert_down(act, W.w2, sorted, bexp, npad, tiles, ntiles, max_tiles, M,
                                        H, I, top_k, block, y, s);

@@ -56,7 +56,7 @@ def test_library_links_no_torch(B):
 
 
 def test_strerror_and_version(B):
-    assert B.moe_abi_version() == 102
+    assert B.moe_abi_version() == 103
     for s in (0, -1, -2, -3, -4, 17):
         assert isinstance(B.moe_strerror(s), str) and B.moe_strerror(s)
 
@@ -148,6 +148,14 @@ def test_gemm_tile_rows_follows_tokens_per_expert(B):
     assert B.moe_gemm_tile_rows(2048, 256, 16, 100) == 0
     assert B.moe_gemm_tile_rows(8, 0, 1, 2048) == 0
     assert B.moe_gemm_tile_rows(-1, 256, 16, 2048) == 0
+    # MXFP8 weights: streaming below 16 tokens per expert, I a multiple of 256
+    assert B.moe_gemm_tile_rows_mx(8, 256, 16, 2048) == 16
+    assert B.moe_gemm_tile_rows_mx(128, 256, 16, 2048) == 16
+    assert B.moe_gemm_tile_rows_mx(255, 256, 16, 2048) == 16
+    assert B.moe_gemm_tile_rows_mx(256, 256, 16, 2048) == 64
+    assert B.moe_gemm_tile_rows_mx(512, 256, 16, 2048) == 128
+    assert B.moe_gemm_tile_rows_mx(2048, 256, 16, 2048) == 128
+    assert B.moe_gemm_tile_rows_mx(2048, 256, 16, 384) == 0
 
 
 def test_read_probe_library_is_built_apart_from_the_layer(B):

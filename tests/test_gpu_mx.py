@@ -143,10 +143,15 @@ class _OracleMxExperts:
         return mxo.mx_dequantize_bf16_bits(c, s)
 
 
+# expected tokens per expert M * top_k / E: below 16 the streaming kernels (mx_tiny 1,
+# mx_mid 4.6, mx_one_token 0.1), 16..31 the 64-row LDS tiles (mx_tiles64 24), from 32 the
+# 128-row tiles (mx_many 150)
 SMALL_MX = {
     "mx_tiny": mi.LayerConfig("mx_tiny", M=4, H=256, E=8, top_k=2, I=512, block=16),
     "mx_mid": mi.LayerConfig("mx_mid", M=37, H=1024, E=32, top_k=4, I=256, block=16),
     # H=768: three 256-value K groups over four waves (one wave streams none)
+    "mx_tiles64": mi.LayerConfig("mx_tiles64", M=48, H=512, E=8, top_k=4, I=256, block=32,
+                                 zipf_s=1.0),
     "mx_many": mi.LayerConfig("mx_many", M=300, H=768, E=8, top_k=4, I=512, block=64,
                               zipf_s=1.0),
     # I=256: one K group, so one down K half is empty
@@ -192,14 +197,28 @@ def test_forward_mx_rejects_unsupported_widths(B, dev):
     assert ei.value.status == -2
 
 
-def test_forward_mx_full_decode(B, dev):
-    """The decode workload (M=8, H=7168, E=256, k=16, I=2048) with MXFP8 weights: routing and
-    plan bit-exact for every token; codes of the experts a sampled token uses bit-exact;
-    that token's output against the oracle on the oracle's own dequantized weights."""
-    cfg = mi.CONFIGS["decode_m8"]
-    print("forward_mx full-size decode", flush=True)
-    L = mi.make_layer(cfg, device=dev, seed=0)
-    mx = _mx_weights(B, L, dev)
+MX_FULL = ["decode_m8", "batch_m128", "prefill_m2048"]
+
+
+@pytest.fixture(scope="module")
+def mx_full(B, dev):
+    """The real-shape expert weights (E=256, H=7168, I=2048) and their MXFP8 codes."""
+    L = mi.make_layer(mi.CONFIGS["decode_m8"], device=dev, seed=0)
+    weights = {k: L[k] for k in ("w13", "w2", "router_w", "norm_w")}
+    return weights, _mx_weights(B, L, dev)
+
+
+@pytest.mark.parametrize("name", MX_FULL)
+def test_forward_mx_full_size(B, dev, mx_full, name):
+    """The real-shape workloads with MXFP8 weights -- the streaming kernels at M=8 and
+    M=128, LDS tiles of 128 rows at M=2048: routing and plan bit-exact for
+    every token; codes of the experts a sampled token uses bit-exact; that token's output
+    against the oracle on the oracle's own dequantized weights."""
+    cfg = mi.CONFIGS[name]
+    print(f"forward_mx full-size {name} M={cfg.M}", flush=True)
+    weights, mx = mx_full
+    L = mi.make_layer(cfg, device=dev, seed=0, with_experts=False)
+    L.update(weights)
     r = _run_forward_mx(B, L, dev, mx)
     k = cfg.top_k
     ref_ids, ref_w, _ = orc.route(bits(L["x"]), bits(L["router_w"]), _bias_np(L), k)
@@ -209,7 +228,7 @@ def test_forward_mx_full_decode(B, dev):
     assert np.array_equal(r["sorted"].cpu().numpy()[:n_pad], sorted_ids)
     out = r["out"].float().cpu().numpy()
     assert np.isfinite(out).all()
-    t = 3
+    t = cfg.M // 2 + 3 if cfg.M > 8 else 3
     for e in ref_ids[t][:2]:   # two of its experts' codes, bit for bit
         c, s = mxo.mx_quantize(bits(L["w13"][int(e)]))
         assert np.array_equal(mx[0][int(e)].cpu().numpy(), c) and np.array_equal(mx[1][int(e)].cpu().numpy(), s)
@@ -218,5 +237,5 @@ def test_forward_mx_full_decode(B, dev):
                                                   _OracleMxExperts(L["w2"]), bits(L["residual"]),
                                                   bits(L["norm_w"]), L["eps"], k)
     assert np.array_equal(s_ids, ref_ids[[t]])
-    _check_close(r["out"][[t]], ref_out, "decode mx sampled out")
-    _check_close(r["rout"][[t]], ref_z, "decode mx sampled residual_out")
+    _check_close(r["out"][[t]], ref_out, f"{name} mx sampled out")
+    _check_close(r["rout"][[t]], ref_z, f"{name} mx sampled residual_out")

@@ -10,8 +10,8 @@
 //
 // One workgroup of 1024 threads per token; each thread owns V groups of 4 hidden values,
 // so z stays in registers between the sum of squares and the scaling.  The y rows of 8
-// picks are requested together (all V groups), so a token costs about k/8 memory round
-// trips rather than k.  All arithmetic is fp32 with a single bf16 rounding (RNE) at the
+// picks are requested together (all V groups), with the residual and norm weight in the
+// first batch, so a token costs about k/8 memory round trips rather than k + 2.  All arithmetic is fp32 with a single bf16 rounding (RNE) at the
 // store; the combine adds the picks in ascending j.
 #include "device_common.h"
 #include "launchers.h"
@@ -33,6 +33,18 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   float4 m[V];
 #pragma unroll
   for (int v = 0; v < V; ++v) m[v] = make_float4(0.f, 0.f, 0.f, 0.f);
+
+  // residual and norm weight are requested with the first batch of y rows, so a token
+  // costs ceil(k / 8) memory round trips in all
+  const uint2* rr = reinterpret_cast<const uint2*>(residual + (size_t)t * H);
+  const uint2* gw = reinterpret_cast<const uint2*>(norm_w);
+  uint2 res[V], gv[V];
+#pragma unroll
+  for (int v = 0; v < V; ++v) {
+    const int c = tid + kFinThreads * v;
+    res[v] = c < ngroups ? rr[c] : uint2{0u, 0u};
+    gv[v] = c < ngroups ? gw[c] : uint2{0u, 0u};
+  }
 
   const float* yt = y + (size_t)t * top_k * H;
   const float* wt = topk_w + (size_t)t * top_k;
@@ -62,13 +74,12 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     }
   }
 
-  const uint2* rr = reinterpret_cast<const uint2*>(residual + (size_t)t * H);
   float ss = 0.f;
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     const int c = tid + kFinThreads * v;
     if (c < ngroups) {
-      const uint2 r = rr[c];
+      const uint2 r = res[v];
       m[v].x += bf16lo(r.x);
       m[v].y += bf16hi(r.x);
       m[v].z += bf16lo(r.y);
@@ -87,14 +98,13 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   for (int w = 0; w < kFinThreads / kWave; ++w) total += part[w];
   const float inv = 1.0f / sqrtf(total / (float)H + eps);
 
-  const uint2* gw = reinterpret_cast<const uint2*>(norm_w);
   uint2* ot = reinterpret_cast<uint2*>(out + (size_t)t * H);
   uint2* rt = residual_out ? reinterpret_cast<uint2*>(residual_out + (size_t)t * H) : nullptr;
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     const int c = tid + kFinThreads * v;
     if (c < ngroups) {
-      const uint2 g = gw[c];
+      const uint2 g = gv[v];
       uint2 o;
       o.x = pack_bf16x2(m[v].x * inv * bf16lo(g.x), m[v].y * inv * bf16hi(g.x));
       o.y = pack_bf16x2(m[v].z * inv * bf16lo(g.y), m[v].w * inv * bf16hi(g.y));

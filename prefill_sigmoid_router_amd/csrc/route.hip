@@ -124,6 +124,46 @@ __device__ __forceinline__ void count_ahead(const double* vals, int n, const dou
   }
 }
 
+// Order-preserving 32-bit key of a lower bound lo of expert e: lo rounded toward -inf to
+// fp32, mapped to an unsigned integer that orders like the value, its low 10 bits replaced
+// by 1023 - e (keys are unique; equal truncated values order by ascending id).  Clearing
+// those bits can only lower the value, and the k-th largest key decodes (key_floor) to a
+// value at or below the k-th largest lo: a valid, slightly lower threshold for the
+// candidate filter, found with integer compares instead of fp64 ones.
+__device__ __forceinline__ uint32_t lo_key(double lo, int e) {
+  const uint32_t b = __float_as_uint(__double2float_rd(lo));
+  const uint32_t ord = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return (ord & ~0x3FFu) | (uint32_t)(1023 - e);
+}
+__device__ __forceinline__ double key_floor(uint32_t key) {
+  const uint32_t ord = key & ~0x3FFu;
+  const uint32_t b = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
+  const float f = __uint_as_float(b);
+  return isfinite(f) ? (double)f : -INFINITY;   // non-finite bounds: every expert is a candidate
+}
+
+// rank[s] = number of keys in vals[0, n) greater than v[s] (sixteen LDS values per step)
+template <int SL>
+__device__ __forceinline__ void count_greater(const uint32_t* vals, int n, const uint32_t (&v)[SL],
+                                              int (&rank)[SL]) {
+#pragma unroll
+  for (int s = 0; s < SL; ++s) rank[s] = 0;
+  int j = 0;
+  for (; j + 16 <= n; j += 16) {
+    uint4 b[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) b[u] = reinterpret_cast<const uint4*>(vals + j)[u];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int s = 0; s < SL; ++s)
+        rank[s] += (b[u].x > v[s]) + (b[u].y > v[s]) + (b[u].z > v[s]) + (b[u].w > v[s]);
+  }
+  for (; j < n; ++j)
+#pragma unroll
+    for (int s = 0; s < SL; ++s) rank[s] += vals[j] > v[s] ? 1 : 0;
+}
+
 // One workgroup per token.  Thread i owns experts i, i + 256, ... (SL of them).  The
 // token's keys (logit + bias) sit in LDS; each owned expert's rank is the number of
 // experts ahead of it -- a larger key, or an equal key with a lower id -- counted against
@@ -186,9 +226,9 @@ __global__ __launch_bounds__(kTopkThreads) void router_topk_kernel(const double*
 //    fp64.
 // 2. router_select_kernel, one workgroup per token: with d = n 2^-23 A (1 + 2^-9) plus an
 //    absolute floor for flushed subnormal products and the fp64 key rounding, lo = L + b
-//    - d and hi = L + b + d, T = the k-th largest lo.  An expert with hi < T has an exact
-//    key below at least k other exact keys, so it cannot be picked; every other expert is
-//    a candidate.  The candidates' keys are recomputed as fp64 dot products and ranked
+//    - d and hi = L + b + d, T at or below the k-th largest lo (found on 32-bit keys, see
+//    lo_key).  An expert with hi < T has an exact key below at least k other exact keys,
+//    so it cannot be picked; every other expert is a candidate.  The candidates' keys are recomputed as fp64 dot products and ranked
 //    exactly as the fp64 path ranks them (key descending, ties to the lower id).
 // ---------------------------------------------------------------------------------------
 constexpr int kLgTokens = 32;               // tokens per workgroup
@@ -337,7 +377,9 @@ __global__ __launch_bounds__(kTopkThreads) void router_select_kernel(
   for (int ch = tid; ch < (H >> 3); ch += kTopkThreads) s_x[ch] = ld16(x + (size_t)t * H + (size_t)ch * 8);
 
   const double rel = (double)nround * 0x1p-23 * (1.0 + 0x1p-9);
+  uint32_t* s_k32 = reinterpret_cast<uint32_t*>(s_lo);   // 32-bit keys of the lower bounds
   double lo[SL], hi[SL];
+  uint32_t mykey[SL];
 #pragma unroll
   for (int s = 0; s < SL; ++s) {
     const int e = tid + kTopkThreads * s;
@@ -352,18 +394,17 @@ __global__ __launch_bounds__(kTopkThreads) void router_select_kernel(
       const double d = a * rel + fabs(key) * 0x1p-50 + (double)H * 0x1p-126 + 1e-300;
       lo[s] = key - d;
       hi[s] = key + d;
-      s_lo[e] = lo[s];
     }
+    mykey[s] = lo_key(lo[s], e);
+    if (e < E) s_k32[e] = mykey[s];
   }
   __syncthreads();
-  // T = the top_k-th largest lower bound (rank top_k - 1 by (lo desc, id asc))
-  int rank[SL], myid[SL];
-#pragma unroll
-  for (int s = 0; s < SL; ++s) myid[s] = tid + kTopkThreads * s;
-  count_ahead<SL>(s_lo, E, lo, myid, rank);
+  // T = the decoded top_k-th largest key: at or below the top_k-th largest lower bound
+  int rank[SL];
+  count_greater<SL>(s_k32, E, mykey, rank);
 #pragma unroll
   for (int s = 0; s < SL; ++s)
-    if (tid + kTopkThreads * s < E && rank[s] == top_k - 1) s_T = lo[s];
+    if (tid + kTopkThreads * s < E && rank[s] == top_k - 1) s_T = key_floor(mykey[s]);
   __syncthreads();
   const double T = s_T;
 

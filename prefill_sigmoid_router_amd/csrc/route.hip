@@ -358,7 +358,10 @@ __global__ __launch_bounds__(256) void router_logits_mfma_kernel(
 }
 
 template <int SL>
-__global__ __launch_bounds__(kTopkThreads) void router_select_kernel(
+// At most 128 registers for E <= 512 (four workgroups per CU instead of three: the fp64
+// recompute of the candidates is bound by L2 latency; measured at M=2048: 118 -> 110 us).
+__global__ __launch_bounds__(kTopkThreads)
+__attribute__((amdgpu_waves_per_eu(SL <= 2 ? 4 : 1))) void router_select_kernel(
     const uint16_t* __restrict__ x, const uint16_t* __restrict__ wr, const float* __restrict__ bias,
     const float* __restrict__ logits, const float* __restrict__ absdot, int parts, int nround,
     int M, int H, int E, int top_k, int32_t* __restrict__ ids, float* __restrict__ weights) {

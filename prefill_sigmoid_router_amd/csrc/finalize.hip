@@ -137,4 +137,112 @@ hipError_t launch_finalize(const float* y, const float* topk_w, const uint16_t* 
   return launch_fin<4>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
 }
 
+
+// Few tokens (fewer than CUs): one workgroup per token would read k rows of y through a
+// single CU.  Instead, kernel 1 splits every row into slices of 1024 values over
+// (slice, token) workgroups -- z = combine + residual for the slice, its sum of squares
+// per slice -- and kernel 2 adds a token's slice sums in slice order and scales its z.
+// Same fp32 arithmetic as finalize_kernel; only the order of the sum of squares differs.
+constexpr int kFinSliceThreads = 256;
+constexpr int kFinSlice = 4 * kFinSliceThreads;     // hidden values per slice
+
+__global__ __launch_bounds__(kFinSliceThreads) void finalize_slice_kernel(
+    const float* __restrict__ y, const float* __restrict__ topk_w,
+    const uint16_t* __restrict__ residual, int H, int top_k, float* __restrict__ z,
+    float* __restrict__ slice_ss) {
+  __shared__ float part[kFinSliceThreads / kWave];
+  const int sl = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+  const int c = sl * kFinSliceThreads + tid;          // group of 4 hidden values
+  const bool in = c < (H >> 2);
+  const float* yt = y + (size_t)t * top_k * H;
+  const float* wt = topk_w + (size_t)t * top_k;
+  float4 m = make_float4(0.f, 0.f, 0.f, 0.f);
+  uint2 r = uint2{0u, 0u};
+  if (in) r = reinterpret_cast<const uint2*>(residual + (size_t)t * H)[c];
+  for (int j0 = 0; j0 < top_k; j0 += 16) {
+    float4 a[16];
+#pragma unroll
+    for (int u = 0; u < 16; ++u)
+      a[u] = (in && j0 + u < top_k) ? reinterpret_cast<const float4*>(yt + (size_t)(j0 + u) * H)[c]
+                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      if (j0 + u < top_k) {
+        const float w = wt[j0 + u];
+        m.x = fmaf(w, a[u].x, m.x);
+        m.y = fmaf(w, a[u].y, m.y);
+        m.z = fmaf(w, a[u].z, m.z);
+        m.w = fmaf(w, a[u].w, m.w);
+      }
+    }
+  }
+  m.x += bf16lo(r.x);
+  m.y += bf16hi(r.x);
+  m.z += bf16lo(r.y);
+  m.w += bf16hi(r.y);
+  float ss = 0.f;
+  if (in) {
+    ss = fmaf(m.x, m.x, ss);
+    ss = fmaf(m.y, m.y, ss);
+    ss = fmaf(m.z, m.z, ss);
+    ss = fmaf(m.w, m.w, ss);
+    reinterpret_cast<float4*>(z + (size_t)t * H)[c] = m;
+  }
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) part[tid >> 6] = ss;
+  __syncthreads();
+  if (tid == 0) {
+    float total = 0.f;
+#pragma unroll
+    for (int w = 0; w < kFinSliceThreads / kWave; ++w) total += part[w];
+    slice_ss[(size_t)t * gridDim.x + sl] = total;
+  }
+}
+
+__global__ __launch_bounds__(kFinSliceThreads) void finalize_scale_kernel(
+    const float* __restrict__ z, const float* __restrict__ slice_ss,
+    const uint16_t* __restrict__ norm_w, float eps, int H, uint16_t* __restrict__ out,
+    uint16_t* __restrict__ residual_out) {
+  const int sl = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
+  const int c = sl * kFinSliceThreads + tid;
+  if (c >= (H >> 2)) return;
+  float total = 0.f;
+  for (int s = 0; s < (int)gridDim.x; ++s) total += slice_ss[(size_t)t * gridDim.x + s];
+  const float inv = 1.0f / sqrtf(total / (float)H + eps);
+  const float4 m = reinterpret_cast<const float4*>(z + (size_t)t * H)[c];
+  const uint2 g = reinterpret_cast<const uint2*>(norm_w)[c];
+  uint2 o;
+  o.x = pack_bf16x2(m.x * inv * bf16lo(g.x), m.y * inv * bf16hi(g.x));
+  o.y = pack_bf16x2(m.z * inv * bf16lo(g.y), m.w * inv * bf16hi(g.y));
+  reinterpret_cast<uint2*>(out + (size_t)t * H)[c] = o;
+  if (residual_out) {
+    uint2 zr;
+    zr.x = pack_bf16x2(m.x, m.y);
+    zr.y = pack_bf16x2(m.z, m.w);
+    reinterpret_cast<uint2*>(residual_out + (size_t)t * H)[c] = zr;
+  }
+}
+
+size_t finalize_slices_scratch_bytes(int M, int H) {
+  const int slices = (H / 4 + kFinSliceThreads - 1) / kFinSliceThreads;
+  return (size_t)M * H * sizeof(float) + (size_t)M * slices * sizeof(float);
+}
+
+hipError_t launch_finalize_slices(const float* y, const float* topk_w, const uint16_t* residual,
+                                  const uint16_t* norm_w, float eps, int M, int H, int top_k,
+                                  uint16_t* out, uint16_t* residual_out, float* scratch,
+                                  hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  const int slices = (H / 4 + kFinSliceThreads - 1) / kFinSliceThreads;
+  float* z = scratch;
+  float* slice_ss = scratch + (size_t)M * H;
+  hipLaunchKernelGGL(finalize_slice_kernel, dim3(slices, M), dim3(kFinSliceThreads), 0, s, y,
+                     topk_w, residual, H, top_k, z, slice_ss);
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  hipLaunchKernelGGL(finalize_scale_kernel, dim3(slices, M), dim3(kFinSliceThreads), 0, s, z,
+                     slice_ss, norm_w, eps, H, out, residual_out);
+  return hipGetLastError();
+}
+
 }  // namespace moe

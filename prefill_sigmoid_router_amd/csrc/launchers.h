@@ -89,5 +89,13 @@ hipError_t launch_expert_down_mx(const uint16_t* act, const uint8_t* w2c, const 
 hipError_t launch_finalize(const float* y, const float* topk_w, const uint16_t* residual,
                            const uint16_t* norm_w, float eps, int M, int H, int top_k,
                            uint16_t* out, uint16_t* residual_out, hipStream_t s);
+// The same step for fewer tokens than CUs: rows split into slices over (slice, token)
+// workgroups, then a second kernel scales; scratch of finalize_slices_scratch_bytes.
+constexpr int kFinSlicesMaxTokens = 256;
+size_t finalize_slices_scratch_bytes(int M, int H);
+hipError_t launch_finalize_slices(const float* y, const float* topk_w, const uint16_t* residual,
+                                  const uint16_t* norm_w, float eps, int M, int H, int top_k,
+                                  uint16_t* out, uint16_t* residual_out, float* scratch,
+                                  hipStream_t s);
 
 }  // namespace moe

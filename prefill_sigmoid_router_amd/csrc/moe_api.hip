@@ -38,7 +38,7 @@ size_t capacity_of(int32_t M, int32_t top_k, int32_t E, int32_t block) {
 
 // Workspace layout of moe_forward; every region starts on a 256-byte boundary.
 struct Layout {
-  size_t keys, ids, w, sorted, bexp, npad, tiles, ntiles, act, y, total;
+  size_t keys, ids, w, sorted, bexp, npad, tiles, ntiles, act, y, fin, total;
   int max_tiles;
 };
 
@@ -58,6 +58,8 @@ Layout layout_of(int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k, int3
   L.ntiles = off; off += kAlign;
   L.act = off;    off += round_up(cap * (size_t)I * sizeof(uint16_t), kAlign);
   L.y = off;      off += round_up(n * (size_t)H * sizeof(float), kAlign);
+  L.fin = off;    // z and per-slice sums of the sliced finalize (few tokens only)
+  if (M < moe::kFinSlicesMaxTokens) off += round_up(moe::finalize_slices_scratch_bytes(M, H), kAlign);
   L.total = off;
   return L;
 }
@@ -303,9 +305,12 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
                                              trows, M, H, I, top_k, block, y, s);
   if (down_err != hipSuccess) return MOE_ERR_HIP;
   if (!mark(4)) return MOE_ERR_HIP;
-  if (moe::launch_finalize(y, w, residual, norm_w, eps, M, H, top_k, out, residual_out, s) !=
-      hipSuccess)
-    return MOE_ERR_HIP;
+  const hipError_t fin_err =
+      M < moe::kFinSlicesMaxTokens
+          ? moe::launch_finalize_slices(y, w, residual, norm_w, eps, M, H, top_k, out,
+                                        residual_out, reinterpret_cast<float*>(ws + L.fin), s)
+          : moe::launch_finalize(y, w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
+  if (fin_err != hipSuccess) return MOE_ERR_HIP;
   if (!mark(5)) return MOE_ERR_HIP;
   return MOE_OK;
 }

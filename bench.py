@@ -36,7 +36,6 @@ BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 METRIC = "MoE-layer tokens/s and µs/layer at M=8/128/2048; % HBM or MFMA roofline"
 STAGES = ("route", "align", "up", "down", "finalize")
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_expert_up_decode_m8.json")
-UP_SOURCE = os.path.join(ROOT, "prefill_sigmoid_router_amd", "csrc", "expert_gemm.hip")
 
 
 def source_hash(path: str) -> str:
@@ -204,7 +203,8 @@ def load_traffic():
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("source_sha256_16") != source_hash(UP_SOURCE):
+    src = os.path.join(ROOT, "prefill_sigmoid_router_amd", "csrc", t.get("source_file", ""))
+    if not os.path.isfile(src) or t.get("source_sha256_16") != source_hash(src):
         return None     # the kernel changed since the counters were taken
     return t
 
@@ -306,7 +306,7 @@ def main():
     traffic = load_traffic()
     rows = B.moe_gemm_tile_rows(head.M, head.E, head.top_k, head.I)
     up_kernel = ("expert_up_stream_kernel" if rows == 16
-                 else f"expert_tiled_kernel<{rows}, ..., true>")
+                 else f"expert_tiled_kernel<{rows}, ..., true, ...>")
     if traffic is not None and traffic.get("workload") != head.name:
         traffic = None  # counters were taken on another workload
     roof = {

@@ -72,7 +72,7 @@ __device__ __forceinline__ void wait_chunks_after(int after) {
   }
 }
 
-template <int BM, int WN, int WM, int S, bool UP>
+template <int BM, int WN, int WM, int S, bool UP, int WPOL>
 __global__ __launch_bounds__(64 * WN * WM) void expert_tiled_kernel(
     const uint16_t* __restrict__ tok_src, const uint16_t* __restrict__ w,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
@@ -150,8 +150,14 @@ __global__ __launch_bounds__(64 * WN * WM) void expert_tiled_kernel(
 #pragma unroll
       for (int i = 0; i < C::FPW; ++i) {
         const int f = wave * C::FPW + i;
-        __builtin_amdgcn_global_load_lds((global_void*)(src[i] + c * kTileKC),
-                                         (lds_void*)(base + f * 1024), 16, 0, 0);
+        // weight rows with the given cache policy (nontemporal when each weight is read by
+        // one token tile), token rows with the default one
+        if (f < 2 * C::WT)
+          __builtin_amdgcn_global_load_lds((global_void*)(src[i] + c * kTileKC),
+                                           (lds_void*)(base + f * 1024), 16, 0, WPOL);
+        else
+          __builtin_amdgcn_global_load_lds((global_void*)(src[i] + c * kTileKC),
+                                           (lds_void*)(base + f * 1024), 16, 0, 0);
       }
     } else {  // partial chunk: zero-filled through registers
 #pragma unroll
@@ -450,7 +456,7 @@ __global__ __launch_bounds__(64 * WN * WM) void expert_tiled_mx_kernel(
   }
 }
 
-template <int BM, int WN, int WM, int S, bool UP>
+template <int BM, int WN, int WM, int S, bool UP, int WPOL>
 static hipError_t launch_tiled(const uint16_t* src, const uint16_t* w, const int32_t* sorted_ids,
                                const int32_t* block_expert, const int2* tiles,
                                const int32_t* num_tiles, int max_tiles, int K, int ncols, int I,
@@ -460,16 +466,22 @@ static hipError_t launch_tiled(const uint16_t* src, const uint16_t* w, const int
   const int n_ntiles = (ncols + per_ntile - 1) / per_ntile;
   const long total = (long)max_tiles * n_ntiles;
   const long grid = (total + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((expert_tiled_kernel<BM, WN, WM, S, UP>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((expert_tiled_kernel<BM, WN, WM, S, UP, WPOL>), dim3((unsigned)grid),
                      dim3(TiledCfg<BM, WN, WM>::THREADS), 0, s, src, w, sorted_ids, block_expert,
                      tiles, num_tiles, n_ntiles, K, ncols, I, top_k, block, act, y);
   return hipGetLastError();
 }
 
-// Both token-tile heights run 8 waves x 512 weight rows (up: 256 act columns) with a
-// 2-chunk ring: 72 KiB (64 rows) or 80 KiB (128 rows) per chunk, one workgroup per CU.
-// Measured on MI355X at H=7168, I=2048: the 256-row tile with a 3-chunk ring re-reads
-// the token rows twice as often, which costs more than the shallower ring.
+// Configurations, measured on MI355X at H=7168, E=256, k=16, I=2048 (two interleaved runs
+// each).  Weights every token tile of an expert shares (many tokens per expert, M=2048):
+// 8 waves x 512 weight rows with a 2-chunk ring (72 / 80 KiB per chunk), one workgroup per
+// CU, default cache policy -- nontemporal copies cost 3 % there, 4 waves x 256 rows with a
+// 3-chunk ring 3.5 %.  Weights read by one token tile (few tokens per expert): the
+// weight copies are nontemporal (a plain read pass streams 6.95 TB/s that way against
+// 6.26 TB/s), and the up GEMM runs 4 waves x 256 weight rows with a 3-chunk ring (two
+// chunks in flight): decode M=8 up 1,027 -> 925 us against the streaming kernels, M=128
+// 2,458 -> 2,181 us; the down GEMM keeps 8 waves x 512 rows (M=8: 499 -> 459 us).
+constexpr int kNT = 2;        // cache policy bits of a nontemporal load (gfx950)
 constexpr int kTileWN = 8;
 constexpr int kTileStages = 2;
 
@@ -477,38 +489,47 @@ int tiled_up_columns() { return 32 * kTileWN; }
 
 hipError_t launch_expert_up_tiled(const uint16_t* x, const uint16_t* w13, const int32_t* sorted_ids,
                                   const int32_t* block_expert, const int2* tiles,
-                                  const int32_t* num_tiles, int max_tiles, int tile_rows, int M,
-                                  int H, int I, int top_k, int block, uint16_t* act,
-                                  hipStream_t s) {
+                                  const int32_t* num_tiles, int max_tiles, int tile_rows,
+                                  bool stream_weights, int M, int H, int I, int top_k, int block,
+                                  uint16_t* act, hipStream_t s) {
   (void)M;
-  if (tile_rows == 64)
-    return launch_tiled<64, kTileWN, 1, kTileStages, true>(x, w13, sorted_ids, block_expert, tiles,
-                                                 num_tiles, max_tiles, H, I, I, top_k, block, act,
-                                                 nullptr, s);
-  if (tile_rows == 128)
-    return launch_tiled<128, kTileWN, 1, kTileStages, true>(x, w13, sorted_ids, block_expert, tiles,
-                                                  num_tiles, max_tiles, H, I, I, top_k, block, act,
-                                                  nullptr, s);
+#define MOE_UP(BM, WN, S, POL)                                                                   \
+  return launch_tiled<BM, WN, 1, S, true, POL>(x, w13, sorted_ids, block_expert, tiles,         \
+                                               num_tiles, max_tiles, H, I, I, top_k, block, act, \
+                                               nullptr, s)
+  if (tile_rows == 64) {
+    if (stream_weights) MOE_UP(64, 4, 3, kNT);
+    MOE_UP(64, kTileWN, kTileStages, 0);
+  }
+  if (tile_rows == 128) {
+    if (stream_weights) MOE_UP(128, 4, 3, kNT);
+    MOE_UP(128, kTileWN, kTileStages, 0);
+  }
+#undef MOE_UP
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_expert_down_tiled(const uint16_t* act, const uint16_t* w2,
                                     const int32_t* sorted_ids, const int32_t* block_expert,
                                     const int2* tiles, const int32_t* num_tiles, int max_tiles,
-                                    int tile_rows, int M, int H, int I, int top_k, int block,
-                                    float* y, hipStream_t s) {
+                                    int tile_rows, bool stream_weights, int M, int H, int I,
+                                    int top_k, int block, float* y, hipStream_t s) {
   (void)M;
-  if (tile_rows == 64)
-    return launch_tiled<64, kTileWN, 1, kTileStages, false>(act, w2, sorted_ids, block_expert, tiles,
-                                                  num_tiles, max_tiles, I, H, I, top_k, block,
-                                                  nullptr, y, s);
-  if (tile_rows == 128)
-    return launch_tiled<128, kTileWN, 1, kTileStages, false>(act, w2, sorted_ids, block_expert, tiles,
-                                                   num_tiles, max_tiles, I, H, I, top_k, block,
-                                                   nullptr, y, s);
+#define MOE_DOWN(BM, POL)                                                                       \
+  return launch_tiled<BM, kTileWN, 1, kTileStages, false, POL>(act, w2, sorted_ids, block_expert, \
+                                                               tiles, num_tiles, max_tiles, I, H, \
+                                                               I, top_k, block, nullptr, y, s)
+  if (tile_rows == 64) {
+    if (stream_weights) MOE_DOWN(64, kNT);
+    MOE_DOWN(64, 0);
+  }
+  if (tile_rows == 128) {
+    if (stream_weights) MOE_DOWN(128, kNT);
+    MOE_DOWN(128, 0);
+  }
+#undef MOE_DOWN
   return hipErrorInvalidValue;
 }
-
 
 template <int BM, bool UP>
 static hipError_t launch_tiled_mx(const uint16_t* src, const uint8_t* wc, const uint8_t* ws,

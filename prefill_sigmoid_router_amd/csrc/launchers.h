@@ -43,16 +43,18 @@ hipError_t launch_expert_down(const uint16_t* act, const uint16_t* w2, const int
 // of height tile_rows (64 or 128) of `tiles`.  The up variant needs I to be a multiple of
 // tiled_up_columns().
 int tiled_up_columns();
+// stream_weights: each expert's weights are read by about one token tile, so they are
+// copied nontemporally (and the up GEMM uses its streaming configuration).
 hipError_t launch_expert_up_tiled(const uint16_t* x, const uint16_t* w13, const int32_t* sorted_ids,
                                   const int32_t* block_expert, const int2* tiles,
-                                  const int32_t* num_tiles, int max_tiles, int tile_rows, int M,
-                                  int H, int I, int top_k, int block, uint16_t* act,
-                                  hipStream_t s);
+                                  const int32_t* num_tiles, int max_tiles, int tile_rows,
+                                  bool stream_weights, int M, int H, int I, int top_k, int block,
+                                  uint16_t* act, hipStream_t s);
 hipError_t launch_expert_down_tiled(const uint16_t* act, const uint16_t* w2,
                                     const int32_t* sorted_ids, const int32_t* block_expert,
                                     const int2* tiles, const int32_t* num_tiles, int max_tiles,
-                                    int tile_rows, int M, int H, int I, int top_k, int block,
-                                    float* y, hipStream_t s);
+                                    int tile_rows, bool stream_weights, int M, int H, int I,
+                                    int top_k, int block, float* y, hipStream_t s);
 
 // The same LDS-tiled kernels on MXFP8 weights (codes dequantized into the LDS tiles); K
 // (H for up, I for down) a multiple of 256, scales 8-byte aligned.

@@ -67,16 +67,17 @@ Layout layout_of(int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k, int3
 inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
 // Grouped-GEMM kernels by expected tokens per expert (M * top_k / E), the M-range
-// dispatch pattern of the FlashInfer MNNVL finalize presets: weight streaming over 16-row
-// tiles when experts see a few tokens, LDS-tiled MFMA over 64- or 128-row token tiles
-// when they see many (thresholds measured on MI355X at H=7168, I=2048, E=256).  Returns
-// the tile height; 16 selects the streaming kernels.
-// MXFP8 weights stay on the streaming kernels longer: their tiled kernels dequantize every
-// weight once per token tile (streaming faster up to 12 tokens per expert, tiled from 16).
+// dispatch pattern of the FlashInfer MNNVL finalize presets (thresholds measured on
+// MI355X at H=7168, I=2048, E=256).  Returns the token-tile height: 64 or 128 for the
+// LDS-tiled kernels, 16 for the weight-streaming kernels.  bf16 weights use the tiled
+// kernels at every size (with nontemporal weight copies they beat the streaming kernels
+// even at decode: M=8 layer 1,551 -> 1,405 us); the streaming kernels serve I that is not
+// a multiple of 256 and MXFP8 weights below 16 tokens per expert (their tiled kernels
+// dequantize every weight once per token tile: streaming faster up to 12, tiled from 16).
 int gemm_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I, bool mx) {
   if (I % moe::tiled_up_columns() != 0) return 16;
   const int64_t per_expert = (int64_t)M * top_k / E;
-  if (per_expert < (mx ? 16 : 4)) return 16;
+  if (mx && per_expert < 16) return 16;
   if (per_expert < 32) return 64;
   return 128;
 }
@@ -270,6 +271,10 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
     return MOE_ERR_HIP;
   if (!mark(1)) return MOE_ERR_HIP;
   const int trows = gemm_tile_rows(M, E, top_k, I, W.mx());
+  // about one token tile per expert: each weight is read once, copied nontemporally
+  // (measured: M=8/128/512 gain, M=2048 -- many tiles of a hot expert share its weights
+  // through the L2 -- loses 3 %)
+  const bool stream_w = (int64_t)M * top_k / E < trows / 2;
   const int max_tiles = moe::tile_capacity(M * top_k, E, trows);
   if (moe::launch_align(ids, M * top_k, E, block, sorted, bexp, npad, trows, tiles, ntiles, s) !=
       hipSuccess)
@@ -287,7 +292,7 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
                                    top_k, block, act, s);
   else
     up_err = moe::launch_expert_up_tiled(x, W.w13, sorted, bexp, tiles, ntiles, max_tiles, trows,
-                                         M, H, I, top_k, block, act, s);
+                                         stream_w, M, H, I, top_k, block, act, s);
   if (up_err != hipSuccess) return MOE_ERR_HIP;
   if (!mark(3)) return MOE_ERR_HIP;
   hipError_t down_err;
@@ -302,7 +307,7 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
                                        H, I, top_k, block, y, s);
   else
     down_err = moe::launch_expert_down_tiled(act, W.w2, sorted, bexp, tiles, ntiles, max_tiles,
-                                             trows, M, H, I, top_k, block, y, s);
+                                             trows, stream_w, M, H, I, top_k, block, y, s);
   if (down_err != hipSuccess) return MOE_ERR_HIP;
   if (!mark(4)) return MOE_ERR_HIP;
   const hipError_t fin_err =

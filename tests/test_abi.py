@@ -136,10 +136,11 @@ def test_route_align_finalize_validation(B):
 
 
 def test_gemm_tile_rows_follows_tokens_per_expert(B):
-    # expected tokens per expert M * top_k / E: < 4 -> 16-row streaming kernels,
-    # < 32 -> 64-row tiles, else 128-row tiles; I must be a multiple of 256 for tiles
-    assert B.moe_gemm_tile_rows(8, 256, 16, 2048) == 16
-    assert B.moe_gemm_tile_rows(63, 256, 16, 2048) == 16
+    # bf16: expected tokens per expert M * top_k / E < 32 -> 64-row tiles, else 128-row
+    # tiles; I not a multiple of 256 -> the 16-row streaming kernels
+    assert B.moe_gemm_tile_rows(8, 256, 16, 2048) == 64
+    assert B.moe_gemm_tile_rows(1, 256, 16, 2048) == 64
+    assert B.moe_gemm_tile_rows(63, 256, 16, 2048) == 64
     assert B.moe_gemm_tile_rows(64, 256, 16, 2048) == 64
     assert B.moe_gemm_tile_rows(128, 256, 16, 2048) == 64
     assert B.moe_gemm_tile_rows(512, 256, 16, 2048) == 128

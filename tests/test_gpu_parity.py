@@ -48,13 +48,18 @@ SMALL = {
     "one_token": mi.LayerConfig("one_token", M=1, H=512, E=64, top_k=8, I=256, block=16),
     "single_expert": mi.LayerConfig("single_expert", M=9, H=256, E=1, top_k=1, I=128, block=16),
     "all_experts": mi.LayerConfig("all_experts", M=5, H=128, E=6, top_k=6, I=64, block=16),
-    # many tokens per expert: moe_forward runs the LDS-tiled GEMMs (moe_gemm_tile_rows 128 /
-    # 64) with a partial last K chunk (H % 64 = 16), a partial last N tile of the down GEMM
-    # (H < 512 columns per tile) and hot experts spanning several token tiles
+    # LDS-tiled GEMMs (moe_gemm_tile_rows 128 / 64) with a partial last K chunk (H % 64 = 16),
+    # a partial last N tile of the down GEMM (H < 512 columns per tile) and hot experts
+    # spanning several token tiles
     "tiled128_zipf": mi.LayerConfig("tiled128_zipf", M=300, H=720, E=8, top_k=4, I=256,
                                     block=64, zipf_s=1.0),
     "tiled64_zipf": mi.LayerConfig("tiled64_zipf", M=40, H=336, E=16, top_k=4, I=512, block=16,
                                    zipf_s=1.0),
+    # 128-row tiles with the streaming-weights configuration (50 tokens per expert, below
+    # half a tile: nontemporal weight copies, 4 waves x 256 rows, 3-chunk ring) and a
+    # partial last K chunk
+    "tiled128_stream": mi.LayerConfig("tiled128_stream", M=100, H=464, E=8, top_k=4, I=256,
+                                      block=32, zipf_s=1.0),
 }
 FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048"]
 

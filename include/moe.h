@@ -87,13 +87,15 @@ size_t moe_workspace_bytes(int32_t M, int32_t H, int32_t E, int32_t I, int32_t t
                            int32_t block);
 
 /*
- * Token-tile height moe_forward uses for its grouped GEMMs at these sizes: 16 selects the
- * weight-streaming kernels (few tokens per expert), 64 or 128 the LDS-tiled MFMA
- * kernels.  Chosen by the expected tokens per expert, M * top_k / E, and whether I is a
- * multiple of the tiled kernels' 256 act columns.  Host-only; 0 for invalid sizes.
+ * Token-tile height moe_forward uses for its grouped GEMMs at these sizes: 64 or 128
+ * select the LDS-tiled MFMA kernels (64 below 32 expected tokens per expert M * top_k / E,
+ * 128 from there), 16 the weight-streaming kernels, used when I is not a multiple of the
+ * tiled kernels' 256 act columns.  Below half a tile of tokens per expert the tiled
+ * kernels copy the weights nontemporally.  Host-only; 0 for invalid sizes.
  */
 int32_t moe_gemm_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I);
-/* The same for moe_forward_mx (MXFP8 weights; I a multiple of 256, else 0). */
+/* The same for moe_forward_mx (MXFP8 weights; I a multiple of 256, else 0): 16 (streaming)
+ * below 16 expected tokens per expert, then 64 / 128 as above. */
 int32_t moe_gemm_tile_rows_mx(int32_t M, int32_t E, int32_t top_k, int32_t I);
 
 /*

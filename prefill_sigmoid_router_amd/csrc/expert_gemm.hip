@@ -1,5 +1,7 @@
 // Grouped expert GEMMs of the routed-MoE layer over the align plan: weight-streaming
-// kernels for 16-row token tiles.
+// kernels for 16-row token tiles.  moe_forward uses them for bf16 weights only when I is
+// not a multiple of 256 (the LDS-tiled kernels serve every size otherwise), for MXFP8
+// weights below 16 tokens per expert, and moe_expert_up / moe_expert_down always.
 //
 // AlphaMoE page (FlashInfer PR #6511 analysis), sections 1-4: the up kernel gathers the
 // token tile of an expert and streams that expert's weights, the down kernel streams

@@ -1,5 +1,6 @@
-// Grouped expert GEMMs for plans whose experts carry many tokens (batched decode and
-// prefill): LDS-tiled MFMA kernels fed by direct global -> LDS copies.
+// Grouped expert GEMMs of moe_forward (bf16 weights at every size, from decode to
+// prefill; MXFP8 weights from 16 tokens per expert): LDS-tiled MFMA kernels fed by direct
+// global -> LDS copies.
 //
 // AlphaMoE page (FlashInfer PR #6511 analysis), section 4: the up kernel of the large
 // batch and prefill routes gathers a tile of tokens per expert; section 2: the down

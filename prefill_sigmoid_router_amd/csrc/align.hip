@@ -30,6 +30,7 @@ namespace moe {
 constexpr int kAlignWaves = 16;
 constexpr int kAlignThreads = kAlignWaves * kWave;
 constexpr int kAlignMaxE = 1024;
+constexpr int kAlignBatch = 8;   // ids per lane requested together
 
 __device__ __forceinline__ int block_exclusive_scan(int v, int* wave_total, int lane, int wave,
                                                     int* total_out) {
@@ -69,10 +70,20 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   const int lo = min(n, wave * seg);
   const int hi = min(n, lo + seg);
 
-  // 1. histogram
-  for (int i = lo + lane; i < hi; i += kWave) {
-    const int e = ids[i];
-    if ((unsigned)e < (unsigned)E) atomicAdd(&cnt[wave][e], 1);
+  // 1. histogram (kAlignBatch ids requested before any is used: one memory round trip per
+  // batch instead of per id)
+  for (int b0 = lo; b0 < hi; b0 += kWave * kAlignBatch) {
+    int ev[kAlignBatch];
+#pragma unroll
+    for (int u = 0; u < kAlignBatch; ++u) {
+      const int i = b0 + kWave * u + lane;
+      ev[u] = i < hi ? ids[i] : -1;
+    }
+#pragma unroll
+    for (int u = 0; u < kAlignBatch; ++u) {
+      if (b0 + kWave * u >= hi) break;         // uniform: past this wave's segment
+      if ((unsigned)ev[u] < (unsigned)E) atomicAdd(&cnt[wave][ev[u]], 1);
+    }
   }
   __syncthreads();
 
@@ -104,20 +115,30 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
 
   // 3. stable scatter
   const uint64_t lower_lanes = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int b0 = lo; b0 < hi; b0 += kWave) {
-    const int i = b0 + lane;
-    const int e = (i < hi) ? ids[i] : -1;
-    const bool valid = (unsigned)e < (unsigned)E;
-    uint64_t same = __ballot(valid);
-    for (int b = 0; b < id_bits; ++b) {
-      const bool bit = valid && ((e >> b) & 1);
-      const uint64_t set = __ballot(bit);
-      same &= bit ? set : ~set;
+  for (int b0 = lo; b0 < hi; b0 += kWave * kAlignBatch) {
+    int ev[kAlignBatch];
+#pragma unroll
+    for (int u = 0; u < kAlignBatch; ++u) {
+      const int i = b0 + kWave * u + lane;
+      ev[u] = i < hi ? ids[i] : -1;
     }
-    if (valid) {
-      const int cursor = cnt[wave][e];
-      sorted_ids[cursor + __popcll(same & lower_lanes)] = i;
-      if ((same >> lane) == 1ull) cnt[wave][e] = cursor + __popcll(same);  // highest lane of the group
+#pragma unroll
+    for (int u = 0; u < kAlignBatch; ++u) {   // in ascending flat index
+      if (b0 + kWave * u >= hi) break;         // uniform: past this wave's segment
+      const int i = b0 + kWave * u + lane;
+      const int e = ev[u];
+      const bool valid = (unsigned)e < (unsigned)E;
+      uint64_t same = __ballot(valid);
+      for (int b = 0; b < id_bits; ++b) {
+        const bool bit = valid && ((e >> b) & 1);
+        const uint64_t set = __ballot(bit);
+        same &= bit ? set : ~set;
+      }
+      if (valid) {
+        const int cursor = cnt[wave][e];
+        sorted_ids[cursor + __popcll(same & lower_lanes)] = i;
+        if ((same >> lane) == 1ull) cnt[wave][e] = cursor + __popcll(same);  // highest lane of the group
+      }
     }
   }
 

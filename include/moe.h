@@ -2,7 +2,9 @@
  * moe.h -- C ABI of the MI355X (gfx950) routed Mixture-of-Experts layer.
  *
  * One call of moe_forward runs the routed-MoE layer of an LLM decode/prefill step on
- * one GPU, in five stream-ordered kernels:
+ * one GPU, in five stream-ordered kernels (four for at most 256 flat ids on bf16 weights,
+ * where the up-GEMM kernel builds the plan itself -- the self-routing up kernels of the
+ * AlphaMoE page, section 6 -- and writes the same plan the align kernel would):
  *
  *   1. router: key[t,e] = sum_h x[t,h] * Wr[e,h] (+ bias[e]), accumulated in fp64;
  *      top-k by (key descending, expert id ascending); weights = sigmoid(key) of the
@@ -169,7 +171,8 @@ int moe_finalize(const float* y, const float* topk_w, const uint16_t* residual,
  *   the step writes there instead of the workspace.
  *   block must be 16, 32, 64 or 128.
  *   stage_events: NULL, or 6 hipEvent_t recorded on `stream` before step 1 and after
- *   each of the five steps (for per-step timing).
+ *   each of the five steps (for per-step timing; with a self-routing up GEMM, events 1
+ *   and 2 enclose no kernel).
  */
 int moe_forward(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
                 const uint16_t* w13, const uint16_t* w2,

@@ -56,6 +56,19 @@ hipError_t launch_expert_down_tiled(const uint16_t* act, const uint16_t* w2,
                                     int tile_rows, bool stream_weights, int M, int H, int I,
                                     int top_k, int block, float* y, hipStream_t s);
 
+// Self-routing variant of the tiled up GEMM for few ids (the align step fused into it):
+// from the flat ids [M * top_k] it writes the same plan and tile list (tile height 64) as
+// launch_align, and act as launch_expert_up_tiled with streamed weights.  Needs
+// M * top_k <= kSelfRouteMaxIds, E <= kSelfRouteMaxE and I a multiple of 128.
+constexpr int kSelfRouteMaxIds = 2048;
+constexpr int kSelfRouteMaxE = 1024;
+constexpr int kSelfRouteTileRows = 64;
+hipError_t launch_expert_up_selfroute(const uint16_t* x, const uint16_t* w13, const int32_t* ids,
+                                      int M, int H, int E, int I, int top_k, int block,
+                                      int32_t* sorted_ids, int32_t* block_expert,
+                                      int32_t* num_padded, int2* tiles, int32_t* num_tiles,
+                                      uint16_t* act, hipStream_t s);
+
 // The same LDS-tiled kernels on MXFP8 weights (codes dequantized into the LDS tiles); K
 // (H for up, I for down) a multiple of 256, scales 8-byte aligned.
 hipError_t launch_expert_up_tiled_mx(const uint16_t* x, const uint8_t* w13c, const uint8_t* w13s,

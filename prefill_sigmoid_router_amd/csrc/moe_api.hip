@@ -66,6 +66,10 @@ Layout layout_of(int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k, int3
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
+// Self-routing (align fused into the up GEMM) up to this many flat ids.
+constexpr int kSelfRouteIds = 256;
+static_assert(kSelfRouteIds <= moe::kSelfRouteMaxIds, "self-routing id limit");
+
 // Grouped-GEMM kernels by expected tokens per expert (M * top_k / E), the M-range
 // dispatch pattern of the FlashInfer MNNVL finalize presets (thresholds measured on
 // MI355X at H=7168, I=2048, E=256).  Returns the token-tile height: 64 or 128 for the
@@ -276,12 +280,19 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   // through the L2 -- loses 3 %)
   const bool stream_w = (int64_t)M * top_k / E < trows / 2;
   const int max_tiles = moe::tile_capacity(M * top_k, E, trows);
-  if (moe::launch_align(ids, M * top_k, E, block, sorted, bexp, npad, trows, tiles, ntiles, s) !=
-      hipSuccess)
+  // few ids: the up GEMM builds the plan itself (no align launch)
+  const bool self_route = !W.mx() && trows == moe::kSelfRouteTileRows && stream_w &&
+                          M * top_k <= kSelfRouteIds && I % 128 == 0;
+  if (!self_route &&
+      moe::launch_align(ids, M * top_k, E, block, sorted, bexp, npad, trows, tiles, ntiles, s) !=
+          hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(2)) return MOE_ERR_HIP;
   hipError_t up_err;
-  if (W.mx() && trows == 16)
+  if (self_route)
+    up_err = moe::launch_expert_up_selfroute(x, W.w13, ids, M, H, E, I, top_k, block, sorted, bexp,
+                                             npad, tiles, ntiles, act, s);
+  else if (W.mx() && trows == 16)
     up_err = moe::launch_expert_up_mx(x, W.w13c, W.w13s, sorted, bexp, npad, tiles, ntiles,
                                       max_tiles, M, H, I, top_k, block, act, s);
   else if (W.mx())

@@ -55,11 +55,28 @@ SMALL = {
                                     block=64, zipf_s=1.0),
     "tiled64_zipf": mi.LayerConfig("tiled64_zipf", M=40, H=336, E=16, top_k=4, I=512, block=16,
                                    zipf_s=1.0),
+    # 64-row tiles with more flat ids than the self-routing up GEMM takes (320 > 256): the
+    # align kernel builds the plan
+    "tiled64_align": mi.LayerConfig("tiled64_align", M=80, H=336, E=64, top_k=4, I=256,
+                                    block=16),
     # 128-row tiles with the streaming-weights configuration (50 tokens per expert, below
     # half a tile: nontemporal weight copies, 4 waves x 256 rows, 3-chunk ring) and a
     # partial last K chunk
     "tiled128_stream": mi.LayerConfig("tiled128_stream", M=100, H=464, E=8, top_k=4, I=256,
                                       block=32, zipf_s=1.0),
+    # the same with whole K chunks (H % 64 = 0): the split-ring kernels with nontemporal
+    # weight copies for both GEMMs
+    "tiled128_streamring": mi.LayerConfig("tiled128_streamring", M=96, H=512, E=8, top_k=4,
+                                          I=256, block=32, zipf_s=1.0),
+    # 128-row tiles whose weights several token tiles share (160 tokens per expert, whole K
+    # chunks: the 4-wave register-fragment kernels), hot experts over several tiles and a
+    # partial last N tile of the down GEMM (640 of 1024 columns)
+    "tiled128_reg": mi.LayerConfig("tiled128_reg", M=320, H=640, E=8, top_k=4, I=512,
+                                   block=64, zipf_s=1.0),
+    # the same kernels with a single K chunk in the up GEMM (H = 64) and a down GEMM whose
+    # one N tile is mostly past the 64 output columns
+    "tiled128_short": mi.LayerConfig("tiled128_short", M=200, H=64, E=4, top_k=2, I=256,
+                                     block=16),
 }
 FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048"]
 

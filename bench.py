@@ -305,8 +305,12 @@ def main():
     read_gbs = read_probe_gbs(torch, dev)
     traffic = load_traffic()
     rows = B.moe_gemm_tile_rows(head.M, head.E, head.top_k, head.I)
-    up_kernel = ("expert_up_stream_kernel" if rows == 16
-                 else f"expert_tiled_kernel<{rows}, ..., true, ...>")
+    if B.moe_forward_self_routes(head.M, head.E, head.top_k, head.I):
+        up_kernel = f"expert_up_selfroute_kernel<{rows}, ...> (align fused in)"
+    elif rows == 16:
+        up_kernel = "expert_up_stream_kernel"
+    else:
+        up_kernel = f"expert_tiled_kernel<{rows}, ..., true, ...>"
     if traffic is not None and traffic.get("workload") != head.name:
         traffic = None  # counters were taken on another workload
     roof = {

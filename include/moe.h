@@ -99,6 +99,12 @@ int32_t moe_gemm_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I);
 /* The same for moe_forward_mx (MXFP8 weights; I a multiple of 256, else 0): 16 (streaming)
  * below 16 expected tokens per expert, then 64 / 128 as above. */
 int32_t moe_gemm_tile_rows_mx(int32_t M, int32_t E, int32_t top_k, int32_t I);
+/* 1 when moe_forward (bf16 weights) builds the plan inside its up-GEMM kernel for these
+ * sizes -- the self-routing up kernels of the AlphaMoE page (FlashInfer PR #6511 analysis),
+ * section 6: 64-row tiles, weights copied nontemporally, at most 256 flat ids M * top_k --
+ * and so runs no align kernel; 0 when it runs the align kernel, and for invalid sizes.
+ * Host-only. */
+int32_t moe_forward_self_routes(int32_t M, int32_t E, int32_t top_k, int32_t I);
 
 /*
  * Router (step 1).

@@ -18,7 +18,7 @@ __all__ = [
     "moe_strerror", "moe_abi_version", "moe_align_capacity", "moe_route_workspace_bytes",
     "moe_workspace_bytes", "moe_route", "moe_align", "moe_expert_up", "moe_expert_down",
     "moe_finalize", "moe_forward", "moe_mx_quantize", "moe_mx_dequantize", "moe_forward_mx",
-    "moe_gemm_tile_rows", "moe_gemm_tile_rows_mx",
+    "moe_gemm_tile_rows", "moe_gemm_tile_rows_mx", "moe_forward_self_routes",
     "HipEvent",
 ]
 
@@ -40,6 +40,7 @@ _PROTOS = {
     "moe_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "moe_gemm_tile_rows": (_i32, [_i32, _i32, _i32, _i32]),
     "moe_gemm_tile_rows_mx": (_i32, [_i32, _i32, _i32, _i32]),
+    "moe_forward_self_routes": (_i32, [_i32, _i32, _i32, _i32]),
     "moe_route": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p, _sz, _p]),
     "moe_align": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _p, _p, _p, _p]),
     "moe_expert_up": (ctypes.c_int, [_p, _p, _p, _p, _p, _i32, _i32, _i32, _i32, _i32, _i32, _i32,
@@ -145,6 +146,10 @@ def moe_gemm_tile_rows(M: int, E: int, top_k: int, I: int) -> int:
 
 def moe_gemm_tile_rows_mx(M: int, E: int, top_k: int, I: int) -> int:
     return int(load_library().moe_gemm_tile_rows_mx(M, E, top_k, I))
+
+
+def moe_forward_self_routes(M: int, E: int, top_k: int, I: int) -> bool:
+    return bool(load_library().moe_forward_self_routes(M, E, top_k, I))
 
 
 def moe_route(x, router_w, router_bias, top_k: int, topk_ids, topk_w, workspace, stream=None):

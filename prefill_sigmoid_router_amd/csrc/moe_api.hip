@@ -66,9 +66,7 @@ Layout layout_of(int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k, int3
 
 inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_HIP; }
 
-// Self-routing (align fused into the up GEMM) up to this many flat ids.
-constexpr int kSelfRouteIds = 256;
-static_assert(kSelfRouteIds <= moe::kSelfRouteMaxIds, "self-routing id limit");
+
 
 // Grouped-GEMM kernels by expected tokens per expert (M * top_k / E), the M-range
 // dispatch pattern of the FlashInfer MNNVL finalize presets (thresholds measured on
@@ -86,6 +84,22 @@ int gemm_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I, bool mx) {
   return 128;
 }
 
+// Self-routing (align fused into the up GEMM, bf16 weights): 64-row tiles with streamed
+// weights and at most this many flat ids (measured: -3 us per layer at 128 ids, +16 us at
+// 2048).
+constexpr int kSelfRouteIds = 256;
+static_assert(kSelfRouteIds <= moe::kSelfRouteMaxIds, "self-routing id limit");
+
+bool stream_weights(int32_t M, int32_t E, int32_t top_k, int trows) {
+  return (int64_t)M * top_k / E < trows / 2;
+}
+
+bool self_routes(int32_t M, int32_t E, int32_t top_k, int32_t I) {
+  const int trows = gemm_tile_rows(M, E, top_k, I, false);
+  return trows == moe::kSelfRouteTileRows && stream_weights(M, E, top_k, trows) &&
+         (int64_t)M * top_k <= kSelfRouteIds && I % 128 == 0;
+}
+
 }  // namespace
 
 extern "C" {
@@ -101,7 +115,7 @@ const char* moe_strerror(int status) {
   }
 }
 
-int moe_abi_version(void) { return 103; }
+int moe_abi_version(void) { return 104; }
 
 size_t moe_align_capacity(int32_t M, int32_t top_k, int32_t E, int32_t block) {
   if (M < 0 || top_k < 1 || E < 1 || block < 1) return 0;
@@ -122,6 +136,11 @@ int32_t moe_gemm_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I) {
 int32_t moe_gemm_tile_rows_mx(int32_t M, int32_t E, int32_t top_k, int32_t I) {
   if (M < 0 || E < 1 || E > kMaxE || top_k < 1 || top_k > E || I < 256 || I % 256 != 0) return 0;
   return gemm_tile_rows(M, E, top_k, I, true);
+}
+
+int32_t moe_forward_self_routes(int32_t M, int32_t E, int32_t top_k, int32_t I) {
+  if (M < 0 || E < 1 || E > kMaxE || top_k < 1 || top_k > E || I < 64 || I % 64 != 0) return 0;
+  return self_routes(M, E, top_k, I) ? 1 : 0;
 }
 
 size_t moe_workspace_bytes(int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k,
@@ -278,11 +297,10 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   // about one token tile per expert: each weight is read once, copied nontemporally
   // (measured: M=8/128/512 gain, M=2048 -- many tiles of a hot expert share its weights
   // through the L2 -- loses 3 %)
-  const bool stream_w = (int64_t)M * top_k / E < trows / 2;
+  const bool stream_w = stream_weights(M, E, top_k, trows);
   const int max_tiles = moe::tile_capacity(M * top_k, E, trows);
   // few ids: the up GEMM builds the plan itself (no align launch)
-  const bool self_route = !W.mx() && trows == moe::kSelfRouteTileRows && stream_w &&
-                          M * top_k <= kSelfRouteIds && I % 128 == 0;
+  const bool self_route = !W.mx() && self_routes(M, E, top_k, I);
   if (!self_route &&
       moe::launch_align(ids, M * top_k, E, block, sorted, bexp, npad, trows, tiles, ntiles, s) !=
           hipSuccess)

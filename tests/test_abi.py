@@ -56,7 +56,7 @@ def test_library_links_no_torch(B):
 
 
 def test_strerror_and_version(B):
-    assert B.moe_abi_version() == 103
+    assert B.moe_abi_version() == 104
     for s in (0, -1, -2, -3, -4, 17):
         assert isinstance(B.moe_strerror(s), str) and B.moe_strerror(s)
 
@@ -133,6 +133,21 @@ def test_route_align_finalize_validation(B):
     assert lib.moe_expert_up(p(16), p(16), p(16), p(16), p(16), 4, 256, 8, 512, 2, 16, 16, p(16), None) == -1
     assert lib.moe_expert_up(p(16), p(16), p(16), p(16), p(16), 4, 256, 8, 512, 2, 24, 240, p(16), None) == -2
     assert lib.moe_expert_down(p(16), p(16), p(16), p(16), p(16), 4, 256, 8, 512, 2, 16, 16, p(16), None) == -1
+
+
+def test_forward_self_routes_for_few_ids(B):
+    # the up GEMM builds the plan itself for 64-row tiles with streamed weights and at most
+    # 256 flat ids; otherwise the align kernel runs
+    assert B.moe_forward_self_routes(8, 256, 16, 2048)
+    assert B.moe_forward_self_routes(1, 256, 16, 2048)
+    assert B.moe_forward_self_routes(16, 256, 16, 2048)        # 256 ids
+    assert not B.moe_forward_self_routes(17, 256, 16, 2048)    # 272 ids
+    assert not B.moe_forward_self_routes(128, 256, 16, 2048)
+    assert not B.moe_forward_self_routes(2048, 256, 16, 2048)  # 128-row tiles
+    assert not B.moe_forward_self_routes(8, 256, 16, 192)      # streaming kernels (16 rows)
+    assert B.moe_forward_self_routes(40, 16, 4, 512)           # 160 ids, 10 per expert
+    assert not B.moe_forward_self_routes(8, 0, 1, 2048)
+    assert not B.moe_forward_self_routes(-1, 256, 16, 2048)
 
 
 def test_gemm_tile_rows_follows_tokens_per_expert(B):

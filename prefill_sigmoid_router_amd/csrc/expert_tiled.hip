@@ -93,8 +93,10 @@ __device__ __forceinline__ bool tiled_item(int ntiles_live, int n_ntiles, int& n
 }
 
 // One work item of the tiled GEMM: plan rows start..start+nlive-1 of expert e (row_ids[r] =
-// the flat index of plan row start + r) against the weight rows of N tile `ntile`.
-template <int BM, int WN, int WM, int S, bool UP, int WPOL>
+// the flat index of plan row start + r) against the weight rows of N tile `ntile`.  SYNC:
+// row_ids and other data the caller keeps in `lds` are read before a barrier that precedes
+// the first copy into the ring.
+template <int BM, int WN, int WM, int S, bool UP, int WPOL, bool SYNC = false>
 __device__ __forceinline__ void tiled_gemm(
     unsigned char* __restrict__ lds, const uint16_t* __restrict__ tok_src,
     const uint16_t* __restrict__ w, const int32_t* row_ids, int start, int nlive, int e,
@@ -208,6 +210,7 @@ __device__ __forceinline__ void tiled_gemm(
     }
   };
 
+  if constexpr (SYNC) __syncthreads();
 #pragma unroll
   for (int p = 0; p < S - 1; ++p)
     if (p < nch) issue(p);
@@ -292,17 +295,18 @@ __global__ __launch_bounds__(64 * WN) void expert_up_selfroute_kernel(
   constexpr int EPT = kSelfRouteMaxE / T;        // experts per thread in the scans
   static_assert(EPT * T == kSelfRouteMaxE, "the experts must split evenly over the threads");
   static_assert(S >= 2 && (S - 2) * C::FPW <= 63, "the copies in flight must fit the vmcnt counter");
-  static_assert(S * C::FRAGS * 1024 + BM * 4 + 2 * WN * 4 <= 160 * 1024, "the ring must fit the LDS");
-  static_assert((kSelfRouteMaxIds + 3 * kSelfRouteMaxE + 2) * 4 <= S * C::FRAGS * 1024,
+  static_assert(S * C::FRAGS * 1024 <= 160 * 1024, "the ring must fit the LDS");
+  static_assert((kSelfRouteMaxIds + 3 * kSelfRouteMaxE + 2 + BM + 2 * WN) * 4 <=
+                    S * C::FRAGS * 1024,
                 "the plan scratch must fit the ring");
   __shared__ __align__(16) unsigned char lds[S * C::FRAGS * 1024];
-  __shared__ int s_rows[BM];                     // flat index of each row of this tile
-  __shared__ int s_wsum[2][WN];
-  // plan scratch in the ring, read only before the ring's first copy
+  // plan scratch in the ring, read only before the barrier ahead of the ring's first copy
   int* const s_ids = reinterpret_cast<int*>(lds);          // [n]
   int* const s_cnt = s_ids + kSelfRouteMaxIds;             // [E]
   int* const s_pre = s_cnt + kSelfRouteMaxE;               // [E + 1] plan offsets
   int* const s_tpre = s_pre + kSelfRouteMaxE + 1;          // [E + 1] tile list offsets
+  int* const s_rows = s_tpre + kSelfRouteMaxE + 1;         // [BM] flat index of each row
+  int (*const s_wsum)[WN] = reinterpret_cast<int (*)[WN]>(s_rows + BM);  // [2][WN]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < E; e += T) s_cnt[e] = 0;
@@ -399,9 +403,9 @@ __global__ __launch_bounds__(64 * WN) void expert_up_selfroute_kernel(
       for (int b = s_pre[e] / block + tid; b < seg_end / block; b += T) block_expert[b] = e;
     if (tid == 0) tiles[ti] = make_int2(start, nlive);
   }
-  __syncthreads();  // the ring's first copies overwrite the plan scratch
-  tiled_gemm<BM, WN, 1, S, true, WPOL>(lds, x, w13, s_rows, start, nlive, e, ntile, K, I, I,
-                                       top_k, act, nullptr);
+  // the GEMM reads s_rows, then a barrier, then its first copies overwrite the scratch
+  tiled_gemm<BM, WN, 1, S, true, WPOL, true>(lds, x, w13, s_rows, start, nlive, e, ntile, K, I,
+                                             I, top_k, act, nullptr);
 }
 
 // Variant for weights that several token tiles share (many tokens per expert): the same

@@ -55,6 +55,15 @@ SMALL = {
                                     block=64, zipf_s=1.0),
     "tiled64_zipf": mi.LayerConfig("tiled64_zipf", M=40, H=336, E=16, top_k=4, I=512, block=16,
                                    zipf_s=1.0),
+    # the self-routing up GEMM (plan built inside the up kernel) at its limits: 1024 experts
+    # (the scans' largest expert count), exactly 256 flat ids, and a block larger than the
+    # 64-row tile (padding rows past the expert's last tile)
+    "selfroute_e1024": mi.LayerConfig("selfroute_e1024", M=4, H=256, E=1024, top_k=8, I=256,
+                                      block=16),
+    "selfroute_256ids": mi.LayerConfig("selfroute_256ids", M=32, H=320, E=64, top_k=8, I=512,
+                                       block=32, zipf_s=1.0),
+    "selfroute_block128": mi.LayerConfig("selfroute_block128", M=24, H=192, E=12, top_k=3,
+                                         I=256, block=128),
     # 64-row tiles with more flat ids than the self-routing up GEMM takes (320 > 256): the
     # align kernel builds the plan
     "tiled64_align": mi.LayerConfig("tiled64_align", M=80, H=336, E=64, top_k=4, I=256,
@@ -405,6 +414,10 @@ def test_forward_small(B, dev, name):
     print(f"forward parity {name} (GEMM token tile {rows})", flush=True)
     if name.startswith("tiled"):
         assert rows == int(name[5:name.index("_")])
+    if name.startswith("selfroute"):
+        assert B.moe_forward_self_routes(cfg.M, cfg.E, cfg.top_k, cfg.I)
+    if name == "tiled64_align":
+        assert not B.moe_forward_self_routes(cfg.M, cfg.E, cfg.top_k, cfg.I)
     L = mi.make_layer(cfg, device=dev, seed=3)
     r = _run_forward(B, L, dev)
     ref = orc.forward(bits(L["x"]), bits(L["router_w"]), _bias_np(L), bits(L["w13"]), bits(L["w2"]),

@@ -306,7 +306,7 @@ def main():
     traffic = load_traffic()
     rows = B.moe_gemm_tile_rows(head.M, head.E, head.top_k, head.I)
     if B.moe_forward_self_routes(head.M, head.E, head.top_k, head.I):
-        up_kernel = f"expert_up_selfroute_kernel<{rows}, ...> (align fused in)"
+        up_kernel = f"expert_up_selfroute_kernel<{rows}, ...>, align fused in,"
     elif rows == 16:
         up_kernel = "expert_up_stream_kernel"
     else:

@@ -25,7 +25,10 @@
 //
 // Work order: the hardware hands workgroup p to XCD p % 8.  Each XCD gets an equal,
 // contiguous share of the live (tile, N tile) items (the tile count is read on the
-// device), ordered N tile by N tile.
+// device), ordered N tile by N tile.  With 64-row tiles (few tokens per expert) the grid
+// is one workgroup per CU, each walking its XCD's share, so that an item's epilogue stores
+// drain while the next item's copies stream (a wave that ends waits for its stores first).
+// The up GEMMs store act only for a tile's real rows: the down GEMM never reads the others.
 //
 // Besides that kernel: a self-routing up kernel that builds the plan itself (few ids, no
 // align launch), a split-ring kernel with separate weight and token rings (two weight
@@ -79,7 +82,8 @@ __device__ __forceinline__ void wait_chunks_after(int after) {
 
 // Work item -> (N tile, tile) for live_items = ntiles_live * n_ntiles items: workgroup p
 // runs on XCD p % 8, and each XCD takes an equal contiguous share, N tile by N tile.
-// Returns false for a workgroup past the items.
+// Returns false for a workgroup past the items.  (Kernels that take one item per
+// workgroup; the others walk their share with TiledWalk.)
 __device__ __forceinline__ bool tiled_item(int ntiles_live, int n_ntiles, int& ntile, int& ti) {
   const int live_items = ntiles_live * n_ntiles;
   const int per_xcd = (live_items + kXcds - 1) / kXcds;
@@ -92,11 +96,32 @@ __device__ __forceinline__ bool tiled_item(int ntiles_live, int n_ntiles, int& n
   return true;
 }
 
+// The same items, walked by a grid of any multiple of 8 workgroups: each XCD's workgroups
+// step through its share with a stride of their count.  A grid as large as the items gives
+// one item per workgroup; the launchers use one workgroup per CU instead, so a workgroup's
+// epilogue stores drain while its next item's first copies are in flight (a wave that ends
+// waits for its outstanding stores, holding the CU's LDS meanwhile).
+struct TiledWalk {
+  int ntiles_live, live, per_xcd, first, slot, stride;
+  __device__ TiledWalk(int ntl, int n_ntiles)
+      : ntiles_live(ntl), live(ntl * n_ntiles), per_xcd((live + kXcds - 1) / kXcds),
+        first((blockIdx.x % kXcds) * per_xcd), slot(blockIdx.x / kXcds),
+        stride(gridDim.x / kXcds) {}
+  // this workgroup's next item; false once its share is done
+  __device__ bool next(int& ntile, int& ti) {
+    if (slot >= per_xcd) return false;
+    const int logical = first + slot;
+    if (logical >= live) return false;
+    slot += stride;
+    ntile = logical / ntiles_live;
+    ti = logical % ntiles_live;
+    return true;
+  }
+};
+
 // One work item of the tiled GEMM: plan rows start..start+nlive-1 of expert e (row_ids[r] =
-// the flat index of plan row start + r) against the weight rows of N tile `ntile`.  SYNC:
-// row_ids and other data the caller keeps in `lds` are read before a barrier that precedes
-// the first copy into the ring.
-template <int BM, int WN, int WM, int S, bool UP, int WPOL, bool SYNC = false>
+// the flat index of plan row start + r) against the weight rows of N tile `ntile`.
+template <int BM, int WN, int WM, int S, bool UP, int WPOL>
 __device__ __forceinline__ void tiled_gemm(
     unsigned char* __restrict__ lds, const uint16_t* __restrict__ tok_src,
     const uint16_t* __restrict__ w, const int32_t* row_ids, int start, int nlive, int e,
@@ -210,7 +235,6 @@ __device__ __forceinline__ void tiled_gemm(
     }
   };
 
-  if constexpr (SYNC) __syncthreads();
 #pragma unroll
   for (int p = 0; p < S - 1; ++p)
     if (p < nch) issue(p);
@@ -230,7 +254,7 @@ __device__ __forceinline__ void tiled_gemm(
   for (int s = 0; s < C::MTW; ++s) {
     if (s >= my_active) continue;
     const int r = 16 * (wm * C::MTW + s) + li;
-    if (UP) {
+    if (UP && r < nlive) {  // padding rows of the tile are never read
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int n = col0 + wn * 32 + h * 16 + 4 * lg;
@@ -242,7 +266,7 @@ __device__ __forceinline__ void tiled_gemm(
         v.y = pack_bf16x2(a[2], a[3]);
         *reinterpret_cast<uint2*>(act + (size_t)(start + r) * I + n) = v;
       }
-    } else if (r < nlive) {
+    } else if (!UP && r < nlive) {
       const int dst = row_ids[r];
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
@@ -265,13 +289,16 @@ __global__ __launch_bounds__(64 * WN * WM) void expert_tiled_kernel(
   static_assert(S >= 2 && (S - 2) * C::FPW <= 63, "the copies in flight must fit the vmcnt counter");
   static_assert(S * C::FRAGS * 1024 <= 160 * 1024, "the ring must fit the LDS");
   __shared__ __align__(16) unsigned char lds[S * C::FRAGS * 1024];
+  TiledWalk walk(*num_tiles, n_ntiles);
   int ntile, ti;
-  if (!tiled_item(*num_tiles, n_ntiles, ntile, ti)) return;
-  const int2 tile = tiles[ti];
-  const int start = tile.x, nlive = tile.y;
-  tiled_gemm<BM, WN, WM, S, UP, WPOL>(lds, tok_src, w, sorted_ids + start, start, nlive,
-                                      block_expert[start / block], ntile, K, ncols, I, top_k,
-                                      act, y);
+  while (walk.next(ntile, ti)) {
+    const int2 tile = tiles[ti];
+    const int start = tile.x, nlive = tile.y;
+    tiled_gemm<BM, WN, WM, S, UP, WPOL>(lds, tok_src, w, sorted_ids + start, start, nlive,
+                                        block_expert[start / block], ntile, K, ncols, I, top_k,
+                                        act, y);
+    __syncthreads();  // the next item's first copies reuse the ring
+  }
 }
 
 // Self-routing up GEMM (the align step fused into it, after the AlphaMoE page's section 6
@@ -295,18 +322,17 @@ __global__ __launch_bounds__(64 * WN) void expert_up_selfroute_kernel(
   constexpr int EPT = kSelfRouteMaxE / T;        // experts per thread in the scans
   static_assert(EPT * T == kSelfRouteMaxE, "the experts must split evenly over the threads");
   static_assert(S >= 2 && (S - 2) * C::FPW <= 63, "the copies in flight must fit the vmcnt counter");
-  static_assert(S * C::FRAGS * 1024 <= 160 * 1024, "the ring must fit the LDS");
-  static_assert((kSelfRouteMaxIds + 3 * kSelfRouteMaxE + 2 + BM + 2 * WN) * 4 <=
-                    S * C::FRAGS * 1024,
-                "the plan scratch must fit the ring");
+  static_assert(S * C::FRAGS * 1024 +
+                        (kSelfRouteMaxIds + 3 * kSelfRouteMaxE + 2 + BM + 2 * WN) * 4 <=
+                    160 * 1024,
+                "the ring and the plan must fit the LDS");
   __shared__ __align__(16) unsigned char lds[S * C::FRAGS * 1024];
-  // plan scratch in the ring, read only before the barrier ahead of the ring's first copy
-  int* const s_ids = reinterpret_cast<int*>(lds);          // [n]
-  int* const s_cnt = s_ids + kSelfRouteMaxIds;             // [E]
-  int* const s_pre = s_cnt + kSelfRouteMaxE;               // [E + 1] plan offsets
-  int* const s_tpre = s_pre + kSelfRouteMaxE + 1;          // [E + 1] tile list offsets
-  int* const s_rows = s_tpre + kSelfRouteMaxE + 1;         // [BM] flat index of each row
-  int (*const s_wsum)[WN] = reinterpret_cast<int (*)[WN]>(s_rows + BM);  // [2][WN]
+  __shared__ int s_ids[kSelfRouteMaxIds];        // the flat ids
+  __shared__ int s_cnt[kSelfRouteMaxE];          // per-expert counts
+  __shared__ int s_pre[kSelfRouteMaxE + 1];      // plan offsets
+  __shared__ int s_tpre[kSelfRouteMaxE + 1];     // tile list offsets
+  __shared__ int s_rows[BM];                     // flat index of each row of the current tile
+  __shared__ int s_wsum[2][WN];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int e = tid; e < E; e += T) s_cnt[e] = 0;
@@ -366,46 +392,48 @@ __global__ __launch_bounds__(64 * WN) void expert_up_selfroute_kernel(
     *num_padded = s_pre[E];
     *num_tiles = ntiles_live;
   }
+  TiledWalk walk(ntiles_live, n_ntiles);
   int ntile, ti;
-  if (!tiled_item(ntiles_live, n_ntiles, ntile, ti)) return;
-  // expert of tile ti: the last e with s_tpre[e] <= ti
-  int lo = 0, hi = E;
-  while (hi - lo > 1) {
-    const int mid = (lo + hi) >> 1;
-    if (s_tpre[mid] <= ti) lo = mid;
-    else hi = mid;
-  }
-  const int e = lo;
-  const int m = ti - s_tpre[e];
-  const int cnt = s_cnt[e];
-  const int start = s_pre[e] + m * BM;
-  const int nlive = min(BM, cnt - m * BM);
-  if (wave == 0) {  // occurrences m BM .. m BM + nlive - 1 of e, in ascending flat index
-    const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
-    const int r_lo = m * BM, r_hi = r_lo + nlive;
-    int base = 0;
-    for (int b0 = 0; b0 < n && base < r_hi; b0 += kWave) {
-      const int i = b0 + lane;
-      const bool hit = i < n && s_ids[i] == e;
-      const uint64_t bal = __ballot(hit);
-      const int r = base + __popcll(bal & lower);
-      if (hit && r >= r_lo && r < r_hi) s_rows[r - r_lo] = i;
-      base += __popcll(bal);
+  while (walk.next(ntile, ti)) {
+    // expert of tile ti: the last e with s_tpre[e] <= ti
+    int lo = 0, hi = E;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_tpre[mid] <= ti) lo = mid;
+      else hi = mid;
     }
+    const int e = lo;
+    const int m = ti - s_tpre[e];
+    const int cnt = s_cnt[e];
+    const int start = s_pre[e] + m * BM;
+    const int nlive = min(BM, cnt - m * BM);
+    if (wave == 0) {  // occurrences m BM .. m BM + nlive - 1 of e, in ascending flat index
+      const uint64_t lower = lane == 0 ? 0ull : (~0ull >> (kWave - lane));
+      const int r_lo = m * BM, r_hi = r_lo + nlive;
+      int base = 0;
+      for (int b0 = 0; b0 < n && base < r_hi; b0 += kWave) {
+        const int i = b0 + lane;
+        const bool hit = i < n && s_ids[i] == e;
+        const uint64_t bal = __ballot(hit);
+        const int r = base + __popcll(bal & lower);
+        if (hit && r >= r_lo && r < r_hi) s_rows[r - r_lo] = i;
+        base += __popcll(bal);
+      }
+    }
+    __syncthreads();
+    if (ntile == 0) {  // the plan of this tile (and of the rest of e's segment)
+      for (int r = tid; r < nlive; r += T) sorted_ids[start + r] = s_rows[r];
+      const int seg_end = s_pre[e + 1];
+      if (m == (cnt + BM - 1) / BM - 1)
+        for (int r = s_pre[e] + cnt + tid; r < seg_end; r += T) sorted_ids[r] = n;  // sentinel
+      if (m == 0)
+        for (int b = s_pre[e] / block + tid; b < seg_end / block; b += T) block_expert[b] = e;
+      if (tid == 0) tiles[ti] = make_int2(start, nlive);
+    }
+    tiled_gemm<BM, WN, 1, S, true, WPOL>(lds, x, w13, s_rows, start, nlive, e, ntile, K, I, I,
+                                         top_k, act, nullptr);
+    __syncthreads();  // s_rows and the ring are reused by the next item
   }
-  __syncthreads();
-  if (ntile == 0) {  // the plan of this tile (and of the rest of e's segment)
-    for (int r = tid; r < nlive; r += T) sorted_ids[start + r] = s_rows[r];
-    const int seg_end = s_pre[e + 1];
-    if (m == (cnt + BM - 1) / BM - 1)
-      for (int r = s_pre[e] + cnt + tid; r < seg_end; r += T) sorted_ids[r] = n;  // sentinel
-    if (m == 0)
-      for (int b = s_pre[e] / block + tid; b < seg_end / block; b += T) block_expert[b] = e;
-    if (tid == 0) tiles[ti] = make_int2(start, nlive);
-  }
-  // the GEMM reads s_rows, then a barrier, then its first copies overwrite the scratch
-  tiled_gemm<BM, WN, 1, S, true, WPOL, true>(lds, x, w13, s_rows, start, nlive, e, ntile, K, I,
-                                             I, top_k, act, nullptr);
 }
 
 // Variant for weights that several token tiles share (many tokens per expert): the same
@@ -432,159 +460,159 @@ __global__ __launch_bounds__(512) void expert_tiled_reg_kernel(
   constexpr int TCPW = MT * 2 / NW;              // token copies per wave per chunk
   constexpr int WSTAGE = WT * 2048, TSTAGE = MT * 2048;
   static_assert(WCPW + TCPW <= 63, "one chunk's copies must fit the vmcnt counter");
-  static_assert(WCPW * NW == WT * 2 && TCPW * NW == MT * 2, "copies must split evenly over the waves");
+  static_assert(WCPW * NW == WT * 2 && TCPW * NW == MT * 2,
+                "copies must split evenly over the waves");
   __shared__ __align__(16) unsigned char lds[2 * WSTAGE + 2 * TSTAGE];
   unsigned char* const wlds = lds;
   unsigned char* const tlds = lds + 2 * WSTAGE;
 
-  const int ntiles_live = *num_tiles;
-  const int live_items = ntiles_live * n_ntiles;
-  const int per_xcd = (live_items + kXcds - 1) / kXcds;
-  const int slot = blockIdx.x / kXcds;
-  if (slot >= per_xcd) return;
-  const int logical = (blockIdx.x % kXcds) * per_xcd + slot;
-  if (logical >= live_items) return;
-  const int ntile = logical / ntiles_live;
-  const int ti = logical % ntiles_live;
-  const int2 tile = tiles[ti];
-  const int start = tile.x, nlive = tile.y;
-  const int mt_active = (nlive + 15) >> 4;
-  const int e = block_expert[start / block];
+  TiledWalk walk(*num_tiles, n_ntiles);
+  int ntile, ti;
+  while (walk.next(ntile, ti)) {
+    const int2 tile = tiles[ti];
+    const int start = tile.x, nlive = tile.y;
+    const int mt_active = (nlive + 15) >> 4;
+    const int e = block_expert[start / block];
 
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int li = lane & 15, lg = lane >> 4;
-  const int col0 = UP ? ntile * 256 : ntile * 512;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int li = lane & 15, lg = lane >> 4;
+    const int col0 = UP ? ntile * 256 : ntile * 512;
 
-  // copy f of a ring: rows 8h..8h+7 (h = f % 2) of row tile f / 2; lane l copies 16 bytes of
-  // row 8h + l / 8 into slot l % 8, holding K chunk (l % 8) ^ (row % 8) ^ h of the row.
-  // Weight tiles 0..31 (up: gate rows in 0..15, up rows in 16..31), token tiles 0..7.
-  const int rr = lane >> 3;
-  const uint16_t* wsrc[WCPW];
-  const uint16_t* tsrc[TCPW];
-  const size_t wexp = UP ? (size_t)e * 2 * I * K : (size_t)e * ncols * K;
+    // copy f of a ring: rows 8h..8h+7 (h = f % 2) of row tile f / 2; lane l copies 16 bytes of
+    // row 8h + l / 8 into slot l % 8, holding K chunk (l % 8) ^ (row % 8) ^ h of the row.
+    // Weight tiles 0..31 (up: gate rows in 0..15, up rows in 16..31), token tiles 0..7.
+    const int rr = lane >> 3;
+    const uint16_t* wsrc[WCPW];
+    const uint16_t* tsrc[TCPW];
+    const size_t wexp = UP ? (size_t)e * 2 * I * K : (size_t)e * ncols * K;
 #pragma unroll
-  for (int i = 0; i < WCPW; ++i) {
-    const int f = wave * WCPW + i;
-    const int rt = f >> 1, h = f & 1;
-    const int koff = 8 * ((lane & 7) ^ rr ^ h);
-    int row;
-    if (UP) row = (rt < WT / 2) ? col0 + rt * 16 + 8 * h + rr : I + col0 + (rt - WT / 2) * 16 + 8 * h + rr;
-    else row = col0 + rt * 16 + 8 * h + rr;
-    const bool on = UP || row < ncols;
-    wsrc[i] = w + wexp + (size_t)(on ? row : 0) * K + koff;
-  }
-#pragma unroll
-  for (int i = 0; i < TCPW; ++i) {
-    const int f = wave * TCPW + i;
-    const int rt = f >> 1, h = f & 1;
-    const int koff = 8 * ((lane & 7) ^ rr ^ h);
-    const int r = 16 * rt + 8 * h + rr;
-    const bool on = r < nlive;
-    const int prow = start + (on ? r : 0);
-    if (UP) {
-      const int sid = on ? sorted_ids[prow] : 0;
-      tsrc[i] = tok_src + (size_t)(sid < 0 ? 0 : sid / top_k) * K + koff;
-    } else {
-      tsrc[i] = tok_src + (size_t)prow * K + koff;
+    for (int i = 0; i < WCPW; ++i) {
+      const int f = wave * WCPW + i;
+      const int rt = f >> 1, h = f & 1;
+      const int koff = 8 * ((lane & 7) ^ rr ^ h);
+      int row;
+      if (UP)
+        row = (rt < WT / 2) ? col0 + rt * 16 + 8 * h + rr
+                            : I + col0 + (rt - WT / 2) * 16 + 8 * h + rr;
+      else row = col0 + rt * 16 + 8 * h + rr;
+      const bool on = UP || row < ncols;
+      wsrc[i] = w + wexp + (size_t)(on ? row : 0) * K + koff;
     }
-  }
-  // this wave's weight tiles: up -- gate tiles 2w, 2w+1 and the up tiles of the same act
-  // columns; down -- tiles 4w..4w+3
-  int wtile[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) wtile[j] = UP ? ((j < 2) ? 2 * wave + j : WT / 2 + 2 * wave + j - 2) : 4 * wave + j;
+    for (int i = 0; i < TCPW; ++i) {
+      const int f = wave * TCPW + i;
+      const int rt = f >> 1, h = f & 1;
+      const int koff = 8 * ((lane & 7) ^ rr ^ h);
+      const int r = 16 * rt + 8 * h + rr;
+      const bool on = r < nlive;
+      const int prow = start + (on ? r : 0);
+      if (UP) {
+        const int sid = on ? sorted_ids[prow] : 0;
+        tsrc[i] = tok_src + (size_t)(sid < 0 ? 0 : sid / top_k) * K + koff;
+      } else {
+        tsrc[i] = tok_src + (size_t)prow * K + koff;
+      }
+    }
+    // this wave's weight tiles: up -- gate tiles 2w, 2w+1 and the up tiles of the same act
+    // columns; down -- tiles 4w..4w+3
+    int wtile[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      wtile[j] = UP ? ((j < 2) ? 2 * wave + j : WT / 2 + 2 * wave + j - 2) : 4 * wave + j;
 
-  const int nch = K / kTileKC;
-  auto issue_w = [&](int c) {
-    unsigned char* base = wlds + (size_t)(c & 1) * WSTAGE;
+    const int nch = K / kTileKC;
+    auto issue_w = [&](int c) {
+      unsigned char* base = wlds + (size_t)(c & 1) * WSTAGE;
 #pragma unroll
-    for (int i = 0; i < WCPW; ++i)
-      __builtin_amdgcn_global_load_lds((global_void*)(wsrc[i] + c * kTileKC),
-                                       (lds_void*)(base + (wave * WCPW + i) * 1024), 16, 0, WPOL);
-  };
-  auto issue_t = [&](int c) {
-    unsigned char* base = tlds + (size_t)(c & 1) * TSTAGE;
+      for (int i = 0; i < WCPW; ++i)
+        __builtin_amdgcn_global_load_lds((global_void*)(wsrc[i] + c * kTileKC),
+                                         (lds_void*)(base + (wave * WCPW + i) * 1024), 16, 0, WPOL);
+    };
+    auto issue_t = [&](int c) {
+      unsigned char* base = tlds + (size_t)(c & 1) * TSTAGE;
 #pragma unroll
-    for (int i = 0; i < TCPW; ++i)
-      __builtin_amdgcn_global_load_lds((global_void*)(tsrc[i] + c * kTileKC),
-                                       (lds_void*)(base + (wave * TCPW + i) * 1024), 16, 0, 0);
-  };
-  // MFMA fragment (16 rows x 32 K values) ks of the row tile at `tbase`: lane (li, lg)
-  // reads row li, K chunk lg + 4 ks, from its swizzled slot
-  const int frag_off = (li >> 3) * 1024 + (li & 7) * 128;
-  auto frag = [&](const unsigned char* tbase, int ks) -> u32x4 {
-    const int q = (lg + 4 * ks) ^ (li & 7) ^ (li >> 3);
-    return *reinterpret_cast<const u32x4*>(tbase + frag_off + q * 16);
-  };
+      for (int i = 0; i < TCPW; ++i)
+        __builtin_amdgcn_global_load_lds((global_void*)(tsrc[i] + c * kTileKC),
+                                         (lds_void*)(base + (wave * TCPW + i) * 1024), 16, 0, 0);
+    };
+    // MFMA fragment (16 rows x 32 K values) ks of the row tile at `tbase`: lane (li, lg)
+    // reads row li, K chunk lg + 4 ks, from its swizzled slot
+    const int frag_off = (li >> 3) * 1024 + (li & 7) * 128;
+    auto frag = [&](const unsigned char* tbase, int ks) -> u32x4 {
+      const int q = (lg + 4 * ks) ^ (li & 7) ^ (li >> 3);
+      return *reinterpret_cast<const u32x4*>(tbase + frag_off + q * 16);
+    };
 
-  f32x4 acc[4][MT];
+    f32x4 acc[4][MT];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < 4; ++j)
 #pragma unroll
-    for (int s = 0; s < MT; ++s) acc[j][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int s = 0; s < MT; ++s) acc[j][s] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  issue_w(0);
-  issue_t(0);
-  if (nch > 1) {
-    issue_w(1);
-    issue_t(1);
-  }
-  for (int c = 0; c < nch; ++c) {
-    // this wave's copies of chunk c are done (those of c + 1 may be in flight) ...
-    if (c + 1 < nch) wait_vmcnt<WCPW + TCPW>();
-    else wait_vmcnt<0>();
-    // ... and every wave's
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    const unsigned char* wb = wlds + (size_t)(c & 1) * WSTAGE;
-    const unsigned char* tb = tlds + (size_t)(c & 1) * TSTAGE;
-    u32x4 wa[kTileKS][4];
+    issue_w(0);
+    issue_t(0);
+    if (nch > 1) {
+      issue_w(1);
+      issue_t(1);
+    }
+    for (int c = 0; c < nch; ++c) {
+      // this wave's copies of chunk c are done (those of c + 1 may be in flight) ...
+      if (c + 1 < nch) wait_vmcnt<WCPW + TCPW>();
+      else wait_vmcnt<0>();
+      // ... and every wave's
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      const unsigned char* wb = wlds + (size_t)(c & 1) * WSTAGE;
+      const unsigned char* tb = tlds + (size_t)(c & 1) * TSTAGE;
+      u32x4 wa[kTileKS][4];
 #pragma unroll
-    for (int ks = 0; ks < kTileKS; ++ks)
+      for (int ks = 0; ks < kTileKS; ++ks)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wa[ks][j] = frag(wb + wtile[j] * 2048, ks);
-    // every wave holds its weight fragments of chunk c: the weight stage takes chunk c + 2
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (c + 2 < nch) issue_w(c + 2);
+        for (int j = 0; j < 4; ++j) wa[ks][j] = frag(wb + wtile[j] * 2048, ks);
+      // every wave holds its weight fragments of chunk c: the weight stage takes chunk c + 2
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (c + 2 < nch) issue_w(c + 2);
 #pragma unroll
-    for (int ks = 0; ks < kTileKS; ++ks)
+      for (int ks = 0; ks < kTileKS; ++ks)
 #pragma unroll
-      for (int s = 0; s < MT; ++s)
-        if (s < mt_active) {
-          const u32x4 xb = frag(tb + s * 2048, ks);
+        for (int s = 0; s < MT; ++s)
+          if (s < mt_active) {
+            const u32x4 xb = frag(tb + s * 2048, ks);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[j][s] = mfma16x16x32(wa[ks][j], xb, acc[j][s]);
+            for (int j = 0; j < 4; ++j) acc[j][s] = mfma16x16x32(wa[ks][j], xb, acc[j][s]);
+          }
+      // every wave has read its token fragments of chunk c: the token stage takes c + 2
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      if (c + 2 < nch) issue_t(c + 2);
+    }
+
+#pragma unroll
+    for (int s = 0; s < MT; ++s) {
+      if (s >= mt_active) continue;
+      const int r = 16 * s + li;
+      if (UP && r < nlive) {  // padding rows of the tile are never read
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int n = col0 + 32 * wave + 16 * h + 4 * lg;
+          float a[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) a[q] = silu_f32(acc[h][s][q]) * acc[2 + h][s][q];
+          uint2 v;
+          v.x = pack_bf16x2(a[0], a[1]);
+          v.y = pack_bf16x2(a[2], a[3]);
+          *reinterpret_cast<uint2*>(act + (size_t)(start + r) * I + n) = v;
         }
-    // every wave has read its token fragments of chunk c: the token stage takes c + 2
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-    if (c + 2 < nch) issue_t(c + 2);
-  }
-
+      } else if (!UP && r < nlive) {
+        const int dst = sorted_ids[start + r];
 #pragma unroll
-  for (int s = 0; s < MT; ++s) {
-    if (s >= mt_active) continue;
-    const int r = 16 * s + li;
-    if (UP) {
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int n = col0 + 32 * wave + 16 * h + 4 * lg;
-        float a[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) a[q] = silu_f32(acc[h][s][q]) * acc[2 + h][s][q];
-        uint2 v;
-        v.x = pack_bf16x2(a[0], a[1]);
-        v.y = pack_bf16x2(a[2], a[3]);
-        *reinterpret_cast<uint2*>(act + (size_t)(start + r) * I + n) = v;
-      }
-    } else if (r < nlive) {
-      const int dst = sorted_ids[start + r];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = col0 + 64 * wave + 16 * j + 4 * lg;
-        if (n < ncols)
-          *reinterpret_cast<float4*>(y + (size_t)dst * ncols + n) =
-              make_float4(acc[j][s][0], acc[j][s][1], acc[j][s][2], acc[j][s][3]);
+        for (int j = 0; j < 4; ++j) {
+          const int n = col0 + 64 * wave + 16 * j + 4 * lg;
+          if (n < ncols)
+            *reinterpret_cast<float4*>(y + (size_t)dst * ncols + n) =
+                make_float4(acc[j][s][0], acc[j][s][1], acc[j][s][2], acc[j][s][3]);
+        }
       }
     }
+    __syncthreads();  // the next item's first copies reuse the rings
   }
 }
 
@@ -797,6 +825,21 @@ __global__ __launch_bounds__(64 * WN * WM) void expert_tiled_mx_kernel(
   }
 }
 
+// Grid of the item-walking kernels: at most as many workgroups as fit on the device at once
+// (the CU count times the workgroups one CU's 160 KiB of LDS holds, a multiple of the 8
+// XCDs), and no more than the items need.
+static long walk_grid(long items, size_t lds_bytes) {
+  const long all = (items + kXcds - 1) / kXcds * kXcds;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      cus < kXcds)
+    return all;
+  const long per_cu = lds_bytes > 0 ? (long)((160 * 1024) / lds_bytes) : 1;
+  const long resident = (long)cus * (per_cu > 0 ? per_cu : 1) / kXcds * kXcds;
+  return all < resident ? all : resident;
+}
+
 template <int BM, int WN, int WM, int S, bool UP, int WPOL>
 static hipError_t launch_tiled(const uint16_t* src, const uint16_t* w, const int32_t* sorted_ids,
                                const int32_t* block_expert, const int2* tiles,
@@ -805,8 +848,11 @@ static hipError_t launch_tiled(const uint16_t* src, const uint16_t* w, const int
   const int per_ntile = UP ? 32 * WN : 64 * WN;
   if (UP && I % per_ntile != 0) return hipErrorInvalidValue;
   const int n_ntiles = (ncols + per_ntile - 1) / per_ntile;
-  const long total = (long)max_tiles * n_ntiles;
-  const long grid = (total + kXcds - 1) / kXcds * kXcds;
+  // 64-row tiles (few tokens per expert) walk several items per workgroup; 128-row tiles
+  // take one each (measured: walking costs 1-2 % at M=512 and M=2048)
+  const long items = (long)max_tiles * n_ntiles;
+  const long grid = BM == 64 ? walk_grid(items, S * TiledCfg<BM, WN, WM>::FRAGS * 1024)
+                             : (items + kXcds - 1) / kXcds * kXcds;
   hipLaunchKernelGGL((expert_tiled_kernel<BM, WN, WM, S, UP, WPOL>), dim3((unsigned)grid),
                      dim3(TiledCfg<BM, WN, WM>::THREADS), 0, s, src, w, sorted_ids, block_expert,
                      tiles, num_tiles, n_ntiles, K, ncols, I, top_k, block, act, y);
@@ -822,8 +868,8 @@ static hipError_t launch_tiled_reg(const uint16_t* src, const uint16_t* w,
   const int per_ntile = UP ? 256 : 512;
   if (K % kTileKC != 0 || (UP && I % per_ntile != 0)) return hipErrorInvalidValue;
   const int n_ntiles = (ncols + per_ntile - 1) / per_ntile;
-  const long total = (long)max_tiles * n_ntiles;
-  const long grid = (total + kXcds - 1) / kXcds * kXcds;
+  const long items = (long)max_tiles * n_ntiles;
+  const long grid = (items + kXcds - 1) / kXcds * kXcds;  // one item per workgroup
   hipLaunchKernelGGL((expert_tiled_reg_kernel<BM, UP, WPOL>), dim3((unsigned)grid), dim3(512), 0, s,
                      src, w, sorted_ids, block_expert, tiles, num_tiles, n_ntiles, K, ncols, I,
                      top_k, block, act, y);
@@ -858,8 +904,7 @@ hipError_t launch_expert_up_selfroute(const uint16_t* x, const uint16_t* w13, co
   const int per_ntile = 32 * WN;
   if (n > kSelfRouteMaxIds || E > kSelfRouteMaxE || I % per_ntile != 0) return hipErrorInvalidValue;
   const int n_ntiles = I / per_ntile;
-  const long total = (long)tile_capacity(n, E, BM) * n_ntiles;
-  const long grid = (total + kXcds - 1) / kXcds * kXcds;
+  const long grid = walk_grid((long)tile_capacity(n, E, BM) * n_ntiles, 160 * 1024);
   hipLaunchKernelGGL((expert_up_selfroute_kernel<BM, WN, 3, kNT>), dim3((unsigned)grid),
                      dim3(TiledCfg<BM, WN, 1>::THREADS), 0, s, x, w13, ids, n, E, block,
                      n_ntiles, H, I, top_k, sorted_ids, block_expert, num_padded, tiles,

@@ -12,9 +12,9 @@ between two kernels adds a few microseconds of idle, so that pass is not the hea
 of the headline workload (decode, M=8); `sweep` holds the same measurement at M=128,
 512 and 2048 on the same weights.  `roofline` is for the dominant kernel (the grouped
 up-GEMM + SwiGLU, which streams W13) against the 8 TB/s HBM peak, and against the read
-rate this device reaches with a plain streaming read (`measured_read_peak`, from the
-probe library built next to the layer's); `cpu_baseline` is the CPU oracle timed on a
-bounded sample of the decode workload.  `mxfp8_decode` times the same decode layer with
+rate this device reaches with a plain streaming read of the resident W13
+(`measured_read_peak`, from the probe library built next to the layer's);
+`cpu_baseline` is the CPU oracle timed on a bounded sample of the decode workload.  `mxfp8_decode` times the same decode layer with
 the expert weights quantized to MXFP8 (moe_forward_mx); it is a separate measurement, not
 the headline, whose weights are bf16.
 """
@@ -162,17 +162,20 @@ def cpu_baseline(mi, torch):
     }
 
 
-def read_probe_gbs(torch, dev, gib=4, reps=5):
+def read_probe_gbs(torch, dev, gib=4, reps=5, buf=None):
     """Achievable HBM read rate on this device: best of `reps` timed passes of the read
-    probe (prefill_sigmoid_router_amd/probe/read_bw.hip) over a `gib` GiB buffer."""
+    probe (prefill_sigmoid_router_amd/probe/read_bw.hip) over `buf` (a resident tensor,
+    read as raw bytes) or, without one, a fresh `gib` GiB buffer."""
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "prefill_sigmoid_router_amd", "libmoe_probe.so"))
     lib.moe_probe_read.restype = ctypes.c_int
     lib.moe_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                    ctypes.c_void_p]
     lib.moe_probe_read_grid.restype = ctypes.c_int
-    n = gib << 30
-    buf = torch.ones(n // 4, dtype=torch.int32, device=dev)
+    own = buf is None
+    if own:
+        buf = torch.ones((gib << 30) // 4, dtype=torch.int32, device=dev)
+    n = buf.numel() * buf.element_size() // 16 * 16
     sink = torch.empty(lib.moe_probe_read_grid(), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
@@ -193,7 +196,9 @@ def read_probe_gbs(torch, dev, gib=4, reps=5):
         b.record(stream)
         b.synchronize()
         best = min(best, a.elapsed_time(b))
-    del buf, sink
+    del sink
+    if own:
+        del buf
     return n / (best * 1e-3) / 1e9
 
 
@@ -301,8 +306,9 @@ def main():
         del mx
         torch.cuda.empty_cache()
 
+    # the read probe over the resident W13 (the bytes the up GEMM streams)
     print("bench: timing the HBM read probe", file=sys.stderr, flush=True)
-    read_gbs = read_probe_gbs(torch, dev)
+    read_gbs = read_probe_gbs(torch, dev, buf=weights["w13"])
     traffic = load_traffic()
     rows = B.moe_gemm_tile_rows(head.M, head.E, head.top_k, head.I)
     if B.moe_forward_self_routes(head.M, head.E, head.top_k, head.I):

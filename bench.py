@@ -290,7 +290,7 @@ def main():
                          dev, mx=mx)
         mx_line = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
         mx_line["weights"] = "MXFP8 (E4M3 + E8M0 per 32 values along K), activations bf16"
-        mx_line["up_kernel"] = "expert_up_mx_kernel"
+        mx_line["up_kernel"] = "expert_mx_decode_kernel<true> (codes copied into LDS, 32-row tiles)"
         mx_line["up_hbm_frac"] = round(r["up_gbs"] / HBM_PEAK_GBS, 4)
         if not args.no_sweep:
             mx_sweep = {}

@@ -37,12 +37,12 @@
 
 #include "device_common.h"
 #include "launchers.h"
+#include "tiled_common.h"
 
 namespace moe {
 
 constexpr int kTileKC = 64;                     // K values per chunk: one 128-byte line per row
 constexpr int kTileKS = kTileKC / 32;           // MFMA K steps per chunk
-constexpr int kXcds = 8;                        // MI355X: 8 XCDs, round-robin dispatch
 
 // Workgroup of WN x WM waves.  Weight rows: 64 * WN (4 row tiles of 16 per wave along
 // WN); token rows: BM (BM / 16 / WM row tiles per wave along WM).  Each wave accumulates
@@ -59,15 +59,6 @@ struct TiledCfg {
   static_assert(MT % WM == 0, "token tiles must split evenly over the waves");
 };
 
-typedef __attribute__((address_space(1))) void global_void;
-typedef __attribute__((address_space(3))) void lds_void;
-
-// Wait until at most N vector-memory operations of this wave are outstanding.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
-}
-
 // Wait until only this wave's copies of the `after` chunks issued after the one needed
 // are outstanding (FPW copies per chunk; after <= A).
 template <int FPW, int A>
@@ -79,45 +70,6 @@ __device__ __forceinline__ void wait_chunks_after(int after) {
     else wait_chunks_after<FPW, A - 1>(after);
   }
 }
-
-// Work item -> (N tile, tile) for live_items = ntiles_live * n_ntiles items: workgroup p
-// runs on XCD p % 8, and each XCD takes an equal contiguous share, N tile by N tile.
-// Returns false for a workgroup past the items.  (Kernels that take one item per
-// workgroup; the others walk their share with TiledWalk.)
-__device__ __forceinline__ bool tiled_item(int ntiles_live, int n_ntiles, int& ntile, int& ti) {
-  const int live_items = ntiles_live * n_ntiles;
-  const int per_xcd = (live_items + kXcds - 1) / kXcds;
-  const int slot = blockIdx.x / kXcds;
-  if (slot >= per_xcd) return false;
-  const int logical = (blockIdx.x % kXcds) * per_xcd + slot;
-  if (logical >= live_items) return false;
-  ntile = logical / ntiles_live;
-  ti = logical % ntiles_live;
-  return true;
-}
-
-// The same items, walked by a grid of any multiple of 8 workgroups: each XCD's workgroups
-// step through its share with a stride of their count.  A grid as large as the items gives
-// one item per workgroup; the launchers use one workgroup per CU instead, so a workgroup's
-// epilogue stores drain while its next item's first copies are in flight (a wave that ends
-// waits for its outstanding stores, holding the CU's LDS meanwhile).
-struct TiledWalk {
-  int ntiles_live, live, per_xcd, first, slot, stride;
-  __device__ TiledWalk(int ntl, int n_ntiles)
-      : ntiles_live(ntl), live(ntl * n_ntiles), per_xcd((live + kXcds - 1) / kXcds),
-        first((blockIdx.x % kXcds) * per_xcd), slot(blockIdx.x / kXcds),
-        stride(gridDim.x / kXcds) {}
-  // this workgroup's next item; false once its share is done
-  __device__ bool next(int& ntile, int& ti) {
-    if (slot >= per_xcd) return false;
-    const int logical = first + slot;
-    if (logical >= live) return false;
-    slot += stride;
-    ntile = logical / ntiles_live;
-    ti = logical % ntiles_live;
-    return true;
-  }
-};
 
 // One work item of the tiled GEMM: plan rows start..start+nlive-1 of expert e (row_ids[r] =
 // the flat index of plan row start + r) against the weight rows of N tile `ntile`.
@@ -827,21 +779,6 @@ __global__ __launch_bounds__(64 * WN * WM) void expert_tiled_mx_kernel(
       }
     }
   }
-}
-
-// Grid of the item-walking kernels: at most as many workgroups as fit on the device at once
-// (the CU count times the workgroups one CU's 160 KiB of LDS holds, a multiple of the 8
-// XCDs), and no more than the items need.
-static long walk_grid(long items, size_t lds_bytes) {
-  const long all = (items + kXcds - 1) / kXcds * kXcds;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      cus < kXcds)
-    return all;
-  const long per_cu = lds_bytes > 0 ? (long)((160 * 1024) / lds_bytes) : 1;
-  const long resident = (long)cus * (per_cu > 0 ? per_cu : 1) / kXcds * kXcds;
-  return all < resident ? all : resident;
 }
 
 template <int BM, int WN, int WM, int S, bool UP, int WPOL>

@@ -82,23 +82,27 @@ hipError_t launch_expert_down_tiled_mx(const uint16_t* act, const uint8_t* w2c, 
                                        int tile_rows, int M, int H, int I, int top_k, int block,
                                        float* y, hipStream_t s);
 
+// MXFP8 GEMMs for few tokens per expert: the codes are copied whole lines at a time into
+// LDS and dequantized from there into the MFMA operands; work items are the tiles of height
+// kMxDecodeTileRows of `tiles`.  H and I multiples of 128, scales 4-byte aligned.
+constexpr int kMxDecodeTileRows = 32;
+hipError_t launch_expert_up_mx_decode(const uint16_t* x, const uint8_t* w13c, const uint8_t* w13s,
+                                      const int32_t* sorted_ids, const int32_t* block_expert,
+                                      const int2* tiles, const int32_t* num_tiles, int max_tiles,
+                                      int H, int I, int top_k, int block, uint16_t* act,
+                                      hipStream_t s);
+hipError_t launch_expert_down_mx_decode(const uint16_t* act, const uint8_t* w2c,
+                                        const uint8_t* w2s, const int32_t* sorted_ids,
+                                        const int32_t* block_expert, const int2* tiles,
+                                        const int32_t* num_tiles, int max_tiles, int H, int I,
+                                        int top_k, int block, float* y, hipStream_t s);
+
 // MXFP8 weights (E4M3 codes, one E8M0 scale byte per 32 values along K): quantize bf16
-// [rows, K] (K % 32 == 0), dequantize back to bf16, and the streaming GEMMs on them
-// (same work items as launch_expert_up / launch_expert_down; H resp. I % 128 == 0).
+// [rows, K] (K % 32 == 0) and dequantize back to bf16.
 hipError_t launch_mx_quantize(const uint16_t* w, int64_t rows, int K, uint8_t* codes,
                               uint8_t* scales, hipStream_t s);
 hipError_t launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int K,
                                 uint16_t* w, hipStream_t s);
-hipError_t launch_expert_up_mx(const uint16_t* x, const uint8_t* w13c, const uint8_t* w13s,
-                               const int32_t* sorted_ids, const int32_t* block_expert,
-                               const int32_t* num_padded, const int2* tiles,
-                               const int32_t* num_tiles, int max_tiles, int M, int H, int I,
-                               int top_k, int block, uint16_t* act, hipStream_t s);
-hipError_t launch_expert_down_mx(const uint16_t* act, const uint8_t* w2c, const uint8_t* w2s,
-                                 const int32_t* sorted_ids, const int32_t* block_expert,
-                                 const int32_t* num_padded, const int2* tiles,
-                                 const int32_t* num_tiles, int max_tiles, int M, int H, int I,
-                                 int top_k, int block, float* y, hipStream_t s);
 
 // Weighted top-k combine + residual add + RMSNorm.
 hipError_t launch_finalize(const float* y, const float* topk_w, const uint16_t* residual,

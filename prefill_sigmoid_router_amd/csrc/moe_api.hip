@@ -71,15 +71,18 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 // Grouped-GEMM kernels by expected tokens per expert (M * top_k / E), the M-range
 // dispatch pattern of the FlashInfer MNNVL finalize presets (thresholds measured on
 // MI355X at H=7168, I=2048, E=256).  Returns the token-tile height: 64 or 128 for the
-// LDS-tiled kernels, 16 for the weight-streaming kernels.  bf16 weights use the tiled
-// kernels at every size (with nontemporal weight copies they beat the streaming kernels
-// even at decode: M=8 layer 1,551 -> 1,405 us); the streaming kernels serve I that is not
-// a multiple of 256 and MXFP8 weights below 16 tokens per expert (their tiled kernels
-// dequantize every weight once per token tile: streaming faster up to 12, tiled from 16).
+// LDS-tiled kernels, 16 for the weight-streaming kernels, 32 for the MXFP8 kernels of few
+// tokens per expert.  bf16 weights use the tiled kernels at every size (with nontemporal
+// weight copies they beat the streaming kernels even at decode: M=8 layer 1,551 -> 1,405
+// us); the streaming kernels serve I that is not a multiple of 256.  MXFP8 weights below 16
+// tokens per expert run the kernels that copy the codes into LDS and dequantize them into
+// the MFMA operands (M=8 layer 867 -> 796-832 us, M=128 2,528 -> 1,909-2,019 us against the
+// streaming MXFP8 kernels they replaced); from 16, the tiled kernels that dequantize the
+// codes into the LDS tiles.
 int gemm_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I, bool mx) {
   if (I % moe::tiled_up_columns() != 0) return 16;
   const int64_t per_expert = (int64_t)M * top_k / E;
-  if (mx && per_expert < 16) return 16;
+  if (mx && per_expert < 16) return moe::kMxDecodeTileRows;
   if (per_expert < 32) return 64;
   return 128;
 }
@@ -310,9 +313,9 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   if (self_route)
     up_err = moe::launch_expert_up_selfroute(x, W.w13, ids, M, H, E, I, top_k, block, sorted, bexp,
                                              npad, tiles, ntiles, act, s);
-  else if (W.mx() && trows == 16)
-    up_err = moe::launch_expert_up_mx(x, W.w13c, W.w13s, sorted, bexp, npad, tiles, ntiles,
-                                      max_tiles, M, H, I, top_k, block, act, s);
+  else if (W.mx() && trows == moe::kMxDecodeTileRows)
+    up_err = moe::launch_expert_up_mx_decode(x, W.w13c, W.w13s, sorted, bexp, tiles, ntiles,
+                                             max_tiles, H, I, top_k, block, act, s);
   else if (W.mx())
     up_err = moe::launch_expert_up_tiled_mx(x, W.w13c, W.w13s, sorted, bexp, tiles, ntiles,
                                             max_tiles, trows, M, H, I, top_k, block, act, s);
@@ -325,9 +328,9 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   if (up_err != hipSuccess) return MOE_ERR_HIP;
   if (!mark(3)) return MOE_ERR_HIP;
   hipError_t down_err;
-  if (W.mx() && trows == 16)
-    down_err = moe::launch_expert_down_mx(act, W.w2c, W.w2s, sorted, bexp, npad, tiles, ntiles,
-                                          max_tiles, M, H, I, top_k, block, y, s);
+  if (W.mx() && trows == moe::kMxDecodeTileRows)
+    down_err = moe::launch_expert_down_mx_decode(act, W.w2c, W.w2s, sorted, bexp, tiles, ntiles,
+                                                 max_tiles, H, I, top_k, block, y, s);
   else if (W.mx())
     down_err = moe::launch_expert_down_tiled_mx(act, W.w2c, W.w2s, sorted, bexp, tiles, ntiles,
                                                 max_tiles, trows, M, H, I, top_k, block, y, s);

@@ -164,10 +164,10 @@ def test_gemm_tile_rows_follows_tokens_per_expert(B):
     assert B.moe_gemm_tile_rows(2048, 256, 16, 100) == 0
     assert B.moe_gemm_tile_rows(8, 0, 1, 2048) == 0
     assert B.moe_gemm_tile_rows(-1, 256, 16, 2048) == 0
-    # MXFP8 weights: streaming below 16 tokens per expert, I a multiple of 256
-    assert B.moe_gemm_tile_rows_mx(8, 256, 16, 2048) == 16
-    assert B.moe_gemm_tile_rows_mx(128, 256, 16, 2048) == 16
-    assert B.moe_gemm_tile_rows_mx(255, 256, 16, 2048) == 16
+    # MXFP8 weights: 32-row tiles of LDS codes below 16 tokens per expert, I a multiple of 256
+    assert B.moe_gemm_tile_rows_mx(8, 256, 16, 2048) == 32
+    assert B.moe_gemm_tile_rows_mx(128, 256, 16, 2048) == 32
+    assert B.moe_gemm_tile_rows_mx(255, 256, 16, 2048) == 32
     assert B.moe_gemm_tile_rows_mx(256, 256, 16, 2048) == 64
     assert B.moe_gemm_tile_rows_mx(512, 256, 16, 2048) == 128
     assert B.moe_gemm_tile_rows_mx(2048, 256, 16, 2048) == 128

@@ -143,9 +143,10 @@ class _OracleMxExperts:
         return mxo.mx_dequantize_bf16_bits(c, s)
 
 
-# expected tokens per expert M * top_k / E: below 16 the streaming kernels (mx_tiny 1,
-# mx_mid 4.6, mx_one_token 0.1), 16..31 the 64-row LDS tiles (mx_tiles64 24), from 32 the
-# 128-row tiles (mx_many 150)
+# expected tokens per expert M * top_k / E: below 16 the kernels that copy the codes into
+# LDS (32-row tiles: mx_tiny 1, mx_mid 4.6, mx_one_token 0.1, mx_dec_partial 10,
+# mx_dec_groups 6), 16..31 the 64-row LDS tiles (mx_tiles64 24), from 32 the 128-row tiles
+# (mx_many 150)
 SMALL_MX = {
     "mx_tiny": mi.LayerConfig("mx_tiny", M=4, H=256, E=8, top_k=2, I=512, block=16),
     "mx_mid": mi.LayerConfig("mx_mid", M=37, H=1024, E=32, top_k=4, I=256, block=16),
@@ -156,6 +157,14 @@ SMALL_MX = {
                               zipf_s=1.0),
     # I=256: one K group, so one down K half is empty
     "mx_one_token": mi.LayerConfig("mx_one_token", M=1, H=512, E=64, top_k=8, I=256, block=16),
+    # 32-row tiles: H=768 is 6 K chunks of 128 with 24 scale bytes per row (one partial
+    # group of 8 chunks), and Zipf routing gives the hot expert more than 16 rows (both
+    # token row tiles of its tile live)
+    "mx_dec_partial": mi.LayerConfig("mx_dec_partial", M=40, H=768, E=8, top_k=2, I=256,
+                                     block=16, zipf_s=1.0),
+    # H=1280: 10 K chunks, a whole scale group then a partial one (8 of 32 bytes)
+    "mx_dec_groups": mi.LayerConfig("mx_dec_groups", M=24, H=1280, E=16, top_k=4, I=512,
+                                    block=32),
 }
 
 
@@ -210,7 +219,7 @@ def mx_full(B, dev):
 
 @pytest.mark.parametrize("name", MX_FULL)
 def test_forward_mx_full_size(B, dev, mx_full, name):
-    """The real-shape workloads with MXFP8 weights -- the streaming kernels at M=8 and
+    """The real-shape workloads with MXFP8 weights -- 32-row tiles of LDS codes at M=8 and
     M=128, LDS tiles of 128 rows at M=2048: routing and plan bit-exact for
     every token; codes of the experts a sampled token uses bit-exact; that token's output
     against the oracle on the oracle's own dequantized weights."""
@@ -243,7 +252,7 @@ def test_forward_mx_full_size(B, dev, mx_full, name):
 
 @pytest.mark.parametrize("name", ["mx_tiny", "mx_many"])
 def test_forward_mx_graph_replay(B, dev, name):
-    """moe_forward_mx captured in a HIP graph (streaming kernels for mx_tiny, 128-row tiles
+    """moe_forward_mx captured in a HIP graph (32-row tiles of LDS codes for mx_tiny, 128-row tiles
     for mx_many): each replay, with new inputs copied in and eager work between replays,
     equals bit for bit an eager call on the same inputs on a side stream."""
     cfg = SMALL_MX[name]

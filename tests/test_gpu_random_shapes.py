@@ -1,7 +1,7 @@
 """GPU parity of the whole layer on seeded random shapes (bf16 and MXFP8 experts), through
 the C ABI, against the CPU oracle: routing and plan bit-exact, outputs to the bf16 bar
 (max-abs 2e-2, relative-L2 1e-2).  The shapes mix token counts that land on every GEMM
-path (16-row streaming, 64- and 128-row LDS tiles), K tails, partial N tiles, single and
+path (16-row streaming, 32-row MXFP8 LDS codes, 64- and 128-row LDS tiles), K tails, partial N tiles, single and
 many experts, every block size and both routing recipes."""
 import numpy as np
 import pytest

@@ -8,8 +8,8 @@
 // paragraph, rules 1-2: keep the working set on chip, split each weight stream over many
 // programs so that small-batch decode runs at memory bandwidth.
 //
-// Workgroup: 4 waves, 256 weight rows (up: the gate and up rows of 128 act columns; down:
-// 256 output columns) x a 32-row token tile of one expert.  K runs in chunks of 128
+// Workgroup: 8 waves, 256 weight rows (up: the gate and up rows of 128 act columns; down:
+// 256 output columns; each wave 2 row tiles of 16) x a 32-row token tile of one expert.  K runs in chunks of 128
 // values: one 128-byte line of codes per weight row (32 KiB) and 256 bytes of bf16 token
 // row per token row (8 KiB), both copied global -> LDS with global_load_lds_dwordx4 into a
 // 3-stage ring, so two chunks are in flight while one is computed; the code copies are
@@ -31,7 +31,8 @@ namespace {
 
 constexpr int kKC = 128;                              // K values (code bytes) per chunk
 constexpr int kRows = 256;                            // weight rows per workgroup
-constexpr int kWaves = 4;
+constexpr int kWaves = 8;                             // 2 per SIMD (4: decode up 506 -> 486 us)
+constexpr int kTW = 16 / kWaves;                      // row tiles per wave
 constexpr int kBM = kMxDecodeTileRows;                // token rows per tile
 constexpr int kMT = kBM / 16;                         // token row tiles
 constexpr int kStages = 3;
@@ -67,8 +68,8 @@ __device__ __forceinline__ u32x4 dequant8(uint2 codes, uint32_t scale_byte) {
 // __restrict__ pointers, as in the bf16 tiled GEMMs: the compiler then leaves the ordering
 // of the global -> LDS copies and the LDS reads to the explicit waits and barriers below
 // (otherwise it drains every copy in flight before each chunk's first LDS read).
-// This wave's 4 of the 16 row tiles: up -> gate tiles 2w, 2w+1 and up tiles 8+2w, 9+2w
-// (act columns 32w .. 32w+31 of the N tile); down -> tiles 4w .. 4w+3.
+// This wave's kTW of the 16 row tiles: up -> gate tiles w kTW/2 .. and the up tiles 8 later
+// (act columns 16 w kTW/2 .. of the N tile); down -> tiles w kTW ...
 template <bool UP>
 __device__ __forceinline__ void mx_decode_item(
     unsigned char* __restrict__ ring, unsigned char* __restrict__ sring, int ntile, int ti,
@@ -82,10 +83,11 @@ __device__ __forceinline__ void mx_decode_item(
   const int ngroups = (nch + kGroup - 1) / kGroup;
   const int srow = K / 32;
   const int rows_e = UP ? 2 * I : ncols;
-  int wtile[4];
+  int wtile[kTW];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
-    wtile[j] = UP ? ((j < 2) ? 2 * wave + j : 8 + 2 * wave + (j - 2)) : 4 * wave + j;
+  for (int j = 0; j < kTW; ++j)
+    wtile[j] = UP ? ((j < kTW / 2) ? kTW / 2 * wave + j : 8 + kTW / 2 * wave + (j - kTW / 2))
+                  : kTW * wave + j;
   // weight row, within the expert, of workgroup row R of N tile nt
   auto wrow = [&](int nt, int R) -> int {
     const int t = R >> 4, rr = R & 15;
@@ -160,9 +162,9 @@ __device__ __forceinline__ void mx_decode_item(
                                        0);
   };
 
-  f32x4 acc[4][kMT];
+  f32x4 acc[kTW][kMT];
 #pragma unroll
-  for (int j = 0; j < 4; ++j)
+  for (int j = 0; j < kTW; ++j)
 #pragma unroll
     for (int s = 0; s < kMT; ++s) acc[j][s] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int mt_active = (nlive + 15) >> 4;
@@ -170,17 +172,17 @@ __device__ __forceinline__ void mx_decode_item(
   auto compute = [&](int c) {
     const unsigned char* base = ring + (c % kStages) * kStage;
     const unsigned char* sb = sring + ((c / kGroup) & 1) * kScaleStage + (c % kGroup) * 4;
-    uint32_t sc[4];                                    // scale bytes of the 4 K steps
+    uint32_t sc[kTW];                                  // scale bytes of the 4 K steps
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < kTW; ++j)
       sc[j] = *reinterpret_cast<const uint32_t*>(sb + (16 * wtile[j] + li) * 32);
 #pragma unroll
     for (int ks = 0; ks < kKC / 32; ++ks) {
       // codes K 32 ks + 8 lg .. + 8 of row li: 16-byte slot 2 ks + lg / 2, half lg % 2
       const int cq = ((2 * ks + (lg >> 1)) ^ (li & 7) ^ (li >> 3)) * 16 + (lg & 1) * 8;
-      u32x4 wa[4];
+      u32x4 wa[kTW];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < kTW; ++j) {
         const uint2 cw = *reinterpret_cast<const uint2*>(base + wtile[j] * 2048 + li * 128 + cq);
         wa[j] = dequant8(cw, (sc[j] >> (8 * ks)) & 0xFFu);
       }
@@ -190,7 +192,7 @@ __device__ __forceinline__ void mx_decode_item(
           const u32x4 xb = *reinterpret_cast<const u32x4*>(
               base + kCodeStage + (16 * s + li) * 256 + (((4 * ks + lg) ^ li) * 16));
 #pragma unroll
-          for (int j = 0; j < 4; ++j) acc[j][s] = mfma16x16x32(wa[j], xb, acc[j][s]);
+          for (int j = 0; j < kTW; ++j) acc[j][s] = mfma16x16x32(wa[j], xb, acc[j][s]);
         }
       }
     }
@@ -224,11 +226,11 @@ __device__ __forceinline__ void mx_decode_item(
     if (r >= nlive) continue;                          // padding rows are never read
     if (UP) {
 #pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const int n = ntile * 128 + 32 * wave + 16 * h + 4 * lg;
+      for (int h = 0; h < kTW / 2; ++h) {
+        const int n = ntile * 128 + 16 * (kTW / 2 * wave + h) + 4 * lg;
         float a[4];
 #pragma unroll
-        for (int q = 0; q < 4; ++q) a[q] = silu_f32(acc[h][s][q]) * acc[2 + h][s][q];
+        for (int q = 0; q < 4; ++q) a[q] = silu_f32(acc[h][s][q]) * acc[kTW / 2 + h][s][q];
         uint2 v;
         v.x = pack_bf16x2(a[0], a[1]);
         v.y = pack_bf16x2(a[2], a[3]);
@@ -237,8 +239,8 @@ __device__ __forceinline__ void mx_decode_item(
     } else {
       const int dst = sorted_ids[start + r];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int n = ntile * kRows + 64 * wave + 16 * j + 4 * lg;
+      for (int j = 0; j < kTW; ++j) {
+        const int n = ntile * kRows + 16 * (kTW * wave + j) + 4 * lg;
         if (n < ncols)
           __builtin_nontemporal_store(acc[j][s],
                                       reinterpret_cast<f32x4*>(y + (size_t)dst * ncols + n));

@@ -573,7 +573,9 @@ __global__ __launch_bounds__(512) void expert_tiled_reg_kernel(
 }
 
 // MXFP8 weights (E4M3 codes, one E8M0 scale byte per 32 values along K) in the tiled
-// kernels.  Same workgroup tile, work order, LDS ring layout and MFMA loop as
+// kernels; moe_forward_mx runs it for the up GEMM from 64 tokens per expert, where the
+// 128-row tiles of a hot expert share its codes (its other GEMMs copy the codes into LDS,
+// expert_mx_decode.hip).  Same workgroup tile, work order, LDS ring layout and MFMA loop as
 // expert_tiled_kernel; the weight part of a ring stage is filled from the codes instead of
 // by copies: each thread loads PIECES pieces of 16 codes (4 lanes cover a row's 64 codes
 // of a chunk: 16 rows x 64 bytes per wave load), dequantizes them exactly to bf16 with
@@ -933,27 +935,9 @@ hipError_t launch_expert_up_tiled_mx(const uint16_t* x, const uint8_t* w13c, con
                                      int tile_rows, int M, int H, int I, int top_k, int block,
                                      uint16_t* act, hipStream_t s) {
   (void)M;
-  if (tile_rows == 64)
-    return launch_tiled_mx<64, true>(x, w13c, w13s, sorted_ids, block_expert, tiles, num_tiles,
-                                     max_tiles, H, I, I, top_k, block, act, nullptr, s);
   if (tile_rows == 128)
     return launch_tiled_mx<128, true>(x, w13c, w13s, sorted_ids, block_expert, tiles, num_tiles,
                                       max_tiles, H, I, I, top_k, block, act, nullptr, s);
-  return hipErrorInvalidValue;
-}
-
-hipError_t launch_expert_down_tiled_mx(const uint16_t* act, const uint8_t* w2c, const uint8_t* w2s,
-                                       const int32_t* sorted_ids, const int32_t* block_expert,
-                                       const int2* tiles, const int32_t* num_tiles, int max_tiles,
-                                       int tile_rows, int M, int H, int I, int top_k, int block,
-                                       float* y, hipStream_t s) {
-  (void)M;
-  if (tile_rows == 64)
-    return launch_tiled_mx<64, false>(act, w2c, w2s, sorted_ids, block_expert, tiles, num_tiles,
-                                      max_tiles, I, H, I, top_k, block, nullptr, y, s);
-  if (tile_rows == 128)
-    return launch_tiled_mx<128, false>(act, w2c, w2s, sorted_ids, block_expert, tiles, num_tiles,
-                                       max_tiles, I, H, I, top_k, block, nullptr, y, s);
   return hipErrorInvalidValue;
 }
 

@@ -69,33 +69,30 @@ hipError_t launch_expert_up_selfroute(const uint16_t* x, const uint16_t* w13, co
                                       int32_t* num_padded, int2* tiles, int32_t* num_tiles,
                                       uint16_t* act, hipStream_t s);
 
-// The same LDS-tiled kernels on MXFP8 weights (codes dequantized into the LDS tiles); K
-// (H for up, I for down) a multiple of 256, scales 8-byte aligned.
+// The LDS-tiled up GEMM on MXFP8 weights (codes dequantized into the LDS tiles; tile_rows
+// 128); H a multiple of 256, scales 8-byte aligned.
 hipError_t launch_expert_up_tiled_mx(const uint16_t* x, const uint8_t* w13c, const uint8_t* w13s,
                                      const int32_t* sorted_ids, const int32_t* block_expert,
                                      const int2* tiles, const int32_t* num_tiles, int max_tiles,
                                      int tile_rows, int M, int H, int I, int top_k, int block,
                                      uint16_t* act, hipStream_t s);
-hipError_t launch_expert_down_tiled_mx(const uint16_t* act, const uint8_t* w2c, const uint8_t* w2s,
-                                       const int32_t* sorted_ids, const int32_t* block_expert,
-                                       const int2* tiles, const int32_t* num_tiles, int max_tiles,
-                                       int tile_rows, int M, int H, int I, int top_k, int block,
-                                       float* y, hipStream_t s);
 
-// MXFP8 GEMMs for few tokens per expert: the codes are copied whole lines at a time into
-// LDS and dequantized from there into the MFMA operands; work items are the tiles of height
-// kMxDecodeTileRows of `tiles`.  H and I multiples of 128, scales 4-byte aligned.
+// MXFP8 GEMMs with the codes copied whole lines at a time into LDS and dequantized from
+// there into the MFMA operands; work items are the tiles of height tile_rows (32, 64 or
+// 128) of `tiles`; stream_weights: copy the codes nontemporally (each expert's weights are
+// read by about one token tile).  H and I multiples of 128, scales 4-byte aligned.
+// moe_forward_mx uses them below 16 tokens per expert, at tile height kMxDecodeTileRows.
 constexpr int kMxDecodeTileRows = 32;
-hipError_t launch_expert_up_mx_decode(const uint16_t* x, const uint8_t* w13c, const uint8_t* w13s,
-                                      const int32_t* sorted_ids, const int32_t* block_expert,
-                                      const int2* tiles, const int32_t* num_tiles, int max_tiles,
-                                      int H, int I, int top_k, int block, uint16_t* act,
-                                      hipStream_t s);
-hipError_t launch_expert_down_mx_decode(const uint16_t* act, const uint8_t* w2c,
-                                        const uint8_t* w2s, const int32_t* sorted_ids,
-                                        const int32_t* block_expert, const int2* tiles,
-                                        const int32_t* num_tiles, int max_tiles, int H, int I,
-                                        int top_k, int block, float* y, hipStream_t s);
+hipError_t launch_expert_up_mx_lds(const uint16_t* x, const uint8_t* w13c, const uint8_t* w13s,
+                                   const int32_t* sorted_ids, const int32_t* block_expert,
+                                   const int2* tiles, const int32_t* num_tiles, int max_tiles,
+                                   int tile_rows, bool stream_weights, int H, int I, int top_k,
+                                   int block, uint16_t* act, hipStream_t s);
+hipError_t launch_expert_down_mx_lds(const uint16_t* act, const uint8_t* w2c, const uint8_t* w2s,
+                                     const int32_t* sorted_ids, const int32_t* block_expert,
+                                     const int2* tiles, const int32_t* num_tiles, int max_tiles,
+                                     int tile_rows, bool stream_weights, int H, int I, int top_k,
+                                     int block, float* y, hipStream_t s);
 
 // MXFP8 weights (E4M3 codes, one E8M0 scale byte per 32 values along K): quantize bf16
 // [rows, K] (K % 32 == 0) and dequantize back to bf16.

@@ -74,11 +74,13 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 // LDS-tiled kernels, 16 for the weight-streaming kernels, 32 for the MXFP8 kernels of few
 // tokens per expert.  bf16 weights use the tiled kernels at every size (with nontemporal
 // weight copies they beat the streaming kernels even at decode: M=8 layer 1,551 -> 1,405
-// us); the streaming kernels serve I that is not a multiple of 256.  MXFP8 weights below 16
-// tokens per expert run the kernels that copy the codes into LDS and dequantize them into
-// the MFMA operands (M=8 layer 867 -> 796-832 us, M=128 2,528 -> 1,909-2,019 us against the
-// streaming MXFP8 kernels they replaced); from 16, the tiled kernels that dequantize the
-// codes into the LDS tiles.
+// us); the streaming kernels serve I that is not a multiple of 256.  MXFP8 weights run the
+// kernels that copy the codes into LDS and dequantize them into the MFMA operands -- 32-row
+// tiles below 16 tokens per expert (M=8 layer 867 -> 773-790 us, M=128 2,528 -> 1,900 us
+// against the streaming MXFP8 kernels they replaced), 64 / 128 from there (M=512 3,399 ->
+// 2,987 us against the kernels that dequantize into the LDS tiles) -- except the up GEMM
+// from 64 tokens per expert, where the tiles of a hot expert share its codes and the
+// dequantize-into-LDS kernel is 2 % faster (M=2048 up 3,368 against 3,445 us).
 int gemm_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I, bool mx) {
   if (I % moe::tiled_up_columns() != 0) return 16;
   const int64_t per_expert = (int64_t)M * top_k / E;
@@ -313,9 +315,9 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   if (self_route)
     up_err = moe::launch_expert_up_selfroute(x, W.w13, ids, M, H, E, I, top_k, block, sorted, bexp,
                                              npad, tiles, ntiles, act, s);
-  else if (W.mx() && trows == moe::kMxDecodeTileRows)
-    up_err = moe::launch_expert_up_mx_decode(x, W.w13c, W.w13s, sorted, bexp, tiles, ntiles,
-                                             max_tiles, H, I, top_k, block, act, s);
+  else if (W.mx() && stream_w)  // MXFP8, weights read by about one token tile
+    up_err = moe::launch_expert_up_mx_lds(x, W.w13c, W.w13s, sorted, bexp, tiles, ntiles,
+                                          max_tiles, trows, stream_w, H, I, top_k, block, act, s);
   else if (W.mx())
     up_err = moe::launch_expert_up_tiled_mx(x, W.w13c, W.w13s, sorted, bexp, tiles, ntiles,
                                             max_tiles, trows, M, H, I, top_k, block, act, s);
@@ -328,12 +330,9 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   if (up_err != hipSuccess) return MOE_ERR_HIP;
   if (!mark(3)) return MOE_ERR_HIP;
   hipError_t down_err;
-  if (W.mx() && trows == moe::kMxDecodeTileRows)
-    down_err = moe::launch_expert_down_mx_decode(act, W.w2c, W.w2s, sorted, bexp, tiles, ntiles,
-                                                 max_tiles, H, I, top_k, block, y, s);
-  else if (W.mx())
-    down_err = moe::launch_expert_down_tiled_mx(act, W.w2c, W.w2s, sorted, bexp, tiles, ntiles,
-                                                max_tiles, trows, M, H, I, top_k, block, y, s);
+  if (W.mx())
+    down_err = moe::launch_expert_down_mx_lds(act, W.w2c, W.w2s, sorted, bexp, tiles, ntiles,
+                                              max_tiles, trows, stream_w, H, I, top_k, block, y, s);
   else if (trows == 16)
     down_err = moe::launch_expert_down(act, W.w2, sorted, bexp, npad, tiles, ntiles, max_tiles, M,
                                        H, I, top_k, block, y, s);

@@ -143,10 +143,10 @@ class _OracleMxExperts:
         return mxo.mx_dequantize_bf16_bits(c, s)
 
 
-# expected tokens per expert M * top_k / E: below 16 the kernels that copy the codes into
-# LDS (32-row tiles: mx_tiny 1, mx_mid 4.6, mx_one_token 0.1, mx_dec_partial 10,
-# mx_dec_groups 6), 16..31 the 64-row LDS tiles (mx_tiles64 24), from 32 the 128-row tiles
-# (mx_many 150)
+# expected tokens per expert M * top_k / E, with the kernels that copy the codes into LDS:
+# below 16 32-row tiles (mx_tiny 1, mx_mid 4.6, mx_one_token 0.1, mx_dec_partial 10,
+# mx_dec_groups 6), 16..31 64-row tiles (mx_tiles64 24), from 32 128-row tiles; from 64 the
+# up GEMM dequantizes into the LDS tiles of the tiled kernel (mx_many 150)
 SMALL_MX = {
     "mx_tiny": mi.LayerConfig("mx_tiny", M=4, H=256, E=8, top_k=2, I=512, block=16),
     "mx_mid": mi.LayerConfig("mx_mid", M=37, H=1024, E=32, top_k=4, I=256, block=16),

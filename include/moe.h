@@ -97,9 +97,9 @@ size_t moe_workspace_bytes(int32_t M, int32_t H, int32_t E, int32_t I, int32_t t
  */
 int32_t moe_gemm_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I);
 /* The same for moe_forward_mx (MXFP8 weights; I a multiple of 256, else 0): 32 below 16
- * expected tokens per expert, then 64 / 128 as above.  Its GEMMs copy the codes into LDS and
- * dequantize them into the MFMA operands, except the up GEMM from 64 tokens per expert,
- * which dequantizes them into the LDS tiles of the tiled kernel. */
+ * expected tokens per expert, 64 below 64, then 128.  Its GEMMs copy the codes into LDS and
+ * dequantize them into the MFMA operands, except the up GEMM at 128-row tiles, which
+ * dequantizes them into the LDS tiles of the tiled kernel. */
 int32_t moe_gemm_tile_rows_mx(int32_t M, int32_t E, int32_t top_k, int32_t I);
 /* 1 when moe_forward (bf16 weights) builds the plan inside its up-GEMM kernel for these
  * sizes -- the self-routing up kernels of the AlphaMoE page (FlashInfer PR #6511 analysis),
@@ -223,7 +223,8 @@ int moe_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows,
  * multiples of 256 (MOE_ERR_UNSUPPORTED otherwise); codes 16-byte and scales 8-byte
  * aligned (MOE_ERR_INVALID_ARG otherwise).  The GEMMs copy the codes into LDS and
  * dequantize them from there into the MFMA operands; the up GEMM from 64 tokens per expert
- * dequantizes them into the LDS tiles of the tiled kernel instead (moe_gemm_tile_rows_mx).
+ * (128-row tiles) dequantizes them into the LDS tiles of the tiled kernel instead
+ * (moe_gemm_tile_rows_mx).
  */
 int moe_forward_mx(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
                    const uint8_t* w13_codes, const uint8_t* w13_scales,

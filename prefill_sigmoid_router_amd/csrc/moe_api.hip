@@ -77,14 +77,15 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? MOE_OK : MOE_ERR_
 // us); the streaming kernels serve I that is not a multiple of 256.  MXFP8 weights run the
 // kernels that copy the codes into LDS and dequantize them into the MFMA operands -- 32-row
 // tiles below 16 tokens per expert (M=8 layer 867 -> 773-790 us, M=128 2,528 -> 1,900 us
-// against the streaming MXFP8 kernels they replaced), 64 / 128 from there (M=512 3,399 ->
-// 2,987 us against the kernels that dequantize into the LDS tiles) -- except the up GEMM
-// from 64 tokens per expert, where the tiles of a hot expert share its codes and the
-// dequantize-into-LDS kernel is 2 % faster (M=2048 up 3,368 against 3,445 us).
+// against the streaming MXFP8 kernels they replaced), 64-row tiles up to 63 (M=512 3,399 ->
+// 2,790 us against the kernels that dequantize into the LDS tiles; 2,987 with 128-row
+// tiles), 128-row tiles from 64 (M=2048: 64-row tiles 7 % slower) -- and there the up GEMM
+// runs the dequantize-into-LDS kernel, 2 % faster when the tiles of a hot expert share its
+// codes (M=2048 up 3,368 against 3,445 us).
 int gemm_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I, bool mx) {
   if (I % moe::tiled_up_columns() != 0) return 16;
   const int64_t per_expert = (int64_t)M * top_k / E;
-  if (mx && per_expert < 16) return moe::kMxDecodeTileRows;
+  if (mx) return per_expert < 16 ? moe::kMxDecodeTileRows : per_expert < 64 ? 64 : 128;
   if (per_expert < 32) return 64;
   return 128;
 }
@@ -315,7 +316,7 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   if (self_route)
     up_err = moe::launch_expert_up_selfroute(x, W.w13, ids, M, H, E, I, top_k, block, sorted, bexp,
                                              npad, tiles, ntiles, act, s);
-  else if (W.mx() && stream_w)  // MXFP8, weights read by about one token tile
+  else if (W.mx() && trows <= 64)
     up_err = moe::launch_expert_up_mx_lds(x, W.w13c, W.w13s, sorted, bexp, tiles, ntiles,
                                           max_tiles, trows, stream_w, H, I, top_k, block, act, s);
   else if (W.mx())

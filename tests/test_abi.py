@@ -169,7 +169,9 @@ def test_gemm_tile_rows_follows_tokens_per_expert(B):
     assert B.moe_gemm_tile_rows_mx(128, 256, 16, 2048) == 32
     assert B.moe_gemm_tile_rows_mx(255, 256, 16, 2048) == 32
     assert B.moe_gemm_tile_rows_mx(256, 256, 16, 2048) == 64
-    assert B.moe_gemm_tile_rows_mx(512, 256, 16, 2048) == 128
+    assert B.moe_gemm_tile_rows_mx(512, 256, 16, 2048) == 64
+    assert B.moe_gemm_tile_rows_mx(1023, 256, 16, 2048) == 64
+    assert B.moe_gemm_tile_rows_mx(1024, 256, 16, 2048) == 128
     assert B.moe_gemm_tile_rows_mx(2048, 256, 16, 2048) == 128
     assert B.moe_gemm_tile_rows_mx(2048, 256, 16, 384) == 0
 

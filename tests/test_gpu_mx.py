@@ -145,8 +145,9 @@ class _OracleMxExperts:
 
 # expected tokens per expert M * top_k / E, with the kernels that copy the codes into LDS:
 # below 16 32-row tiles (mx_tiny 1, mx_mid 4.6, mx_one_token 0.1, mx_dec_partial 10,
-# mx_dec_groups 6), 16..31 64-row tiles (mx_tiles64 24), from 32 128-row tiles; from 64 the
-# up GEMM dequantizes into the LDS tiles of the tiled kernel (mx_many 150)
+# mx_dec_groups 6), 16..63 64-row tiles (mx_tiles64 24 with nontemporal code copies,
+# mx_tiles64_shared 50 without), from 64 128-row tiles, where the up GEMM dequantizes into
+# the LDS tiles of the tiled kernel (mx_many 150)
 SMALL_MX = {
     "mx_tiny": mi.LayerConfig("mx_tiny", M=4, H=256, E=8, top_k=2, I=512, block=16),
     "mx_mid": mi.LayerConfig("mx_mid", M=37, H=1024, E=32, top_k=4, I=256, block=16),
@@ -157,6 +158,8 @@ SMALL_MX = {
                               zipf_s=1.0),
     # I=256: one K group, so one down K half is empty
     "mx_one_token": mi.LayerConfig("mx_one_token", M=1, H=512, E=64, top_k=8, I=256, block=16),
+    "mx_tiles64_shared": mi.LayerConfig("mx_tiles64_shared", M=200, H=512, E=8, top_k=2,
+                                        I=256, block=64, zipf_s=1.0),
     # 32-row tiles: H=768 is 6 K chunks of 128 with 24 scale bytes per row (one partial
     # group of 8 chunks), and Zipf routing gives the hot expert more than 16 rows (both
     # token row tiles of its tile live)

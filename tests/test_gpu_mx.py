@@ -209,7 +209,7 @@ def test_forward_mx_rejects_unsupported_widths(B, dev):
     assert ei.value.status == -2
 
 
-MX_FULL = ["decode_m8", "batch_m128", "prefill_m2048"]
+MX_FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048"]
 
 
 @pytest.fixture(scope="module")
@@ -223,7 +223,7 @@ def mx_full(B, dev):
 @pytest.mark.parametrize("name", MX_FULL)
 def test_forward_mx_full_size(B, dev, mx_full, name):
     """The real-shape workloads with MXFP8 weights -- 32-row tiles of LDS codes at M=8 and
-    M=128, LDS tiles of 128 rows at M=2048: routing and plan bit-exact for
+    M=128, 64-row tiles at M=512 (Zipf), 128-row tiles at M=2048: routing and plan bit-exact for
     every token; codes of the experts a sampled token uses bit-exact; that token's output
     against the oracle on the oracle's own dequantized weights."""
     cfg = mi.CONFIGS[name]

@@ -82,7 +82,7 @@ size_t moe_route_workspace_bytes(int32_t M, int32_t E);
 
 /*
  * Workspace bytes moe_forward needs for these sizes: routing ids/weights, the plan,
- * the router keys, the bf16 SwiGLU activations [capacity, I] and the fp32 per-pick
+ * the router keys, the bf16 SwiGLU activations [capacity, I] and the bf16 per-pick
  * down-projection rows [M*top_k, H].  0 for invalid sizes.
  */
 size_t moe_workspace_bytes(int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k,

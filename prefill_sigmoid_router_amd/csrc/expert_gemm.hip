@@ -23,6 +23,8 @@
 //
 // D fragment of lane l: weight rows 4*(l/16)+q (q = 0..3) for token column l%16, so a
 // lane writes 4 consecutive outputs of one token row (8 bytes of act, 16 bytes of y).
+#include <type_traits>
+
 #include "device_common.h"
 #include "launchers.h"
 
@@ -148,13 +150,13 @@ __global__ __launch_bounds__(256) void expert_up_stream_kernel(
   *reinterpret_cast<uint2*>(act + (size_t)(start + li) * I + n0 + 4 * lg) = v;
 }
 
-template <int U>
+template <int U, typename Y>
 __global__ __launch_bounds__(256) void expert_down_stream_kernel(
     const uint16_t* __restrict__ act, const uint16_t* __restrict__ w2,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
     const int32_t* __restrict__ num_padded, const int2* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, int H, int I, int block, int sentinel,
-    float* __restrict__ y) {
+    Y* __restrict__ y) {
   __shared__ f32x4 red[2][kWave];
   int start, nlive;
   if (!tile_of(tiles, num_tiles, sorted_ids, num_padded, sentinel, start, nlive)) return;
@@ -177,8 +179,15 @@ __global__ __launch_bounds__(256) void expert_down_stream_kernel(
   if (wk == 1 || !n_in || !live) return;
   acc[0] += red[wn][lane];
   const int dst = sorted_ids[start + li];
-  *reinterpret_cast<float4*>(y + (size_t)dst * H + n0 + 4 * lg) =
-      make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
+  if constexpr (std::is_same<Y, float>::value) {
+    *reinterpret_cast<float4*>(y + (size_t)dst * H + n0 + 4 * lg) =
+        make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
+  } else {                                           // bf16 y, nearest even
+    uint2 v;
+    v.x = pack_bf16x2(acc[0][0], acc[0][1]);
+    v.y = pack_bf16x2(acc[0][2], acc[0][3]);
+    *reinterpret_cast<uint2*>(y + (size_t)dst * H + n0 + 4 * lg) = v;
+  }
 }
 
 hipError_t launch_expert_up(const uint16_t* x, const uint16_t* w13, const int32_t* sorted_ids,
@@ -192,15 +201,31 @@ hipError_t launch_expert_up(const uint16_t* x, const uint16_t* w13, const int32_
   return hipGetLastError();
 }
 
+template <typename Y>
+static hipError_t launch_down_rows(const uint16_t* act, const uint16_t* w2, const int32_t* sorted_ids,
+                              const int32_t* block_expert, const int32_t* num_padded,
+                              const int2* tiles, const int32_t* num_tiles, int max_tiles, int M,
+                              int H, int I, int top_k, int block, Y* y, hipStream_t s) {
+  dim3 grid((H + 31) / 32, max_tiles);
+  hipLaunchKernelGGL((expert_down_stream_kernel<kDownStreamU, Y>), grid, dim3(256), 0, s, act, w2,
+                     sorted_ids, block_expert, num_padded, tiles, num_tiles, H, I, block,
+                     M * top_k, y);
+  return hipGetLastError();
+}
+
 hipError_t launch_expert_down(const uint16_t* act, const uint16_t* w2, const int32_t* sorted_ids,
                               const int32_t* block_expert, const int32_t* num_padded,
                               const int2* tiles, const int32_t* num_tiles, int max_tiles, int M,
                               int H, int I, int top_k, int block, float* y, hipStream_t s) {
-  dim3 grid((H + 31) / 32, max_tiles);
-  hipLaunchKernelGGL((expert_down_stream_kernel<kDownStreamU>), grid, dim3(256), 0, s, act, w2,
-                     sorted_ids, block_expert, num_padded, tiles, num_tiles, H, I, block,
-                     M * top_k, y);
-  return hipGetLastError();
+  return launch_down_rows(act, w2, sorted_ids, block_expert, num_padded, tiles, num_tiles,
+                          max_tiles, M, H, I, top_k, block, y, s);
+}
+hipError_t launch_expert_down(const uint16_t* act, const uint16_t* w2, const int32_t* sorted_ids,
+                              const int32_t* block_expert, const int32_t* num_padded,
+                              const int2* tiles, const int32_t* num_tiles, int max_tiles, int M,
+                              int H, int I, int top_k, int block, uint16_t* y, hipStream_t s) {
+  return launch_down_rows(act, w2, sorted_ids, block_expert, num_padded, tiles, num_tiles,
+                          max_tiles, M, H, I, top_k, block, y, s);
 }
 
 }  // namespace moe

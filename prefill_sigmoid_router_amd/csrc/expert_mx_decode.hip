@@ -84,7 +84,7 @@ __device__ __forceinline__ void mx_decode_item(
     const uint16_t* __restrict__ tok_src, const uint8_t* __restrict__ wc,
     const uint8_t* __restrict__ ws, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int2* __restrict__ tiles, int K, int ncols,
-    int I, int top_k, int block, uint16_t* __restrict__ act, float* __restrict__ y) {
+    int I, int top_k, int block, uint16_t* __restrict__ act, uint16_t* __restrict__ y) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 15, lg = lane >> 4;
   const int nch = K / kKC;
@@ -252,9 +252,10 @@ __device__ __forceinline__ void mx_decode_item(
 #pragma unroll
       for (int j = 0; j < kTW; ++j) {
         const int n = ntile * kRows + 16 * (kTW * wave + j) + 4 * lg;
-        if (n < ncols)
-          __builtin_nontemporal_store(acc[j][s],
-                                      reinterpret_cast<f32x4*>(y + (size_t)dst * ncols + n));
+        if (n < ncols)                                   // y in bf16 (nearest even)
+          *reinterpret_cast<uint64_t*>(y + (size_t)dst * ncols + n) =
+              pack_bf16x2(acc[j][s][0], acc[j][s][1]) |
+                  ((uint64_t)pack_bf16x2(acc[j][s][2], acc[j][s][3]) << 32);
       }
     }
   }
@@ -266,7 +267,7 @@ __global__ __launch_bounds__(64 * kWaves) void expert_mx_decode_kernel(
     const uint8_t* __restrict__ ws, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int2* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, int n_ntiles, int K, int ncols, int I, int top_k,
-    int block, uint16_t* __restrict__ act, float* __restrict__ y) {
+    int block, uint16_t* __restrict__ act, uint16_t* __restrict__ y) {
   using C = MxdCfg<BM>;
   __shared__ __align__(16) unsigned char lds[C::LDS];
   TiledWalk walk(*num_tiles, n_ntiles);
@@ -282,7 +283,7 @@ template <int BM, int WPOL, bool UP>
 hipError_t launch_mx_lds(const uint16_t* src, const uint8_t* wc, const uint8_t* ws,
                          const int32_t* sorted_ids, const int32_t* block_expert, const int2* tiles,
                          const int32_t* num_tiles, int max_tiles, int K, int ncols, int I,
-                         int top_k, int block, uint16_t* act, float* y, hipStream_t s) {
+                         int top_k, int block, uint16_t* act, uint16_t* y, hipStream_t s) {
   if (K % kKC != 0 || (UP && I % 128 != 0) || (uintptr_t)ws % 4 != 0) return hipErrorInvalidValue;
   const int per_ntile = UP ? 128 : kRows;
   const int n_ntiles = (ncols + per_ntile - 1) / per_ntile;
@@ -299,7 +300,7 @@ hipError_t launch_mx_lds_rows(const uint16_t* src, const uint8_t* wc, const uint
                               const int32_t* sorted_ids, const int32_t* block_expert,
                               const int2* tiles, const int32_t* num_tiles, int max_tiles,
                               int tile_rows, bool stream_weights, int K, int ncols, int I,
-                              int top_k, int block, uint16_t* act, float* y, hipStream_t s) {
+                              int top_k, int block, uint16_t* act, uint16_t* y, hipStream_t s) {
 #define MOE_MXL(BM, POL)                                                                      \
   return launch_mx_lds<BM, POL, UP>(src, wc, ws, sorted_ids, block_expert, tiles, num_tiles, \
                                     max_tiles, K, ncols, I, top_k, block, act, y, s)
@@ -335,7 +336,7 @@ hipError_t launch_expert_down_mx_lds(const uint16_t* act, const uint8_t* w2c, co
                                      const int32_t* sorted_ids, const int32_t* block_expert,
                                      const int2* tiles, const int32_t* num_tiles, int max_tiles,
                                      int tile_rows, bool stream_weights, int H, int I, int top_k,
-                                     int block, float* y, hipStream_t s) {
+                                     int block, uint16_t* y, hipStream_t s) {
   return launch_mx_lds_rows<false>(act, w2c, w2s, sorted_ids, block_expert, tiles, num_tiles,
                                    max_tiles, tile_rows, stream_weights, I, H, I, top_k, block,
                                    nullptr, y, s);

@@ -78,7 +78,7 @@ __device__ __forceinline__ void tiled_gemm(
     unsigned char* __restrict__ lds, const uint16_t* __restrict__ tok_src,
     const uint16_t* __restrict__ w, const int32_t* row_ids, int start, int nlive, int e,
     int ntile, int K, int ncols, int I, int top_k, uint16_t* __restrict__ act,
-    float* __restrict__ y) {
+    uint16_t* __restrict__ y) {
   using C = TiledCfg<BM, WN, WM>;
   const int mt_active = (nlive + 15) >> 4;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -224,11 +224,12 @@ __device__ __forceinline__ void tiled_gemm(
       for (int j = 0; j < 4; ++j) {
         const int n = col0 + wn * 64 + j * 16 + 4 * lg;
         if (n < ncols) {
-          f32x4* dp = reinterpret_cast<f32x4*>(y + (size_t)dst * ncols + n);
-          // with streamed weights y leaves nontemporally too: the next item's first wait
-          // also covers these stores, which then drain sooner (M=128 down 1,255 -> 1,180 us)
-          if constexpr (WPOL != 0) __builtin_nontemporal_store(acc[j][s], dp);
-          else *dp = acc[j][s];
+          // y in bf16 (round to nearest even), plain stores: nontemporal stores of these
+          // 8-byte pieces drain slower (decode finalize 13 -> 15 us, MXFP8 M=2048 down
+          // 1,803 -> 1,879 us); with fp32 y nontemporal stores had been the faster ones
+          *reinterpret_cast<uint64_t*>(y + (size_t)dst * ncols + n) =
+              pack_bf16x2(acc[j][s][0], acc[j][s][1]) |
+              ((uint64_t)pack_bf16x2(acc[j][s][2], acc[j][s][3]) << 32);
         }
       }
     }
@@ -240,7 +241,7 @@ __global__ __launch_bounds__(64 * WN * WM) void expert_tiled_kernel(
     const uint16_t* __restrict__ tok_src, const uint16_t* __restrict__ w,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
     const int2* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int n_ntiles, int K,
-    int ncols, int I, int top_k, int block, uint16_t* __restrict__ act, float* __restrict__ y) {
+    int ncols, int I, int top_k, int block, uint16_t* __restrict__ act, uint16_t* __restrict__ y) {
   using C = TiledCfg<BM, WN, WM>;
   static_assert(S >= 2 && (S - 2) * C::FPW <= 63, "the copies in flight must fit the vmcnt counter");
   static_assert(S * C::FRAGS * 1024 <= 160 * 1024, "the ring must fit the LDS");
@@ -408,7 +409,7 @@ __global__ __launch_bounds__(512) void expert_tiled_reg_kernel(
     const uint16_t* __restrict__ tok_src, const uint16_t* __restrict__ w,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
     const int2* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int n_ntiles, int K,
-    int ncols, int I, int top_k, int block, uint16_t* __restrict__ act, float* __restrict__ y) {
+    int ncols, int I, int top_k, int block, uint16_t* __restrict__ act, uint16_t* __restrict__ y) {
   constexpr int NW = 8;                          // waves
   constexpr int WT = 32;                         // weight row tiles (512 rows)
   constexpr int MT = BM / 16;                    // token row tiles
@@ -562,9 +563,12 @@ __global__ __launch_bounds__(512) void expert_tiled_reg_kernel(
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int n = col0 + 64 * wave + 16 * j + 4 * lg;
-          if (n < ncols)
-            *reinterpret_cast<float4*>(y + (size_t)dst * ncols + n) =
-                make_float4(acc[j][s][0], acc[j][s][1], acc[j][s][2], acc[j][s][3]);
+          if (n < ncols) {                               // y in bf16 (nearest even)
+            uint2 v;
+            v.x = pack_bf16x2(acc[j][s][0], acc[j][s][1]);
+            v.y = pack_bf16x2(acc[j][s][2], acc[j][s][3]);
+            *reinterpret_cast<uint2*>(y + (size_t)dst * ncols + n) = v;
+          }
         }
       }
     }
@@ -787,7 +791,7 @@ template <int BM, int WN, int WM, int S, bool UP, int WPOL>
 static hipError_t launch_tiled(const uint16_t* src, const uint16_t* w, const int32_t* sorted_ids,
                                const int32_t* block_expert, const int2* tiles,
                                const int32_t* num_tiles, int max_tiles, int K, int ncols, int I,
-                               int top_k, int block, uint16_t* act, float* y, hipStream_t s) {
+                               int top_k, int block, uint16_t* act, uint16_t* y, hipStream_t s) {
   const int per_ntile = UP ? 32 * WN : 64 * WN;
   if (UP && I % per_ntile != 0) return hipErrorInvalidValue;
   const int n_ntiles = (ncols + per_ntile - 1) / per_ntile;
@@ -807,7 +811,7 @@ static hipError_t launch_tiled_reg(const uint16_t* src, const uint16_t* w,
                                    const int32_t* sorted_ids, const int32_t* block_expert,
                                    const int2* tiles, const int32_t* num_tiles, int max_tiles,
                                    int K, int ncols, int I, int top_k, int block, uint16_t* act,
-                                   float* y, hipStream_t s) {
+                                   uint16_t* y, hipStream_t s) {
   const int per_ntile = UP ? 256 : 512;
   if (K % kTileKC != 0 || (UP && I % per_ntile != 0)) return hipErrorInvalidValue;
   const int n_ntiles = (ncols + per_ntile - 1) / per_ntile;
@@ -885,7 +889,7 @@ hipError_t launch_expert_down_tiled(const uint16_t* act, const uint16_t* w2,
                                     const int32_t* sorted_ids, const int32_t* block_expert,
                                     const int2* tiles, const int32_t* num_tiles, int max_tiles,
                                     int tile_rows, bool stream_weights, int M, int H, int I,
-                                    int top_k, int block, float* y, hipStream_t s) {
+                                    int top_k, int block, uint16_t* y, hipStream_t s) {
   (void)M;
 #define MOE_DOWN(BM, POL)                                                                       \
   return launch_tiled<BM, kTileWN, 1, kTileStages, false, POL>(act, w2, sorted_ids, block_expert, \

@@ -21,9 +21,19 @@ namespace moe {
 constexpr int kFinThreads = 1024;
 constexpr int kFinBatch = 8;
 
-template <int V>
+// Values 4 c .. 4 c + 3 of a y row as fp32: fp32 rows (moe_finalize) or bf16 rows
+// (moe_forward, whose down GEMMs round y to bf16).
+__device__ __forceinline__ float4 y4(const float* row, int c) {
+  return reinterpret_cast<const float4*>(row)[c];
+}
+__device__ __forceinline__ float4 y4(const uint16_t* row, int c) {
+  const uint2 v = reinterpret_cast<const uint2*>(row)[c];
+  return make_float4(bf16lo(v.x), bf16hi(v.x), bf16lo(v.y), bf16hi(v.y));
+}
+
+template <int V, typename Y>
 __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
-    const float* __restrict__ y, const float* __restrict__ topk_w,
+    const Y* __restrict__ y, const float* __restrict__ topk_w,
     const uint16_t* __restrict__ residual, const uint16_t* __restrict__ norm_w, float eps, int H,
     int top_k, uint16_t* __restrict__ out, uint16_t* __restrict__ residual_out) {
   __shared__ float part[kFinThreads / kWave];
@@ -46,7 +56,7 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     gv[v] = c < ngroups ? gw[c] : uint2{0u, 0u};
   }
 
-  const float* yt = y + (size_t)t * top_k * H;
+  const Y* yt = y + (size_t)t * top_k * H;
   const float* wt = topk_w + (size_t)t * top_k;
   for (int j0 = 0; j0 < top_k; j0 += kFinBatch) {
     float4 a[kFinBatch][V];
@@ -55,9 +65,8 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         const int c = tid + kFinThreads * v;
-        a[u][v] = (j0 + u < top_k && c < ngroups)
-                      ? reinterpret_cast<const float4*>(yt + (size_t)(j0 + u) * H)[c]
-                      : make_float4(0.f, 0.f, 0.f, 0.f);
+        a[u][v] = (j0 + u < top_k && c < ngroups) ? y4(yt + (size_t)(j0 + u) * H, c)
+                                                  : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
     for (int u = 0; u < kFinBatch; ++u) {
@@ -119,22 +128,34 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
   }
 }
 
-template <int V>
-static hipError_t launch_fin(const float* y, const float* w, const uint16_t* res, const uint16_t* g,
+template <int V, typename Y>
+static hipError_t launch_fin(const Y* y, const float* w, const uint16_t* res, const uint16_t* g,
                              float eps, int M, int H, int k, uint16_t* out, uint16_t* rout,
                              hipStream_t s) {
-  hipLaunchKernelGGL((finalize_kernel<V>), dim3(M), dim3(kFinThreads), 0, s, y, w, res, g, eps, H, k,
-                     out, rout);
+  hipLaunchKernelGGL((finalize_kernel<V, Y>), dim3(M), dim3(kFinThreads), 0, s, y, w, res, g, eps,
+                     H, k, out, rout);
   return hipGetLastError();
+}
+
+template <typename Y>
+static hipError_t launch_fin_rows(const Y* y, const float* topk_w, const uint16_t* residual,
+                                  const uint16_t* norm_w, float eps, int M, int H, int top_k,
+                                  uint16_t* out, uint16_t* residual_out, hipStream_t s) {
+  const int per_thread = (H / 4 + kFinThreads - 1) / kFinThreads;
+  if (per_thread <= 1) return launch_fin<1>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
+  if (per_thread <= 2) return launch_fin<2>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
+  return launch_fin<4>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
 }
 
 hipError_t launch_finalize(const float* y, const float* topk_w, const uint16_t* residual,
                            const uint16_t* norm_w, float eps, int M, int H, int top_k,
                            uint16_t* out, uint16_t* residual_out, hipStream_t s) {
-  const int per_thread = (H / 4 + kFinThreads - 1) / kFinThreads;
-  if (per_thread <= 1) return launch_fin<1>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
-  if (per_thread <= 2) return launch_fin<2>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
-  return launch_fin<4>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
+  return launch_fin_rows(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
+}
+hipError_t launch_finalize(const uint16_t* y, const float* topk_w, const uint16_t* residual,
+                           const uint16_t* norm_w, float eps, int M, int H, int top_k,
+                           uint16_t* out, uint16_t* residual_out, hipStream_t s) {
+  return launch_fin_rows(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
 }
 
 
@@ -146,15 +167,16 @@ hipError_t launch_finalize(const float* y, const float* topk_w, const uint16_t* 
 constexpr int kFinSliceThreads = 256;
 constexpr int kFinSlice = 4 * kFinSliceThreads;     // hidden values per slice
 
+template <typename Y>
 __global__ __launch_bounds__(kFinSliceThreads) void finalize_slice_kernel(
-    const float* __restrict__ y, const float* __restrict__ topk_w,
+    const Y* __restrict__ y, const float* __restrict__ topk_w,
     const uint16_t* __restrict__ residual, int H, int top_k, float* __restrict__ z,
     float* __restrict__ slice_ss) {
   __shared__ float part[kFinSliceThreads / kWave];
   const int sl = blockIdx.x, t = blockIdx.y, tid = threadIdx.x;
   const int c = sl * kFinSliceThreads + tid;          // group of 4 hidden values
   const bool in = c < (H >> 2);
-  const float* yt = y + (size_t)t * top_k * H;
+  const Y* yt = y + (size_t)t * top_k * H;
   const float* wt = topk_w + (size_t)t * top_k;
   float4 m = make_float4(0.f, 0.f, 0.f, 0.f);
   uint2 r = uint2{0u, 0u};
@@ -163,7 +185,7 @@ __global__ __launch_bounds__(kFinSliceThreads) void finalize_slice_kernel(
     float4 a[16];
 #pragma unroll
     for (int u = 0; u < 16; ++u)
-      a[u] = (in && j0 + u < top_k) ? reinterpret_cast<const float4*>(yt + (size_t)(j0 + u) * H)[c]
+      a[u] = (in && j0 + u < top_k) ? y4(yt + (size_t)(j0 + u) * H, c)
                                     : make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
@@ -228,21 +250,37 @@ size_t finalize_slices_scratch_bytes(int M, int H) {
   return (size_t)M * H * sizeof(float) + (size_t)M * slices * sizeof(float);
 }
 
-hipError_t launch_finalize_slices(const float* y, const float* topk_w, const uint16_t* residual,
-                                  const uint16_t* norm_w, float eps, int M, int H, int top_k,
-                                  uint16_t* out, uint16_t* residual_out, float* scratch,
-                                  hipStream_t s) {
+template <typename Y>
+static hipError_t launch_fin_slices(const Y* y, const float* topk_w, const uint16_t* residual,
+                                    const uint16_t* norm_w, float eps, int M, int H, int top_k,
+                                    uint16_t* out, uint16_t* residual_out, float* scratch,
+                                    hipStream_t s) {
   if (M == 0) return hipSuccess;
   const int slices = (H / 4 + kFinSliceThreads - 1) / kFinSliceThreads;
   float* z = scratch;
   float* slice_ss = scratch + (size_t)M * H;
-  hipLaunchKernelGGL(finalize_slice_kernel, dim3(slices, M), dim3(kFinSliceThreads), 0, s, y,
+  hipLaunchKernelGGL((finalize_slice_kernel<Y>), dim3(slices, M), dim3(kFinSliceThreads), 0, s, y,
                      topk_w, residual, H, top_k, z, slice_ss);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(finalize_scale_kernel, dim3(slices, M), dim3(kFinSliceThreads), 0, s, z,
                      slice_ss, norm_w, eps, H, out, residual_out);
   return hipGetLastError();
+}
+
+hipError_t launch_finalize_slices(const float* y, const float* topk_w, const uint16_t* residual,
+                                  const uint16_t* norm_w, float eps, int M, int H, int top_k,
+                                  uint16_t* out, uint16_t* residual_out, float* scratch,
+                                  hipStream_t s) {
+  return launch_fin_slices(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out,
+                           scratch, s);
+}
+hipError_t launch_finalize_slices(const uint16_t* y, const float* topk_w, const uint16_t* residual,
+                                  const uint16_t* norm_w, float eps, int M, int H, int top_k,
+                                  uint16_t* out, uint16_t* residual_out, float* scratch,
+                                  hipStream_t s) {
+  return launch_fin_slices(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out,
+                           scratch, s);
 }
 
 }  // namespace moe

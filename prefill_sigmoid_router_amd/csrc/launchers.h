@@ -33,11 +33,16 @@ hipError_t launch_expert_up(const uint16_t* x, const uint16_t* w13, const int32_
                             const int2* tiles, const int32_t* num_tiles, int max_tiles, int M,
                             int H, int I, int top_k, int block, uint16_t* act, hipStream_t s);
 
-// Grouped down-GEMM over the plan: y [M*top_k, H] fp32.  Work items as for the up GEMM.
+// Grouped down-GEMM over the plan: y [M*top_k, H] in fp32 (moe_expert_down) or bf16
+// (moe_forward, like every down GEMM of its LDS-tiled paths).  Work items as for the up GEMM.
 hipError_t launch_expert_down(const uint16_t* act, const uint16_t* w2, const int32_t* sorted_ids,
                               const int32_t* block_expert, const int32_t* num_padded,
                               const int2* tiles, const int32_t* num_tiles, int max_tiles, int M,
                               int H, int I, int top_k, int block, float* y, hipStream_t s);
+hipError_t launch_expert_down(const uint16_t* act, const uint16_t* w2, const int32_t* sorted_ids,
+                              const int32_t* block_expert, const int32_t* num_padded,
+                              const int2* tiles, const int32_t* num_tiles, int max_tiles, int M,
+                              int H, int I, int top_k, int block, uint16_t* y, hipStream_t s);
 
 // LDS-tiled variants for plans whose experts carry many tokens: work items are the tiles
 // of height tile_rows (64 or 128) of `tiles`.  The up variant needs I to be a multiple of
@@ -54,7 +59,7 @@ hipError_t launch_expert_down_tiled(const uint16_t* act, const uint16_t* w2,
                                     const int32_t* sorted_ids, const int32_t* block_expert,
                                     const int2* tiles, const int32_t* num_tiles, int max_tiles,
                                     int tile_rows, bool stream_weights, int M, int H, int I,
-                                    int top_k, int block, float* y, hipStream_t s);
+                                    int top_k, int block, uint16_t* y, hipStream_t s);
 
 // Self-routing variant of the tiled up GEMM for few ids (the align step fused into it):
 // from the flat ids [M * top_k] it writes the same plan and tile list (tile height 64) as
@@ -92,7 +97,7 @@ hipError_t launch_expert_down_mx_lds(const uint16_t* act, const uint8_t* w2c, co
                                      const int32_t* sorted_ids, const int32_t* block_expert,
                                      const int2* tiles, const int32_t* num_tiles, int max_tiles,
                                      int tile_rows, bool stream_weights, int H, int I, int top_k,
-                                     int block, float* y, hipStream_t s);
+                                     int block, uint16_t* y, hipStream_t s);
 
 // MXFP8 weights (E4M3 codes, one E8M0 scale byte per 32 values along K): quantize bf16
 // [rows, K] (K % 32 == 0) and dequantize back to bf16.
@@ -101,8 +106,11 @@ hipError_t launch_mx_quantize(const uint16_t* w, int64_t rows, int K, uint8_t* c
 hipError_t launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int K,
                                 uint16_t* w, hipStream_t s);
 
-// Weighted top-k combine + residual add + RMSNorm.
+// Weighted top-k combine + residual add + RMSNorm over fp32 or bf16 rows of y.
 hipError_t launch_finalize(const float* y, const float* topk_w, const uint16_t* residual,
+                           const uint16_t* norm_w, float eps, int M, int H, int top_k,
+                           uint16_t* out, uint16_t* residual_out, hipStream_t s);
+hipError_t launch_finalize(const uint16_t* y, const float* topk_w, const uint16_t* residual,
                            const uint16_t* norm_w, float eps, int M, int H, int top_k,
                            uint16_t* out, uint16_t* residual_out, hipStream_t s);
 // The same step for fewer tokens than CUs: rows split into slices over (slice, token)
@@ -110,6 +118,10 @@ hipError_t launch_finalize(const float* y, const float* topk_w, const uint16_t* 
 constexpr int kFinSlicesMaxTokens = 256;
 size_t finalize_slices_scratch_bytes(int M, int H);
 hipError_t launch_finalize_slices(const float* y, const float* topk_w, const uint16_t* residual,
+                                  const uint16_t* norm_w, float eps, int M, int H, int top_k,
+                                  uint16_t* out, uint16_t* residual_out, float* scratch,
+                                  hipStream_t s);
+hipError_t launch_finalize_slices(const uint16_t* y, const float* topk_w, const uint16_t* residual,
                                   const uint16_t* norm_w, float eps, int M, int H, int top_k,
                                   uint16_t* out, uint16_t* residual_out, float* scratch,
                                   hipStream_t s);

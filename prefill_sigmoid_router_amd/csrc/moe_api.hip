@@ -57,7 +57,7 @@ Layout layout_of(int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k, int3
   L.tiles = off;  off += round_up((size_t)L.max_tiles * sizeof(int2), kAlign);
   L.ntiles = off; off += kAlign;
   L.act = off;    off += round_up(cap * (size_t)I * sizeof(uint16_t), kAlign);
-  L.y = off;      off += round_up(n * (size_t)H * sizeof(float), kAlign);
+  L.y = off;      off += round_up(n * (size_t)H * sizeof(uint16_t), kAlign);  // bf16 y
   L.fin = off;    // z and per-slice sums of the sliced finalize (few tokens only)
   if (M < moe::kFinSlicesMaxTokens) off += round_up(moe::finalize_slices_scratch_bytes(M, H), kAlign);
   L.total = off;
@@ -289,7 +289,7 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   int2* tiles = reinterpret_cast<int2*>(ws + L.tiles);
   int32_t* ntiles = reinterpret_cast<int32_t*>(ws + L.ntiles);
   uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
-  float* y = reinterpret_cast<float*>(ws + L.y);
+  uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.y);
   hipStream_t s = (hipStream_t)stream;
 
   auto mark = [&](int i) -> bool {

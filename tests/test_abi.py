@@ -73,7 +73,7 @@ def test_workspace_bytes_cover_the_buffers(B):
     cap = B.moe_align_capacity(M, k, E, blk)
     tiles16 = (M * k + 15) // 16 + min(E, M * k)      # 16-row tiles of real entries, at most
     need = (M * E * 32 + 2 * M * k * 4 + cap * 4 + cap // blk * 4 + 4 + tiles16 * 8 + 4
-            + cap * I * 2 + M * k * H * 4)
+            + cap * I * 2 + M * k * H * 2)
     got = B.moe_workspace_bytes(M, H, E, I, k, blk)
     assert need <= got <= need + 10 * 256
     assert B.moe_workspace_bytes(M, H, E, I, k, 48) == 0          # no kernel for block 48

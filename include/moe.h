@@ -36,8 +36,9 @@
  *   - Arguments are validated on the host before anything is launched.  Errors are
  *     returned as status codes (never abort); on error nothing has been launched,
  *     except MOE_ERR_HIP, which reports a failed launch.
- *   - Sizes: 1 <= top_k <= E <= 1024, H % 16 == 0 and 16 <= H <= 16384, I % 64 == 0,
- *     M >= 0 (M == 0 is a successful no-op), M * top_k < 2^31.
+ *   - Sizes: 1 <= top_k <= E <= 1024, H % 8 == 0 and 8 <= H <= 16384, I % 16 == 0 and
+ *     I >= 16, M >= 0 (M == 0 is a successful no-op), M * top_k < 2^31.  (moe_forward_mx
+ *     needs H and I to be multiples of 256.)
  */
 #ifndef MOE_MI355X_H
 #define MOE_MI355X_H
@@ -63,7 +64,7 @@ enum {
 /* Human-readable text of a status code.  Never NULL; static storage. */
 const char* moe_strerror(int status);
 
-/* ABI version of this header (major * 100 + minor): 103. */
+/* ABI version of this header (major * 100 + minor): 105. */
 int moe_abi_version(void);
 
 /*

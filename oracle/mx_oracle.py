@@ -110,3 +110,106 @@ def mx_dequantize_bf16_bits(codes, scales, block: int = MX_BLOCK) -> np.ndarray:
     bits = f32.view(np.uint32)
     assert np.all((bits & 0xFFFF) == 0), "dequantized value not exact in bf16"
     return (bits >> 16).astype(np.uint16)
+
+
+# ----------------------------------------------------------------------------------------
+# The same conversion as tables over every bf16 bit pattern (for whole expert stacks)
+# ----------------------------------------------------------------------------------------
+# The scale of a block depends only on its largest magnitude, and a value's code only on
+# its own bf16 bit pattern and that scale.  So the conversion above can be tabulated once:
+# for every scale byte b (s = b - 127) and every bf16 pattern p, the code e4m3_encode(p / 2^s)
+# and the dequantized bf16 pattern.  The tables are filled by the functions above and
+# nothing else; mx_quantize_lut equals mx_quantize bit for bit (pinned by tests), it is
+# only fast enough to convert all 256 experts of the real-shape layer.
+_LUT = {}
+
+
+def _luts():
+    if not _LUT:
+        patterns = np.arange(1 << 16, dtype=np.uint32)
+        enc = np.empty((255, 1 << 16), dtype=np.uint8)
+        dq = np.empty((255, 256), dtype=np.uint16)
+        exact = np.empty((255, 256), dtype=bool)    # code * 2^s exact in bf16 (and finite)
+        codes = np.arange(256, dtype=np.uint8)
+        with np.errstate(all="ignore"):
+            vals = (patterns << np.uint32(16)).view(np.float32).astype(np.float64)
+            finite = np.isfinite(vals)
+            vals = np.where(finite, vals, 0.0)
+            for b in range(255):
+                s = float(b) - 127.0
+                enc[b] = np.where(finite, e4m3_encode(vals / np.exp2(s)), 0x7F)
+                v = e4m3_decode(codes) * np.exp2(s)
+                f32 = np.where(np.isfinite(v), v, 0.0).astype(np.float32)
+                u = f32.view(np.uint32)
+                exact[b] = np.isfinite(v) & (f32.astype(np.float64) == v) & ((u & 0xFFFF) == 0)
+                dq[b] = (u >> 16).astype(np.uint16)
+        _LUT["enc"], _LUT["dq"], _LUT["exact"] = enc, dq, exact
+    return _LUT["enc"], _LUT["dq"]
+
+
+def _block_scale_bytes(blocks_bits) -> np.ndarray:
+    """E8M0 byte of each 32-value block of bf16 patterns [..., 32]: s = floor(log2 amax) - 8,
+    clamped to [-127, 127], byte s + 127 (blocks of zeros -> 0).  For a finite bf16 the
+    magnitude bits order like the magnitudes, and floor(log2) of a normal value is its
+    exponent field - 127 (subnormal and zero maxima clamp to s = -127)."""
+    amax = (blocks_bits & np.uint16(0x7FFF)).max(axis=-1)
+    e = (amax >> 7).astype(np.int64)
+    s = np.where(e > 0, e - 127 - 8, -127)
+    return (np.clip(s, -127, 127) + 127).astype(np.uint8)
+
+
+def mx_quantize_lut(w_bits, block: int = MX_BLOCK, rows_per_pass: int = 1024):
+    """mx_quantize through the tables: (codes [..., K], scale bytes [..., K / block])."""
+    enc, _ = _luts()
+    w = np.asarray(w_bits, dtype=np.uint16)
+    K = w.shape[-1]
+    assert K % block == 0, "K must be a multiple of the block"
+    flat = w.reshape(-1, K)
+    codes = np.empty(flat.shape, dtype=np.uint8)
+    scales = np.empty((flat.shape[0], K // block), dtype=np.uint8)
+    enc_flat = enc.reshape(-1)
+    for r0 in range(0, flat.shape[0], rows_per_pass):
+        blk = flat[r0:r0 + rows_per_pass].reshape(-1, K // block, block)
+        sb = _block_scale_bytes(blk)
+        idx = (sb[..., None].astype(np.int64) << 16) | blk.astype(np.int64)
+        codes[r0:r0 + rows_per_pass] = enc_flat[idx].reshape(-1, K)
+        scales[r0:r0 + rows_per_pass] = sb
+    return codes.reshape(w.shape), scales.reshape(w.shape[:-1] + (K // block,))
+
+
+def _rt_table():
+    """rt[b, p]: bf16 pattern of the dequantized value of pattern p under scale byte b."""
+    if "rt" not in _LUT:
+        enc, dq = _luts()
+        rt = np.take_along_axis(dq, enc.astype(np.int64), axis=1)
+        ok = np.take_along_axis(_LUT["exact"], enc.astype(np.int64), axis=1)
+        # as mx_dequantize_bf16_bits asserts: the dequantized value of every pattern a block
+        # can hold under scale byte b is a bf16 number (checked here once for the table).
+        # Byte b comes from a finite block maximum with exponent field b + 8 <= 254 (or
+        # less, for b = 0), so the block's patterns have exponent fields <= b + 8.
+        p = np.arange(1 << 16, dtype=np.int64)
+        b = np.arange(255)[:, None]
+        reachable = (((p >> 7) & 0xFF)[None, :] <= b + 8) & (b + 8 <= 254)
+        assert ok[reachable].all(), "dequantized value not exact in bf16"
+        _LUT["rt"] = rt
+    return _LUT["rt"]
+
+
+def mx_roundtrip_bf16_bits_lut(w_bits, block: int = MX_BLOCK, rows_per_pass: int = 1024):
+    """bf16 patterns of the dequantized MXFP8 weights, mx_dequantize_bf16_bits(mx_quantize(w)),
+    through the tables."""
+    rt = _rt_table().reshape(-1)
+    w = np.asarray(w_bits, dtype=np.uint16)
+    K = w.shape[-1]
+    assert K % block == 0, "K must be a multiple of the block"
+    flat = w.reshape(-1, K)
+    out = np.empty(flat.shape, dtype=np.uint16)
+    for r0 in range(0, flat.shape[0], rows_per_pass):
+        blk = flat[r0:r0 + rows_per_pass].reshape(-1, K // block, block)
+        sb = _block_scale_bytes(blk).astype(np.uint32)
+        idx = (sb[..., None] << np.uint32(16)) | blk
+        out[r0:r0 + rows_per_pass] = rt[idx].reshape(-1, K)
+    return out.reshape(w.shape)
+
+
+__all__ += ["mx_quantize_lut", "mx_roundtrip_bf16_bits_lut"]

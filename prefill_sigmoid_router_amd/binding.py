@@ -181,6 +181,19 @@ def moe_align(topk_ids, E: int, block: int, sorted_ids, block_expert, num_padded
         _ptr(num_padded), _stream(stream)))
 
 
+def _need_plan(sorted_ids, block_expert, num_padded, block: int) -> int:
+    """The plan tensors of moe_align: int32 device tensors; returns the capacity."""
+    _need(sorted_ids, "sorted_ids", torch.int32)
+    _need(block_expert, "block_expert", torch.int32)
+    _need(num_padded, "num_padded", torch.int32)
+    cap = sorted_ids.numel()
+    if block < 1 or block_expert.numel() < cap // block:
+        raise ValueError("block_expert must hold capacity / block entries")
+    if num_padded.numel() < 1:
+        raise ValueError("num_padded must hold one entry")
+    return cap
+
+
 def moe_expert_up(x, w13, sorted_ids, block_expert, num_padded, top_k: int, block: int, act,
                   stream=None):
     M, H = x.shape
@@ -188,7 +201,7 @@ def moe_expert_up(x, w13, sorted_ids, block_expert, num_padded, top_k: int, bloc
     I = two_i // 2
     _need(x, "x", torch.bfloat16)
     _need(w13, "w13", torch.bfloat16, (E, 2 * I, H))
-    cap = sorted_ids.numel()
+    cap = _need_plan(sorted_ids, block_expert, num_padded, block)
     _need(act, "act", torch.bfloat16)
     if act.numel() < cap * I:
         raise ValueError("act must hold [capacity, I] values")
@@ -203,7 +216,9 @@ def moe_expert_down(act, w2, sorted_ids, block_expert, num_padded, M: int, top_k
     _need(w2, "w2", torch.bfloat16)
     _need(act, "act", torch.bfloat16)
     _need(y, "y", torch.float32, (M * top_k, H))
-    cap = sorted_ids.numel()
+    cap = _need_plan(sorted_ids, block_expert, num_padded, block)
+    if act.numel() < cap * I:
+        raise ValueError("act must hold [capacity, I] values")
     _check("moe_expert_down", load_library().moe_expert_down(
         _ptr(act), _ptr(w2), _ptr(sorted_ids), _ptr(block_expert), _ptr(num_padded),
         M, H, E, I, top_k, block, cap, _ptr(y), _stream(stream)))

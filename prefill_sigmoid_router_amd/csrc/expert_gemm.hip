@@ -131,11 +131,14 @@ __global__ __launch_bounds__(256) void expert_up_stream_kernel(
   const bool live = li < nlive;
   const int tok = sorted_ids[start + (live ? li : 0)] / top_k;  // dead lanes: lane 0's row
   const int n0 = blockIdx.x * 16;
-  const int khalf = H >> 1;
-  const int kb = wk * khalf + 8 * lg;
+  // K halves split on a multiple of 8 values, so both start on a 16-byte boundary (H is a
+  // multiple of 8, not necessarily of 16)
+  const int klo = ((H >> 1) + 7) & ~7;
+  const int kb = (wk ? klo : 0) + 8 * lg;
+  const int klen = wk ? H - klo : klo;
   const uint16_t* wr[1] = {w13 + (size_t)e * 2 * I * H + (size_t)(gu * I + n0 + li) * H + kb};
   f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
-  stream_k<1, U, false>(wr, x + (size_t)tok * H + kb, live, khalf, lg, acc);
+  stream_k<1, U, false>(wr, x + (size_t)tok * H + kb, live, klen, lg, acc);
   if (wave != 0) red[wave - 1][lane] = acc[0];   // wave 1: up low-K, 2: gate high-K, 3: up high-K
   __syncthreads();
   if (wave != 0) return;
@@ -167,16 +170,18 @@ __global__ __launch_bounds__(256) void expert_down_stream_kernel(
 
   const bool live = li < nlive;
   const int n0 = blockIdx.x * 32 + wn * 16;
-  const bool n_in = n0 < H;  // H is a multiple of 16: a wave's 16 columns are all in or all out
-  const int khalf = I >> 1;
+  // a wave's 16 output columns: all in, all out, or (H a multiple of 8 only) the first 8 in;
+  // weight rows past H read row 0 and their outputs are never stored
+  const bool n_in = n0 < H;
+  const int khalf = I >> 1;  // I is a multiple of 16: both halves start on 16 bytes
   const int kb = wk * khalf + 8 * lg;
-  const uint16_t* wr[1] = {w2 + (size_t)e * H * I + (size_t)(n_in ? n0 + li : 0) * I + kb};
+  const uint16_t* wr[1] = {w2 + (size_t)e * H * I + (size_t)(n0 + li < H ? n0 + li : 0) * I + kb};
   f32x4 acc[1] = {f32x4{0.f, 0.f, 0.f, 0.f}};
   if (n_in) stream_k<1, U, true>(wr, act + (size_t)(start + li) * I + kb, live, khalf, lg, acc);
 
   if (wk == 1) red[wn][lane] = acc[0];
   __syncthreads();
-  if (wk == 1 || !n_in || !live) return;
+  if (wk == 1 || !n_in || !live || n0 + 4 * lg >= H) return;  // columns n0 + 4 lg .. + 3
   acc[0] += red[wn][lane];
   const int dst = sorted_ids[start + li];
   if constexpr (std::is_same<Y, float>::value) {

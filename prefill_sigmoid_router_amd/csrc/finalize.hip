@@ -265,12 +265,11 @@ hipError_t launch_finalize(const float* y, const float* topk_w, const uint16_t* 
 hipError_t launch_finalize(const uint16_t* y, const float* topk_w, const uint16_t* residual,
                            const uint16_t* norm_w, float eps, int M, int H, int top_k,
                            uint16_t* out, uint16_t* residual_out, hipStream_t s) {
-  if (H % 8 == 0 && H / 8 <= 2 * kFinThreads) {
-    if (H / 8 <= kFinThreads)
-      return launch_fin_bf16<1>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
-    return launch_fin_bf16<2>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
-  }
-  return launch_fin_rows(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
+  // every H the API accepts (a multiple of 8, at most 16384) fits one of the two
+  if (H % 8 != 0 || H / 8 > 2 * kFinThreads) return hipErrorInvalidValue;
+  if (H / 8 <= kFinThreads)
+    return launch_fin_bf16<1>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
+  return launch_fin_bf16<2>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
 }
 
 

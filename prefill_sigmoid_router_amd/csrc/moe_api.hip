@@ -19,8 +19,8 @@ inline bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 bool sizes_ok(int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k) {
   if (M < 0 || E < 1 || E > kMaxE || top_k < 1 || top_k > E) return false;
-  if (H < 16 || H > kMaxH || H % 16 != 0) return false;
-  if (I < 64 || I % 64 != 0) return false;
+  if (H < 8 || H > kMaxH || H % 8 != 0) return false;
+  if (I < 16 || I % 16 != 0) return false;
   if ((int64_t)M * top_k >= ((int64_t)1 << 31)) return false;
   return true;
 }
@@ -121,7 +121,7 @@ const char* moe_strerror(int status) {
   }
 }
 
-int moe_abi_version(void) { return 104; }
+int moe_abi_version(void) { return 105; }
 
 size_t moe_align_capacity(int32_t M, int32_t top_k, int32_t E, int32_t block) {
   if (M < 0 || top_k < 1 || E < 1 || block < 1) return 0;
@@ -135,7 +135,7 @@ size_t moe_route_workspace_bytes(int32_t M, int32_t E) {
 }
 
 int32_t moe_gemm_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I) {
-  if (M < 0 || E < 1 || E > kMaxE || top_k < 1 || top_k > E || I < 64 || I % 64 != 0) return 0;
+  if (M < 0 || E < 1 || E > kMaxE || top_k < 1 || top_k > E || I < 16 || I % 16 != 0) return 0;
   return gemm_tile_rows(M, E, top_k, I, false);
 }
 
@@ -145,7 +145,7 @@ int32_t moe_gemm_tile_rows_mx(int32_t M, int32_t E, int32_t top_k, int32_t I) {
 }
 
 int32_t moe_forward_self_routes(int32_t M, int32_t E, int32_t top_k, int32_t I) {
-  if (M < 0 || E < 1 || E > kMaxE || top_k < 1 || top_k > E || I < 64 || I % 64 != 0) return 0;
+  if (M < 0 || E < 1 || E > kMaxE || top_k < 1 || top_k > E || I < 16 || I % 16 != 0) return 0;
   return self_routes(M, E, top_k, I) ? 1 : 0;
 }
 
@@ -158,8 +158,8 @@ size_t moe_workspace_bytes(int32_t M, int32_t H, int32_t E, int32_t I, int32_t t
 int moe_route(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
               int32_t M, int32_t H, int32_t E, int32_t top_k, int32_t* topk_ids, float* topk_w,
               void* workspace, size_t workspace_bytes, moe_stream_t stream) {
-  if (M < 0 || E < 1 || E > kMaxE || top_k < 1 || top_k > E || H < 16 || H > kMaxH ||
-      H % 16 != 0 || (int64_t)M * top_k >= ((int64_t)1 << 31))
+  if (M < 0 || E < 1 || E > kMaxE || top_k < 1 || top_k > E || H < 8 || H > kMaxH ||
+      H % 8 != 0 || (int64_t)M * top_k >= ((int64_t)1 << 31))
     return MOE_ERR_INVALID_ARG;
   if (M == 0) return MOE_OK;
   if (!x || !router_w || !topk_ids || !topk_w) return MOE_ERR_INVALID_ARG;
@@ -224,7 +224,7 @@ int moe_expert_down(const uint16_t* act, const uint16_t* w2, const int32_t* sort
 int moe_finalize(const float* y, const float* topk_w, const uint16_t* residual,
                  const uint16_t* norm_w, float eps, int32_t M, int32_t H, int32_t top_k,
                  uint16_t* out, uint16_t* residual_out, moe_stream_t stream) {
-  if (M < 0 || top_k < 1 || H < 16 || H > kMaxH || H % 16 != 0 || !(eps > 0.0f) || !isfinite(eps) ||
+  if (M < 0 || top_k < 1 || H < 8 || H > kMaxH || H % 8 != 0 || !(eps > 0.0f) || !isfinite(eps) ||
       (int64_t)M * top_k >= ((int64_t)1 << 31))
     return MOE_ERR_INVALID_ARG;
   if (M == 0) return MOE_OK;

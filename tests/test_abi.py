@@ -56,7 +56,7 @@ def test_library_links_no_torch(B):
 
 
 def test_strerror_and_version(B):
-    assert B.moe_abi_version() == 104
+    assert B.moe_abi_version() == 105
     for s in (0, -1, -2, -3, -4, 17):
         assert isinstance(B.moe_strerror(s), str) and B.moe_strerror(s)
 
@@ -77,7 +77,9 @@ def test_workspace_bytes_cover_the_buffers(B):
     got = B.moe_workspace_bytes(M, H, E, I, k, blk)
     assert need <= got <= need + 10 * 256
     assert B.moe_workspace_bytes(M, H, E, I, k, 48) == 0          # no kernel for block 48
-    assert B.moe_workspace_bytes(M, 7160, E, I, k, blk) == 0      # H % 16 != 0
+    assert B.moe_workspace_bytes(M, 7164, E, I, k, blk) == 0      # H % 8 != 0
+    assert B.moe_workspace_bytes(M, 7160, E, 2032, k, blk) > 0   # H % 8 == 0, I % 16 == 0
+    assert B.moe_workspace_bytes(M, H, E, 2044, k, blk) == 0      # I % 16 != 0
     assert B.moe_workspace_bytes(M, H, 2000, I, k, blk) == 0      # E > 1024
     assert B.moe_route_workspace_bytes(M, E) >= M * E * 32
 
@@ -98,7 +100,7 @@ def _fwd(lib, **kw):
 
 @pytest.mark.parametrize("bad,code", [
     (dict(M=-1), -1), (dict(k=0), -1), (dict(k=9), -1), (dict(E=1025, k=2), -1),
-    (dict(H=250), -1), (dict(I=100), -1), (dict(eps=0.0), -1), (dict(eps=float("nan")), -1),
+    (dict(H=250), -1), (dict(H=4), -1), (dict(I=100), -1), (dict(I=8), -1), (dict(eps=0.0), -1), (dict(eps=float("nan")), -1),
     (dict(block=48), -2), (dict(block=8), -2), (dict(x=None), -1), (dict(out=None), -1),
     (dict(w13=None), -1), (dict(x=9), -1), (dict(ws=None), -3), (dict(wsb=16), -3),
     (dict(ws=64), -3),
@@ -114,9 +116,9 @@ def test_forward_zero_tokens_is_a_noop(B):
 def test_route_align_finalize_validation(B):
     lib = B.load_library()
     p = ctypes.c_void_p
-    # route: top_k > E, H % 16, workspace too small
+    # route: top_k > E, H % 8, workspace too small
     assert lib.moe_route(p(16), p(16), None, 4, 256, 8, 9, p(16), p(16), p(256), 1 << 30, None) == -1
-    assert lib.moe_route(p(16), p(16), None, 4, 200, 8, 2, p(16), p(16), p(256), 1 << 30, None) == -1
+    assert lib.moe_route(p(16), p(16), None, 4, 204, 8, 2, p(16), p(16), p(256), 1 << 30, None) == -1
     assert lib.moe_route(p(16), p(16), None, 4, 256, 8, 2, p(16), p(16), p(256), 8, None) == -3
     assert lib.moe_route(None, p(16), None, 4, 256, 8, 2, p(16), p(16), p(256), 1 << 30, None) == -1
     assert lib.moe_route(None, None, None, 0, 256, 8, 2, None, None, None, 0, None) == 0
@@ -125,7 +127,7 @@ def test_route_align_finalize_validation(B):
     assert lib.moe_align(p(16), 4, 2, 1025, 16, p(16), p(16), p(16), None) == -1
     assert lib.moe_align(p(16), 4, 2, 8, 16, None, p(16), p(16), None) == -1
     assert lib.moe_align(p(16), 4, 2, 8, 16, p(16), p(16), p(18), None) == -1   # misaligned
-    # finalize: eps <= 0, H % 16, null y
+    # finalize: eps <= 0, H % 8, null y
     assert lib.moe_finalize(p(16), p(16), p(16), p(16), 0.0, 4, 256, 2, p(16), None, None) == -1
     assert lib.moe_finalize(p(16), p(16), p(16), p(16), 1e-5, 4, 250, 2, p(16), None, None) == -1
     assert lib.moe_finalize(None, p(16), p(16), p(16), 1e-5, 4, 256, 2, p(16), None, None) == -1
@@ -162,6 +164,7 @@ def test_gemm_tile_rows_follows_tokens_per_expert(B):
     assert B.moe_gemm_tile_rows(2048, 256, 16, 2048) == 128
     assert B.moe_gemm_tile_rows(2048, 256, 16, 192) == 16
     assert B.moe_gemm_tile_rows(2048, 256, 16, 100) == 0
+    assert B.moe_gemm_tile_rows(2048, 256, 16, 48) == 16        # I % 16 == 0: streaming kernels
     assert B.moe_gemm_tile_rows(8, 0, 1, 2048) == 0
     assert B.moe_gemm_tile_rows(-1, 256, 16, 2048) == 0
     # MXFP8 weights: 32-row tiles of LDS codes below 16 tokens per expert, I a multiple of 256
@@ -212,4 +215,16 @@ def test_mx_entry_points_validate_on_the_host(B):
     assert fwd_mx(w13c=None) == -1
     assert fwd_mx(w13s=260) == -1          # scales must be 8-byte aligned
     assert fwd_mx(w2s=252) == -1
-    assert fwd_mx(H=250) == -1             # H % 16 != 0 fails the shared size checks first
+    assert fwd_mx(H=250) == -1             # H % 8 != 0 fails the shared size checks first
+    assert fwd_mx(H=200) == -2             # H % 8 == 0 but not a multiple of 256
+
+
+def test_size_contract_is_h_mod_8_and_i_mod_16(B):
+    """The boundary accepts H % 8 == 0 (8 <= H <= 16384) and I % 16 == 0 (I >= 16): shapes
+    with I not a multiple of 256 run the 16-row weight-streaming kernels."""
+    for H, I, ok in [(8, 16, True), (200, 48, True), (264, 256, True), (16384, 64, True),
+                     (4, 16, False), (12, 16, False), (16392, 16, False), (200, 8, False),
+                     (200, 40, False)]:
+        assert (B.moe_workspace_bytes(4, H, 8, I, 2, 16) > 0) == ok, (H, I)
+    assert B.moe_gemm_tile_rows(64, 8, 2, 48) == 16
+    assert B.moe_gemm_tile_rows(64, 8, 2, 256) == 64

@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import _fullsize as fs
 import moe_inputs as mi
 from oracle import moe_oracle as orc
 from oracle import mx_oracle as mxo
@@ -129,20 +130,6 @@ def _bias_np(L):
     return None if L["router_bias"] is None else L["router_bias"].cpu().numpy()
 
 
-class _OracleMxExperts:
-    """Expert e of a device bf16 stack, quantized and dequantized by the oracle."""
-
-    def __init__(self, stack):
-        self.stack = stack
-
-    def __len__(self):
-        return self.stack.shape[0]
-
-    def __getitem__(self, e):
-        c, s = mxo.mx_quantize(bits(self.stack[int(e)]))
-        return mxo.mx_dequantize_bf16_bits(c, s)
-
-
 # expected tokens per expert M * top_k / E, with the kernels that copy the codes into LDS:
 # below 16 32-row tiles (mx_tiny 1, mx_mid 4.6, mx_one_token 0.1, mx_dec_partial 10,
 # mx_dec_groups 6), 16..63 64-row tiles (mx_tiles64 24 with nontemporal code copies,
@@ -220,37 +207,100 @@ def mx_full(B, dev):
     return weights, _mx_weights(B, L, dev)
 
 
-@pytest.mark.parametrize("name", MX_FULL)
-def test_forward_mx_full_size(B, dev, mx_full, name):
-    """The real-shape workloads with MXFP8 weights -- 32-row tiles of LDS codes at M=8 and
-    M=128, 64-row tiles at M=512 (Zipf), 128-row tiles at M=2048: routing and plan bit-exact for
-    every token; codes of the experts a sampled token uses bit-exact; that token's output
-    against the oracle on the oracle's own dequantized weights."""
-    cfg = mi.CONFIGS[name]
-    print(f"forward_mx full-size {name} M={cfg.M}", flush=True)
+@pytest.fixture(scope="module")
+def mx_full_runs(B, dev, mx_full):
+    """The four real-shape workloads through moe_forward_mx, results on the host."""
     weights, mx = mx_full
-    L = mi.make_layer(cfg, device=dev, seed=0, with_experts=False)
-    L.update(weights)
-    r = _run_forward_mx(B, L, dev, mx)
-    k = cfg.top_k
-    ref_ids, ref_w, _ = orc.route(bits(L["x"]), bits(L["router_w"]), _bias_np(L), k)
-    assert np.array_equal(r["ids"].cpu().numpy(), ref_ids)
-    sorted_ids, bexp, n_pad, _, _ = orc.align(ref_ids, cfg.E, cfg.block)
-    assert int(r["npad"].item()) == n_pad
-    assert np.array_equal(r["sorted"].cpu().numpy()[:n_pad], sorted_ids)
-    out = r["out"].float().cpu().numpy()
-    assert np.isfinite(out).all()
-    t = cfg.M // 2 + 3 if cfg.M > 8 else 3
-    for e in ref_ids[t][:2]:   # two of its experts' codes, bit for bit
-        c, s = mxo.mx_quantize(bits(L["w13"][int(e)]))
-        assert np.array_equal(mx[0][int(e)].cpu().numpy(), c) and np.array_equal(mx[1][int(e)].cpu().numpy(), s)
-    ref_out, ref_z, s_ids, _ = orc.forward_tokens([t], bits(L["x"]), bits(L["router_w"]),
-                                                  _bias_np(L), _OracleMxExperts(L["w13"]),
-                                                  _OracleMxExperts(L["w2"]), bits(L["residual"]),
-                                                  bits(L["norm_w"]), L["eps"], k)
-    assert np.array_equal(s_ids, ref_ids[[t]])
-    _check_close(r["out"][[t]], ref_out, f"{name} mx sampled out")
-    _check_close(r["rout"][[t]], ref_z, f"{name} mx sampled residual_out")
+    runs = {}
+    for name in MX_FULL:
+        cfg = mi.CONFIGS[name]
+        print(f"forward_mx full-size {name} M={cfg.M}", flush=True)
+        L = mi.make_layer(cfg, device=dev, seed=0, with_experts=False)
+        L.update(weights)
+        r = _run_forward_mx(B, L, dev, mx)
+        runs[name] = {
+            "cfg": cfg, "eps": L["eps"], "x": bits(L["x"]), "residual": bits(L["residual"]),
+            "bias": _bias_np(L), "router_w": bits(L["router_w"]), "norm_w": bits(L["norm_w"]),
+            "ids": r["ids"].cpu().numpy(), "sorted": r["sorted"].cpu().numpy(),
+            "npad": int(r["npad"].item()),
+            "out": r["out"].float().cpu().numpy().astype(np.float64),
+            "rout": r["rout"].float().cpu().numpy().astype(np.float64),
+        }
+        del r, L
+        torch.cuda.empty_cache()
+    return runs
+
+
+@pytest.mark.parametrize("name", MX_FULL)
+def test_forward_mx_full_size_routing_and_plan(mx_full_runs, name):
+    """32-row tiles of LDS codes at M=8 and M=128, 64-row tiles at M=512 (Zipf), 128-row tiles
+    at M=2048: routing and plan bit-exact for every token, every output row finite."""
+    run = mx_full_runs[name]
+    cfg = run["cfg"]
+    ref_ids, _, _ = orc.route(run["x"], run["router_w"], run["bias"], cfg.top_k)
+    assert np.array_equal(run["ids"], ref_ids)
+    sorted_ids, _, n_pad, _, _ = orc.align(ref_ids, cfg.E, cfg.block)
+    assert run["npad"] == n_pad
+    assert np.array_equal(run["sorted"][:n_pad], sorted_ids)
+    assert np.isfinite(run["out"]).all() and np.isfinite(run["rout"]).all()
+
+
+def test_mx_full_size_codes_bit_exact(mx_full):
+    """The device quantizer on real-shape experts (every 17th expert and the last): codes
+    and scale bytes equal the oracle's."""
+    weights, mx = mx_full
+    for e in list(range(0, 256, 17)) + [255]:
+        c, sc = mxo.mx_quantize_lut(bits(weights["w13"][e]))
+        assert np.array_equal(mx[0][e].cpu().numpy(), c) and np.array_equal(mx[1][e].cpu().numpy(), sc), e
+        c, sc = mxo.mx_quantize_lut(bits(weights["w2"][e]))
+        assert np.array_equal(mx[2][e].cpu().numpy(), c) and np.array_equal(mx[3][e].cpu().numpy(), sc), e
+
+
+@pytest.fixture(scope="module")
+def mx_full_oracle(mx_full_runs, mx_full):
+    """The oracle on the sampled tokens of all four workloads, on the oracle's own
+    dequantized MXFP8 weights, in one pass over the experts."""
+    weights, _ = mx_full
+    jobs, meta = {}, {}
+    for name, run in mx_full_runs.items():
+        cfg = run["cfg"]
+        ref_ids, ref_w, _ = orc.route(run["x"], run["router_w"], run["bias"], cfg.top_k)
+        sample = fs.sample_tokens(ref_ids, n_min=256, all_up_to=128, seed=cfg.M + 1)
+        jobs[name] = (orc.bf16_to_f64(run["x"][sample]), ref_ids[sample])
+        meta[name] = (sample, ref_w[sample])
+    print(f"oracle pass over the MXFP8 experts for {sum(len(m[0]) for m in meta.values())} "
+          "tokens", flush=True)
+    w13 = lambda e: mxo.mx_roundtrip_bf16_bits_lut(bits(weights["w13"][int(e)]))  # noqa: E731
+    w2 = lambda e: mxo.mx_roundtrip_bf16_bits_lut(bits(weights["w2"][int(e)]))    # noqa: E731
+    ys = fs.stream_expert_rows(jobs, w13, w2, mi.CONFIGS["decode_m8"].I)
+    res = {}
+    for name, run in mx_full_runs.items():
+        sample, w = meta[name]
+        out, z = orc.finalize(ys[name], w, run["residual"][sample], run["norm_w"], run["eps"])
+        res[name] = (sample, out, z)
+    return res
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("name", MX_FULL)
+def test_forward_mx_full_size_against_oracle(mx_full_runs, mx_full_oracle, name):
+    """Sampled tokens against the oracle layer on the oracle's dequantized weights: all 8
+    tokens at decode; from M=128 at least 256 tokens (all 128 at M=128) including token M-1
+    and, for every expert, the first and the last token that picked it."""
+    run = mx_full_runs[name]
+    cfg = run["cfg"]
+    sample, out, z = mx_full_oracle[name]
+    if cfg.M <= 128:
+        assert len(sample) == cfg.M
+    else:
+        assert len(sample) >= 256 and sample[-1] == cfg.M - 1
+        ids = run["ids"]
+        for e in np.unique(ids):
+            rows = np.nonzero((ids == e).any(axis=1))[0]
+            assert rows[-1] in sample and rows[0] in sample
+    print(f"{name}: {len(sample)} tokens against the oracle", flush=True)
+    _check_close(torch.from_numpy(run["out"][sample]), out, f"{name} mx out")
+    _check_close(torch.from_numpy(run["rout"][sample]), z, f"{name} mx residual_out")
 
 
 @pytest.mark.parametrize("name", ["mx_tiny", "mx_many"])

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import _fullsize as fs
 import moe_inputs as mi
 from oracle import moe_oracle as orc
 
@@ -86,6 +87,21 @@ SMALL = {
     # one N tile is mostly past the 64 output columns
     "tiled128_short": mi.LayerConfig("tiled128_short", M=200, H=64, E=4, top_k=2, I=256,
                                      block=16),
+    # the boundary's smallest granules: H a multiple of 8 but not 16 (K halves of the up
+    # streaming kernel split at 104 / 96 values, the last 16 output columns of the down
+    # streaming kernel half past H) and I a multiple of 16 but not 64 (streaming kernels)
+    "hmod8_stream": mi.LayerConfig("hmod8_stream", M=21, H=200, E=8, top_k=3, I=48, block=16),
+    # H % 64 = 8 on the self-routing 64-row tiled up GEMM (a one-slot partial K chunk)
+    "hmod8_tiled64": mi.LayerConfig("hmod8_tiled64", M=40, H=264, E=16, top_k=4, I=256,
+                                    block=16),
+    # H % 8 on the many-token router (fp32 MFMA logits, partial K chunk), 128-row tiles with
+    # a partial K chunk in the up GEMM and a partial N tile (328 of 512 columns) in the down
+    "hmod8_many": mi.LayerConfig("hmod8_many", M=300, H=328, E=8, top_k=4, I=256, block=64,
+                                 zipf_s=1.0),
+    # the per-token bf16 finalize with two 8-value groups per thread (8192 < H <= 16384)
+    "fin_h16384": mi.LayerConfig("fin_h16384", M=256, H=16384, E=4, top_k=2, I=64, block=16),
+    # the per-token finalize with a second batch of picks (top_k > 8) from 256 tokens
+    "fin_topk12": mi.LayerConfig("fin_topk12", M=264, H=256, E=32, top_k=12, I=256, block=32),
 }
 FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048"]
 
@@ -309,7 +325,8 @@ def _plan_on_gpu(B, L, dev):
     return ids, w, s, b, npd
 
 
-@pytest.mark.parametrize("name", ["tiny", "mid", "ragged_ktail", "block64_zipf", "block128"])
+@pytest.mark.parametrize("name", ["tiny", "mid", "ragged_ktail", "block64_zipf", "block128",
+                                  "hmod8_stream"])
 def test_expert_up_swiglu(B, dev, name):
     cfg = SMALL[name]
     print(f"expert_up parity {name}", flush=True)
@@ -342,7 +359,8 @@ def test_expert_up_swiglu(B, dev, name):
         assert np.all(a[pad_rows] == 0.0), (name, blk_i)
 
 
-@pytest.mark.parametrize("name", ["tiny", "mid", "ragged_ktail", "block64_zipf", "block128"])
+@pytest.mark.parametrize("name", ["tiny", "mid", "ragged_ktail", "block64_zipf", "block128",
+                                  "hmod8_stream"])
 def test_expert_down(B, dev, name):
     cfg = SMALL[name]
     print(f"expert_down parity {name}", flush=True)
@@ -490,37 +508,91 @@ def full_weights(dev):
     return {"w13": L["w13"], "w2": L["w2"], "router_w": L["router_w"], "norm_w": L["norm_w"]}
 
 
+@pytest.fixture(scope="module")
+def full_runs(B, dev, full_weights):
+    """The four real-shape workloads through moe_forward (the kernels the benchmark times),
+    their results copied to the host."""
+    runs = {}
+    for name in FULL:
+        cfg = mi.CONFIGS[name]
+        print(f"forward full-size {name} M={cfg.M}", flush=True)
+        L = mi.make_layer(cfg, device=dev, seed=0, with_experts=False)
+        L.update(full_weights)
+        r = _run_forward(B, L, dev)
+        runs[name] = {
+            "cfg": cfg, "eps": L["eps"], "x": bits(L["x"]), "residual": bits(L["residual"]),
+            "bias": _bias_np(L), "router_w": bits(L["router_w"]), "norm_w": bits(L["norm_w"]),
+            "ids": r["ids"].cpu().numpy(), "w": r["w"].cpu().numpy(),
+            "sorted": r["sorted"].cpu().numpy(), "bexp": r["bexp"].cpu().numpy(),
+            "npad": int(r["npad"].item()),
+            "out": r["out"].float().cpu().numpy().astype(np.float64),
+            "rout": r["rout"].float().cpu().numpy().astype(np.float64),
+            "tile_rows": B.moe_gemm_tile_rows(cfg.M, cfg.E, cfg.top_k, cfg.I),
+        }
+        del r, L
+        torch.cuda.empty_cache()
+    return runs
+
+
 @pytest.mark.parametrize("name", FULL)
-def test_forward_full_size(B, dev, full_weights, name):
-    cfg = mi.CONFIGS[name]
-    print(f"forward full-size parity {name} M={cfg.M}", flush=True)
-    L = mi.make_layer(cfg, device=dev, seed=0, with_experts=False)
-    L.update(full_weights)
-    r = _run_forward(B, L, dev)
-    M, k = cfg.M, cfg.top_k
-    # routing and plan over every token, bit-exact
-    ref_ids, ref_w, _ = orc.route(bits(L["x"]), bits(L["router_w"]), _bias_np(L), k)
-    assert np.array_equal(r["ids"].cpu().numpy(), ref_ids)
-    np.testing.assert_allclose(r["w"].cpu().numpy(), ref_w, rtol=0, atol=1e-6)
-    sorted_ids, bexp, n_pad, counts, _ = orc.align(ref_ids, cfg.E, cfg.block)
-    _check_plan(r, {"sorted_ids": sorted_ids, "block_expert": bexp, "num_padded": n_pad}, cfg.block, name)
-    # properties of every token: finite, and out = RMSNorm(residual_out) * g within bf16 rounding
-    out = r["out"].float().cpu().numpy().astype(np.float64)
-    z = r["rout"].float().cpu().numpy().astype(np.float64)
-    g = orc.bf16_to_f64(bits(L["norm_w"]))
-    assert np.isfinite(out).all() and np.isfinite(z).all()
-    renorm = z / np.sqrt(np.mean(z * z, axis=1, keepdims=True) + L["eps"]) * g
-    assert np.abs(out - renorm).max() <= 4e-2
-    # sampled tokens against the oracle, one by one
-    rng = np.random.default_rng(cfg.M)
-    sample = sorted(set([0, M - 1] + rng.choice(M, size=min(M, 2), replace=False).tolist()))
-    if M > 8:
-        sample = sample[:3]
-    w13 = mi.DeviceExpertsAsBits(L["w13"])
-    w2 = mi.DeviceExpertsAsBits(L["w2"])
-    ref_out, ref_z, s_ids, _ = orc.forward_tokens(sample, bits(L["x"]), bits(L["router_w"]),
-                                                  _bias_np(L), w13, w2, bits(L["residual"]),
-                                                  bits(L["norm_w"]), L["eps"], k)
-    assert np.array_equal(s_ids, ref_ids[sample])
-    _check_close(r["out"][sample], ref_out, f"{name} sampled out")
-    _check_close(r["rout"][sample], ref_z, f"{name} sampled residual_out")
+def test_forward_full_size_routing_and_plan(full_runs, name):
+    """Every token: routing ids bit-exact, weights within 1e-6, the plan bit-exact; every
+    output row finite."""
+    run = full_runs[name]
+    cfg = run["cfg"]
+    ref_ids, ref_w, _ = orc.route(run["x"], run["router_w"], run["bias"], cfg.top_k)
+    assert np.array_equal(run["ids"], ref_ids)
+    np.testing.assert_allclose(run["w"], ref_w, rtol=0, atol=1e-6)
+    sorted_ids, bexp, n_pad, _, _ = orc.align(ref_ids, cfg.E, cfg.block)
+    assert run["npad"] == n_pad
+    assert np.array_equal(run["sorted"][:n_pad], sorted_ids)
+    assert np.array_equal(run["bexp"][:n_pad // cfg.block], bexp)
+    assert np.isfinite(run["out"]).all() and np.isfinite(run["rout"]).all()
+
+
+@pytest.fixture(scope="module")
+def full_oracle(full_runs, full_weights):
+    """The oracle on the sampled tokens of all four workloads, in one pass over the experts
+    (each expert copied to the host and decoded once)."""
+    jobs, meta = {}, {}
+    for name, run in full_runs.items():
+        cfg = run["cfg"]
+        ref_ids, ref_w, _ = orc.route(run["x"], run["router_w"], run["bias"], cfg.top_k)
+        sample = fs.sample_tokens(ref_ids, n_min=256, all_up_to=128, seed=cfg.M)
+        jobs[name] = (orc.bf16_to_f64(run["x"][sample]), ref_ids[sample])
+        meta[name] = (sample, ref_w[sample])
+    print(f"oracle pass over the experts for {sum(len(m[0]) for m in meta.values())} tokens",
+          flush=True)
+    w13 = mi.DeviceExpertsAsBits(full_weights["w13"])
+    w2 = mi.DeviceExpertsAsBits(full_weights["w2"])
+    ys = fs.stream_expert_rows(jobs, w13.__getitem__, w2.__getitem__, mi.CONFIGS["decode_m8"].I)
+    res = {}
+    for name, run in full_runs.items():
+        sample, w = meta[name]
+        out, z = orc.finalize(ys[name], w, run["residual"][sample], run["norm_w"], run["eps"])
+        res[name] = (sample, out, z)
+    return res
+
+
+@pytest.mark.timeout(1200)
+@pytest.mark.parametrize("name", FULL)
+def test_forward_full_size_against_oracle(full_runs, full_oracle, name):
+    """Sampled tokens of the real-shape layer against the oracle: every token at M=8 and
+    M=128; at M=512 and M=2048 at least 256 tokens including token M-1 and, for every
+    expert, the first and the last token that picked it, so every expert's first and last
+    token tile of both grouped GEMMs (all K chunks, all N tiles) holds a checked row."""
+    run = full_runs[name]
+    cfg = run["cfg"]
+    sample, out, z = full_oracle[name]
+    M = cfg.M
+    if M <= 128:
+        assert len(sample) == M
+    else:
+        assert len(sample) >= 256 and sample[-1] == M - 1
+        ids = run["ids"]
+        for e in np.unique(ids):
+            rows = np.nonzero((ids == e).any(axis=1))[0]
+            assert rows[-1] in sample and rows[0] in sample
+    print(f"{name}: {len(sample)} tokens against the oracle", flush=True)
+    _check_close(torch.from_numpy(run["out"][sample]), out, f"{name} out")
+    _check_close(torch.from_numpy(run["rout"][sample]), z, f"{name} residual_out")

@@ -2,6 +2,7 @@
 E4M3 values printed from the field layout, a brute-force nearest-value encoder, tie and
 saturation cases, and hand-worked MX blocks.  CPU only."""
 import numpy as np
+import pytest
 
 from oracle import mx_oracle as mx
 
@@ -117,3 +118,52 @@ def test_mx_quantization_error_bound_and_exact_bf16():
     bits = mx.mx_dequantize_bf16_bits(codes, scales)
     back = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
     assert np.array_equal(back, deq)
+
+
+def _trunc_bf16(values):
+    """bf16 bit patterns of values, truncated (any pattern will do for these pins)."""
+    return (np.asarray(values, dtype=np.float32).view(np.uint32) >> 16).astype(np.uint16)
+
+
+def _lut_cases():
+    """bf16 bit patterns [rows, K] covering the conversion's branches: several magnitudes,
+    blocks spanning many binades, midpoints between E4M3 neighbours (ties), maxima that clamp
+    to 448, zero and negative-zero blocks, and bf16 subnormals."""
+    rng = np.random.default_rng(11)
+    cases = []
+    for sd in (0.02, 1.0, 1e-6, 3e4):
+        cases.append(_trunc_bf16(rng.normal(0, sd, (16, 256))))
+    wide = rng.normal(0, 1, (16, 256)) * np.exp2(rng.integers(-30, 30, (16, 256)))
+    cases.append(_trunc_bf16(wide))
+    pos = mx.e4m3_decode(np.arange(0x00, 0x7F, dtype=np.uint8))
+    mids = (pos[1:] + pos[:-1]) / 2
+    t = np.zeros((4, 256), dtype=np.float32)
+    t[0, :125] = mids[:125] / 256.0
+    t[0, 200] = 1.0
+    t[1, :125] = -mids[:125] / 256.0 * 8
+    t[2, 32:64] = -0.0
+    t[3, 5] = 1.875
+    cases.append(_trunc_bf16(t))
+    sub = np.zeros((2, 64), dtype=np.uint16)
+    sub[0, :32] = np.arange(1, 33, dtype=np.uint16)             # bf16 subnormals only
+    sub[1, :32] = 0x8000                                        # negative zeros
+    sub[1, 32:] = np.arange(0x0080, 0x00A0, dtype=np.uint16)    # smallest normals
+    cases.append(sub)
+    return cases
+
+
+def test_lut_quantize_equals_the_definition():
+    """The tabulated conversion (used to convert whole expert stacks) against mx_quantize."""
+    for w in _lut_cases():
+        c0, s0 = mx.mx_quantize(w)
+        c1, s1 = mx.mx_quantize_lut(w, rows_per_pass=5)
+        assert np.array_equal(s0, s1)
+        assert np.array_equal(c0, c1)
+
+
+def test_lut_roundtrip_equals_the_definition():
+    # (dequantized values of bf16 inputs are always bf16 numbers: the E4M3 grid below a block's
+    # scale never gets finer than the bf16 values it rounds, so the subnormal case is exact too)
+    for w in _lut_cases():
+        c0, s0 = mx.mx_quantize(w)
+        assert np.array_equal(mx.mx_roundtrip_bf16_bits_lut(w), mx.mx_dequantize_bf16_bits(c0, s0))

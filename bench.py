@@ -8,15 +8,21 @@ Prints ONE JSON line.  A step is one moe_forward call (all five kernels) over re
 inputs of the workload; K steps are timed between two synchronisations (wall clock and
 HIP events on the launch stream, the larger is used).  A second pass of K steps records
 six HIP events per step around the five kernels for the per-kernel durations (an event
-between two kernels adds a few microseconds of idle, so that pass is not the headline).  `value` is tokens/s
-of the headline workload (decode, M=8); `sweep` holds the same measurement at M=128,
-512 and 2048 on the same weights.  `roofline` is for the dominant kernel (the grouped
-up-GEMM + SwiGLU, which streams W13) against the 8 TB/s HBM peak, and against the read
-rate this device reaches with a plain streaming read of the resident W13
-(`measured_read_peak`, from the probe library built next to the layer's);
-`cpu_baseline` is the CPU oracle timed on a bounded sample of the decode workload.  `mxfp8_decode` times the same decode layer with
-the expert weights quantized to MXFP8 (moe_forward_mx); it is a separate measurement, not
-the headline, whose weights are bf16.
+between two kernels adds a few microseconds of idle, so that pass is not the headline).
+`value` is tokens/s of the headline workload (decode, M=8); `sweep` holds the same
+measurement at M=128, 512 and 2048 on the same weights, each with its own `roofline`.
+
+`roofline` is for the dominant kernel (the grouped up-GEMM + SwiGLU, which streams W13):
+algorithmic bytes per launch / its average duration from the HIP events, against the
+8 TB/s HBM peak, with the MFMA rate of the same launch against the 2.5 PFLOP/s bf16 dense
+peak beside it; `traffic` is the HBM bytes that rocprofv3's FETCH_SIZE + WRITE_SIZE
+counters read for that kernel (profiles/traffic_*.json, null once the kernel source has
+changed since).  `measured_read_peak` is the larger of two read probes over the resident
+W13 (probe/read_bw.hip): a plain nontemporal vector-load pass, and the tiled GEMMs' own
+copy path (nontemporal global_load_lds whole-line copies into a 3-stage LDS ring).
+`cpu_baseline` is the CPU oracle timed on the GPU run's own inputs (copied to the host).
+`mxfp8_decode` times the same layer with the expert weights quantized to MXFP8
+(moe_forward_mx); it is a separate measurement, not the headline, whose weights are bf16.
 """
 from __future__ import annotations
 
@@ -35,7 +41,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 BF16_PEAK_TFLOPS = 2500.0      # MI355X dense bf16 MFMA, vendor figure
 METRIC = "MoE-layer tokens/s and µs/layer at M=8/128/2048; % HBM or MFMA roofline"
 STAGES = ("route", "align", "up", "down", "finalize")
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_expert_up_decode_m8.json")
+PROFILES = os.path.join(ROOT, "profiles")
+SWEEP = ("batch_m128", "batch_m512", "prefill_m2048")
 
 
 def source_hash(path: str) -> str:
@@ -62,8 +69,23 @@ def up_bytes(cfg, M, touched, mx=False):
             + M * cfg.top_k * cfg.I * 2)
 
 
+def down_bytes(cfg, M, touched, mx=False):
+    """Algorithmic bytes of the down kernel: W2 of every touched expert, one bf16 act row
+    read and one bf16 y row written per (token, pick)."""
+    return (int(touched * cfg.H * cfg.I * weight_bytes_per_value(mx))
+            + M * cfg.top_k * (cfg.I + cfg.H) * 2)
+
+
 def layer_flops(cfg, M):
     return 2 * M * cfg.E * cfg.H + 6 * M * cfg.top_k * cfg.H * cfg.I
+
+
+def up_flops(cfg, M):
+    return 4 * M * cfg.top_k * cfg.H * cfg.I
+
+
+def down_flops(cfg, M):
+    return 2 * M * cfg.top_k * cfg.I * cfg.H
 
 
 def run_workload(B, mi, torch, cfg, weights, steps, warmup, dev, mx=None):
@@ -72,7 +94,6 @@ def run_workload(B, mi, torch, cfg, weights, steps, warmup, dev, mx=None):
     L = mi.make_layer(cfg, device=dev, seed=0, with_experts=False)
     L.update(weights)
     M, H, E, I, k, blk = cfg.M, cfg.H, cfg.E, cfg.I, cfg.top_k, cfg.block
-    cap = B.moe_align_capacity(M, k, E, blk)
     out = torch.empty((M, H), dtype=torch.bfloat16, device=dev)
     ids = torch.empty((M, k), dtype=torch.int32, device=dev)
     ws = torch.empty(B.moe_workspace_bytes(M, H, E, I, k, blk), dtype=torch.uint8, device=dev)
@@ -115,10 +136,16 @@ def run_workload(B, mi, torch, cfg, weights, steps, warmup, dev, mx=None):
     counts = torch.bincount(ids.flatten().long(), minlength=E)
     lb = layer_bytes(cfg, M, touched, mx is not None)
     ub = up_bytes(cfg, M, touched, mx is not None)
+    db = down_bytes(cfg, M, touched, mx is not None)
+    stages = {n: round(v * 1e3, 2) for n, v in stage_ms.items()}
+    self_routed = mx is None and B.moe_forward_self_routes(M, E, k, I)
+    if self_routed:
+        # the up GEMM builds the plan: no align kernel runs, the event pair encloses none
+        stages["align"] = None
     return {
         "M": M, "ms_per_step": ms, "us_per_layer": ms * 1e3, "tokens_per_s": M / (ms / 1e3),
-        "wall_ms": wall_ms, "event_span_ms": span_ms,
-        "stages_us": {n: round(v * 1e3, 2) for n, v in stage_ms.items()},
+        "wall_ms": wall_ms, "event_span_ms": span_ms, "stages_us": stages,
+        "align": "fused into the up GEMM (self-routing)" if self_routed else "align kernel",
         "touched_experts": touched, "max_expert_count": int(counts.max().item()),
         "plan_rows": int(sum(((c + blk - 1) // blk) * blk for c in counts.tolist())),
         "layer_bytes": lb, "layer_gbs": lb / (ms / 1e3) / 1e9,
@@ -126,65 +153,202 @@ def run_workload(B, mi, torch, cfg, weights, steps, warmup, dev, mx=None):
         "layer_mfma_frac": layer_flops(cfg, M) / (ms / 1e3) / 1e12 / BF16_PEAK_TFLOPS,
         "up_bytes": ub, "up_us": stage_ms["up"] * 1e3,
         "up_gbs": ub / (stage_ms["up"] / 1e3) / 1e9,
+        "up_tflops": up_flops(cfg, M) / (stage_ms["up"] / 1e3) / 1e12,
+        "down_bytes": db, "down_us": stage_ms["down"] * 1e3,
+        "down_gbs": db / (stage_ms["down"] / 1e3) / 1e9,
+        "down_tflops": down_flops(cfg, M) / (stage_ms["down"] / 1e3) / 1e12,
     }
 
 
-def cpu_baseline(mi, torch):
-    """The oracle (plan-based forward, fp64 numpy) on the host over the decode batch."""
-    from oracle import moe_oracle as orc
+def up_kernel_name(B, cfg, mx=False):
+    M, E, k, I = cfg.M, cfg.E, cfg.top_k, cfg.I
+    if mx:
+        rows = B.moe_gemm_tile_rows_mx(M, E, k, I)
+        return (f"expert_tiled_mx_kernel<{rows}, ...>" if rows == 128
+                else f"expert_mx_decode_kernel<true> ({rows}-row tiles)")
+    rows = B.moe_gemm_tile_rows(M, E, k, I)
+    if B.moe_forward_self_routes(M, E, k, I):
+        return f"expert_up_selfroute_kernel<{rows}, ...> (align fused in)"
+    if rows == 16:
+        return "expert_up_stream_kernel"
+    return f"expert_tiled ({rows}-row tiles, up)"
+
+
+def load_profile(name: str, workload: str):
+    """A counter summary under profiles/ (FETCH_SIZE / WRITE_SIZE, MFMA busy), or None when
+    it is missing, was taken on another workload, or the kernel source changed since."""
+    try:
+        with open(os.path.join(PROFILES, name)) as f:
+            t = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if t.get("workload") != workload:
+        return None
+    src = os.path.join(ROOT, "prefill_sigmoid_router_amd", "csrc", t.get("source_file", ""))
+    if not os.path.isfile(src) or t.get("source_sha256_16") != source_hash(src):
+        return None
+    return t
+
+
+def roofline(res, kernel, read_peak, prof):
+    """The roofline object of a leg: the up GEMM's algorithmic bytes and flops over its
+    average launch duration (HIP events on the launch stream)."""
+    r = {
+        "bound": "hbm", "kernel": f"{kernel} (grouped up-GEMM + SwiGLU)",
+        "achieved": round(res["up_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(res["up_gbs"] / HBM_PEAK_GBS, 4),
+        "traffic": None if prof is None else prof.get("traffic_gbs"),
+        "traffic_bytes_per_launch": None if prof is None else prof.get("traffic_bytes_per_launch"),
+        "algorithmic_bytes_per_launch": res["up_bytes"], "avg_launch_us": round(res["up_us"], 2),
+        "mfma_achieved_tflops": round(res["up_tflops"], 1), "mfma_peak_tflops": BF16_PEAK_TFLOPS,
+        "mfma_frac": round(res["up_tflops"] / BF16_PEAK_TFLOPS, 4),
+        "down_gbs": round(res["down_gbs"], 1),
+        "down_frac": round(res["down_gbs"] / HBM_PEAK_GBS, 4),
+        "down_mfma_frac": round(res["down_tflops"] / BF16_PEAK_TFLOPS, 4),
+    }
+    if read_peak:
+        r["measured_read_peak"] = round(read_peak, 1)
+        r["frac_of_measured_read"] = round(res["up_gbs"] / read_peak, 4)
+    if prof is not None and prof.get("mfma_busy_frac") is not None:
+        r["mfma_busy_frac_counter"] = prof["mfma_busy_frac"]
+    return r
+
+
+# ---------------------------------------------------------------------------------------
+# CPU baseline: the oracle on the GPU run's own inputs
+# ---------------------------------------------------------------------------------------
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _blas_threads() -> int:
     try:
         from threadpoolctl import threadpool_info
-        blas_threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        return int(max([i.get("num_threads", 1) for i in threadpool_info()] or [1]))
     except Exception:
-        blas_threads = 1
-    cfg = mi.CONFIGS["decode_m8"]
-    L = mi.make_layer(cfg, device="cpu", seed=0, with_experts=False)
+        return 1
+
+
+def _host_inputs(mi, cfg, weights, dev):
+    """The GPU run's inputs of workload cfg, as host bit patterns."""
+    L = mi.make_layer(cfg, device=dev, seed=0, with_experts=False)
     bits = mi.bf16_bits
-    xb, rb = bits(L["x"]), bits(L["residual"])
-    wrb, gb = bits(L["router_w"]), bits(L["norm_w"])
-    ids, _, _ = orc.route(xb, wrb, None, cfg.top_k)
+    return {"x": bits(L["x"]), "residual": bits(L["residual"]),
+            "router_w": bits(weights["router_w"]), "norm_w": bits(weights["norm_w"]),
+            "bias": None if L["router_bias"] is None else L["router_bias"].cpu().numpy(),
+            "eps": L["eps"]}
+
+
+def cpu_decode(mi, weights, dev, runs=3):
+    """The oracle's whole-layer forward (fp64 numpy, plan based) over all tokens of the
+    decode workload, on the GPU's inputs and experts copied to the host; median of runs."""
+    from oracle import moe_oracle as orc
+    cfg = mi.CONFIGS["decode_m8"]
+    h = _host_inputs(mi, cfg, weights, dev)
+    ids, _, _ = orc.route(h["x"], h["router_w"], h["bias"], cfg.top_k)
     need = sorted(set(int(e) for e in ids.ravel()))
-    w13 = {e: bits(mi.expert_w13(cfg, e, "cpu", 0)) for e in need}   # generated before timing
-    w2 = {e: bits(mi.expert_w2(cfg, e, "cpu", 0)) for e in need}
+    w13 = {e: mi.bf16_bits(weights["w13"][e]) for e in need}       # copied before timing
+    w2 = {e: mi.bf16_bits(weights["w2"][e]) for e in need}
     times = []
-    while len(times) < 3 and sum(times) < 20.0:
+    for _ in range(runs):
         t0 = time.perf_counter()
-        orc.forward(xb, wrb, None, w13, w2, rb, gb, cfg.eps, cfg.top_k, cfg.block)
+        orc.forward(h["x"], h["router_w"], h["bias"], w13, w2, h["residual"], h["norm_w"],
+                    h["eps"], cfg.top_k, cfg.block)
         times.append(time.perf_counter() - t0)
     sec = sorted(times)[len(times) // 2]
-    return {
-        "value": cfg.M / sec, "unit": "tokens/s", "cores": int(blas_threads),
-        "kind": "oracle",
-        "sample": (f"decode_m8 workload (host-generated, same recipe): all {cfg.M} tokens through "
-                   f"the whole layer, {len(need)} experts, fp64 numpy with bf16 weights decoded "
-                   f"inside the timed region; median of {len(times)} runs = {sec:.2f} s; "
-                   f"BLAS threads {blas_threads}, host cpus {len(os.sched_getaffinity(0))}"),
+    return sec, len(need), times
+
+
+def cpu_sampled(mi, cfg, weights, dev, n_experts=16, seed=0):
+    """The oracle's steps on the GPU's inputs of a larger workload, with the expert step on
+    a bounded sample: route and align over every token, the up and down projections of the
+    plan blocks of n_experts seeded experts (scaled to all touched experts by their share
+    of plan blocks), the finalize over every token.  Returns the estimated seconds."""
+    import numpy as np
+    from oracle import moe_oracle as orc
+    h = _host_inputs(mi, cfg, weights, dev)
+    t0 = time.perf_counter()
+    ids, w, _ = orc.route(h["x"], h["router_w"], h["bias"], cfg.top_k)
+    sorted_ids, bexp, n_pad, counts, _ = orc.align(ids, cfg.E, cfg.block)
+    t_plan = time.perf_counter() - t0
+    touched = np.nonzero(counts)[0]
+    pick = set(np.random.default_rng(seed).choice(touched, size=min(n_experts, len(touched)),
+                                                  replace=False).tolist())
+    x = orc.bf16_to_f64(h["x"])
+    n = cfg.M * cfg.top_k
+    blocks = [b for b in range(n_pad // cfg.block) if int(bexp[b]) in pick]
+    w13 = {e: mi.bf16_bits(weights["w13"][e]) for e in pick}       # copied before timing
+    w2 = {e: mi.bf16_bits(weights["w2"][e]) for e in pick}
+    y = np.zeros((n, cfg.H))
+    t0 = time.perf_counter()
+    for b in blocks:
+        e = int(bexp[b])
+        rows = sorted_ids[b * cfg.block:(b + 1) * cfg.block]
+        live = rows[rows < n]
+        if live.size:
+            act = orc.expert_swiglu(x[live // cfg.top_k], w13[e], cfg.I)
+            y[live] = orc.expert_down(act, w2[e])
+    t_exp = time.perf_counter() - t0
+    t0 = time.perf_counter()
+    orc.finalize(y, w, h["residual"], h["norm_w"], h["eps"])
+    t_fin = time.perf_counter() - t0
+    all_blocks = n_pad // cfg.block
+    return t_plan + t_exp * all_blocks / max(1, len(blocks)) + t_fin, len(blocks), all_blocks
+
+
+def cpu_baseline(mi, torch, weights, dev, sweep=True):
+    cores = len(os.sched_getaffinity(0))
+    blas = _blas_threads()
+    sec, touched, times = cpu_decode(mi, weights, dev)
+    cfg = mi.CONFIGS["decode_m8"]
+    line = {
+        "value": cfg.M / sec, "unit": "tokens/s", "cores": blas, "kind": "oracle",
+        "sample": (f"decode_m8, the GPU run's own inputs and experts copied to the host: all "
+                   f"{cfg.M} tokens through the oracle's whole layer (fp64 numpy, bf16 weights "
+                   f"decoded inside the timed region), {touched} experts; median of "
+                   f"{len(times)} runs = {sec:.2f} s"),
+        "cpu_model": _cpu_model(), "host_cpus": cores, "blas_threads": blas,
     }
+    if sweep:
+        est = {}
+        for name, runs in (("batch_m128", 3), ("batch_m512", 1), ("prefill_m2048", 1)):
+            c = mi.CONFIGS[name]
+            vals = [cpu_sampled(mi, c, weights, dev, seed=r) for r in range(runs)]
+            s = sorted(v[0] for v in vals)[len(vals) // 2]
+            est[name] = {"value": round(c.M / s, 3), "unit": "tokens/s", "seconds": round(s, 2),
+                         "runs": runs,
+                         "sample": (f"route, align and finalize over all {c.M} tokens; up and "
+                                    f"down projections of the plan blocks of 16 seeded experts "
+                                    f"({vals[0][1]} of {vals[0][2]} blocks), scaled to every "
+                                    f"block")}
+        line["sweep_estimates"] = est
+    return line
 
 
-def read_probe_gbs(torch, dev, gib=4, reps=5, buf=None):
-    """Achievable HBM read rate on this device: best of `reps` timed passes of the read
-    probe (prefill_sigmoid_router_amd/probe/read_bw.hip) over `buf` (a resident tensor,
-    read as raw bytes) or, without one, a fresh `gib` GiB buffer."""
+# ---------------------------------------------------------------------------------------
+# Read probes
+# ---------------------------------------------------------------------------------------
+def _probe_lib():
     import ctypes
     lib = ctypes.CDLL(os.path.join(ROOT, "prefill_sigmoid_router_amd", "libmoe_probe.so"))
     lib.moe_probe_read.restype = ctypes.c_int
     lib.moe_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p,
                                    ctypes.c_void_p]
     lib.moe_probe_read_grid.restype = ctypes.c_int
-    own = buf is None
-    if own:
-        buf = torch.ones((gib << 30) // 4, dtype=torch.int32, device=dev)
-    n = buf.numel() * buf.element_size() // 16 * 16
-    sink = torch.empty(lib.moe_probe_read_grid(), dtype=torch.int32, device=dev)
-    stream = torch.cuda.current_stream()
+    lib.moe_probe_read_lds.restype = ctypes.c_int
+    lib.moe_probe_read_lds.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    return lib
 
-    def once():
-        st = lib.moe_probe_read(ctypes.c_void_p(buf.data_ptr()), n,
-                                ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
-        if st != 0:
-            raise RuntimeError(f"moe_probe_read failed with status {st}")
 
+def _best_ms(torch, stream, once, reps):
     once()
     torch.cuda.synchronize()
     best = float("inf")
@@ -196,22 +360,52 @@ def read_probe_gbs(torch, dev, gib=4, reps=5, buf=None):
         b.record(stream)
         b.synchronize()
         best = min(best, a.elapsed_time(b))
-    del sink
-    if own:
-        del buf
-    return n / (best * 1e-3) / 1e9
+    return best
 
 
-def load_traffic():
-    try:
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-    except (OSError, ValueError):
-        return None
-    src = os.path.join(ROOT, "prefill_sigmoid_router_amd", "csrc", t.get("source_file", ""))
-    if not os.path.isfile(src) or t.get("source_sha256_16") != source_hash(src):
-        return None     # the kernel changed since the counters were taken
-    return t
+def read_probe_gbs(torch, dev, buf, reps=5):
+    """Plain pass: coalesced nontemporal vector loads over `buf`, best of reps."""
+    import ctypes
+    lib = _probe_lib()
+    n = buf.numel() * buf.element_size() // 16 * 16
+    sink = torch.empty(lib.moe_probe_read_grid(), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def once():
+        st = lib.moe_probe_read(ctypes.c_void_p(buf.data_ptr()), n,
+                                ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"moe_probe_read failed with status {st}")
+
+    return n / (_best_ms(torch, stream, once, reps) * 1e-3) / 1e9
+
+
+def read_probe_lds_gbs(torch, dev, w13, reps=5):
+    """The tiled up GEMM's copy path over the W13 stack [E, 2I, H]: nontemporal
+    global_load_lds whole-line copies of items of 128 gate + 128 up rows in the kernel's
+    XCD-aware order, one 4-wave workgroup per CU, no arithmetic, through LDS rings of 3, 4
+    and 5 stages of 32 KiB; the best rate of each ring depth over reps passes."""
+    import ctypes
+    lib = _probe_lib()
+    E, two_i, K = w13.shape
+    grid = torch.cuda.get_device_properties(dev).multi_processor_count // 8 * 8
+    sink = torch.empty(grid, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream()
+    rates = {}
+    for stages in (3, 4, 5):
+        def once():
+            st = lib.moe_probe_read_lds(ctypes.c_void_p(w13.data_ptr()), E, two_i // 2, K, stages,
+                                        grid, ctypes.c_void_p(sink.data_ptr()),
+                                        ctypes.c_void_p(stream.cuda_stream))
+            if st != 0:
+                raise RuntimeError(f"moe_probe_read_lds failed with status {st}")
+
+        rates[stages] = w13.numel() * 2 / (_best_ms(torch, stream, once, reps) * 1e-3) / 1e9
+    return rates
+
+
+def _rounded(r):
+    return {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
 
 
 def main():
@@ -223,7 +417,7 @@ def main():
     ap.add_argument("--no-sweep", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mx", action="store_true",
-                    help="skip the decode leg with MXFP8 expert weights")
+                    help="skip the legs with MXFP8 expert weights")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -264,17 +458,16 @@ def main():
     res = run_workload(B, mi, torch, head, weights, args.steps, args.warmup, dev)
     sweep = {}
     if not args.no_sweep:
-        for name in ("batch_m128", "batch_m512", "prefill_m2048"):
+        for name in SWEEP:
             if name == args.workload:
                 continue
             print(f"bench: timing {name}", file=sys.stderr, flush=True)
-            r = run_workload(B, mi, torch, mi.CONFIGS[name], weights, max(3, args.steps // 2),
-                             max(1, args.warmup // 2), dev)
-            sweep[name] = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+            sweep[name] = run_workload(B, mi, torch, mi.CONFIGS[name], weights,
+                                       max(3, args.steps // 2), max(1, args.warmup // 2), dev)
 
     mx_line = None
     if not args.no_mx:
-        # the same decode layer with MXFP8 expert weights (quantized on the device)
+        # the same layer with MXFP8 expert weights (quantized on the device)
         print("bench: quantizing the experts to MXFP8 and timing decode_m8", file=sys.stderr,
               flush=True)
         mx = []
@@ -286,53 +479,49 @@ def main():
             B.moe_mx_quantize(w, c, sc)
             mx += [c, sc]
         torch.cuda.synchronize()
-        r = run_workload(B, mi, torch, mi.CONFIGS["decode_m8"], weights, args.steps, args.warmup,
-                         dev, mx=mx)
-        mx_line = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+        dcfg = mi.CONFIGS["decode_m8"]
+        r = run_workload(B, mi, torch, dcfg, weights, args.steps, args.warmup, dev, mx=mx)
+        mx_line = _rounded(r)
         mx_line["weights"] = "MXFP8 (E4M3 + E8M0 per 32 values along K), activations bf16"
-        mx_line["up_kernel"] = "expert_mx_decode_kernel<true> (codes copied into LDS, 32-row tiles)"
+        mx_line["up_kernel"] = up_kernel_name(B, dcfg, mx=True)
         mx_line["up_hbm_frac"] = round(r["up_gbs"] / HBM_PEAK_GBS, 4)
         if not args.no_sweep:
             mx_sweep = {}
-            for name in ("batch_m128", "batch_m512", "prefill_m2048"):
+            for name in SWEEP:
                 print(f"bench: timing {name} with MXFP8 experts", file=sys.stderr, flush=True)
-                rs = run_workload(B, mi, torch, mi.CONFIGS[name], weights, max(3, args.steps // 2),
+                c = mi.CONFIGS[name]
+                rs = run_workload(B, mi, torch, c, weights, max(3, args.steps // 2),
                                   max(1, args.warmup // 2), dev, mx=mx)
-                mx_sweep[name] = {k: (round(v, 4) if isinstance(v, float) else v)
-                                  for k, v in rs.items()}
-                mx_sweep[name]["tile_rows"] = B.moe_gemm_tile_rows_mx(
-                    rs["M"], head.E, head.top_k, head.I)
+                mx_sweep[name] = _rounded(rs)
+                mx_sweep[name]["tile_rows"] = B.moe_gemm_tile_rows_mx(c.M, c.E, c.top_k, c.I)
+                mx_sweep[name]["up_kernel"] = up_kernel_name(B, c, mx=True)
+                mx_sweep[name]["up_hbm_frac"] = round(rs["up_gbs"] / HBM_PEAK_GBS, 4)
             mx_line["sweep"] = mx_sweep
         del mx
         torch.cuda.empty_cache()
 
-    # the read probe over the resident W13 (the bytes the up GEMM streams)
-    print("bench: timing the HBM read probe", file=sys.stderr, flush=True)
-    read_gbs = read_probe_gbs(torch, dev, buf=weights["w13"])
-    traffic = load_traffic()
-    rows = B.moe_gemm_tile_rows(head.M, head.E, head.top_k, head.I)
-    if B.moe_forward_self_routes(head.M, head.E, head.top_k, head.I):
-        up_kernel = f"expert_up_selfroute_kernel<{rows}, ...>, align fused in,"
-    elif rows == 16:
-        up_kernel = "expert_up_stream_kernel"
-    else:
-        up_kernel = f"expert_tiled_kernel<{rows}, ..., true, ...>"
-    if traffic is not None and traffic.get("workload") != head.name:
-        traffic = None  # counters were taken on another workload
-    roof = {
-        "bound": "hbm", "kernel": f"{up_kernel} (grouped up-GEMM + SwiGLU)",
-        "achieved": round(res["up_gbs"], 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(res["up_gbs"] / HBM_PEAK_GBS, 4),
-        "traffic": None if traffic is None else traffic.get("traffic_gbs"),
-        "traffic_bytes_per_launch": None if traffic is None else traffic.get("traffic_bytes_per_launch"),
-        "algorithmic_bytes_per_launch": res["up_bytes"], "avg_launch_us": round(res["up_us"], 2),
-        "measured_read_peak": round(read_gbs, 1),
-        "frac_of_measured_read": round(res["up_gbs"] / read_gbs, 4),
-    }
+    # read probes over the resident W13 (the bytes the up GEMM streams)
+    print("bench: timing the HBM read probes", file=sys.stderr, flush=True)
+    plain_gbs = read_probe_gbs(torch, dev, weights["w13"])
+    lds_rates = read_probe_lds_gbs(torch, dev, weights["w13"])
+    read_gbs = max(plain_gbs, *lds_rates.values())
+
+    roof = roofline(res, up_kernel_name(B, head), read_gbs,
+                    load_profile(f"traffic_expert_up_{head.name}.json", head.name))
+    roof["read_probes_gbs"] = {"plain_nontemporal_loads": round(plain_gbs, 1)}
+    for stages, g in lds_rates.items():
+        roof["read_probes_gbs"][f"global_load_lds_nt_ring_{stages}_stages"] = round(g, 1)
+    sweep_out = {}
+    for name, r in sweep.items():
+        c = mi.CONFIGS[name]
+        sweep_out[name] = _rounded(r)
+        sweep_out[name]["roofline"] = roofline(r, up_kernel_name(B, c), read_gbs,
+                                               load_profile(f"traffic_expert_up_{name}.json", name))
+
     cpu = None
     if not args.no_cpu_baseline:
-        print("bench: timing the CPU oracle sample", file=sys.stderr, flush=True)
-        cpu = cpu_baseline(mi, torch)
+        print("bench: timing the CPU oracle", file=sys.stderr, flush=True)
+        cpu = cpu_baseline(mi, torch, weights, dev, sweep=not args.no_sweep)
 
     line = {
         "metric": METRIC,
@@ -354,12 +543,13 @@ def main():
                    "touched_experts": res["touched_experts"], "plan_rows": res["plan_rows"],
                    "parallelism": "single GPU"},
         "stages_us": res["stages_us"],
+        "align": res["align"],
         "layer_hbm_frac": round(res["layer_hbm_frac"], 4),
         "layer_gbs": round(res["layer_gbs"], 1),
         "layer_frac_of_measured_read": round(res["layer_gbs"] / read_gbs, 4),
         "roofline": roof,
         "cpu_baseline": cpu,
-        "sweep": sweep,
+        "sweep": sweep_out,
         "mxfp8_decode": mx_line,
     }
     print(json.dumps(line), flush=True)

@@ -99,7 +99,10 @@ SMALL = {
     "hmod8_many": mi.LayerConfig("hmod8_many", M=300, H=328, E=8, top_k=4, I=256, block=64,
                                  zipf_s=1.0),
     # the per-token bf16 finalize with two 8-value groups per thread (8192 < H <= 16384)
-    "fin_h16384": mi.LayerConfig("fin_h16384", M=256, H=16384, E=4, top_k=2, I=64, block=16),
+    # (weights N(0, 0.01): at H=16384 N(0, 0.02) weights make |y| large enough that its bf16
+    # rounding plus the half-ulp of |z| >= 4 passes the 2e-2 bar by itself)
+    "fin_h16384": mi.LayerConfig("fin_h16384", M=256, H=16384, E=4, top_k=2, I=64, block=16,
+                                 w_std=0.01),
     # the per-token finalize with a second batch of picks (top_k > 8) from 256 tokens
     "fin_topk12": mi.LayerConfig("fin_topk12", M=264, H=256, E=32, top_k=12, I=256, block=32),
 }

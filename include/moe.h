@@ -194,6 +194,30 @@ int moe_forward(const uint16_t* x, const uint16_t* router_w, const float* router
                 const moe_event_t* stage_events, moe_stream_t stream);
 
 /*
+ * moe_forward for callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc): the same five steps and outputs as
+ * moe_forward, with the workspace taken from a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on until the process
+ * ends.  It allocates nothing and takes no workspace or stage events.  Sizes whose
+ * moe_workspace_bytes exceed MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_WORKSPACE before
+ * anything is launched (the real-shape layer, H=7168, E=256, top_k=16, I=2048, fits up to
+ * 154 tokens with block 16, 15 with block 64).  Every call on a GPU shares that GPU's array,
+ * which keeps the last call's contents (nothing in it needs to start at zero): calls that
+ * overlap on one GPU -- on different streams, or from different host threads -- race and
+ * must be ordered by the caller.  The first call on a device looks up that device's array
+ * address (hipGetSymbolAddress) with the device current; a failed lookup is MOE_ERR_HIP.
+ */
+#define MOE_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_forward_noalloc(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
+                        const uint16_t* w13, const uint16_t* w2,
+                        const uint16_t* residual, const uint16_t* norm_w, float eps,
+                        int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k, int32_t block,
+                        uint16_t* out, uint16_t* residual_out,
+                        int32_t* topk_ids_out, float* topk_w_out,
+                        int32_t* sorted_ids_out, int32_t* block_expert_out,
+                        int32_t* num_padded_out, moe_stream_t stream);
+
+/*
  * MXFP8 expert weights.  The AlphaMoE page (FlashInfer PR #6511 analysis, section 1)
  * streams block-scaled narrow expert weights to cut the bytes of a decode step and gives
  * no recipe; the one here is the OCP Microscaling (MX) v1.0 conversion with FP8 E4M3

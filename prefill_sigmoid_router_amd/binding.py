@@ -19,7 +19,7 @@ __all__ = [
     "moe_workspace_bytes", "moe_route", "moe_align", "moe_expert_up", "moe_expert_down",
     "moe_finalize", "moe_forward", "moe_mx_quantize", "moe_mx_dequantize", "moe_forward_mx",
     "moe_gemm_tile_rows", "moe_gemm_tile_rows_mx", "moe_forward_self_routes",
-    "HipEvent",
+    "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "HipEvent",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -51,6 +51,9 @@ _PROTOS = {
     "moe_forward": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, ctypes.c_float,
                                    _i32, _i32, _i32, _i32, _i32, _i32,
                                    _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
+    "moe_forward_noalloc": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, ctypes.c_float,
+                                           _i32, _i32, _i32, _i32, _i32, _i32,
+                                           _p, _p, _p, _p, _p, _p, _p, _p]),
     "moe_mx_quantize": (ctypes.c_int, [_p, ctypes.c_int64, _i32, _p, _p, _p]),
     "moe_mx_dequantize": (ctypes.c_int, [_p, _p, ctypes.c_int64, _i32, _p, _p]),
     "moe_forward_mx": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float,
@@ -284,6 +287,52 @@ def moe_forward(x, router_w, router_bias, w13, w2, residual, norm_w, eps: float,
         _ptr(norm_w), float(eps), M, H, E, I, top_k, block, _ptr(out), _ptr(residual_out),
         _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(sorted_ids_out), _ptr(block_expert_out),
         _ptr(num_padded_out), _ptr(workspace), workspace.numel(), ev, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h
+
+
+def moe_forward_noalloc(x, router_w, router_bias, w13, w2, residual, norm_w, eps: float,
+                        top_k: int, block: int, out, residual_out=None, topk_ids_out=None,
+                        topk_w_out=None, sorted_ids_out=None, block_expert_out=None,
+                        num_padded_out=None, stream=None):
+    """moe_forward with the library's static per-GPU scratch instead of a workspace (for
+    callers that cannot allocate); sizes whose workspace exceeds NOALLOC_SCRATCH_BYTES
+    fail with MOE_ERR_WORKSPACE.  Calls that overlap on one GPU race."""
+    M, H = x.shape
+    E, two_i, _ = w13.shape
+    I = two_i // 2
+    _need(x, "x", torch.bfloat16)
+    _need(router_w, "router_w", torch.bfloat16, (E, H))
+    if router_bias is not None:
+        _need(router_bias, "router_bias", torch.float32, (E,))
+    _need(w13, "w13", torch.bfloat16, (E, 2 * I, H))
+    _need(w2, "w2", torch.bfloat16, (E, H, I))
+    _need(residual, "residual", torch.bfloat16, (M, H))
+    _need(norm_w, "norm_w", torch.bfloat16, (H,))
+    _need(out, "out", torch.bfloat16, (M, H))
+    if residual_out is not None:
+        _need(residual_out, "residual_out", torch.bfloat16, (M, H))
+    cap = moe_align_capacity(M, top_k, E, block)
+    if topk_ids_out is not None:
+        _need(topk_ids_out, "topk_ids_out", torch.int32, (M, top_k))
+    if topk_w_out is not None:
+        _need(topk_w_out, "topk_w_out", torch.float32, (M, top_k))
+    if sorted_ids_out is not None:
+        _need(sorted_ids_out, "sorted_ids_out", torch.int32)
+        if sorted_ids_out.numel() < cap:
+            raise ValueError("sorted_ids_out smaller than the plan capacity")
+    if block_expert_out is not None:
+        _need(block_expert_out, "block_expert_out", torch.int32)
+        if block_expert_out.numel() < cap // block:
+            raise ValueError("block_expert_out smaller than capacity / block")
+    if num_padded_out is not None:
+        _need(num_padded_out, "num_padded_out", torch.int32)
+    _check("moe_forward_noalloc", load_library().moe_forward_noalloc(
+        _ptr(x), _ptr(router_w), _ptr(router_bias), _ptr(w13), _ptr(w2), _ptr(residual),
+        _ptr(norm_w), float(eps), M, H, E, I, top_k, block, _ptr(out), _ptr(residual_out),
+        _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(sorted_ids_out), _ptr(block_expert_out),
+        _ptr(num_padded_out), _stream(stream)))
 
 
 def moe_mx_quantize(w, codes, scales, stream=None):

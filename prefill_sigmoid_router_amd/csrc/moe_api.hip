@@ -4,6 +4,8 @@
 #include <math.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "launchers.h"
 
@@ -240,6 +242,30 @@ int moe_finalize(const float* y, const float* topk_w, const uint16_t* residual,
 
 namespace {
 
+// Scratch of moe_forward_noalloc, for callers that cannot allocate: one static array per
+// GPU the library runs on (each device holds its own copy until the process ends).  In host
+// code `scratch` names a host-side stand-in, never a device address: the device address of
+// each GPU's copy comes from hipGetSymbolAddress, taken once per device with that device
+// current, and only that address is handed to kernels.
+__device__ __align__(256) unsigned char scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// The current device's scratch address (MOE_ERR_HIP if the device or the symbol lookup fails).
+int device_scratch(void** ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return MOE_ERR_HIP;
+  std::call_once(g_scratch_once[dev], [dev] {
+    g_scratch_err[dev] = hipGetSymbolAddress(&g_scratch_ptr[dev], HIP_SYMBOL(scratch));
+  });
+  if (g_scratch_err[dev] != hipSuccess || g_scratch_ptr[dev] == nullptr) return MOE_ERR_HIP;
+  *ptr = g_scratch_ptr[dev];
+  return MOE_OK;
+}
+
 // Expert weights of one call: bf16 (w13, w2) or MXFP8 (codes and scale bytes).
 struct ExpertWeights {
   const uint16_t* w13 = nullptr;
@@ -389,6 +415,31 @@ int moe_forward_mx(const uint16_t* x, const uint16_t* router_w, const float* rou
   return forward_impl(x, router_w, router_bias, W, residual, norm_w, eps, M, H, E, I, top_k, block,
                       out, residual_out, topk_ids_out, topk_w_out, sorted_ids_out,
                       block_expert_out, num_padded_out, workspace, workspace_bytes, stage_events,
+                      stream);
+}
+
+int moe_forward_noalloc(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
+                        const uint16_t* w13, const uint16_t* w2, const uint16_t* residual,
+                        const uint16_t* norm_w, float eps, int32_t M, int32_t H, int32_t E,
+                        int32_t I, int32_t top_k, int32_t block, uint16_t* out,
+                        uint16_t* residual_out, int32_t* topk_ids_out, float* topk_w_out,
+                        int32_t* sorted_ids_out, int32_t* block_expert_out,
+                        int32_t* num_padded_out, moe_stream_t stream) {
+  if (!sizes_ok(M, H, E, I, top_k) || !(eps > 0.0f) || !isfinite(eps)) return MOE_ERR_INVALID_ARG;
+  if (!gemm_block_ok(block)) return MOE_ERR_UNSUPPORTED;
+  if (M == 0) return MOE_OK;
+  // the sizes' workspace must fit the static scratch: checked before anything runs
+  const Layout L = layout_of(M, H, E, I, top_k, block);
+  if (L.total > MOE_NOALLOC_SCRATCH_BYTES) return MOE_ERR_WORKSPACE;
+  void* ws = nullptr;
+  const int st = device_scratch(&ws);
+  if (st != MOE_OK) return st;
+  ExpertWeights W;
+  W.w13 = w13;
+  W.w2 = w2;
+  return forward_impl(x, router_w, router_bias, W, residual, norm_w, eps, M, H, E, I, top_k, block,
+                      out, residual_out, topk_ids_out, topk_w_out, sorted_ids_out,
+                      block_expert_out, num_padded_out, ws, MOE_NOALLOC_SCRATCH_BYTES, nullptr,
                       stream);
 }
 

@@ -88,9 +88,10 @@ def down_flops(cfg, M):
     return 2 * M * cfg.top_k * cfg.I * cfg.H
 
 
-def run_workload(B, mi, torch, cfg, weights, steps, warmup, dev, mx=None):
-    """Times moe_forward (bf16 experts), or moe_forward_mx when `mx` holds the MXFP8
-    (w13 codes, w13 scales, w2 codes, w2 scales)."""
+def run_workload(B, mi, torch, cfg, weights, steps, warmup, dev, mx=None, prepared=None):
+    """Times moe_forward (bf16 experts), moe_forward_mx when `mx` holds the MXFP8
+    (w13 codes, w13 scales, w2 codes, w2 scales), or moe_forward_prepared when `prepared`
+    holds the prepared (w13, w2) stacks."""
     L = mi.make_layer(cfg, device=dev, seed=0, with_experts=False)
     L.update(weights)
     M, H, E, I, k, blk = cfg.M, cfg.H, cfg.E, cfg.I, cfg.top_k, cfg.block
@@ -100,7 +101,11 @@ def run_workload(B, mi, torch, cfg, weights, steps, warmup, dev, mx=None):
     stream = torch.cuda.current_stream()
 
     def step(events=None):
-        if mx is None:
+        if prepared is not None:
+            B.moe_forward_prepared(L["x"], L["router_w"], L["router_bias"], prepared[0],
+                                   prepared[1], I, L["residual"], L["norm_w"], L["eps"], k, blk,
+                                   out, ws, topk_ids_out=ids, stage_events=events, stream=stream)
+        elif mx is None:
             B.moe_forward(L["x"], L["router_w"], L["router_bias"], L["w13"], L["w2"],
                           L["residual"], L["norm_w"], L["eps"], k, blk, out, ws,
                           topk_ids_out=ids, stage_events=events, stream=stream)
@@ -138,7 +143,7 @@ def run_workload(B, mi, torch, cfg, weights, steps, warmup, dev, mx=None):
     ub = up_bytes(cfg, M, touched, mx is not None)
     db = down_bytes(cfg, M, touched, mx is not None)
     stages = {n: round(v * 1e3, 2) for n, v in stage_ms.items()}
-    self_routed = mx is None and B.moe_forward_self_routes(M, E, k, I)
+    self_routed = mx is None and prepared is None and B.moe_forward_self_routes(M, E, k, I)
     if self_routed:
         # the up GEMM builds the plan: no align kernel runs, the event pair encloses none
         stages["align"] = None
@@ -418,6 +423,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-mx", action="store_true",
                     help="skip the legs with MXFP8 expert weights")
+    ap.add_argument("--no-prepared", action="store_true",
+                    help="skip the legs on prepared (fragment-panel) weights")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -500,6 +507,35 @@ def main():
         del mx
         torch.cuda.empty_cache()
 
+    prep_line = None
+    if not args.no_prepared:
+        # the same layer on weights re-laid-out once into fragment panels (moe_forward_prepared)
+        print("bench: preparing fragment-panel weights", file=sys.stderr, flush=True)
+        E, H, I = head.E, head.H, head.I
+        p13 = torch.empty(B.moe_prepared_w13_bytes(E, H, I) // 2, dtype=torch.bfloat16, device=dev)
+        p2 = torch.empty(B.moe_prepared_w2_bytes(E, H, I) // 2, dtype=torch.bfloat16, device=dev)
+        B.moe_prepare_weights(weights["w13"], weights["w2"], p13, p2)
+        torch.cuda.synchronize()
+        prep_line = {}
+        for name in (head.name,) + (() if args.no_sweep else SWEEP):
+            if name in prep_line:
+                continue
+            print(f"bench: timing {name} on prepared weights", file=sys.stderr, flush=True)
+            c = mi.CONFIGS[name]
+            quick = name != head.name
+            r = run_workload(B, mi, torch, c, weights,
+                             max(3, args.steps // 2) if quick else args.steps,
+                             max(1, args.warmup // 2) if quick else args.warmup, dev,
+                             prepared=(p13, p2))
+            prep_line[name] = _rounded(r)
+            prep_line[name]["up_hbm_frac"] = round(r["up_gbs"] / HBM_PEAK_GBS, 4)
+            prep_line[name]["up_mfma_frac"] = round(r["up_tflops"] / BF16_PEAK_TFLOPS, 4)
+            prep_line[name]["down_hbm_frac"] = round(r["down_gbs"] / HBM_PEAK_GBS, 4)
+            prep_line[name]["up_kernel"] = (
+                f"expert_frag_kernel<{B.moe_gemm_tile_rows(c.M, c.E, c.top_k, c.I)}, true, ...>")
+        del p13, p2
+        torch.cuda.empty_cache()
+
     # read probes over the resident W13 (the bytes the up GEMM streams)
     print("bench: timing the HBM read probes", file=sys.stderr, flush=True)
     plain_gbs = read_probe_gbs(torch, dev, weights["w13"])
@@ -551,6 +587,7 @@ def main():
         "cpu_baseline": cpu,
         "sweep": sweep_out,
         "mxfp8_decode": mx_line,
+        "prepared_weights": prep_line,
     }
     print(json.dumps(line), flush=True)
 

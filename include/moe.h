@@ -194,6 +194,42 @@ int moe_forward(const uint16_t* x, const uint16_t* router_w, const float* router
                 const moe_event_t* stage_events, moe_stream_t stream);
 
 /*
+ * Prepared expert weights: the offline weight re-layout of the AlphaMoE page (FlashInfer
+ * PR #6511 analysis, section 2, where the down kernel streams W2 from panels prepared once).
+ * moe_prepare_weights re-lays the natural stacks W13 [E, 2I, H] and W2 [E, H, I] out once
+ * into "fragment panels": for every expert and N tile of the grouped GEMMs (256 act columns
+ * = 512 W13 rows, gate and up rows interleaved; 512 W2 rows), each of the GEMM's 8 waves
+ * finds the MFMA operand fragments of its 64 weight rows for consecutive 32-wide K steps in
+ * one contiguous stream, so every weight load is 1 KiB of contiguous memory that lands
+ * directly in registers.  Layout (bf16, last index fastest):
+ *   W13p [E][I/256][8][H/32][4][64][8]: tile j of wave w, N tile n holds rows
+ *        n*256 + 32w + 16j + l%16 (j < 2, gate) or I + n*256 + 32w + 16(j-2) + l%16 (up)
+ *        for lane l, K values 32 s + 8 (l / 16) + v of step s;
+ *   W2p  [E][ceil(H/512)][8][I/32][4][64][8]: rows n*512 + 64w + 16j + l%16 (zero past H).
+ * Needs H % 64 == 0 and I % 256 == 0 (MOE_ERR_UNSUPPORTED otherwise; the *_bytes queries
+ * return 0).  The caller allocates the prepared stacks (moe_prepared_w13_bytes /
+ * moe_prepared_w2_bytes bytes); either pair (w13, w13_prepared) or (w2, w2_prepared) may be
+ * NULL to prepare only the other.  Asynchronous on `stream`; allocates nothing.
+ *
+ * moe_forward_prepared is moe_forward on the prepared stacks, with the same arguments,
+ * workspace and results (it always runs the align kernel: the self-routing up kernel reads
+ * the natural layout).
+ */
+size_t moe_prepared_w13_bytes(int32_t E, int32_t H, int32_t I);
+size_t moe_prepared_w2_bytes(int32_t E, int32_t H, int32_t I);
+int moe_prepare_weights(const uint16_t* w13, const uint16_t* w2, int32_t E, int32_t H, int32_t I,
+                        uint16_t* w13_prepared, uint16_t* w2_prepared, moe_stream_t stream);
+int moe_forward_prepared(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
+                         const uint16_t* w13_prepared, const uint16_t* w2_prepared,
+                         const uint16_t* residual, const uint16_t* norm_w, float eps,
+                         int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k, int32_t block,
+                         uint16_t* out, uint16_t* residual_out,
+                         int32_t* topk_ids_out, float* topk_w_out,
+                         int32_t* sorted_ids_out, int32_t* block_expert_out, int32_t* num_padded_out,
+                         void* workspace, size_t workspace_bytes,
+                         const moe_event_t* stage_events, moe_stream_t stream);
+
+/*
  * moe_forward for callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): the same five steps and outputs as
  * moe_forward, with the workspace taken from a static device array of

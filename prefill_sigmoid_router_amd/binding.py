@@ -19,7 +19,8 @@ __all__ = [
     "moe_workspace_bytes", "moe_route", "moe_align", "moe_expert_up", "moe_expert_down",
     "moe_finalize", "moe_forward", "moe_mx_quantize", "moe_mx_dequantize", "moe_forward_mx",
     "moe_gemm_tile_rows", "moe_gemm_tile_rows_mx", "moe_forward_self_routes",
-    "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "HipEvent",
+    "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "moe_prepared_w13_bytes",
+    "moe_prepared_w2_bytes", "moe_prepare_weights", "moe_forward_prepared", "HipEvent",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -54,6 +55,12 @@ _PROTOS = {
     "moe_forward_noalloc": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, ctypes.c_float,
                                            _i32, _i32, _i32, _i32, _i32, _i32,
                                            _p, _p, _p, _p, _p, _p, _p, _p]),
+    "moe_prepared_w13_bytes": (_sz, [_i32, _i32, _i32]),
+    "moe_prepared_w2_bytes": (_sz, [_i32, _i32, _i32]),
+    "moe_prepare_weights": (ctypes.c_int, [_p, _p, _i32, _i32, _i32, _p, _p, _p]),
+    "moe_forward_prepared": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, ctypes.c_float,
+                                            _i32, _i32, _i32, _i32, _i32, _i32,
+                                            _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
     "moe_mx_quantize": (ctypes.c_int, [_p, ctypes.c_int64, _i32, _p, _p, _p]),
     "moe_mx_dequantize": (ctypes.c_int, [_p, _p, ctypes.c_int64, _i32, _p, _p]),
     "moe_forward_mx": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float,
@@ -287,6 +294,92 @@ def moe_forward(x, router_w, router_bias, w13, w2, residual, norm_w, eps: float,
         _ptr(norm_w), float(eps), M, H, E, I, top_k, block, _ptr(out), _ptr(residual_out),
         _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(sorted_ids_out), _ptr(block_expert_out),
         _ptr(num_padded_out), _ptr(workspace), workspace.numel(), ev, _stream(stream)))
+
+
+def moe_prepared_w13_bytes(E: int, H: int, I: int) -> int:
+    return int(load_library().moe_prepared_w13_bytes(E, H, I))
+
+
+def moe_prepared_w2_bytes(E: int, H: int, I: int) -> int:
+    return int(load_library().moe_prepared_w2_bytes(E, H, I))
+
+
+def moe_prepare_weights(w13, w2, w13_prepared, w2_prepared, stream=None):
+    """Re-lay W13 [E, 2I, H] / W2 [E, H, I] out into the fragment panels moe_forward_prepared
+    streams.  The prepared tensors are bf16 device tensors of moe_prepared_w13_bytes /
+    moe_prepared_w2_bytes bytes (any shape, e.g. torch.empty_like(w13)); a (w, w_prepared)
+    pair may be None to prepare only the other."""
+    ref = w13 if w13 is not None else w2
+    if ref is None:
+        raise ValueError("nothing to prepare")
+    if w13 is not None:
+        E, two_i, H = w13.shape
+        I = two_i // 2
+    else:
+        E, H, I = w2.shape
+    for name, w, wp, shape, nbytes in (
+            ("w13", w13, w13_prepared, (E, 2 * I, H), moe_prepared_w13_bytes(E, H, I)),
+            ("w2", w2, w2_prepared, (E, H, I), moe_prepared_w2_bytes(E, H, I))):
+        if (w is None) != (wp is None):
+            raise ValueError(f"{name} and {name}_prepared must be given together")
+        if w is not None:
+            _need(w, name, torch.bfloat16, shape)
+            _need(wp, name + "_prepared", torch.bfloat16)
+            if nbytes == 0 or wp.numel() * 2 < nbytes:
+                raise ValueError(f"{name}_prepared must hold {nbytes} bytes (H % 64, I % 256)")
+    _check("moe_prepare_weights", load_library().moe_prepare_weights(
+        _ptr(w13), _ptr(w2), E, H, I, _ptr(w13_prepared), _ptr(w2_prepared), _stream(stream)))
+
+
+def moe_forward_prepared(x, router_w, router_bias, w13_prepared, w2_prepared, I: int, residual,
+                         norm_w, eps: float, top_k: int, block: int, out, workspace,
+                         residual_out=None, topk_ids_out=None, topk_w_out=None,
+                         sorted_ids_out=None, block_expert_out=None, num_padded_out=None,
+                         stage_events: Optional[Sequence["HipEvent"]] = None, stream=None):
+    """moe_forward on the prepared stacks of moe_prepare_weights (intermediate size I)."""
+    M, H = x.shape
+    E = router_w.shape[0]
+    _need(x, "x", torch.bfloat16)
+    _need(router_w, "router_w", torch.bfloat16, (E, H))
+    if router_bias is not None:
+        _need(router_bias, "router_bias", torch.float32, (E,))
+    _need(w13_prepared, "w13_prepared", torch.bfloat16)
+    _need(w2_prepared, "w2_prepared", torch.bfloat16)
+    n13, n2 = moe_prepared_w13_bytes(E, H, I), moe_prepared_w2_bytes(E, H, I)
+    if n13 == 0 or w13_prepared.numel() * 2 < n13 or w2_prepared.numel() * 2 < n2:
+        raise ValueError("prepared stacks smaller than moe_prepared_w13/w2_bytes (H % 64, I % 256)")
+    _need(residual, "residual", torch.bfloat16, (M, H))
+    _need(norm_w, "norm_w", torch.bfloat16, (H,))
+    _need(out, "out", torch.bfloat16, (M, H))
+    _need(workspace, "workspace", torch.uint8)
+    if residual_out is not None:
+        _need(residual_out, "residual_out", torch.bfloat16, (M, H))
+    cap = moe_align_capacity(M, top_k, E, block)
+    if topk_ids_out is not None:
+        _need(topk_ids_out, "topk_ids_out", torch.int32, (M, top_k))
+    if topk_w_out is not None:
+        _need(topk_w_out, "topk_w_out", torch.float32, (M, top_k))
+    if sorted_ids_out is not None:
+        _need(sorted_ids_out, "sorted_ids_out", torch.int32)
+        if sorted_ids_out.numel() < cap:
+            raise ValueError("sorted_ids_out smaller than the plan capacity")
+    if block_expert_out is not None:
+        _need(block_expert_out, "block_expert_out", torch.int32)
+        if block_expert_out.numel() < cap // block:
+            raise ValueError("block_expert_out smaller than capacity / block")
+    if num_padded_out is not None:
+        _need(num_padded_out, "num_padded_out", torch.int32)
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != 6:
+            raise ValueError("stage_events must hold 6 events")
+        ev = (ctypes.c_void_p * 6)(*[e.handle for e in stage_events])
+    _check("moe_forward_prepared", load_library().moe_forward_prepared(
+        _ptr(x), _ptr(router_w), _ptr(router_bias), _ptr(w13_prepared), _ptr(w2_prepared),
+        _ptr(residual), _ptr(norm_w), float(eps), M, H, E, I, top_k, block, _ptr(out),
+        _ptr(residual_out), _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(sorted_ids_out),
+        _ptr(block_expert_out), _ptr(num_padded_out), _ptr(workspace), workspace.numel(), ev,
+        _stream(stream)))
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     const int32_t* __restrict__ ids, int n, int E, int block, int id_bits,
     int32_t* __restrict__ sorted_ids, int32_t* __restrict__ block_expert,
     int32_t* __restrict__ num_padded, int tile_rows, int2* __restrict__ tiles,
-    int32_t* __restrict__ num_tiles) {
+    int32_t* __restrict__ num_tiles, int2* __restrict__ tile_groups) {
   __shared__ int32_t cnt[kAlignWaves][kAlignMaxE];  // count, then cursor, per (wave, expert)
   __shared__ int32_t prefix[kAlignMaxE + 1];
   __shared__ int32_t wave_total[kAlignWaves];
@@ -165,6 +165,8 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
       for (int j = 0; j < ntile_e; ++j) {
         const int left = total - j * tile_rows;
         tiles[first + j] = make_int2(excl + j * tile_rows, left < tile_rows ? left : tile_rows);
+        // optional: each tile's expert as {its first tile, its tile count}
+        if (tile_groups != nullptr) tile_groups[first + j] = make_int2(first, ntile_e);
       }
     }
     if (tid == 0) *num_tiles = all_tiles;
@@ -173,11 +175,12 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
 
 hipError_t launch_align(const int32_t* ids, int n, int E, int block, int32_t* sorted_ids,
                         int32_t* block_expert, int32_t* num_padded, int tile_rows, int2* tiles,
-                        int32_t* num_tiles, hipStream_t s) {
+                        int32_t* num_tiles, hipStream_t s, int2* tile_groups) {
   int id_bits = 0;
   while ((1 << id_bits) < E) ++id_bits;
   hipLaunchKernelGGL(align_kernel, dim3(1), dim3(kAlignThreads), 0, s, ids, n, E, block, id_bits,
-                     sorted_ids, block_expert, num_padded, tile_rows, tiles, num_tiles);
+                     sorted_ids, block_expert, num_padded, tile_rows, tiles, num_tiles,
+                     tile_groups);
   return hipGetLastError();
 }
 

@@ -1,0 +1,426 @@
+// Grouped expert GEMMs on prepared weights (the offline weight re-layout of the AlphaMoE
+// page, FlashInfer PR #6511 analysis, section 2: the down kernel streams W2 from panels
+// prepared once, prepare_*_k256).  Here the panels are laid out in MFMA-fragment order so
+// that every weight load of a wave is 1 KiB of contiguous memory -- eight whole 128-byte
+// lines -- that lands directly in the A operand of v_mfma_f32_16x16x32_bf16: no LDS staging,
+// no barrier between the waves for weights.  Only the token rows, which all 8 waves share,
+// go through an LDS ring (whole-line global_load_lds copies, XOR-swizzled, as in the tiled
+// kernels).
+//
+// Prepared layout (bf16, 16-byte groups of 8 values; "frag" = 64 lanes x 16 bytes):
+//   W13p [E][I/256][8 waves][H/32 K steps][4 tiles][64 lanes][8 values]
+//        wave w, N tile n, tile j: rows n*256 + 32w + 16j + lane%16 of the gate half (j < 2)
+//        or I + n*256 + 32w + 16(j-2) + lane%16 of the up half (j >= 2);
+//        K values 32 s + 8 (lane / 16) + v of step s.
+//   W2p  [E][ceil(H/512)][8][I/32][4][64][8]
+//        rows n*512 + 64w + 16j + lane%16 (zero past H), K values as above.
+// A wave's whole weight stream for one (expert, N tile) is contiguous: (K/32) x 4 KiB.
+//
+// Workgroup = 8 waves; item = one token tile (BM = 64 or 128 plan rows of one expert) x one
+// N tile (up: 256 act columns = 512 weight rows; down: 512 output columns).  Wave w owns 4
+// weight row tiles (64 rows) x all BM/16 token tiles.  Per MFMA K step of 32 values a wave
+// loads its 4 weight fragments (4 KiB) into a register ring of RS steps (the weights of
+// RS - 1 steps, 16 KiB per wave and 128 KiB per CU, in flight while one step is computed),
+// and per K chunk of 64 values 2 (BM = 128) or 1 (BM = 64) 1 KiB token copies into an LDS
+// ring of TS stages.
+#include <algorithm>
+
+#include "device_common.h"
+#include "launchers.h"
+#include "tiled_common.h"
+
+namespace moe {
+
+constexpr int kFragWaves = 8;
+constexpr int kFragKC = 64;            // K values per chunk (2 MFMA K steps)
+constexpr int kFragRS = 4;             // weight register ring, in K steps of 32 values
+constexpr int kFragTS = 4;             // token LDS ring stages
+
+int frag_up_columns() { return 256; }
+
+// ---------------------------------------------------------------------------------------
+// Preparation: natural row-major [rows, K] stacks -> fragment panels.  One thread per
+// 16-byte group of the output; it reads the 16 bytes (8 consecutive K values of one row)
+// from the natural layout.  Rows past the weight (W2 with H not a multiple of 512) are 0.
+// ---------------------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void prepare_w13_kernel(const uint16_t* __restrict__ w13,
+                                                          int E, int H, int I,
+                                                          uint16_t* __restrict__ out) {
+  const size_t groups = (size_t)E * 2 * I * H / 8;
+  const int steps = H / 32;
+  for (size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups;
+       g += (size_t)gridDim.x * blockDim.x) {
+    size_t r = g;
+    const int lane = (int)(r % 64); r /= 64;
+    const int j = (int)(r % 4); r /= 4;
+    const int s = (int)(r % steps); r /= steps;
+    const int w = (int)(r % kFragWaves); r /= kFragWaves;
+    const int n = (int)(r % (I / 256)); r /= (I / 256);
+    const int e = (int)r;
+    const int col = n * 256 + 32 * w + 16 * (j & 1) + (lane & 15);
+    const int row = j < 2 ? col : I + col;
+    const int k = 32 * s + 8 * (lane >> 4);
+    st16(out + g * 8, ld16(w13 + ((size_t)e * 2 * I + row) * H + k));
+  }
+}
+
+__global__ __launch_bounds__(256) void prepare_w2_kernel(const uint16_t* __restrict__ w2, int E,
+                                                         int H, int I,
+                                                         uint16_t* __restrict__ out) {
+  const int nt = (H + 511) / 512;
+  const size_t groups = (size_t)E * nt * 512 * I / 8;
+  const int steps = I / 32;
+  for (size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x; g < groups;
+       g += (size_t)gridDim.x * blockDim.x) {
+    size_t r = g;
+    const int lane = (int)(r % 64); r /= 64;
+    const int j = (int)(r % 4); r /= 4;
+    const int s = (int)(r % steps); r /= steps;
+    const int w = (int)(r % kFragWaves); r /= kFragWaves;
+    const int n = (int)(r % nt); r /= nt;
+    const int e = (int)r;
+    const int row = n * 512 + 64 * w + 16 * j + (lane & 15);
+    const int k = 32 * s + 8 * (lane >> 4);
+    const u32x4 v = row < H ? ld16(w2 + ((size_t)e * H + row) * I + k) : u32x4{0, 0, 0, 0};
+    st16(out + g * 8, v);
+  }
+}
+
+size_t frag_w13_elems(int E, int H, int I) { return (size_t)E * 2 * I * H; }
+size_t frag_w2_elems(int E, int H, int I) { return (size_t)E * ((H + 511) / 512) * 512 * I; }
+
+hipError_t launch_prepare_weights(const uint16_t* w13, const uint16_t* w2, int E, int H, int I,
+                                  uint16_t* w13p, uint16_t* w2p, hipStream_t s) {
+  if (H % 64 != 0 || I % 256 != 0) return hipErrorInvalidValue;
+  const long g13 = (long)(frag_w13_elems(E, H, I) / 8);
+  const long g2 = (long)(frag_w2_elems(E, H, I) / 8);
+  const long grid13 = std::min<long>((g13 + 255) / 256, 1L << 20);
+  const long grid2 = std::min<long>((g2 + 255) / 256, 1L << 20);
+  if (w13 != nullptr) {
+    hipLaunchKernelGGL(prepare_w13_kernel, dim3((unsigned)grid13), dim3(256), 0, s, w13, E, H, I,
+                       w13p);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (w2 != nullptr) {
+    hipLaunchKernelGGL(prepare_w2_kernel, dim3((unsigned)grid2), dim3(256), 0, s, w2, E, H, I,
+                       w2p);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+// ---------------------------------------------------------------------------------------
+// The GEMM
+// ---------------------------------------------------------------------------------------
+template <int BM>
+struct FragCfg {
+  static constexpr int MT = BM / 16;                  // token row tiles
+  static constexpr int TSTAGE = MT * 2048;            // bytes of one token chunk
+  static constexpr int TCOPIES = MT * 2;              // 1 KiB copies per token chunk
+  static constexpr int WPC = 8;                       // weight loads per wave per chunk
+};
+
+// s_waitcnt vmcnt(N) (expcnt and lgkmcnt left open) through the builtin, which the
+// compiler's own wait insertion takes into account -- it then adds no wait of its own for
+// the loads this one already covers.  gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
+// lgkmcnt[11:8] | vmcnt[5:4] << 14.
+template <int N>
+__device__ __forceinline__ void frag_wait_vmcnt() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
+
+// Buffer resource over one wave's weight stream (`bytes` long, 4-byte aligned base): raw,
+// untyped 32-bit data, so loads past `bytes` return zero instead of touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const void* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// One work item: plan rows start..start+nlive-1 of expert e (their flat indices row_ids[r])
+// against N tile `ntile` of the prepared weights, computing the first NA token tiles (at
+// least the tiles holding real rows: the inner loop then has no branch, which keeps the
+// compiler's own load waits exact).  The ring is a __restrict__ parameter so that the
+// compiler can tell the token copies in flight apart from the LDS reads (without it, it
+// drains every load before each fragment read).
+template <int BM, bool UP, int WPOL, int NA>
+__device__ __forceinline__ void frag_item(
+    unsigned char* __restrict__ tlds, const uint16_t* __restrict__ tok_src,
+    const uint16_t* __restrict__ wp, const int32_t* __restrict__ row_ids, int start, int nlive,
+    int e, int ntile, int n_ntiles, int K, int ncols, int I, int top_k,
+    uint16_t* __restrict__ act, uint16_t* __restrict__ y) {
+  using C = FragCfg<BM>;
+  constexpr int MT = C::MT;
+  constexpr int TS = kFragTS, RS = kFragRS;
+  // token copies: copy f (0 .. TCOPIES-1) of a chunk covers rows 8h..8h+7 (h = f % 2) of
+  // token tile f / 2; wave w issues copies w, w + 8, ... (BM = 64: one each of the 8;
+  // BM = 128: two each of the 16)
+  constexpr int TCPW = C::TCOPIES / kFragWaves;
+  static_assert(TCPW * kFragWaves == C::TCOPIES, "token copies must split evenly over the waves");
+  // Every chunk issues the token copies of chunk c + TS - 1, then the weights of steps
+  // 2c + RS and 2c + 1 + RS (4 loads each) -- always, with the chunk and step clamped to the
+  // last one, so the count of this wave's loads issued after the token copies of chunk c is
+  // fixed: 8 + (TS - 2) (TCPW + 8) in the steady state, at least (TS - 2) TCPW + 4 RS after
+  // the prologue (token copies of chunks 0..TS-2, then the weights of steps 0..RS-1).
+  constexpr int kAfterT = 2 * 4 + (TS - 2) * (TCPW + 2 * 4);
+  constexpr int kAfterT0 = (TS - 2) * TCPW + RS * 4;
+  constexpr int kWaitT = kAfterT < kAfterT0 ? kAfterT : kAfterT0;
+  static_assert(kWaitT <= 63, "vmcnt range");
+  // The weights of step st were issued at the end of step st - RS (or in the prologue);
+  // after them this wave issued at least the weights of RS - 1 more steps and the token
+  // copies of one chunk start, so they have landed once at most that many loads are
+  // outstanding.
+  constexpr int kWaitW = 4 * (RS - 1) + TCPW;
+
+  // the wave index as a scalar: the weight stream's base is the same for the whole wave
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int lane = threadIdx.x & 63;
+  const int li = lane & 15, lg = lane >> 4;
+  const int nch = K / kFragKC;
+  const int nsteps = K / 32;
+
+  // this wave's weight stream (nsteps x 4 KiB, contiguous): fragment (step s, tile j) at byte
+  // s * 4096 + j * 1024, lane l's 16 bytes at + 16 l; loaded through a buffer resource (the
+  // step offset in a scalar register, one vector register for all lanes' offsets)
+  const __amdgpu_buffer_rsrc_t wrsrc = stream_rsrc(
+      wp + (((size_t)e * n_ntiles + ntile) * kFragWaves + wave) * (size_t)nsteps * 2048,
+      nsteps * 4096);
+  const int lane_off = lane * 16;
+  // token copies of this wave; rows past the tile's real rows read its first row
+  const uint16_t* tsrc[TCPW];
+#pragma unroll
+  for (int i = 0; i < TCPW; ++i) {
+    const int f = wave + kFragWaves * i;
+    const int rt = f >> 1, h = f & 1;
+    const int r = 16 * rt + 8 * h + (lane >> 3);
+    const int koff = 8 * ((lane & 7) ^ (lane >> 3) ^ h);
+    const bool on = r < nlive;
+    if (UP) {
+      const int sid = row_ids[on ? r : 0];
+      tsrc[i] = tok_src + (size_t)(sid < 0 ? 0 : sid / top_k) * K + koff;
+    } else {
+      tsrc[i] = tok_src + (size_t)(start + (on ? r : 0)) * K + koff;
+    }
+  }
+  auto issue_t = [&](int c) {  // into stage c % TS; c is clamped to the last chunk
+    const int cc = c < nch ? c : nch - 1;
+    unsigned char* base = tlds + (size_t)(c % TS) * C::TSTAGE;
+#pragma unroll
+    for (int i = 0; i < TCPW; ++i)
+      __builtin_amdgcn_global_load_lds((global_void*)(tsrc[i] + cc * kFragKC),
+                                       (lds_void*)(base + (wave + kFragWaves * i) * 1024), 16, 0,
+                                       0);
+  };
+  const int frag_off = (li >> 3) * 1024 + (li & 7) * 128;
+  auto tfrag = [&](int c, int t, int ks) -> u32x4 {
+    const int q = (lg + 4 * ks) ^ (li & 7) ^ (li >> 3);
+    return *reinterpret_cast<const u32x4*>(tlds + (size_t)(c % TS) * C::TSTAGE + t * 2048 +
+                                           frag_off + q * 16);
+  };
+  u32x4 wr[RS][4];
+  auto issue_w = [&](int st, u32x4 (&dst)[4]) {  // st is clamped to the last step
+    const int ss = st < nsteps ? st : nsteps - 1;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      dst[j] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, lane_off, ss * 4096 + j * 1024, WPOL));
+  };
+
+  static_assert(NA >= 1 && NA <= MT, "computed token tiles");
+  f32x4 acc[4][NA];
+#pragma unroll
+  for (int j = 0; j < 4; ++j)
+#pragma unroll
+    for (int s = 0; s < NA; ++s) acc[j][s] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll
+  for (int p = 0; p < TS - 1; ++p) issue_t(p);
+#pragma unroll
+  for (int u = 0; u < RS; ++u) issue_w(u, wr[u]);
+
+  // step st (ring slot u % RS, u compile-time after unrolling): on a chunk's first step wait
+  // for its token copies, publish them and start the copies TS - 1 chunks ahead; NA token
+  // tiles x 4 weight tiles of MFMAs; the weights RS steps ahead into the freed slot
+  auto step = [&](int st, int u) {
+    const int c = st >> 1, ks = u & 1;
+    if (ks == 0) {
+      // this wave's token copies of chunk c have landed ...
+      frag_wait_vmcnt<kWaitT>();
+      // ... for every wave, and chunk c - 1 is consumed: stage (c + TS - 1) % TS is free
+      asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      issue_t(c + TS - 1);
+    }
+    frag_wait_vmcnt<kWaitW>();   // this step's weights are in registers
+#pragma unroll
+    for (int s = 0; s < NA; ++s) {
+      const u32x4 xb = tfrag(c, s, ks);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[j][s] = mfma16x16x32(wr[u % RS][j], xb, acc[j][s]);
+    }
+    issue_w(st + RS, wr[u % RS]);
+  };
+  // whole groups of 2 RS steps (whole chunks) without a branch, then the rest
+  int s0 = 0;
+  for (; s0 + 2 * RS <= nsteps; s0 += 2 * RS) {
+#pragma unroll
+    for (int u = 0; u < 2 * RS; ++u) step(s0 + u, u);
+  }
+#pragma unroll
+  for (int u = 0; u < 2 * RS; ++u)
+    if (s0 + u < nsteps) step(s0 + u, u);
+  // the clamped loads past the last step are discarded: let them land before the registers
+  // and the ring are reused
+  frag_wait_vmcnt<0>();
+
+  // epilogue (as in the tiled kernels): act rows in bf16 for the up GEMM, y rows in bf16
+  // for the down GEMM, real rows only
+#pragma unroll
+  for (int s = 0; s < NA; ++s) {
+    const int r = 16 * s + li;
+    if (r >= nlive) continue;
+    if (UP) {
+      const int col0 = ntile * 256 + 32 * wave;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int n = col0 + 16 * h + 4 * lg;
+        float a[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) a[q] = silu_f32(acc[h][s][q]) * acc[2 + h][s][q];
+        uint2 v;
+        v.x = pack_bf16x2(a[0], a[1]);
+        v.y = pack_bf16x2(a[2], a[3]);
+        *reinterpret_cast<uint2*>(act + (size_t)(start + r) * I + n) = v;
+      }
+    } else {
+      const int dst = row_ids[r];
+      const int col0 = ntile * 512 + 64 * wave;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int n = col0 + 16 * j + 4 * lg;
+        if (n < ncols) {
+          uint2 v;
+          v.x = pack_bf16x2(acc[j][s][0], acc[j][s][1]);
+          v.y = pack_bf16x2(acc[j][s][2], acc[j][s][3]);
+          *reinterpret_cast<uint2*>(y + (size_t)dst * ncols + n) = v;
+        }
+      }
+    }
+  }
+}
+
+// Work items (tile, N tile) in expert-major order: the tiles of one expert for its first N
+// tile, then for the next, and so on, expert after expert; each XCD takes an equal
+// contiguous share, so the ~32 items it runs at a time are a few N tiles of one expert
+// (its tiles share each weight line through the XCD's L2) or all N tiles of the one tile of
+// a cold expert (which share its token rows).  Items of expert e occupy the logical range
+// [first tile x n_ntiles, (first tile + tiles) x n_ntiles), so item L belongs to the expert
+// of tile L / n_ntiles.
+struct ExpertMajorWalk {
+  TiledWalk w;
+  const int2* groups;
+  int n_ntiles;
+  __device__ ExpertMajorWalk(int ntl, int nnt, const int2* g) : w(ntl, nnt), groups(g), n_ntiles(nnt) {}
+  __device__ bool next(int& ntile, int& ti) {
+    int a, b;
+    if (!w.next(a, b)) return false;
+    const int logical = a * w.ntiles_live + b;
+    const int2 g = groups[logical / n_ntiles];
+    const int local = logical - g.x * n_ntiles;
+    ntile = local / g.y;
+    ti = g.x + local % g.y;
+    return true;
+  }
+};
+
+template <int BM, bool UP, int WPOL>
+__global__ __launch_bounds__(64 * kFragWaves) void expert_frag_kernel(
+    const uint16_t* __restrict__ tok_src, const uint16_t* __restrict__ wp,
+    const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
+    const int2* __restrict__ tiles, const int2* __restrict__ tile_groups,
+    const int32_t* __restrict__ num_tiles, int n_ntiles, int K, int ncols, int I, int top_k,
+    int block, uint16_t* __restrict__ act, uint16_t* __restrict__ y) {
+  __shared__ __align__(16) unsigned char tlds[kFragTS * FragCfg<BM>::TSTAGE];
+  ExpertMajorWalk walk(*num_tiles, n_ntiles, tile_groups);
+  int ntile, ti;
+  while (walk.next(ntile, ti)) {
+    const int2 tile = tiles[ti];
+    // token tiles computed: all of them, or the first quarter (64-row tiles) / half
+    // (128-row tiles) when that holds every real row (padding rows hold copies of the first
+    // row); each choice is its own branch-free loop, which keeps the compiler's own load
+    // waits exact
+    constexpr int MT = FragCfg<BM>::MT;
+    constexpr int NS = BM == 64 ? 1 : MT / 2;
+    if (tile.y <= 16 * NS)
+      frag_item<BM, UP, WPOL, NS>(tlds, tok_src, wp, sorted_ids + tile.x, tile.x, tile.y,
+                                  block_expert[tile.x / block], ntile, n_ntiles, K, ncols, I,
+                                  top_k, act, y);
+    else
+      frag_item<BM, UP, WPOL, MT>(tlds, tok_src, wp, sorted_ids + tile.x, tile.x, tile.y,
+                                  block_expert[tile.x / block], ntile, n_ntiles, K, ncols, I,
+                                  top_k, act, y);
+    __syncthreads();  // the next item's first token copies reuse the ring
+  }
+}
+
+template <int BM, bool UP, int WPOL>
+static hipError_t launch_frag(const uint16_t* src, const uint16_t* wp, const int32_t* sorted_ids,
+                              const int32_t* block_expert, const int2* tiles,
+                              const int2* tile_groups, const int32_t* num_tiles, int max_tiles,
+                              int K, int ncols, int I, int top_k, int block, uint16_t* act,
+                              uint16_t* y, hipStream_t s) {
+  const int per_ntile = UP ? 256 : 512;
+  if (K % kFragKC != 0 || (UP && I % per_ntile != 0)) return hipErrorInvalidValue;
+  const int n_ntiles = (ncols + per_ntile - 1) / per_ntile;
+  const long items = (long)max_tiles * n_ntiles;
+  // 64-row tiles walk several items per workgroup, 128-row tiles take one each
+  const long grid = BM == 64 ? walk_grid(items, 160 * 1024) : (items + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL((expert_frag_kernel<BM, UP, WPOL>), dim3((unsigned)grid),
+                     dim3(64 * kFragWaves), 0, s, src, wp, sorted_ids, block_expert, tiles,
+                     tile_groups, num_tiles, n_ntiles, K, ncols, I, top_k, block, act, y);
+  return hipGetLastError();
+}
+
+constexpr int kFragNT = 2;  // cache policy bits of a nontemporal load (gfx950)
+
+hipError_t launch_expert_up_frag(const uint16_t* x, const uint16_t* w13p, const int32_t* sorted_ids,
+                                 const int32_t* block_expert, const int2* tiles,
+                                 const int2* tile_groups, const int32_t* num_tiles, int max_tiles,
+                                 int tile_rows, bool stream_weights, int H, int I, int top_k,
+                                 int block, uint16_t* act, hipStream_t s) {
+#define MOE_FRAG_UP(BM, POL)                                                                    \
+  return launch_frag<BM, true, POL>(x, w13p, sorted_ids, block_expert, tiles, tile_groups,     \
+                                    num_tiles, max_tiles, H, I, I, top_k, block, act, nullptr, s)
+  if (tile_rows == 64) {
+    if (stream_weights) MOE_FRAG_UP(64, kFragNT);
+    MOE_FRAG_UP(64, 0);
+  }
+  if (tile_rows == 128) {
+    if (stream_weights) MOE_FRAG_UP(128, kFragNT);
+    MOE_FRAG_UP(128, 0);
+  }
+#undef MOE_FRAG_UP
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_expert_down_frag(const uint16_t* act, const uint16_t* w2p,
+                                   const int32_t* sorted_ids, const int32_t* block_expert,
+                                   const int2* tiles, const int2* tile_groups,
+                                   const int32_t* num_tiles, int max_tiles, int tile_rows,
+                                   bool stream_weights, int H, int I, int top_k, int block,
+                                   uint16_t* y, hipStream_t s) {
+#define MOE_FRAG_DOWN(BM, POL)                                                                  \
+  return launch_frag<BM, false, POL>(act, w2p, sorted_ids, block_expert, tiles, tile_groups,   \
+                                     num_tiles, max_tiles, I, H, I, top_k, block, nullptr, y, s)
+  if (tile_rows == 64) {
+    if (stream_weights) MOE_FRAG_DOWN(64, kFragNT);
+    MOE_FRAG_DOWN(64, 0);
+  }
+  if (tile_rows == 128) {
+    if (stream_weights) MOE_FRAG_DOWN(128, kFragNT);
+    MOE_FRAG_DOWN(128, 0);
+  }
+#undef MOE_FRAG_DOWN
+  return hipErrorInvalidValue;
+}
+
+}  // namespace moe

@@ -17,9 +17,11 @@ hipError_t launch_route(const uint16_t* x, const uint16_t* wr, const float* bias
 // Expert-major plan of the flat ids [n]; sentinel = n.  When `tiles` is not null the
 // kernel also lists the row tiles of height tile_rows holding real entries
 // ({first plan row, real rows}) and their count; at most tile_capacity(n, E, tile_rows).
+// When `tile_groups` is not null too, entry t holds the expert of tile t as {its first
+// tile, its number of tiles} (tiles of one expert are consecutive).
 hipError_t launch_align(const int32_t* ids, int n, int E, int block, int32_t* sorted_ids,
                         int32_t* block_expert, int32_t* num_padded, int tile_rows, int2* tiles,
-                        int32_t* num_tiles, hipStream_t s);
+                        int32_t* num_tiles, hipStream_t s, int2* tile_groups = nullptr);
 
 inline int tile_capacity(int n, int E, int tile_rows) {
   return (n + tile_rows - 1) / tile_rows + (n < E ? n : E);
@@ -105,6 +107,27 @@ hipError_t launch_mx_quantize(const uint16_t* w, int64_t rows, int K, uint8_t* c
                               uint8_t* scales, hipStream_t s);
 hipError_t launch_mx_dequantize(const uint8_t* codes, const uint8_t* scales, int64_t rows, int K,
                                 uint16_t* w, hipStream_t s);
+
+// Prepared ("fragment panel") expert weights: the natural stacks W13 [E, 2I, H] and
+// W2 [E, H, I] re-laid-out once so that each wave of the GEMMs below streams its weight
+// fragments as contiguous 1 KiB loads (H % 64 == 0, I % 256 == 0).  Element counts of the
+// prepared stacks, the preparation, and the grouped GEMMs on them (tile_rows 64 or 128).
+size_t frag_w13_elems(int E, int H, int I);
+size_t frag_w2_elems(int E, int H, int I);
+hipError_t launch_prepare_weights(const uint16_t* w13, const uint16_t* w2, int E, int H, int I,
+                                  uint16_t* w13p, uint16_t* w2p, hipStream_t s);
+// Work items (tile, N tile) walk expert by expert (tile_groups of launch_align).
+hipError_t launch_expert_up_frag(const uint16_t* x, const uint16_t* w13p, const int32_t* sorted_ids,
+                                 const int32_t* block_expert, const int2* tiles,
+                                 const int2* tile_groups, const int32_t* num_tiles, int max_tiles,
+                                 int tile_rows, bool stream_weights, int H, int I, int top_k,
+                                 int block, uint16_t* act, hipStream_t s);
+hipError_t launch_expert_down_frag(const uint16_t* act, const uint16_t* w2p,
+                                   const int32_t* sorted_ids, const int32_t* block_expert,
+                                   const int2* tiles, const int2* tile_groups,
+                                   const int32_t* num_tiles, int max_tiles, int tile_rows,
+                                   bool stream_weights, int H, int I, int top_k, int block,
+                                   uint16_t* y, hipStream_t s);
 
 // Weighted top-k combine + residual add + RMSNorm over fp32 or bf16 rows of y.
 hipError_t launch_finalize(const float* y, const float* topk_w, const uint16_t* residual,

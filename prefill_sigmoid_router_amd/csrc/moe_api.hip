@@ -40,7 +40,7 @@ size_t capacity_of(int32_t M, int32_t top_k, int32_t E, int32_t block) {
 
 // Workspace layout of moe_forward; every region starts on a 256-byte boundary.
 struct Layout {
-  size_t keys, ids, w, sorted, bexp, npad, tiles, ntiles, act, y, fin, total;
+  size_t keys, ids, w, sorted, bexp, npad, tiles, groups, ntiles, act, y, fin, total;
   int max_tiles;
 };
 
@@ -57,6 +57,7 @@ Layout layout_of(int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k, int3
   L.npad = off;   off += kAlign;
   L.max_tiles = moe::tile_capacity((int)n, E, 16);
   L.tiles = off;  off += round_up((size_t)L.max_tiles * sizeof(int2), kAlign);
+  L.groups = off; off += round_up((size_t)L.max_tiles * sizeof(int2), kAlign);  // expert of each tile
   L.ntiles = off; off += kAlign;
   L.act = off;    off += round_up(cap * (size_t)I * sizeof(uint16_t), kAlign);
   L.y = off;      off += round_up(n * (size_t)H * sizeof(uint16_t), kAlign);  // bf16 y
@@ -274,6 +275,7 @@ struct ExpertWeights {
   const uint8_t* w13s = nullptr;
   const uint8_t* w2c = nullptr;
   const uint8_t* w2s = nullptr;
+  bool prepared = false;  // w13 / w2 hold the fragment panels of moe_prepare_weights
   bool mx() const { return w13c != nullptr; }
 };
 
@@ -287,6 +289,7 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   if (!sizes_ok(M, H, E, I, top_k) || !(eps > 0.0f) || !isfinite(eps)) return MOE_ERR_INVALID_ARG;
   if (!gemm_block_ok(block)) return MOE_ERR_UNSUPPORTED;
   if (W.mx() && (H % 256 != 0 || I % 256 != 0)) return MOE_ERR_UNSUPPORTED;
+  if (W.prepared && (H % 64 != 0 || I % 256 != 0)) return MOE_ERR_UNSUPPORTED;
   if (M == 0) return MOE_OK;
   const bool w_ok = W.mx() ? (W.w13c && W.w13s && W.w2c && W.w2s && aligned(W.w13c, 16) &&
                               aligned(W.w2c, 16) && aligned(W.w13s, 8) && aligned(W.w2s, 8))
@@ -313,6 +316,7 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   int32_t* bexp = block_expert_out ? block_expert_out : reinterpret_cast<int32_t*>(ws + L.bexp);
   int32_t* npad = num_padded_out ? num_padded_out : reinterpret_cast<int32_t*>(ws + L.npad);
   int2* tiles = reinterpret_cast<int2*>(ws + L.tiles);
+  int2* groups = reinterpret_cast<int2*>(ws + L.groups);
   int32_t* ntiles = reinterpret_cast<int32_t*>(ws + L.ntiles);
   uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
   uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.y);
@@ -332,14 +336,17 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   const bool stream_w = stream_weights(M, E, top_k, trows);
   const int max_tiles = moe::tile_capacity(M * top_k, E, trows);
   // few ids: the up GEMM builds the plan itself (no align launch)
-  const bool self_route = !W.mx() && self_routes(M, E, top_k, I);
+  const bool self_route = !W.mx() && !W.prepared && self_routes(M, E, top_k, I);
   if (!self_route &&
-      moe::launch_align(ids, M * top_k, E, block, sorted, bexp, npad, trows, tiles, ntiles, s) !=
-          hipSuccess)
+      moe::launch_align(ids, M * top_k, E, block, sorted, bexp, npad, trows, tiles, ntiles, s,
+                        W.prepared ? groups : nullptr) != hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(2)) return MOE_ERR_HIP;
   hipError_t up_err;
-  if (self_route)
+  if (W.prepared)
+    up_err = moe::launch_expert_up_frag(x, W.w13, sorted, bexp, tiles, groups, ntiles, max_tiles,
+                                        trows, stream_w, H, I, top_k, block, act, s);
+  else if (self_route)
     up_err = moe::launch_expert_up_selfroute(x, W.w13, ids, M, H, E, I, top_k, block, sorted, bexp,
                                              npad, tiles, ntiles, act, s);
   else if (W.mx() && trows <= 64)
@@ -357,7 +364,10 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   if (up_err != hipSuccess) return MOE_ERR_HIP;
   if (!mark(3)) return MOE_ERR_HIP;
   hipError_t down_err;
-  if (W.mx())
+  if (W.prepared)
+    down_err = moe::launch_expert_down_frag(act, W.w2, sorted, bexp, tiles, groups, ntiles,
+                                            max_tiles, trows, stream_w, H, I, top_k, block, y, s);
+  else if (W.mx())
     down_err = moe::launch_expert_down_mx_lds(act, W.w2c, W.w2s, sorted, bexp, tiles, ntiles,
                                               max_tiles, trows, stream_w, H, I, top_k, block, y, s);
   else if (trows == 16)
@@ -412,6 +422,49 @@ int moe_forward_mx(const uint16_t* x, const uint16_t* router_w, const float* rou
   W.w2c = w2_codes;
   W.w2s = w2_scales;
   if (!w13_codes) return MOE_ERR_INVALID_ARG;
+  return forward_impl(x, router_w, router_bias, W, residual, norm_w, eps, M, H, E, I, top_k, block,
+                      out, residual_out, topk_ids_out, topk_w_out, sorted_ids_out,
+                      block_expert_out, num_padded_out, workspace, workspace_bytes, stage_events,
+                      stream);
+}
+
+size_t moe_prepared_w13_bytes(int32_t E, int32_t H, int32_t I) {
+  if (E < 1 || E > kMaxE || H < 64 || H > kMaxH || H % 64 != 0 || I < 256 || I % 256 != 0) return 0;
+  return moe::frag_w13_elems(E, H, I) * sizeof(uint16_t);
+}
+
+size_t moe_prepared_w2_bytes(int32_t E, int32_t H, int32_t I) {
+  if (E < 1 || E > kMaxE || H < 64 || H > kMaxH || H % 64 != 0 || I < 256 || I % 256 != 0) return 0;
+  return moe::frag_w2_elems(E, H, I) * sizeof(uint16_t);
+}
+
+int moe_prepare_weights(const uint16_t* w13, const uint16_t* w2, int32_t E, int32_t H, int32_t I,
+                        uint16_t* w13_prepared, uint16_t* w2_prepared, moe_stream_t stream) {
+  if (E < 1 || E > kMaxE || H < 8 || H > kMaxH || H % 8 != 0 || I < 16 || I % 16 != 0)
+    return MOE_ERR_INVALID_ARG;
+  if (H % 64 != 0 || I % 256 != 0) return MOE_ERR_UNSUPPORTED;
+  if ((w13 == nullptr) != (w13_prepared == nullptr) || (w2 == nullptr) != (w2_prepared == nullptr))
+    return MOE_ERR_INVALID_ARG;
+  if ((w13 && (!aligned(w13, 16) || !aligned(w13_prepared, 16))) ||
+      (w2 && (!aligned(w2, 16) || !aligned(w2_prepared, 16))))
+    return MOE_ERR_INVALID_ARG;
+  if (!w13 && !w2) return MOE_OK;
+  return hip_status(moe::launch_prepare_weights(w13, w2, E, H, I, w13_prepared, w2_prepared,
+                                                (hipStream_t)stream));
+}
+
+int moe_forward_prepared(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
+                         const uint16_t* w13_prepared, const uint16_t* w2_prepared,
+                         const uint16_t* residual, const uint16_t* norm_w, float eps, int32_t M,
+                         int32_t H, int32_t E, int32_t I, int32_t top_k, int32_t block,
+                         uint16_t* out, uint16_t* residual_out, int32_t* topk_ids_out,
+                         float* topk_w_out, int32_t* sorted_ids_out, int32_t* block_expert_out,
+                         int32_t* num_padded_out, void* workspace, size_t workspace_bytes,
+                         const moe_event_t* stage_events, moe_stream_t stream) {
+  ExpertWeights W;
+  W.w13 = w13_prepared;
+  W.w2 = w2_prepared;
+  W.prepared = true;
   return forward_impl(x, router_w, router_bias, W, residual, norm_w, eps, M, H, E, I, top_k, block,
                       out, residual_out, topk_ids_out, topk_w_out, sorted_ids_out,
                       block_expert_out, num_padded_out, workspace, workspace_bytes, stage_events,

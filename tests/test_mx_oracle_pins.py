@@ -167,3 +167,100 @@ def test_lut_roundtrip_equals_the_definition():
     for w in _lut_cases():
         c0, s0 = mx.mx_quantize(w)
         assert np.array_equal(mx.mx_roundtrip_bf16_bits_lut(w), mx.mx_dequantize_bf16_bits(c0, s0))
+
+
+# ---------------------------------------------------------------------------------------
+# MXFP4 (E2M1 elements, the same E8M0 block scale)
+# ---------------------------------------------------------------------------------------
+def test_e2m1_decode_known_codes():
+    """All 16 codes from the field layout: S.EE.M, exponent bias 1, field 0 subnormal."""
+    want = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+    assert mx.e2m1_decode(np.arange(8)).tolist() == want
+    assert mx.e2m1_decode(np.arange(8, 16)).tolist() == [-v for v in want]
+    assert mx.E2M1_MAX == 6.0
+
+
+def _brute_encode4(v):
+    """Nearest of the 8 magnitudes; a tie goes to the neighbour with mantissa bit 0."""
+    mags = np.array([0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0])
+    out = []
+    for x in np.atleast_1d(v):
+        a = min(abs(float(x)), 6.0)
+        d = np.abs(mags - a)
+        best = np.flatnonzero(d == d.min())
+        c = int(best[0] if len(best) == 1 else best[best % 2 == 0][0])
+        if x < 0 and c != 0:
+            c |= 0x8
+        out.append(c)
+    return np.array(out, dtype=np.uint8)
+
+
+def test_e2m1_encode_matches_brute_force_nearest():
+    rng = np.random.default_rng(4)
+    mags = mx.e2m1_decode(np.arange(8))
+    mids = (mags[1:] + mags[:-1]) / 2            # every midpoint is a tie
+    v = np.concatenate([rng.normal(0, 2, 3000), rng.uniform(-9, 9, 1000), mids, -mids,
+                        mags, -mags, [6.5, 7.0, 1e9, -1e9, -0.0]])
+    assert np.array_equal(mx.e2m1_encode(v), _brute_encode4(v))
+
+
+def test_e2m1_ties_and_saturation():
+    assert mx.e2m1_encode(0.25) == 0x0        # 0 and 0.5: to 0 (mantissa 0)
+    assert mx.e2m1_encode(0.75) == 0x2        # 0.5 and 1: to 1
+    assert mx.e2m1_encode(1.25) == 0x2        # 1 and 1.5: to 1
+    assert mx.e2m1_encode(1.75) == 0x4        # 1.5 and 2: to 2
+    assert mx.e2m1_encode(2.5) == 0x4         # 2 and 3: to 2
+    assert mx.e2m1_encode(3.5) == 0x6         # 3 and 4: to 4
+    assert mx.e2m1_encode(5.0) == 0x6         # 4 and 6: to 4
+    assert mx.e2m1_encode(5.5) == 0x7
+    assert mx.e2m1_encode(100.0) == 0x7 and mx.e2m1_encode(-100.0) == 0xF
+    assert mx.e2m1_encode(-0.2) == 0x0        # rounds to zero: +0
+
+
+def test_mx4_block_worked_examples():
+    # amax 6: floor(log2 6) = 2 -> s = 0, scale byte 127; elements as they are
+    row = np.zeros(32, dtype=np.float32)
+    row[[0, 1, 2, 3]] = [6.0, -1.5, 0.5, 2.5]
+    codes, scales = mx.mx4_quantize(_bf16(row))
+    assert scales.tolist() == [127]
+    assert codes[:4].tolist() == [0x7, 0xB, 0x1, 0x4]           # 2.5 ties to 2
+    # amax 1: s = -2 (byte 125), elements scaled by 4: 1 -> 4, 0.25 -> 1, 0.125 -> 0.5
+    row2 = np.zeros(32, dtype=np.float32)
+    row2[[5, 6, 7]] = [1.0, 0.25, -0.125]
+    codes2, scales2 = mx.mx4_quantize(_bf16(row2))
+    assert scales2.tolist() == [125] and codes2[[5, 6, 7]].tolist() == [0x6, 0x2, 0x9]
+    # amax 1.875: s = -2, 1.875 * 4 = 7.5 clamps to 6 -> dequantized 1.5
+    row3 = np.zeros(32, dtype=np.float32)
+    row3[9] = 1.875
+    codes3, scales3 = mx.mx4_quantize(_bf16(row3))
+    assert codes3[9] == 0x7 and mx.mx4_dequantize(codes3, scales3)[9] == 1.5
+    # a zero block: scale byte 0, zero codes; blocks of one row are independent
+    row4 = np.zeros(64, dtype=np.float32)
+    row4[40] = 3.0                            # floor(log2 3) = 1 -> s = -1
+    codes4, scales4 = mx.mx4_quantize(_bf16(row4))
+    assert scales4.tolist() == [0, 126] and np.all(codes4[:32] == 0) and codes4[40] == 0x7
+
+
+def test_mx4_quantization_error_bound():
+    rng = np.random.default_rng(2)
+    w_bits = _trunc_bf16(rng.normal(0, 0.02, (8, 512)))
+    wv = (w_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    codes, scales = mx.mx4_quantize(w_bits)
+    deq = mx.mx4_dequantize(codes, scales)
+    s = np.repeat(scales.astype(np.float64) - 127.0, 32, axis=-1)
+    u = np.abs(wv) / np.exp2(s)               # in [0, 8)
+    # half a grid step: 0.25 below 2, 0.5 in [2, 4), 1 in [4, 6]; above 6 the clamp
+    half = np.where(u < 2, 0.25, np.where(u < 4, 0.5, 1.0)) * np.exp2(s)
+    ok = u <= 6
+    assert np.all(np.abs(deq - wv)[ok] <= half[ok])
+    assert np.array_equal(np.abs(deq)[~ok], (6 * np.exp2(s))[~ok])
+    assert np.array_equal(mx.mx4_dequantize_bf16_bits(codes, scales),
+                          (deq.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16))
+
+
+def test_mx4_lut_equals_the_definition():
+    for w in _lut_cases():
+        c0, s0 = mx.mx4_quantize(w)
+        c1, s1 = mx.mx4_quantize_lut(w, rows_per_pass=5)
+        assert np.array_equal(s0, s1) and np.array_equal(c0, c1)
+        assert np.array_equal(mx.mx4_roundtrip_bf16_bits_lut(w), mx.mx4_dequantize_bf16_bits(c0, s0))

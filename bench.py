@@ -50,29 +50,30 @@ def source_hash(path: str) -> str:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def weight_bytes_per_value(mx):
-    """bf16: 2 bytes; MXFP8: one E4M3 byte plus one scale byte per 32 values."""
-    return 1 + 1 / 32 if mx else 2
+def weight_bytes_per_value(fmt):
+    """bf16: 2 bytes; MXFP8: one E4M3 byte plus one scale byte per 32 values; MXFP4: half a
+    byte per E2M1 code plus one scale byte per 32 values."""
+    return {"bf16": 2, "mx8": 1 + 1 / 32, "mx4": 0.5 + 1 / 32}[fmt]
 
 
-def layer_bytes(cfg, M, touched, mx=False):
+def layer_bytes(cfg, M, touched, fmt="bf16"):
     """Algorithmic HBM bytes of one layer: touched experts' W13+W2, the router weight,
     x, residual and out rows, and the norm weight."""
-    per_expert = 3 * cfg.I * cfg.H * weight_bytes_per_value(mx)
+    per_expert = 3 * cfg.I * cfg.H * weight_bytes_per_value(fmt)
     return int(touched * per_expert) + cfg.E * cfg.H * 2 + 3 * M * cfg.H * 2 + cfg.H * 2
 
 
-def up_bytes(cfg, M, touched, mx=False):
+def up_bytes(cfg, M, touched, fmt="bf16"):
     """Algorithmic bytes of the up kernel: W13 of every touched expert, each token's x
     row once, and one bf16 act row per (token, pick)."""
-    return (int(touched * 2 * cfg.I * cfg.H * weight_bytes_per_value(mx)) + M * cfg.H * 2
+    return (int(touched * 2 * cfg.I * cfg.H * weight_bytes_per_value(fmt)) + M * cfg.H * 2
             + M * cfg.top_k * cfg.I * 2)
 
 
-def down_bytes(cfg, M, touched, mx=False):
+def down_bytes(cfg, M, touched, fmt="bf16"):
     """Algorithmic bytes of the down kernel: W2 of every touched expert, one bf16 act row
     read and one bf16 y row written per (token, pick)."""
-    return (int(touched * cfg.H * cfg.I * weight_bytes_per_value(mx))
+    return (int(touched * cfg.H * cfg.I * weight_bytes_per_value(fmt))
             + M * cfg.top_k * (cfg.I + cfg.H) * 2)
 
 
@@ -88,10 +89,12 @@ def down_flops(cfg, M):
     return 2 * M * cfg.top_k * cfg.I * cfg.H
 
 
-def run_workload(B, mi, torch, cfg, weights, steps, warmup, dev, mx=None, prepared=None):
+def run_workload(B, mi, torch, cfg, weights, steps, warmup, dev, mx=None, prepared=None,
+                 mx4=None):
     """Times moe_forward (bf16 experts), moe_forward_mx when `mx` holds the MXFP8
-    (w13 codes, w13 scales, w2 codes, w2 scales), or moe_forward_prepared when `prepared`
-    holds the prepared (w13, w2) stacks."""
+    (w13 codes, w13 scales, w2 codes, w2 scales), moe_forward_prepared when `prepared`
+    holds the prepared (w13, w2) stacks, or moe_forward_mx4 when `mx4` holds the MXFP4
+    panels (w13 codes, w13 scales, w2 codes, w2 scales)."""
     L = mi.make_layer(cfg, device=dev, seed=0, with_experts=False)
     L.update(weights)
     M, H, E, I, k, blk = cfg.M, cfg.H, cfg.E, cfg.I, cfg.top_k, cfg.block
@@ -101,7 +104,11 @@ def run_workload(B, mi, torch, cfg, weights, steps, warmup, dev, mx=None, prepar
     stream = torch.cuda.current_stream()
 
     def step(events=None):
-        if prepared is not None:
+        if mx4 is not None:
+            B.moe_forward_mx4(L["x"], L["router_w"], L["router_bias"], *mx4, I, L["residual"],
+                              L["norm_w"], L["eps"], k, blk, out, ws, topk_ids_out=ids,
+                              stage_events=events, stream=stream)
+        elif prepared is not None:
             B.moe_forward_prepared(L["x"], L["router_w"], L["router_bias"], prepared[0],
                                    prepared[1], I, L["residual"], L["norm_w"], L["eps"], k, blk,
                                    out, ws, topk_ids_out=ids, stage_events=events, stream=stream)
@@ -139,11 +146,13 @@ def run_workload(B, mi, torch, cfg, weights, steps, warmup, dev, mx=None, prepar
     ms = max(wall_ms, span_ms)
     touched = int(torch.unique(ids).numel())
     counts = torch.bincount(ids.flatten().long(), minlength=E)
-    lb = layer_bytes(cfg, M, touched, mx is not None)
-    ub = up_bytes(cfg, M, touched, mx is not None)
-    db = down_bytes(cfg, M, touched, mx is not None)
+    fmt = "mx8" if mx is not None else "mx4" if mx4 is not None else "bf16"
+    lb = layer_bytes(cfg, M, touched, fmt)
+    ub = up_bytes(cfg, M, touched, fmt)
+    db = down_bytes(cfg, M, touched, fmt)
     stages = {n: round(v * 1e3, 2) for n, v in stage_ms.items()}
-    self_routed = mx is None and prepared is None and B.moe_forward_self_routes(M, E, k, I)
+    self_routed = (mx is None and prepared is None and mx4 is None
+                   and B.moe_forward_self_routes(M, E, k, I))
     if self_routed:
         # the up GEMM builds the plan: no align kernel runs, the event pair encloses none
         stages["align"] = None
@@ -425,6 +434,8 @@ def main():
                     help="skip the legs with MXFP8 expert weights")
     ap.add_argument("--no-prepared", action="store_true",
                     help="skip the legs on prepared (fragment-panel) weights")
+    ap.add_argument("--no-mx4", action="store_true",
+                    help="skip the legs with MXFP4 expert weights")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -536,6 +547,34 @@ def main():
         del p13, p2
         torch.cuda.empty_cache()
 
+    mx4_line = None
+    if not args.no_mx4:
+        # the same layer with MXFP4 expert weights (quantized on the device into panels)
+        print("bench: quantizing the experts to MXFP4", file=sys.stderr, flush=True)
+        E, H, I = head.E, head.H, head.I
+        q = [torch.empty(n, dtype=torch.uint8, device=dev) for n in B.moe_mx4_weight_bytes(E, H, I)]
+        B.moe_mx4_quantize(weights["w13"], weights["w2"], *q)
+        torch.cuda.synchronize()
+        mx4_line = {}
+        for name in (head.name,) + (() if args.no_sweep else SWEEP):
+            if name in mx4_line:
+                continue
+            print(f"bench: timing {name} with MXFP4 experts", file=sys.stderr, flush=True)
+            c = mi.CONFIGS[name]
+            quick = name != head.name
+            r = run_workload(B, mi, torch, c, weights,
+                             max(3, args.steps // 2) if quick else args.steps,
+                             max(1, args.warmup // 2) if quick else args.warmup, dev, mx4=q)
+            mx4_line[name] = _rounded(r)
+            mx4_line[name]["up_hbm_frac"] = round(r["up_gbs"] / HBM_PEAK_GBS, 4)
+            mx4_line[name]["down_hbm_frac"] = round(r["down_gbs"] / HBM_PEAK_GBS, 4)
+            mx4_line[name]["up_kernel"] = (
+                f"expert_frag_kernel<{B.moe_gemm_tile_rows(c.M, c.E, c.top_k, c.I)}, true, ..., FP4>")
+        mx4_line["weights"] = ("MXFP4 (E2M1 + E8M0 per 32 values along K, fragment panels), "
+                               "activations bf16")
+        del q
+        torch.cuda.empty_cache()
+
     # read probes over the resident W13 (the bytes the up GEMM streams)
     print("bench: timing the HBM read probes", file=sys.stderr, flush=True)
     plain_gbs = read_probe_gbs(torch, dev, weights["w13"])
@@ -588,6 +627,7 @@ def main():
         "sweep": sweep_out,
         "mxfp8_decode": mx_line,
         "prepared_weights": prep_line,
+        "mxfp4": mx4_line,
     }
     print(json.dumps(line), flush=True)
 

@@ -230,6 +230,52 @@ int moe_forward_prepared(const uint16_t* x, const uint16_t* router_w, const floa
                          const moe_event_t* stage_events, moe_stream_t stream);
 
 /*
+ * MXFP4 expert weights: the 4-bit format of the OCP Microscaling (MX) v1.0 specification --
+ * E2M1 elements (magnitudes 0, 0.5, 1, 1.5, 2, 3, 4, 6) with one E8M0 scale byte
+ * b = s + 127 per 32 consecutive values of a row along K, s = floor(log2(max |v|)) - 2 (a
+ * run of zeros gets b = 0); each value becomes the E2M1 code of v / 2^s, rounded to nearest
+ * even and clamped to +-6.  The AlphaMoE page (FlashInfer PR #6511 analysis, intro and
+ * section 1) streams 4-bit block-scaled expert weights (NVFP4) to cut a decode step's bytes;
+ * MXFP4 is the OCP format with MXFP8's block and scale.  Only W13 and W2 are quantized.
+ *
+ * The codes are stored in the prepared panel order of moe_prepare_weights (H % 64 == 0 and
+ * I % 256 == 0, else MOE_ERR_UNSUPPORTED): for expert e, N tile n, wave w and K step s (one
+ * 32-value block), lane l holds the 8 values of its tile j as 4 code bytes (value 2b in the
+ * low nibble of byte b), the 4 tiles' bytes together, and the step's scale bytes follow as
+ * [16 rows][4 tiles]:
+ *   W13 codes [E][I/256][8][H/32][64][4][4], W13 scales [E][I/256][8][H/32][16][4]
+ *   W2  codes [E][ceil(H/512)][8][I/32][64][4][4], W2 scales [E][ceil(H/512)][8][I/32][16][4]
+ * with tile j of lane l holding row n*256 + 32w + 16(j%2) + l%16 (+ I for j >= 2) of W13 and
+ * row n*512 + 64w + 16j + l%16 of W2 (codes and scales 0 past H), K values 32 s + 8(l/16) + v.
+ *
+ * moe_mx4_weight_bytes: the four buffer sizes (any pointer may be NULL).
+ * moe_mx4_quantize:     natural bf16 W13 [E, 2I, H] and/or W2 [E, H, I] -> codes and scales
+ *                       (a (w, codes, scales) triple may be all NULL to skip that stack).
+ * moe_mx4_dequantize:   codes + scales of W13 (which = 13) or W2 (which = 2) -> the natural
+ *                       bf16 stack, with the conversion the GEMMs use (exact).
+ * moe_forward_mx4:      moe_forward on MXFP4 weights (the layer on the dequantized weights;
+ *                       always runs the align kernel).
+ * Codes 16-byte and scales 4-byte aligned; asynchronous on `stream`; nothing is allocated.
+ */
+int moe_mx4_weight_bytes(int32_t E, int32_t H, int32_t I, size_t* w13_codes, size_t* w13_scales,
+                         size_t* w2_codes, size_t* w2_scales);
+int moe_mx4_quantize(const uint16_t* w13, const uint16_t* w2, int32_t E, int32_t H, int32_t I,
+                     uint8_t* w13_codes, uint8_t* w13_scales, uint8_t* w2_codes,
+                     uint8_t* w2_scales, moe_stream_t stream);
+int moe_mx4_dequantize(const uint8_t* codes, const uint8_t* scales, int32_t which, int32_t E,
+                       int32_t H, int32_t I, uint16_t* w, moe_stream_t stream);
+int moe_forward_mx4(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
+                    const uint8_t* w13_codes, const uint8_t* w13_scales,
+                    const uint8_t* w2_codes, const uint8_t* w2_scales,
+                    const uint16_t* residual, const uint16_t* norm_w, float eps,
+                    int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k, int32_t block,
+                    uint16_t* out, uint16_t* residual_out,
+                    int32_t* topk_ids_out, float* topk_w_out,
+                    int32_t* sorted_ids_out, int32_t* block_expert_out, int32_t* num_padded_out,
+                    void* workspace, size_t workspace_bytes,
+                    const moe_event_t* stage_events, moe_stream_t stream);
+
+/*
  * moe_forward for callers that cannot allocate device memory (code under HIP graph capture,
  * tight serving loops, harnesses that forbid hipMalloc): the same five steps and outputs as
  * moe_forward, with the workspace taken from a static device array of

@@ -20,7 +20,9 @@ __all__ = [
     "moe_finalize", "moe_forward", "moe_mx_quantize", "moe_mx_dequantize", "moe_forward_mx",
     "moe_gemm_tile_rows", "moe_gemm_tile_rows_mx", "moe_forward_self_routes",
     "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "moe_prepared_w13_bytes",
-    "moe_prepared_w2_bytes", "moe_prepare_weights", "moe_forward_prepared", "HipEvent",
+    "moe_prepared_w2_bytes", "moe_prepare_weights", "moe_forward_prepared",
+    "moe_mx4_weight_bytes", "moe_mx4_quantize", "moe_mx4_dequantize", "moe_forward_mx4",
+    "HipEvent",
 ]
 
 _PKG_DIR = os.path.dirname(os.path.abspath(__file__))
@@ -61,6 +63,14 @@ _PROTOS = {
     "moe_forward_prepared": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, ctypes.c_float,
                                             _i32, _i32, _i32, _i32, _i32, _i32,
                                             _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
+    "moe_mx4_weight_bytes": (ctypes.c_int, [_i32, _i32, _i32, ctypes.POINTER(_sz),
+                                            ctypes.POINTER(_sz), ctypes.POINTER(_sz),
+                                            ctypes.POINTER(_sz)]),
+    "moe_mx4_quantize": (ctypes.c_int, [_p, _p, _i32, _i32, _i32, _p, _p, _p, _p, _p]),
+    "moe_mx4_dequantize": (ctypes.c_int, [_p, _p, _i32, _i32, _i32, _i32, _p, _p]),
+    "moe_forward_mx4": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float,
+                                       _i32, _i32, _i32, _i32, _i32, _i32,
+                                       _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
     "moe_mx_quantize": (ctypes.c_int, [_p, ctypes.c_int64, _i32, _p, _p, _p]),
     "moe_mx_dequantize": (ctypes.c_int, [_p, _p, ctypes.c_int64, _i32, _p, _p]),
     "moe_forward_mx": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float,
@@ -380,6 +390,105 @@ def moe_forward_prepared(x, router_w, router_bias, w13_prepared, w2_prepared, I:
         _ptr(residual_out), _ptr(topk_ids_out), _ptr(topk_w_out), _ptr(sorted_ids_out),
         _ptr(block_expert_out), _ptr(num_padded_out), _ptr(workspace), workspace.numel(), ev,
         _stream(stream)))
+
+
+def moe_mx4_weight_bytes(E: int, H: int, I: int):
+    """(W13 codes, W13 scales, W2 codes, W2 scales) bytes of the MXFP4 panels."""
+    out = [_sz() for _ in range(4)]
+    _check("moe_mx4_weight_bytes", load_library().moe_mx4_weight_bytes(
+        E, H, I, *[ctypes.byref(o) for o in out]))
+    return tuple(int(o.value) for o in out)
+
+
+def moe_mx4_quantize(w13, w2, w13_codes, w13_scales, w2_codes, w2_scales, stream=None):
+    """Natural bf16 W13 [E, 2I, H] / W2 [E, H, I] -> MXFP4 panels (uint8 tensors of the sizes
+    moe_mx4_weight_bytes gives); a (w, codes, scales) triple may be all None."""
+    if w13 is not None:
+        E, two_i, H = w13.shape
+        I = two_i // 2
+    elif w2 is not None:
+        E, H, I = w2.shape
+    else:
+        raise ValueError("nothing to quantize")
+    n = moe_mx4_weight_bytes(E, H, I)
+    for name, w, c, sc, shape, nc, ns in (("w13", w13, w13_codes, w13_scales, (E, 2 * I, H), n[0], n[1]),
+                                          ("w2", w2, w2_codes, w2_scales, (E, H, I), n[2], n[3])):
+        if (w is None) != (c is None) or (w is None) != (sc is None):
+            raise ValueError(f"{name}, its codes and scales must be given together")
+        if w is not None:
+            _need(w, name, torch.bfloat16, shape)
+            _need(c, name + "_codes", torch.uint8)
+            _need(sc, name + "_scales", torch.uint8)
+            if c.numel() < nc or sc.numel() < ns:
+                raise ValueError(f"{name} codes / scales smaller than moe_mx4_weight_bytes")
+    _check("moe_mx4_quantize", load_library().moe_mx4_quantize(
+        _ptr(w13), _ptr(w2), E, H, I, _ptr(w13_codes), _ptr(w13_scales), _ptr(w2_codes),
+        _ptr(w2_scales), _stream(stream)))
+
+
+def moe_mx4_dequantize(codes, scales, which: int, E: int, H: int, I: int, w, stream=None):
+    """MXFP4 panels of W13 (which = 13) or W2 (which = 2) -> the natural bf16 stack w."""
+    n = moe_mx4_weight_bytes(E, H, I)
+    nc, ns, shape = (n[0], n[1], (E, 2 * I, H)) if which == 13 else (n[2], n[3], (E, H, I))
+    _need(codes, "codes", torch.uint8)
+    _need(scales, "scales", torch.uint8)
+    _need(w, "w", torch.bfloat16, shape)
+    if codes.numel() < nc or scales.numel() < ns:
+        raise ValueError("codes / scales smaller than moe_mx4_weight_bytes")
+    _check("moe_mx4_dequantize", load_library().moe_mx4_dequantize(
+        _ptr(codes), _ptr(scales), which, E, H, I, _ptr(w), _stream(stream)))
+
+
+def moe_forward_mx4(x, router_w, router_bias, w13_codes, w13_scales, w2_codes, w2_scales, I: int,
+                    residual, norm_w, eps: float, top_k: int, block: int, out, workspace,
+                    residual_out=None, topk_ids_out=None, topk_w_out=None, sorted_ids_out=None,
+                    block_expert_out=None, num_padded_out=None,
+                    stage_events: Optional[Sequence["HipEvent"]] = None, stream=None):
+    """moe_forward on MXFP4 panels (intermediate size I)."""
+    M, H = x.shape
+    E = router_w.shape[0]
+    _need(x, "x", torch.bfloat16)
+    _need(router_w, "router_w", torch.bfloat16, (E, H))
+    if router_bias is not None:
+        _need(router_bias, "router_bias", torch.float32, (E,))
+    n = moe_mx4_weight_bytes(E, H, I)
+    for name, t, nb in (("w13_codes", w13_codes, n[0]), ("w13_scales", w13_scales, n[1]),
+                        ("w2_codes", w2_codes, n[2]), ("w2_scales", w2_scales, n[3])):
+        _need(t, name, torch.uint8)
+        if t.numel() < nb:
+            raise ValueError(f"{name} smaller than moe_mx4_weight_bytes")
+    _need(residual, "residual", torch.bfloat16, (M, H))
+    _need(norm_w, "norm_w", torch.bfloat16, (H,))
+    _need(out, "out", torch.bfloat16, (M, H))
+    _need(workspace, "workspace", torch.uint8)
+    if residual_out is not None:
+        _need(residual_out, "residual_out", torch.bfloat16, (M, H))
+    cap = moe_align_capacity(M, top_k, E, block)
+    if topk_ids_out is not None:
+        _need(topk_ids_out, "topk_ids_out", torch.int32, (M, top_k))
+    if topk_w_out is not None:
+        _need(topk_w_out, "topk_w_out", torch.float32, (M, top_k))
+    if sorted_ids_out is not None:
+        _need(sorted_ids_out, "sorted_ids_out", torch.int32)
+        if sorted_ids_out.numel() < cap:
+            raise ValueError("sorted_ids_out smaller than the plan capacity")
+    if block_expert_out is not None:
+        _need(block_expert_out, "block_expert_out", torch.int32)
+        if block_expert_out.numel() < cap // block:
+            raise ValueError("block_expert_out smaller than capacity / block")
+    if num_padded_out is not None:
+        _need(num_padded_out, "num_padded_out", torch.int32)
+    ev = None
+    if stage_events is not None:
+        if len(stage_events) != 6:
+            raise ValueError("stage_events must hold 6 events")
+        ev = (ctypes.c_void_p * 6)(*[e.handle for e in stage_events])
+    _check("moe_forward_mx4", load_library().moe_forward_mx4(
+        _ptr(x), _ptr(router_w), _ptr(router_bias), _ptr(w13_codes), _ptr(w13_scales),
+        _ptr(w2_codes), _ptr(w2_scales), _ptr(residual), _ptr(norm_w), float(eps), M, H, E, I,
+        top_k, block, _ptr(out), _ptr(residual_out), _ptr(topk_ids_out), _ptr(topk_w_out),
+        _ptr(sorted_ids_out), _ptr(block_expert_out), _ptr(num_padded_out), _ptr(workspace),
+        workspace.numel(), ev, _stream(stream)))
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20   # MOE_NOALLOC_SCRATCH_BYTES of include/moe.h

@@ -16,6 +16,16 @@
 //        rows n*512 + 64w + 16j + lane%16 (zero past H), K values as above.
 // A wave's whole weight stream for one (expert, N tile) is contiguous: (K/32) x 4 KiB.
 //
+// MXFP4 weights (OCP MX: E2M1 elements, one E8M0 scale byte per 32 values along K) use the
+// same panel order: for wave w, N tile n, K step s (one 32-value block), lane l holds the 8
+// values of tile j as 4 code bytes (value 2b in the low nibble of byte b, 2b + 1 in the
+// high one), the 4 tiles' bytes together (16 bytes per lane, 1 KiB per step and wave), and
+// the step's scale bytes follow as [16 rows][4 tiles] (64 bytes per step and wave):
+//   W13q [E][I/256][8][H/32][64 lanes][4 tiles][4 bytes], W13s [E][I/256][8][H/32][16][4]
+//   W2q  [E][ceil(H/512)][8][I/32][64][4][4],             W2s  [E][ceil(H/512)][8][I/32][16][4]
+// with the rows of the bf16 panels (rows past H: codes and scale bytes 0).  Each step's 4
+// weight fragments are dequantized in registers with v_cvt_scalef32_pk_bf16_fp4 (exact).
+//
 // Workgroup = 8 waves; item = one token tile (BM = 64 or 128 plan rows of one expert) x one
 // N tile (up: 256 act columns = 512 weight rows; down: 512 output columns).  Wave w owns 4
 // weight row tiles (64 rows) x all BM/16 token tiles.  Per MFMA K step of 32 values a wave
@@ -33,7 +43,8 @@ namespace moe {
 
 constexpr int kFragWaves = 8;
 constexpr int kFragKC = 64;            // K values per chunk (2 MFMA K steps)
-constexpr int kFragRS = 4;             // weight register ring, in K steps of 32 values
+constexpr int kFragRS = 4;             // weight register ring, in K steps of 32 values (bf16)
+constexpr int kFragRS4 = 6;            // the same for MXFP4 codes
 constexpr int kFragTS = 4;             // token LDS ring stages
 
 int frag_up_columns() { return 256; }
@@ -111,6 +122,178 @@ hipError_t launch_prepare_weights(const uint16_t* w13, const uint16_t* w2, int E
 }
 
 // ---------------------------------------------------------------------------------------
+// MXFP4 panels: quantization (natural bf16 stacks -> panels) and dequantization back
+// ---------------------------------------------------------------------------------------
+// E2M1 code of x (the weight times 2^-s, |x| < 8 by the choice of s): the nearest of
+// 0, 0.5, 1, 1.5, 2, 3, 4, 6, a tie going to the neighbour with mantissa bit 0 -- the
+// comparisons below put every midpoint on that side; above 6 the largest.  Zero of either
+// sign, and anything that rounds to it, is +0.
+__device__ __forceinline__ uint32_t e2m1_code(float x) {
+  const float a = fabsf(x);
+  const uint32_t c = a <= 0.25f ? 0u : a < 0.75f ? 1u : a <= 1.25f ? 2u : a < 1.75f ? 3u
+                   : a <= 2.5f ? 4u : a < 3.5f ? 5u : a <= 5.0f ? 6u : 7u;
+  return (x < 0.0f && c != 0u) ? (c | 8u) : c;
+}
+
+// E8M0 byte of a 32-value block from its largest bf16 magnitude pattern: s = floor(log2
+// amax) - 2 = exponent field - 129 for a normal maximum, clamped to [-127, 127] (zero and
+// subnormal maxima give -127, byte 0).
+__device__ __forceinline__ int mx4_scale_exp(uint32_t amax_bits) {
+  const int e = (int)((amax_bits >> 7) & 0xFF);
+  const int s = e > 0 ? e - 129 : -127;
+  return s < -127 ? -127 : (s > 127 ? 127 : s);
+}
+
+// 4 code bytes (8 E2M1 values) and their block's scale byte -> one bf16 MFMA fragment (8
+// values, exact: a 4-bit significand times a power of two).
+__device__ __forceinline__ u32x4 mx4_dequant8(uint32_t codes, uint32_t scale_byte) {
+  const float scale = __uint_as_float(scale_byte ? scale_byte << 23 : 0x00400000u);
+#define MOE_CVT4(b) \
+  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, b))
+  return u32x4{MOE_CVT4(0), MOE_CVT4(1), MOE_CVT4(2), MOE_CVT4(3)};
+#undef MOE_CVT4
+}
+
+// One thread per (expert, N tile, wave, step, lane): for each of the 4 tiles, the row's
+// 32-value block of this step (read whole, for its maximum), its scale, and the lane's 8
+// values encoded into 4 bytes; lanes 0..15 also write the scale bytes of row `lane`.
+// W13 rows (gate / up interleaved per N tile) when UP, else W2 rows (zero past H).
+template <bool UP>
+__global__ __launch_bounds__(256) void mx4_quantize_panels_kernel(
+    const uint16_t* __restrict__ w, int E, int H, int I, uint8_t* __restrict__ codes,
+    uint8_t* __restrict__ scales) {
+  const int K = UP ? H : I;
+  const int steps = K / 32;
+  const int nnt = UP ? I / 256 : (H + 511) / 512;
+  const size_t threads = (size_t)E * nnt * kFragWaves * steps * 64;
+  for (size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x; g < threads;
+       g += (size_t)gridDim.x * blockDim.x) {
+    size_t r = g;
+    const int lane = (int)(r % 64); r /= 64;
+    const int st = (int)(r % steps); r /= steps;
+    const int wv = (int)(r % kFragWaves); r /= kFragWaves;
+    const int n = (int)(r % nnt); r /= nnt;
+    const int e = (int)r;
+    uint32_t word[4], sbyte[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int row;
+      bool on = true;
+      if (UP) {
+        const int col = n * 256 + 32 * wv + 16 * (j & 1) + (lane & 15);
+        row = j < 2 ? col : I + col;
+      } else {
+        row = n * 512 + 64 * wv + 16 * j + (lane & 15);
+        on = row < H;
+      }
+      word[j] = 0u;
+      sbyte[j] = 0u;
+      if (!on) continue;
+      const uint16_t* blk = w + ((size_t)e * (UP ? 2 * I : H) + row) * K + 32 * st;
+      u32x4 v[4];
+      uint32_t amax = 0u;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        v[q] = ld16(blk + 8 * q);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) {
+          const uint32_t lo = v[q][h] & 0x7FFFu, hi = (v[q][h] >> 16) & 0x7FFFu;
+          amax = max(amax, max(lo, hi));
+        }
+      }
+      const int sexp = mx4_scale_exp(amax);
+      sbyte[j] = (uint32_t)(sexp + 127);
+      const float inv = __uint_as_float((uint32_t)(127 - sexp) << 23);   // 2^-s, exact
+      const u32x4 mine = v[lane >> 4];                                     // this lane's 8 values
+      uint32_t packed = 0u;
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const uint32_t c0 = e2m1_code(bf16lo(mine[h]) * inv);
+        const uint32_t c1 = e2m1_code(bf16hi(mine[h]) * inv);
+        packed |= (c0 | (c1 << 4)) << (8 * h);
+      }
+      word[j] = packed;
+    }
+    const size_t stepi = (((size_t)e * nnt + n) * kFragWaves + wv) * steps + st;
+    st16(codes + stepi * 1024 + lane * 16, u32x4{word[0], word[1], word[2], word[3]});
+    if (lane < 16)
+      *reinterpret_cast<uint32_t*>(scales + stepi * 64 + lane * 4) =
+          sbyte[0] | (sbyte[1] << 8) | (sbyte[2] << 16) | (sbyte[3] << 24);
+  }
+}
+
+// The inverse: panels -> natural bf16 rows (with the GEMMs' dequantization), same threads.
+template <bool UP>
+__global__ __launch_bounds__(256) void mx4_dequantize_panels_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int E, int H, int I,
+    uint16_t* __restrict__ w) {
+  const int K = UP ? H : I;
+  const int steps = K / 32;
+  const int nnt = UP ? I / 256 : (H + 511) / 512;
+  const size_t threads = (size_t)E * nnt * kFragWaves * steps * 64;
+  for (size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x; g < threads;
+       g += (size_t)gridDim.x * blockDim.x) {
+    size_t r = g;
+    const int lane = (int)(r % 64); r /= 64;
+    const int st = (int)(r % steps); r /= steps;
+    const int wv = (int)(r % kFragWaves); r /= kFragWaves;
+    const int n = (int)(r % nnt); r /= nnt;
+    const int e = (int)r;
+    const size_t stepi = (((size_t)e * nnt + n) * kFragWaves + wv) * steps + st;
+    const u32x4 c = ld16(codes + stepi * 1024 + lane * 16);
+    const uint32_t sc = *reinterpret_cast<const uint32_t*>(scales + stepi * 64 + (lane & 15) * 4);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int row;
+      if (UP) {
+        const int col = n * 256 + 32 * wv + 16 * (j & 1) + (lane & 15);
+        row = j < 2 ? col : I + col;
+      } else {
+        row = n * 512 + 64 * wv + 16 * j + (lane & 15);
+        if (row >= H) continue;
+      }
+      st16(w + ((size_t)e * (UP ? 2 * I : H) + row) * K + 32 * st + 8 * (lane >> 4),
+           mx4_dequant8(c[j], (sc >> (8 * j)) & 0xFFu));
+    }
+  }
+}
+
+size_t mx4_codes_bytes(int E, int H, int I, bool w13) {
+  return w13 ? (size_t)E * 2 * I * H / 2 : (size_t)E * ((H + 511) / 512) * 512 * I / 2;
+}
+size_t mx4_scales_bytes(int E, int H, int I, bool w13) {
+  return w13 ? (size_t)E * 2 * I * H / 32 : (size_t)E * ((H + 511) / 512) * 512 * I / 32;
+}
+
+hipError_t launch_mx4_quantize(const uint16_t* w, bool w13, int E, int H, int I, uint8_t* codes,
+                               uint8_t* scales, hipStream_t s) {
+  if (H % 64 != 0 || I % 256 != 0) return hipErrorInvalidValue;
+  const size_t threads = mx4_codes_bytes(E, H, I, w13) / 16;
+  const long grid = std::min<long>((long)((threads + 255) / 256), 1L << 20);
+  if (w13)
+    hipLaunchKernelGGL(mx4_quantize_panels_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s, w,
+                       E, H, I, codes, scales);
+  else
+    hipLaunchKernelGGL(mx4_quantize_panels_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s, w,
+                       E, H, I, codes, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_mx4_dequantize(const uint8_t* codes, const uint8_t* scales, bool w13, int E,
+                                 int H, int I, uint16_t* w, hipStream_t s) {
+  if (H % 64 != 0 || I % 256 != 0) return hipErrorInvalidValue;
+  const size_t threads = mx4_codes_bytes(E, H, I, w13) / 16;
+  const long grid = std::min<long>((long)((threads + 255) / 256), 1L << 20);
+  if (w13)
+    hipLaunchKernelGGL(mx4_dequantize_panels_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s,
+                       codes, scales, E, H, I, w);
+  else
+    hipLaunchKernelGGL(mx4_dequantize_panels_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s,
+                       codes, scales, E, H, I, w);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
 // The GEMM
 // ---------------------------------------------------------------------------------------
 template <int BM>
@@ -143,34 +326,39 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const void* base, 
 // compiler's own load waits exact).  The ring is a __restrict__ parameter so that the
 // compiler can tell the token copies in flight apart from the LDS reads (without it, it
 // drains every load before each fragment read).
-template <int BM, bool UP, int WPOL, int NA>
+template <int BM, bool UP, int WPOL, int NA, bool FP4>
 __device__ __forceinline__ void frag_item(
     unsigned char* __restrict__ tlds, const uint16_t* __restrict__ tok_src,
-    const uint16_t* __restrict__ wp, const int32_t* __restrict__ row_ids, int start, int nlive,
-    int e, int ntile, int n_ntiles, int K, int ncols, int I, int top_k,
-    uint16_t* __restrict__ act, uint16_t* __restrict__ y) {
+    const void* __restrict__ wp, const uint8_t* __restrict__ wsc,
+    const int32_t* __restrict__ row_ids, int start, int nlive, int e, int ntile, int n_ntiles,
+    int K, int ncols, int I, int top_k, uint16_t* __restrict__ act, uint16_t* __restrict__ y) {
   using C = FragCfg<BM>;
   constexpr int MT = C::MT;
-  constexpr int TS = kFragTS, RS = kFragRS;
+  constexpr int TS = kFragTS;
+  // weight ring depth in K steps and loads per step: bf16 4 fragments (16 VGPRs a step);
+  // MXFP4 one 16-byte load of codes and one 4-byte load of scale bytes (5 VGPRs a step)
+  constexpr int RS = FP4 ? kFragRS4 : kFragRS;
+  constexpr int WPS = FP4 ? 2 : 4;
   // token copies: copy f (0 .. TCOPIES-1) of a chunk covers rows 8h..8h+7 (h = f % 2) of
   // token tile f / 2; wave w issues copies w, w + 8, ... (BM = 64: one each of the 8;
   // BM = 128: two each of the 16)
   constexpr int TCPW = C::TCOPIES / kFragWaves;
   static_assert(TCPW * kFragWaves == C::TCOPIES, "token copies must split evenly over the waves");
   // Every chunk issues the token copies of chunk c + TS - 1, then the weights of steps
-  // 2c + RS and 2c + 1 + RS (4 loads each) -- always, with the chunk and step clamped to the
-  // last one, so the count of this wave's loads issued after the token copies of chunk c is
-  // fixed: 8 + (TS - 2) (TCPW + 8) in the steady state, at least (TS - 2) TCPW + 4 RS after
-  // the prologue (token copies of chunks 0..TS-2, then the weights of steps 0..RS-1).
-  constexpr int kAfterT = 2 * 4 + (TS - 2) * (TCPW + 2 * 4);
-  constexpr int kAfterT0 = (TS - 2) * TCPW + RS * 4;
+  // 2c + RS and 2c + 1 + RS (WPS loads each) -- always, with the chunk and step clamped to
+  // the last one, so the count of this wave's loads issued after the token copies of chunk c
+  // is fixed: 2 WPS + (TS - 2) (TCPW + 2 WPS) in the steady state, at least
+  // (TS - 2) TCPW + WPS RS after the prologue (token copies of chunks 0..TS-2, then the
+  // weights of steps 0..RS-1).
+  constexpr int kAfterT = 2 * WPS + (TS - 2) * (TCPW + 2 * WPS);
+  constexpr int kAfterT0 = (TS - 2) * TCPW + RS * WPS;
   constexpr int kWaitT = kAfterT < kAfterT0 ? kAfterT : kAfterT0;
   static_assert(kWaitT <= 63, "vmcnt range");
   // The weights of step st were issued at the end of step st - RS (or in the prologue);
   // after them this wave issued at least the weights of RS - 1 more steps and the token
   // copies of one chunk start, so they have landed once at most that many loads are
   // outstanding.
-  constexpr int kWaitW = 4 * (RS - 1) + TCPW;
+  constexpr int kWaitW = WPS * (RS - 1) + TCPW;
 
   // the wave index as a scalar: the weight stream's base is the same for the whole wave
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -182,10 +370,16 @@ __device__ __forceinline__ void frag_item(
   // this wave's weight stream (nsteps x 4 KiB, contiguous): fragment (step s, tile j) at byte
   // s * 4096 + j * 1024, lane l's 16 bytes at + 16 l; loaded through a buffer resource (the
   // step offset in a scalar register, one vector register for all lanes' offsets)
-  const __amdgpu_buffer_rsrc_t wrsrc = stream_rsrc(
-      wp + (((size_t)e * n_ntiles + ntile) * kFragWaves + wave) * (size_t)nsteps * 2048,
-      nsteps * 4096);
+  // (MXFP4: codes nsteps x 1 KiB, scale bytes nsteps x 64 B, lane l's scale word -- row
+  // l % 16 of the 4 tiles -- at 4 (l % 16))
+  const size_t stream = ((size_t)e * n_ntiles + ntile) * kFragWaves + wave;
+  const __amdgpu_buffer_rsrc_t wrsrc =
+      FP4 ? stream_rsrc(static_cast<const uint8_t*>(wp) + stream * nsteps * 1024, nsteps * 1024)
+          : stream_rsrc(static_cast<const uint16_t*>(wp) + stream * nsteps * 2048, nsteps * 4096);
+  const __amdgpu_buffer_rsrc_t srsrc =
+      stream_rsrc(FP4 ? wsc + stream * nsteps * 64 : static_cast<const uint8_t*>(wp), nsteps * 64);
   const int lane_off = lane * 16;
+  const int scale_off = (lane & 15) * 4;
   // token copies of this wave; rows past the tile's real rows read its first row
   const uint16_t* tsrc[TCPW];
 #pragma unroll
@@ -217,13 +411,22 @@ __device__ __forceinline__ void frag_item(
     return *reinterpret_cast<const u32x4*>(tlds + (size_t)(c % TS) * C::TSTAGE + t * 2048 +
                                            frag_off + q * 16);
   };
-  u32x4 wr[RS][4];
-  auto issue_w = [&](int st, u32x4 (&dst)[4]) {  // st is clamped to the last step
+  // bf16: wr[slot][j] is fragment j; MXFP4: wr[slot][0] holds the 4 tiles' code words and
+  // wsr[slot] their scale bytes
+  u32x4 wr[RS][FP4 ? 1 : 4];
+  uint32_t wsr[FP4 ? RS : 1];
+  auto issue_w = [&](int st, int slot) {  // st is clamped to the last step
     const int ss = st < nsteps ? st : nsteps - 1;
+    if constexpr (FP4) {
+      wr[slot][0] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, lane_off, ss * 1024, WPOL));
+      wsr[slot] = __builtin_amdgcn_raw_buffer_load_b32(srsrc, scale_off, ss * 64, WPOL);
+    } else {
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      dst[j] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, lane_off, ss * 4096 + j * 1024, WPOL));
+      for (int j = 0; j < 4; ++j)
+        wr[slot][j] = __builtin_bit_cast(
+            u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, lane_off, ss * 4096 + j * 1024, WPOL));
+    }
   };
 
   static_assert(NA >= 1 && NA <= MT, "computed token tiles");
@@ -236,7 +439,7 @@ __device__ __forceinline__ void frag_item(
 #pragma unroll
   for (int p = 0; p < TS - 1; ++p) issue_t(p);
 #pragma unroll
-  for (int u = 0; u < RS; ++u) issue_w(u, wr[u]);
+  for (int u = 0; u < RS; ++u) issue_w(u, u);
 
   // step st (ring slot u % RS, u compile-time after unrolling): on a chunk's first step wait
   // for its token copies, publish them and start the copies TS - 1 chunks ahead; NA token
@@ -251,13 +454,26 @@ __device__ __forceinline__ void frag_item(
       issue_t(c + TS - 1);
     }
     frag_wait_vmcnt<kWaitW>();   // this step's weights are in registers
+    if constexpr (FP4) {
+      // keep the dequantization of this step's codes below the wait: the empty asm takes the
+      // registers as inputs and outputs, so nothing computed from them moves above it (the
+      // compiler would otherwise hoist the scale arithmetic of later steps and drain every
+      // load to feed it)
+      asm volatile("" : "+v"(wr[u % RS][0]), "+v"(wsr[u % RS]));
+    }
+    u32x4 wa[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      if constexpr (FP4) wa[j] = mx4_dequant8(wr[u % RS][0][j], (wsr[u % RS] >> (8 * j)) & 0xFFu);
+      else wa[j] = wr[u % RS][j];
+    }
+    issue_w(st + RS, u % RS);
 #pragma unroll
     for (int s = 0; s < NA; ++s) {
       const u32x4 xb = tfrag(c, s, ks);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[j][s] = mfma16x16x32(wr[u % RS][j], xb, acc[j][s]);
+      for (int j = 0; j < 4; ++j) acc[j][s] = mfma16x16x32(wa[j], xb, acc[j][s]);
     }
-    issue_w(st + RS, wr[u % RS]);
   };
   // whole groups of 2 RS steps (whole chunks) without a branch, then the rest
   int s0 = 0;
@@ -332,9 +548,10 @@ struct ExpertMajorWalk {
   }
 };
 
-template <int BM, bool UP, int WPOL>
+template <int BM, bool UP, int WPOL, bool FP4>
 __global__ __launch_bounds__(64 * kFragWaves) void expert_frag_kernel(
-    const uint16_t* __restrict__ tok_src, const uint16_t* __restrict__ wp,
+    const uint16_t* __restrict__ tok_src, const void* __restrict__ wp,
+    const uint8_t* __restrict__ wsc,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
     const int2* __restrict__ tiles, const int2* __restrict__ tile_groups,
     const int32_t* __restrict__ num_tiles, int n_ntiles, int K, int ncols, int I, int top_k,
@@ -351,19 +568,20 @@ __global__ __launch_bounds__(64 * kFragWaves) void expert_frag_kernel(
     constexpr int MT = FragCfg<BM>::MT;
     constexpr int NS = BM == 64 ? 1 : MT / 2;
     if (tile.y <= 16 * NS)
-      frag_item<BM, UP, WPOL, NS>(tlds, tok_src, wp, sorted_ids + tile.x, tile.x, tile.y,
-                                  block_expert[tile.x / block], ntile, n_ntiles, K, ncols, I,
-                                  top_k, act, y);
+      frag_item<BM, UP, WPOL, NS, FP4>(tlds, tok_src, wp, wsc, sorted_ids + tile.x, tile.x,
+                                       tile.y, block_expert[tile.x / block], ntile, n_ntiles, K,
+                                       ncols, I, top_k, act, y);
     else
-      frag_item<BM, UP, WPOL, MT>(tlds, tok_src, wp, sorted_ids + tile.x, tile.x, tile.y,
-                                  block_expert[tile.x / block], ntile, n_ntiles, K, ncols, I,
-                                  top_k, act, y);
+      frag_item<BM, UP, WPOL, MT, FP4>(tlds, tok_src, wp, wsc, sorted_ids + tile.x, tile.x,
+                                       tile.y, block_expert[tile.x / block], ntile, n_ntiles, K,
+                                       ncols, I, top_k, act, y);
     __syncthreads();  // the next item's first token copies reuse the ring
   }
 }
 
-template <int BM, bool UP, int WPOL>
-static hipError_t launch_frag(const uint16_t* src, const uint16_t* wp, const int32_t* sorted_ids,
+template <int BM, bool UP, int WPOL, bool FP4 = false>
+static hipError_t launch_frag(const uint16_t* src, const void* wp, const uint8_t* wsc,
+                              const int32_t* sorted_ids,
                               const int32_t* block_expert, const int2* tiles,
                               const int2* tile_groups, const int32_t* num_tiles, int max_tiles,
                               int K, int ncols, int I, int top_k, int block, uint16_t* act,
@@ -374,8 +592,8 @@ static hipError_t launch_frag(const uint16_t* src, const uint16_t* wp, const int
   const long items = (long)max_tiles * n_ntiles;
   // 64-row tiles walk several items per workgroup, 128-row tiles take one each
   const long grid = BM == 64 ? walk_grid(items, 160 * 1024) : (items + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((expert_frag_kernel<BM, UP, WPOL>), dim3((unsigned)grid),
-                     dim3(64 * kFragWaves), 0, s, src, wp, sorted_ids, block_expert, tiles,
+  hipLaunchKernelGGL((expert_frag_kernel<BM, UP, WPOL, FP4>), dim3((unsigned)grid),
+                     dim3(64 * kFragWaves), 0, s, src, wp, wsc, sorted_ids, block_expert, tiles,
                      tile_groups, num_tiles, n_ntiles, K, ncols, I, top_k, block, act, y);
   return hipGetLastError();
 }
@@ -388,7 +606,8 @@ hipError_t launch_expert_up_frag(const uint16_t* x, const uint16_t* w13p, const 
                                  int tile_rows, bool stream_weights, int H, int I, int top_k,
                                  int block, uint16_t* act, hipStream_t s) {
 #define MOE_FRAG_UP(BM, POL)                                                                    \
-  return launch_frag<BM, true, POL>(x, w13p, sorted_ids, block_expert, tiles, tile_groups,     \
+  return launch_frag<BM, true, POL>(x, w13p, nullptr, sorted_ids, block_expert, tiles,        \
+                                    tile_groups,                                              \
                                     num_tiles, max_tiles, H, I, I, top_k, block, act, nullptr, s)
   if (tile_rows == 64) {
     if (stream_weights) MOE_FRAG_UP(64, kFragNT);
@@ -409,7 +628,8 @@ hipError_t launch_expert_down_frag(const uint16_t* act, const uint16_t* w2p,
                                    bool stream_weights, int H, int I, int top_k, int block,
                                    uint16_t* y, hipStream_t s) {
 #define MOE_FRAG_DOWN(BM, POL)                                                                  \
-  return launch_frag<BM, false, POL>(act, w2p, sorted_ids, block_expert, tiles, tile_groups,   \
+  return launch_frag<BM, false, POL>(act, w2p, nullptr, sorted_ids, block_expert, tiles,       \
+                                     tile_groups,                                             \
                                      num_tiles, max_tiles, I, H, I, top_k, block, nullptr, y, s)
   if (tile_rows == 64) {
     if (stream_weights) MOE_FRAG_DOWN(64, kFragNT);
@@ -420,6 +640,50 @@ hipError_t launch_expert_down_frag(const uint16_t* act, const uint16_t* w2p,
     MOE_FRAG_DOWN(128, 0);
   }
 #undef MOE_FRAG_DOWN
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_expert_up_frag4(const uint16_t* x, const uint8_t* w13q, const uint8_t* w13s,
+                                  const int32_t* sorted_ids, const int32_t* block_expert,
+                                  const int2* tiles, const int2* tile_groups,
+                                  const int32_t* num_tiles, int max_tiles, int tile_rows,
+                                  bool stream_weights, int H, int I, int top_k, int block,
+                                  uint16_t* act, hipStream_t s) {
+#define MOE_FRAG4_UP(BM, POL)                                                                   \
+  return launch_frag<BM, true, POL, true>(x, w13q, w13s, sorted_ids, block_expert, tiles,     \
+                                          tile_groups, num_tiles, max_tiles, H, I, I, top_k,  \
+                                          block, act, nullptr, s)
+  if (tile_rows == 64) {
+    if (stream_weights) MOE_FRAG4_UP(64, kFragNT);
+    MOE_FRAG4_UP(64, 0);
+  }
+  if (tile_rows == 128) {
+    if (stream_weights) MOE_FRAG4_UP(128, kFragNT);
+    MOE_FRAG4_UP(128, 0);
+  }
+#undef MOE_FRAG4_UP
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_expert_down_frag4(const uint16_t* act, const uint8_t* w2q, const uint8_t* w2s,
+                                    const int32_t* sorted_ids, const int32_t* block_expert,
+                                    const int2* tiles, const int2* tile_groups,
+                                    const int32_t* num_tiles, int max_tiles, int tile_rows,
+                                    bool stream_weights, int H, int I, int top_k, int block,
+                                    uint16_t* y, hipStream_t s) {
+#define MOE_FRAG4_DOWN(BM, POL)                                                                 \
+  return launch_frag<BM, false, POL, true>(act, w2q, w2s, sorted_ids, block_expert, tiles,    \
+                                           tile_groups, num_tiles, max_tiles, I, H, I, top_k, \
+                                           block, nullptr, y, s)
+  if (tile_rows == 64) {
+    if (stream_weights) MOE_FRAG4_DOWN(64, kFragNT);
+    MOE_FRAG4_DOWN(64, 0);
+  }
+  if (tile_rows == 128) {
+    if (stream_weights) MOE_FRAG4_DOWN(128, kFragNT);
+    MOE_FRAG4_DOWN(128, 0);
+  }
+#undef MOE_FRAG4_DOWN
   return hipErrorInvalidValue;
 }
 

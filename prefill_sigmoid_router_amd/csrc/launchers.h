@@ -129,6 +129,28 @@ hipError_t launch_expert_down_frag(const uint16_t* act, const uint16_t* w2p,
                                    bool stream_weights, int H, int I, int top_k, int block,
                                    uint16_t* y, hipStream_t s);
 
+// MXFP4 expert weights in the same panel order (E2M1 codes, 4 bytes per lane and tile; E8M0
+// scale bytes per 32-value block): sizes, quantization from / dequantization to the natural
+// stacks (w13 true: W13 [E, 2I, H], false: W2 [E, H, I]), and the grouped GEMMs on them.
+size_t mx4_codes_bytes(int E, int H, int I, bool w13);
+size_t mx4_scales_bytes(int E, int H, int I, bool w13);
+hipError_t launch_mx4_quantize(const uint16_t* w, bool w13, int E, int H, int I, uint8_t* codes,
+                               uint8_t* scales, hipStream_t s);
+hipError_t launch_mx4_dequantize(const uint8_t* codes, const uint8_t* scales, bool w13, int E,
+                                 int H, int I, uint16_t* w, hipStream_t s);
+hipError_t launch_expert_up_frag4(const uint16_t* x, const uint8_t* w13q, const uint8_t* w13s,
+                                  const int32_t* sorted_ids, const int32_t* block_expert,
+                                  const int2* tiles, const int2* tile_groups,
+                                  const int32_t* num_tiles, int max_tiles, int tile_rows,
+                                  bool stream_weights, int H, int I, int top_k, int block,
+                                  uint16_t* act, hipStream_t s);
+hipError_t launch_expert_down_frag4(const uint16_t* act, const uint8_t* w2q, const uint8_t* w2s,
+                                    const int32_t* sorted_ids, const int32_t* block_expert,
+                                    const int2* tiles, const int2* tile_groups,
+                                    const int32_t* num_tiles, int max_tiles, int tile_rows,
+                                    bool stream_weights, int H, int I, int top_k, int block,
+                                    uint16_t* y, hipStream_t s);
+
 // Weighted top-k combine + residual add + RMSNorm over fp32 or bf16 rows of y.
 hipError_t launch_finalize(const float* y, const float* topk_w, const uint16_t* residual,
                            const uint16_t* norm_w, float eps, int M, int H, int top_k,

@@ -276,7 +276,8 @@ struct ExpertWeights {
   const uint8_t* w2c = nullptr;
   const uint8_t* w2s = nullptr;
   bool prepared = false;  // w13 / w2 hold the fragment panels of moe_prepare_weights
-  bool mx() const { return w13c != nullptr; }
+  bool fp4 = false;       // w13c / w13s / w2c / w2s hold the MXFP4 panels of moe_mx4_quantize
+  bool mx() const { return w13c != nullptr && !fp4; }
 };
 
 int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
@@ -289,11 +290,14 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   if (!sizes_ok(M, H, E, I, top_k) || !(eps > 0.0f) || !isfinite(eps)) return MOE_ERR_INVALID_ARG;
   if (!gemm_block_ok(block)) return MOE_ERR_UNSUPPORTED;
   if (W.mx() && (H % 256 != 0 || I % 256 != 0)) return MOE_ERR_UNSUPPORTED;
-  if (W.prepared && (H % 64 != 0 || I % 256 != 0)) return MOE_ERR_UNSUPPORTED;
+  if ((W.prepared || W.fp4) && (H % 64 != 0 || I % 256 != 0)) return MOE_ERR_UNSUPPORTED;
   if (M == 0) return MOE_OK;
-  const bool w_ok = W.mx() ? (W.w13c && W.w13s && W.w2c && W.w2s && aligned(W.w13c, 16) &&
-                              aligned(W.w2c, 16) && aligned(W.w13s, 8) && aligned(W.w2s, 8))
-                           : (W.w13 && W.w2 && aligned(W.w13, 16) && aligned(W.w2, 16));
+  const bool w_ok =
+      W.fp4  ? (W.w13c && W.w13s && W.w2c && W.w2s && aligned(W.w13c, 16) && aligned(W.w2c, 16) &&
+                aligned(W.w13s, 4) && aligned(W.w2s, 4))
+      : W.mx() ? (W.w13c && W.w13s && W.w2c && W.w2s && aligned(W.w13c, 16) &&
+                  aligned(W.w2c, 16) && aligned(W.w13s, 8) && aligned(W.w2s, 8))
+               : (W.w13 && W.w2 && aligned(W.w13, 16) && aligned(W.w2, 16));
   if (!x || !router_w || !w_ok || !residual || !norm_w || !out) return MOE_ERR_INVALID_ARG;
   if (!aligned(x, 16) || !aligned(router_w, 16) || !aligned(residual, 16) ||
       !aligned(norm_w, 16) || !aligned(out, 16) ||
@@ -336,14 +340,17 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   const bool stream_w = stream_weights(M, E, top_k, trows);
   const int max_tiles = moe::tile_capacity(M * top_k, E, trows);
   // few ids: the up GEMM builds the plan itself (no align launch)
-  const bool self_route = !W.mx() && !W.prepared && self_routes(M, E, top_k, I);
+  const bool self_route = !W.mx() && !W.prepared && !W.fp4 && self_routes(M, E, top_k, I);
   if (!self_route &&
       moe::launch_align(ids, M * top_k, E, block, sorted, bexp, npad, trows, tiles, ntiles, s,
-                        W.prepared ? groups : nullptr) != hipSuccess)
+                        (W.prepared || W.fp4) ? groups : nullptr) != hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(2)) return MOE_ERR_HIP;
   hipError_t up_err;
-  if (W.prepared)
+  if (W.fp4)
+    up_err = moe::launch_expert_up_frag4(x, W.w13c, W.w13s, sorted, bexp, tiles, groups, ntiles,
+                                         max_tiles, trows, stream_w, H, I, top_k, block, act, s);
+  else if (W.prepared)
     up_err = moe::launch_expert_up_frag(x, W.w13, sorted, bexp, tiles, groups, ntiles, max_tiles,
                                         trows, stream_w, H, I, top_k, block, act, s);
   else if (self_route)
@@ -364,7 +371,11 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   if (up_err != hipSuccess) return MOE_ERR_HIP;
   if (!mark(3)) return MOE_ERR_HIP;
   hipError_t down_err;
-  if (W.prepared)
+  if (W.fp4)
+    down_err = moe::launch_expert_down_frag4(act, W.w2c, W.w2s, sorted, bexp, tiles, groups,
+                                             ntiles, max_tiles, trows, stream_w, H, I, top_k,
+                                             block, y, s);
+  else if (W.prepared)
     down_err = moe::launch_expert_down_frag(act, W.w2, sorted, bexp, tiles, groups, ntiles,
                                             max_tiles, trows, stream_w, H, I, top_k, block, y, s);
   else if (W.mx())
@@ -465,6 +476,69 @@ int moe_forward_prepared(const uint16_t* x, const uint16_t* router_w, const floa
   W.w13 = w13_prepared;
   W.w2 = w2_prepared;
   W.prepared = true;
+  return forward_impl(x, router_w, router_bias, W, residual, norm_w, eps, M, H, E, I, top_k, block,
+                      out, residual_out, topk_ids_out, topk_w_out, sorted_ids_out,
+                      block_expert_out, num_padded_out, workspace, workspace_bytes, stage_events,
+                      stream);
+}
+
+int moe_mx4_weight_bytes(int32_t E, int32_t H, int32_t I, size_t* w13_codes, size_t* w13_scales,
+                         size_t* w2_codes, size_t* w2_scales) {
+  if (E < 1 || E > kMaxE || H < 8 || H > kMaxH || H % 8 != 0 || I < 16 || I % 16 != 0)
+    return MOE_ERR_INVALID_ARG;
+  if (H % 64 != 0 || I % 256 != 0) return MOE_ERR_UNSUPPORTED;
+  if (w13_codes) *w13_codes = moe::mx4_codes_bytes(E, H, I, true);
+  if (w13_scales) *w13_scales = moe::mx4_scales_bytes(E, H, I, true);
+  if (w2_codes) *w2_codes = moe::mx4_codes_bytes(E, H, I, false);
+  if (w2_scales) *w2_scales = moe::mx4_scales_bytes(E, H, I, false);
+  return MOE_OK;
+}
+
+int moe_mx4_quantize(const uint16_t* w13, const uint16_t* w2, int32_t E, int32_t H, int32_t I,
+                     uint8_t* w13_codes, uint8_t* w13_scales, uint8_t* w2_codes,
+                     uint8_t* w2_scales, moe_stream_t stream) {
+  const int st = moe_mx4_weight_bytes(E, H, I, nullptr, nullptr, nullptr, nullptr);
+  if (st != MOE_OK) return st;
+  if ((w13 == nullptr) != (w13_codes == nullptr) || (w13 == nullptr) != (w13_scales == nullptr) ||
+      (w2 == nullptr) != (w2_codes == nullptr) || (w2 == nullptr) != (w2_scales == nullptr))
+    return MOE_ERR_INVALID_ARG;
+  if ((w13 && (!aligned(w13, 16) || !aligned(w13_codes, 16) || !aligned(w13_scales, 4))) ||
+      (w2 && (!aligned(w2, 16) || !aligned(w2_codes, 16) || !aligned(w2_scales, 4))))
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (w13 && moe::launch_mx4_quantize(w13, true, E, H, I, w13_codes, w13_scales, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (w2 && moe::launch_mx4_quantize(w2, false, E, H, I, w2_codes, w2_scales, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+int moe_mx4_dequantize(const uint8_t* codes, const uint8_t* scales, int32_t which, int32_t E,
+                       int32_t H, int32_t I, uint16_t* w, moe_stream_t stream) {
+  const int st = moe_mx4_weight_bytes(E, H, I, nullptr, nullptr, nullptr, nullptr);
+  if (st != MOE_OK) return st;
+  if ((which != 13 && which != 2) || !codes || !scales || !w || !aligned(codes, 16) ||
+      !aligned(scales, 4) || !aligned(w, 16))
+    return MOE_ERR_INVALID_ARG;
+  return hip_status(moe::launch_mx4_dequantize(codes, scales, which == 13, E, H, I, w,
+                                               (hipStream_t)stream));
+}
+
+int moe_forward_mx4(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
+                    const uint8_t* w13_codes, const uint8_t* w13_scales, const uint8_t* w2_codes,
+                    const uint8_t* w2_scales, const uint16_t* residual, const uint16_t* norm_w,
+                    float eps, int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k,
+                    int32_t block, uint16_t* out, uint16_t* residual_out, int32_t* topk_ids_out,
+                    float* topk_w_out, int32_t* sorted_ids_out, int32_t* block_expert_out,
+                    int32_t* num_padded_out, void* workspace, size_t workspace_bytes,
+                    const moe_event_t* stage_events, moe_stream_t stream) {
+  ExpertWeights W;
+  W.w13c = w13_codes;
+  W.w13s = w13_scales;
+  W.w2c = w2_codes;
+  W.w2s = w2_scales;
+  W.fp4 = true;
+  if (!w13_codes) return MOE_ERR_INVALID_ARG;
   return forward_impl(x, router_w, router_bias, W, residual, norm_w, eps, M, H, E, I, top_k, block,
                       out, residual_out, topk_ids_out, topk_w_out, sorted_ids_out,
                       block_expert_out, num_padded_out, workspace, workspace_bytes, stage_events,

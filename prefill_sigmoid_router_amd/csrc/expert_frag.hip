@@ -44,7 +44,9 @@ namespace moe {
 constexpr int kFragWaves = 8;
 constexpr int kFragKC = 64;            // K values per chunk (2 MFMA K steps)
 constexpr int kFragRS = 4;             // weight register ring, in K steps of 32 values (bf16)
-constexpr int kFragRS4 = 6;            // the same for MXFP4 codes
+constexpr int kFragRS4 = 6;            // the same for MXFP4 codes (128-row tiles)
+constexpr int kFragRS4Small = 16;      // ... and 64-row tiles, whose accumulators leave room
+                                       // (decode: 510 -> 472 us per layer against 6 steps)
 constexpr int kFragTS = 4;             // token LDS ring stages
 
 int frag_up_columns() { return 256; }
@@ -326,24 +328,24 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const void* base, 
 // compiler's own load waits exact).  The ring is a __restrict__ parameter so that the
 // compiler can tell the token copies in flight apart from the LDS reads (without it, it
 // drains every load before each fragment read).
-template <int BM, bool UP, int WPOL, int NA, bool FP4>
+template <int BM, bool UP, int WPOL, int NA, bool FP4, int NWG>
 __device__ __forceinline__ void frag_item(
     unsigned char* __restrict__ tlds, const uint16_t* __restrict__ tok_src,
     const void* __restrict__ wp, const uint8_t* __restrict__ wsc,
-    const int32_t* __restrict__ row_ids, int start, int nlive, int e, int ntile, int n_ntiles,
-    int K, int ncols, int I, int top_k, uint16_t* __restrict__ act, uint16_t* __restrict__ y) {
+    const int32_t* __restrict__ row_ids, int start, int nlive, int e, int ntile, int part,
+    int n_ntiles, int K, int ncols, int I, int top_k, uint16_t* __restrict__ act,
+    uint16_t* __restrict__ y) {
   using C = FragCfg<BM>;
   constexpr int MT = C::MT;
   constexpr int TS = kFragTS;
   // weight ring depth in K steps and loads per step: bf16 4 fragments (16 VGPRs a step);
   // MXFP4 one 16-byte load of codes and one 4-byte load of scale bytes (5 VGPRs a step)
-  constexpr int RS = FP4 ? kFragRS4 : kFragRS;
+  constexpr int RS = FP4 ? (BM == 64 ? kFragRS4Small : kFragRS4) : kFragRS;
   constexpr int WPS = FP4 ? 2 : 4;
   // token copies: copy f (0 .. TCOPIES-1) of a chunk covers rows 8h..8h+7 (h = f % 2) of
-  // token tile f / 2; wave w issues copies w, w + 8, ... (BM = 64: one each of the 8;
-  // BM = 128: two each of the 16)
-  constexpr int TCPW = C::TCOPIES / kFragWaves;
-  static_assert(TCPW * kFragWaves == C::TCOPIES, "token copies must split evenly over the waves");
+  // token tile f / 2; wave w of the NWG issues copies w, w + NWG, ...
+  constexpr int TCPW = C::TCOPIES / NWG;
+  static_assert(TCPW * NWG == C::TCOPIES, "token copies must split evenly over the waves");
   // Every chunk issues the token copies of chunk c + TS - 1, then the weights of steps
   // 2c + RS and 2c + 1 + RS (WPS loads each) -- always, with the chunk and step clamped to
   // the last one, so the count of this wave's loads issued after the token copies of chunk c
@@ -360,8 +362,10 @@ __device__ __forceinline__ void frag_item(
   // outstanding.
   constexpr int kWaitW = WPS * (RS - 1) + TCPW;
 
-  // the wave index as a scalar: the weight stream's base is the same for the whole wave
+  // the wave index as a scalar: the weight stream's base is the same for the whole wave;
+  // a workgroup of NWG < 8 waves takes part `part` of the panel's 8 wave streams
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int pw = part * NWG + wave;
   const int lane = threadIdx.x & 63;
   const int li = lane & 15, lg = lane >> 4;
   const int nch = K / kFragKC;
@@ -372,7 +376,7 @@ __device__ __forceinline__ void frag_item(
   // step offset in a scalar register, one vector register for all lanes' offsets)
   // (MXFP4: codes nsteps x 1 KiB, scale bytes nsteps x 64 B, lane l's scale word -- row
   // l % 16 of the 4 tiles -- at 4 (l % 16))
-  const size_t stream = ((size_t)e * n_ntiles + ntile) * kFragWaves + wave;
+  const size_t stream = ((size_t)e * n_ntiles + ntile) * kFragWaves + pw;
   const __amdgpu_buffer_rsrc_t wrsrc =
       FP4 ? stream_rsrc(static_cast<const uint8_t*>(wp) + stream * nsteps * 1024, nsteps * 1024)
           : stream_rsrc(static_cast<const uint16_t*>(wp) + stream * nsteps * 2048, nsteps * 4096);
@@ -384,7 +388,7 @@ __device__ __forceinline__ void frag_item(
   const uint16_t* tsrc[TCPW];
 #pragma unroll
   for (int i = 0; i < TCPW; ++i) {
-    const int f = wave + kFragWaves * i;
+    const int f = wave + NWG * i;
     const int rt = f >> 1, h = f & 1;
     const int r = 16 * rt + 8 * h + (lane >> 3);
     const int koff = 8 * ((lane & 7) ^ (lane >> 3) ^ h);
@@ -402,8 +406,7 @@ __device__ __forceinline__ void frag_item(
 #pragma unroll
     for (int i = 0; i < TCPW; ++i)
       __builtin_amdgcn_global_load_lds((global_void*)(tsrc[i] + cc * kFragKC),
-                                       (lds_void*)(base + (wave + kFragWaves * i) * 1024), 16, 0,
-                                       0);
+                                       (lds_void*)(base + (wave + NWG * i) * 1024), 16, 0, 0);
   };
   const int frag_off = (li >> 3) * 1024 + (li & 7) * 128;
   auto tfrag = [&](int c, int t, int ks) -> u32x4 {
@@ -495,7 +498,7 @@ __device__ __forceinline__ void frag_item(
     const int r = 16 * s + li;
     if (r >= nlive) continue;
     if (UP) {
-      const int col0 = ntile * 256 + 32 * wave;
+      const int col0 = ntile * 256 + 32 * pw;
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         const int n = col0 + 16 * h + 4 * lg;
@@ -509,7 +512,7 @@ __device__ __forceinline__ void frag_item(
       }
     } else {
       const int dst = row_ids[r];
-      const int col0 = ntile * 512 + 64 * wave;
+      const int col0 = ntile * 512 + 64 * pw;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int n = col0 + 16 * j + 4 * lg;
@@ -548,8 +551,8 @@ struct ExpertMajorWalk {
   }
 };
 
-template <int BM, bool UP, int WPOL, bool FP4>
-__global__ __launch_bounds__(64 * kFragWaves) void expert_frag_kernel(
+template <int BM, bool UP, int WPOL, bool FP4, int NWG>
+__global__ __launch_bounds__(64 * NWG) void expert_frag_kernel(
     const uint16_t* __restrict__ tok_src, const void* __restrict__ wp,
     const uint8_t* __restrict__ wsc,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
@@ -557,9 +560,13 @@ __global__ __launch_bounds__(64 * kFragWaves) void expert_frag_kernel(
     const int32_t* __restrict__ num_tiles, int n_ntiles, int K, int ncols, int I, int top_k,
     int block, uint16_t* __restrict__ act, uint16_t* __restrict__ y) {
   __shared__ __align__(16) unsigned char tlds[kFragTS * FragCfg<BM>::TSTAGE];
-  ExpertMajorWalk walk(*num_tiles, n_ntiles, tile_groups);
-  int ntile, ti;
-  while (walk.next(ntile, ti)) {
+  // items: (tile, N tile of the panels, part); a workgroup of NWG waves does 8 / NWG parts
+  // of an N tile, the parts counted as N tiles of their own in the walk
+  constexpr int PARTS = kFragWaves / NWG;
+  ExpertMajorWalk walk(*num_tiles, n_ntiles * PARTS, tile_groups);
+  int nt_part, ti;
+  while (walk.next(nt_part, ti)) {
+    const int ntile = nt_part / PARTS, part = nt_part % PARTS;
     const int2 tile = tiles[ti];
     // token tiles computed: all of them, or the first quarter (64-row tiles) / half
     // (128-row tiles) when that holds every real row (padding rows hold copies of the first
@@ -568,13 +575,13 @@ __global__ __launch_bounds__(64 * kFragWaves) void expert_frag_kernel(
     constexpr int MT = FragCfg<BM>::MT;
     constexpr int NS = BM == 64 ? 1 : MT / 2;
     if (tile.y <= 16 * NS)
-      frag_item<BM, UP, WPOL, NS, FP4>(tlds, tok_src, wp, wsc, sorted_ids + tile.x, tile.x,
-                                       tile.y, block_expert[tile.x / block], ntile, n_ntiles, K,
-                                       ncols, I, top_k, act, y);
+      frag_item<BM, UP, WPOL, NS, FP4, NWG>(tlds, tok_src, wp, wsc, sorted_ids + tile.x, tile.x,
+                                            tile.y, block_expert[tile.x / block], ntile, part,
+                                            n_ntiles, K, ncols, I, top_k, act, y);
     else
-      frag_item<BM, UP, WPOL, MT, FP4>(tlds, tok_src, wp, wsc, sorted_ids + tile.x, tile.x,
-                                       tile.y, block_expert[tile.x / block], ntile, n_ntiles, K,
-                                       ncols, I, top_k, act, y);
+      frag_item<BM, UP, WPOL, MT, FP4, NWG>(tlds, tok_src, wp, wsc, sorted_ids + tile.x, tile.x,
+                                            tile.y, block_expert[tile.x / block], ntile, part,
+                                            n_ntiles, K, ncols, I, top_k, act, y);
     __syncthreads();  // the next item's first token copies reuse the ring
   }
 }
@@ -589,11 +596,15 @@ static hipError_t launch_frag(const uint16_t* src, const void* wp, const uint8_t
   const int per_ntile = UP ? 256 : 512;
   if (K % kFragKC != 0 || (UP && I % per_ntile != 0)) return hipErrorInvalidValue;
   const int n_ntiles = (ncols + per_ntile - 1) / per_ntile;
-  const long items = (long)max_tiles * n_ntiles;
-  // 64-row tiles walk several items per workgroup, 128-row tiles take one each
-  const long grid = BM == 64 ? walk_grid(items, 160 * 1024) : (items + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((expert_frag_kernel<BM, UP, WPOL, FP4>), dim3((unsigned)grid),
-                     dim3(64 * kFragWaves), 0, s, src, wp, wsc, sorted_ids, block_expert, tiles,
+  // 64-row tiles (few tokens per expert): workgroups of 4 waves, each item half a panel N
+  // tile, two workgroups per CU walking their XCD's share (twice the items of 8-wave
+  // workgroups: a CU's last item is a smaller share of its work); 128-row tiles: 8 waves,
+  // one item per workgroup
+  constexpr int NWG = BM == 64 ? 4 : 8;
+  const long items = (long)max_tiles * n_ntiles * (kFragWaves / NWG);
+  const long grid = BM == 64 ? walk_grid(items, 80 * 1024) : (items + kXcds - 1) / kXcds * kXcds;
+  hipLaunchKernelGGL((expert_frag_kernel<BM, UP, WPOL, FP4, NWG>), dim3((unsigned)grid),
+                     dim3(64 * NWG), 0, s, src, wp, wsc, sorted_ids, block_expert, tiles,
                      tile_groups, num_tiles, n_ntiles, K, ncols, I, top_k, block, act, y);
   return hipGetLastError();
 }

@@ -90,11 +90,12 @@ def down_flops(cfg, M):
 
 
 def run_workload(B, mi, torch, cfg, weights, steps, warmup, dev, mx=None, prepared=None,
-                 mx4=None):
+                 mx4=None, mxp=None):
     """Times moe_forward (bf16 experts), moe_forward_mx when `mx` holds the MXFP8
     (w13 codes, w13 scales, w2 codes, w2 scales), moe_forward_prepared when `prepared`
-    holds the prepared (w13, w2) stacks, or moe_forward_mx4 when `mx4` holds the MXFP4
-    panels (w13 codes, w13 scales, w2 codes, w2 scales)."""
+    holds the prepared (w13, w2) stacks, moe_forward_mx4 when `mx4` holds the MXFP4
+    panels, or moe_forward_mx_prepared when `mxp` holds the MXFP8 panels (each as w13
+    codes, w13 scales, w2 codes, w2 scales)."""
     L = mi.make_layer(cfg, device=dev, seed=0, with_experts=False)
     L.update(weights)
     M, H, E, I, k, blk = cfg.M, cfg.H, cfg.E, cfg.I, cfg.top_k, cfg.block
@@ -104,7 +105,11 @@ def run_workload(B, mi, torch, cfg, weights, steps, warmup, dev, mx=None, prepar
     stream = torch.cuda.current_stream()
 
     def step(events=None):
-        if mx4 is not None:
+        if mxp is not None:
+            B.moe_forward_mx_prepared(L["x"], L["router_w"], L["router_bias"], *mxp, I,
+                                      L["residual"], L["norm_w"], L["eps"], k, blk, out, ws,
+                                      topk_ids_out=ids, stage_events=events, stream=stream)
+        elif mx4 is not None:
             B.moe_forward_mx4(L["x"], L["router_w"], L["router_bias"], *mx4, I, L["residual"],
                               L["norm_w"], L["eps"], k, blk, out, ws, topk_ids_out=ids,
                               stage_events=events, stream=stream)
@@ -146,12 +151,12 @@ def run_workload(B, mi, torch, cfg, weights, steps, warmup, dev, mx=None, prepar
     ms = max(wall_ms, span_ms)
     touched = int(torch.unique(ids).numel())
     counts = torch.bincount(ids.flatten().long(), minlength=E)
-    fmt = "mx8" if mx is not None else "mx4" if mx4 is not None else "bf16"
+    fmt = "mx8" if (mx is not None or mxp is not None) else "mx4" if mx4 is not None else "bf16"
     lb = layer_bytes(cfg, M, touched, fmt)
     ub = up_bytes(cfg, M, touched, fmt)
     db = down_bytes(cfg, M, touched, fmt)
     stages = {n: round(v * 1e3, 2) for n, v in stage_ms.items()}
-    self_routed = (mx is None and prepared is None and mx4 is None
+    self_routed = (mx is None and prepared is None and mx4 is None and mxp is None
                    and B.moe_forward_self_routes(M, E, k, I))
     if self_routed:
         # the up GEMM builds the plan: no align kernel runs, the event pair encloses none
@@ -436,6 +441,8 @@ def main():
                     help="skip the legs on prepared (fragment-panel) weights")
     ap.add_argument("--no-mx4", action="store_true",
                     help="skip the legs with MXFP4 expert weights")
+    ap.add_argument("--no-mx-prepared", action="store_true",
+                    help="skip the legs on MXFP8 fragment panels")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run plain device copies of this many MiB (counter calibration)")
     args = ap.parse_args()
@@ -515,7 +522,41 @@ def main():
                 mx_sweep[name]["up_kernel"] = up_kernel_name(B, c, mx=True)
                 mx_sweep[name]["up_hbm_frac"] = round(rs["up_gbs"] / HBM_PEAK_GBS, 4)
             mx_line["sweep"] = mx_sweep
-        del mx
+        if not args.no_mx_prepared:
+            # the same MXFP8 codes re-laid-out once into fragment panels
+            print("bench: re-laying-out the MXFP8 experts into panels", file=sys.stderr,
+                  flush=True)
+            E, H, I = head.E, head.H, head.I
+            mxp = [torch.empty(n, dtype=torch.uint8, device=dev)
+                   for n in B.moe_mx_prepared_bytes(E, H, I)]
+            B.moe_mx_prepare_weights(*mx, E, H, I, *mxp)
+            torch.cuda.synchronize()
+            del mx
+            torch.cuda.empty_cache()
+            mxp_line = {}
+            for name in (head.name,) + (() if args.no_sweep else SWEEP):
+                if name in mxp_line:
+                    continue
+                print(f"bench: timing {name} on MXFP8 panels", file=sys.stderr, flush=True)
+                c = mi.CONFIGS[name]
+                quick = name != head.name
+                r = run_workload(B, mi, torch, c, weights,
+                                 max(3, args.steps // 2) if quick else args.steps,
+                                 max(1, args.warmup // 2) if quick else args.warmup, dev,
+                                 mxp=mxp)
+                mxp_line[name] = _rounded(r)
+                mxp_line[name]["up_hbm_frac"] = round(r["up_gbs"] / HBM_PEAK_GBS, 4)
+                mxp_line[name]["up_mfma_frac"] = round(r["up_tflops"] / BF16_PEAK_TFLOPS, 4)
+                mxp_line[name]["down_hbm_frac"] = round(r["down_gbs"] / HBM_PEAK_GBS, 4)
+                mxp_line[name]["up_kernel"] = (
+                    f"expert_frag_kernel<{B.moe_gemm_tile_rows(c.M, c.E, c.top_k, c.I)}, "
+                    "true, ..., MXFP8>")
+            mxp_line["weights"] = ("MXFP8 (E4M3 + E8M0 per 32 values along K, fragment "
+                                   "panels), activations bf16")
+            mx_line["prepared_panels"] = mxp_line
+            del mxp
+        else:
+            del mx
         torch.cuda.empty_cache()
 
     prep_line = None
@@ -569,7 +610,7 @@ def main():
             mx4_line[name]["up_hbm_frac"] = round(r["up_gbs"] / HBM_PEAK_GBS, 4)
             mx4_line[name]["down_hbm_frac"] = round(r["down_gbs"] / HBM_PEAK_GBS, 4)
             mx4_line[name]["up_kernel"] = (
-                f"expert_frag_kernel<{B.moe_gemm_tile_rows(c.M, c.E, c.top_k, c.I)}, true, ..., FP4>")
+                f"expert_frag_kernel<{B.moe_gemm_tile_rows(c.M, c.E, c.top_k, c.I)}, true, ..., MXFP4>")
         mx4_line["weights"] = ("MXFP4 (E2M1 + E8M0 per 32 values along K, fragment panels), "
                                "activations bf16")
         del q

@@ -64,7 +64,7 @@ enum {
 /* Human-readable text of a status code.  Never NULL; static storage. */
 const char* moe_strerror(int status);
 
-/* ABI version of this header (major * 100 + minor): 105. */
+/* ABI version of this header (major * 100 + minor): 106. */
 int moe_abi_version(void);
 
 /*
@@ -274,6 +274,47 @@ int moe_forward_mx4(const uint16_t* x, const uint16_t* router_w, const float* ro
                     int32_t* sorted_ids_out, int32_t* block_expert_out, int32_t* num_padded_out,
                     void* workspace, size_t workspace_bytes,
                     const moe_event_t* stage_events, moe_stream_t stream);
+
+/*
+ * MXFP8 expert weights in the prepared panel order, for the fragment GEMMs of
+ * moe_forward_prepared (the offline re-layout of the AlphaMoE page, FlashInfer PR #6511
+ * analysis, section 2, applied to the MXFP8 codes of moe_mx_quantize).  The input is the
+ * natural MXFP8 format of moe_mx_quantize / moe_forward_mx: W13 codes [E, 2I, H] with scale
+ * bytes [E, 2I, H/32], W2 codes [E, H, I] with scale bytes [E, H, I/32].  The output is a
+ * byte permutation of it (nothing is re-quantized): for expert e, N tile n, wave w and K step
+ * s (one 32-value block), two 1 KiB halves, half h holding, for lane l, the 8 codes of tile
+ * 2h then the 8 codes of tile 2h + 1 (value v in byte v); the step's scale bytes follow as
+ * [16 rows][4 tiles], as in the MXFP4 panels:
+ *   W13 codes [E][I/256][8][H/32][2][64][2][8], W13 scales [E][I/256][8][H/32][16][4]
+ *   W2  codes [E][ceil(H/512)][8][I/32][2][64][2][8], W2 scales [E][ceil(H/512)][8][I/32][16][4]
+ * with the rows and K values of the MXFP4 panels (codes and scale bytes 0 past H).
+ * Needs H % 64 == 0 and I % 256 == 0 (MOE_ERR_UNSUPPORTED otherwise).
+ *
+ * moe_mx_prepared_bytes:   the four buffer sizes (any pointer may be NULL).
+ * moe_mx_prepare_weights:  natural codes + scales -> panels, for W13 and/or W2 (the four
+ *                          pointers of a stack all NULL to skip it); natural and panel codes
+ *                          16-byte aligned, panel scales 4-byte aligned.
+ * moe_forward_mx_prepared: moe_forward_mx on the panels (same arguments, workspace and
+ *                          results; always runs the align kernel).
+ * Asynchronous on `stream`; nothing is allocated.
+ */
+int moe_mx_prepared_bytes(int32_t E, int32_t H, int32_t I, size_t* w13_codes,
+                          size_t* w13_scales, size_t* w2_codes, size_t* w2_scales);
+int moe_mx_prepare_weights(const uint8_t* w13_codes, const uint8_t* w13_scales,
+                           const uint8_t* w2_codes, const uint8_t* w2_scales,
+                           int32_t E, int32_t H, int32_t I,
+                           uint8_t* w13_codes_p, uint8_t* w13_scales_p,
+                           uint8_t* w2_codes_p, uint8_t* w2_scales_p, moe_stream_t stream);
+int moe_forward_mx_prepared(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
+                            const uint8_t* w13_codes_p, const uint8_t* w13_scales_p,
+                            const uint8_t* w2_codes_p, const uint8_t* w2_scales_p,
+                            const uint16_t* residual, const uint16_t* norm_w, float eps,
+                            int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k,
+                            int32_t block, uint16_t* out, uint16_t* residual_out,
+                            int32_t* topk_ids_out, float* topk_w_out,
+                            int32_t* sorted_ids_out, int32_t* block_expert_out,
+                            int32_t* num_padded_out, void* workspace, size_t workspace_bytes,
+                            const moe_event_t* stage_events, moe_stream_t stream);
 
 /*
  * moe_forward for callers that cannot allocate device memory (code under HIP graph capture,

@@ -22,6 +22,7 @@ __all__ = [
     "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "moe_prepared_w13_bytes",
     "moe_prepared_w2_bytes", "moe_prepare_weights", "moe_forward_prepared",
     "moe_mx4_weight_bytes", "moe_mx4_quantize", "moe_mx4_dequantize", "moe_forward_mx4",
+    "moe_mx_prepared_bytes", "moe_mx_prepare_weights", "moe_forward_mx_prepared",
     "HipEvent",
 ]
 
@@ -71,6 +72,15 @@ _PROTOS = {
     "moe_forward_mx4": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float,
                                        _i32, _i32, _i32, _i32, _i32, _i32,
                                        _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p, _p]),
+    "moe_mx_prepared_bytes": (ctypes.c_int, [_i32, _i32, _i32, ctypes.POINTER(_sz),
+                                             ctypes.POINTER(_sz), ctypes.POINTER(_sz),
+                                             ctypes.POINTER(_sz)]),
+    "moe_mx_prepare_weights": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32,
+                                              _p, _p, _p, _p, _p]),
+    "moe_forward_mx_prepared": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p,
+                                               ctypes.c_float, _i32, _i32, _i32, _i32, _i32,
+                                               _i32, _p, _p, _p, _p, _p, _p, _p, _p, _sz, _p,
+                                               _p]),
     "moe_mx_quantize": (ctypes.c_int, [_p, ctypes.c_int64, _i32, _p, _p, _p]),
     "moe_mx_dequantize": (ctypes.c_int, [_p, _p, ctypes.c_int64, _i32, _p, _p]),
     "moe_forward_mx": (ctypes.c_int, [_p, _p, _p, _p, _p, _p, _p, _p, _p, ctypes.c_float,
@@ -445,18 +455,74 @@ def moe_forward_mx4(x, router_w, router_bias, w13_codes, w13_scales, w2_codes, w
                     block_expert_out=None, num_padded_out=None,
                     stage_events: Optional[Sequence["HipEvent"]] = None, stream=None):
     """moe_forward on MXFP4 panels (intermediate size I)."""
+    _forward_panels("moe_forward_mx4", moe_mx4_weight_bytes, x, router_w, router_bias,
+                    w13_codes, w13_scales, w2_codes, w2_scales, I, residual, norm_w, eps, top_k,
+                    block, out, workspace, residual_out, topk_ids_out, topk_w_out,
+                    sorted_ids_out, block_expert_out, num_padded_out, stage_events, stream)
+
+
+def moe_mx_prepared_bytes(E: int, H: int, I: int):
+    """(W13 codes, W13 scales, W2 codes, W2 scales) bytes of the MXFP8 panels."""
+    out = [_sz() for _ in range(4)]
+    _check("moe_mx_prepared_bytes", load_library().moe_mx_prepared_bytes(
+        E, H, I, *[ctypes.byref(o) for o in out]))
+    return tuple(int(o.value) for o in out)
+
+
+def moe_mx_prepare_weights(w13_codes, w13_scales, w2_codes, w2_scales, E: int, H: int, I: int,
+                           w13_codes_p, w13_scales_p, w2_codes_p, w2_scales_p, stream=None):
+    """Natural MXFP8 stacks (moe_mx_quantize: codes [E, 2I, H] / [E, H, I], scale bytes
+    [E, 2I, H/32] / [E, H, I/32]) -> MXFP8 panels (uint8 tensors of the sizes
+    moe_mx_prepared_bytes gives); the four tensors of a stack may all be None."""
+    n = moe_mx_prepared_bytes(E, H, I)
+    for name, c, sc, cp, sp, shape, nc, ns in (
+            ("w13", w13_codes, w13_scales, w13_codes_p, w13_scales_p, (E, 2 * I, H), n[0], n[1]),
+            ("w2", w2_codes, w2_scales, w2_codes_p, w2_scales_p, (E, H, I), n[2], n[3])):
+        given = [t is not None for t in (c, sc, cp, sp)]
+        if any(given) != all(given):
+            raise ValueError(f"{name}: codes, scales and both panels must be given together")
+        if c is not None:
+            _need(c, name + "_codes", torch.uint8, shape)
+            _need(sc, name + "_scales", torch.uint8, shape[:2] + (shape[2] // 32,))
+            _need(cp, name + "_codes_p", torch.uint8)
+            _need(sp, name + "_scales_p", torch.uint8)
+            if cp.numel() < nc or sp.numel() < ns:
+                raise ValueError(f"{name} panels smaller than moe_mx_prepared_bytes")
+    _check("moe_mx_prepare_weights", load_library().moe_mx_prepare_weights(
+        _ptr(w13_codes), _ptr(w13_scales), _ptr(w2_codes), _ptr(w2_scales), E, H, I,
+        _ptr(w13_codes_p), _ptr(w13_scales_p), _ptr(w2_codes_p), _ptr(w2_scales_p),
+        _stream(stream)))
+
+
+def moe_forward_mx_prepared(x, router_w, router_bias, w13_codes_p, w13_scales_p, w2_codes_p,
+                            w2_scales_p, I: int, residual, norm_w, eps: float, top_k: int,
+                            block: int, out, workspace, residual_out=None, topk_ids_out=None,
+                            topk_w_out=None, sorted_ids_out=None, block_expert_out=None,
+                            num_padded_out=None,
+                            stage_events: Optional[Sequence["HipEvent"]] = None, stream=None):
+    """moe_forward on MXFP8 panels (intermediate size I)."""
+    _forward_panels("moe_forward_mx_prepared", moe_mx_prepared_bytes, x, router_w, router_bias,
+                    w13_codes_p, w13_scales_p, w2_codes_p, w2_scales_p, I, residual, norm_w, eps,
+                    top_k, block, out, workspace, residual_out, topk_ids_out, topk_w_out,
+                    sorted_ids_out, block_expert_out, num_padded_out, stage_events, stream)
+
+
+def _forward_panels(fn, sizes, x, router_w, router_bias, w13_codes, w13_scales, w2_codes,
+                    w2_scales, I, residual, norm_w, eps, top_k, block, out, workspace,
+                    residual_out, topk_ids_out, topk_w_out, sorted_ids_out, block_expert_out,
+                    num_padded_out, stage_events, stream):
     M, H = x.shape
     E = router_w.shape[0]
     _need(x, "x", torch.bfloat16)
     _need(router_w, "router_w", torch.bfloat16, (E, H))
     if router_bias is not None:
         _need(router_bias, "router_bias", torch.float32, (E,))
-    n = moe_mx4_weight_bytes(E, H, I)
+    n = sizes(E, H, I)
     for name, t, nb in (("w13_codes", w13_codes, n[0]), ("w13_scales", w13_scales, n[1]),
                         ("w2_codes", w2_codes, n[2]), ("w2_scales", w2_scales, n[3])):
         _need(t, name, torch.uint8)
         if t.numel() < nb:
-            raise ValueError(f"{name} smaller than moe_mx4_weight_bytes")
+            raise ValueError(f"{name} smaller than {sizes.__name__}")
     _need(residual, "residual", torch.bfloat16, (M, H))
     _need(norm_w, "norm_w", torch.bfloat16, (H,))
     _need(out, "out", torch.bfloat16, (M, H))
@@ -483,7 +549,7 @@ def moe_forward_mx4(x, router_w, router_bias, w13_codes, w13_scales, w2_codes, w
         if len(stage_events) != 6:
             raise ValueError("stage_events must hold 6 events")
         ev = (ctypes.c_void_p * 6)(*[e.handle for e in stage_events])
-    _check("moe_forward_mx4", load_library().moe_forward_mx4(
+    _check(fn, getattr(load_library(), fn)(
         _ptr(x), _ptr(router_w), _ptr(router_bias), _ptr(w13_codes), _ptr(w13_scales),
         _ptr(w2_codes), _ptr(w2_scales), _ptr(residual), _ptr(norm_w), float(eps), M, H, E, I,
         top_k, block, _ptr(out), _ptr(residual_out), _ptr(topk_ids_out), _ptr(topk_w_out),

@@ -26,6 +26,15 @@
 // with the rows of the bf16 panels (rows past H: codes and scale bytes 0).  Each step's 4
 // weight fragments are dequantized in registers with v_cvt_scalef32_pk_bf16_fp4 (exact).
 //
+// MXFP8 weights (OCP MX: E4M3 elements, one E8M0 scale byte per 32 values along K, the
+// natural format of moe_mx_quantize) re-laid-out into the same order: per (wave, N tile,
+// K step) two 1 KiB halves, half h holding tiles 2h and 2h + 1 -- lane l's 16 bytes are the
+// 8 codes of tile 2h then the 8 of tile 2h + 1 (value v in byte v) -- and the scale bytes as
+// for MXFP4:
+//   W13c8 [E][I/256][8][H/32][2 halves][64 lanes][2 tiles][8 bytes], W13s8 as W13s
+//   W2c8  [E][ceil(H/512)][8][I/32][2][64][2][8],                   W2s8 as W2s
+// dequantized in registers with v_cvt_scalef32_pk_bf16_fp8 (exact).
+//
 // Workgroup = 8 waves; item = one token tile (BM = 64 or 128 plan rows of one expert) x one
 // N tile (up: 256 act columns = 512 weight rows; down: 512 output columns).  Wave w owns 4
 // weight row tiles (64 rows) x all BM/16 token tiles.  Per MFMA K step of 32 values a wave
@@ -47,7 +56,14 @@ constexpr int kFragRS = 4;             // weight register ring, in K steps of 32
 constexpr int kFragRS4 = 6;            // the same for MXFP4 codes (128-row tiles)
 constexpr int kFragRS4Small = 16;      // ... and 64-row tiles, whose accumulators leave room
                                        // (decode: 510 -> 472 us per layer against 6 steps)
+constexpr int kFragRS8 = 4;            // the same for MXFP8 codes (128-row tiles)
+constexpr int kFragRS8Small = 8;       // ... and 64-row tiles
 constexpr int kFragTS = 4;             // token LDS ring stages
+
+// weight formats of the fragment GEMMs
+constexpr int kWBf16 = 0;   // bf16 panels (moe_prepare_weights)
+constexpr int kWMx8 = 1;    // MXFP8 panels (moe_mx_prepare_weights)
+constexpr int kWMx4 = 2;    // MXFP4 panels (moe_mx4_quantize)
 
 int frag_up_columns() { return 256; }
 
@@ -124,6 +140,75 @@ hipError_t launch_prepare_weights(const uint16_t* w13, const uint16_t* w2, int E
 }
 
 // ---------------------------------------------------------------------------------------
+// MXFP8 panels from the natural MXFP8 stacks (codes [rows, K], scale bytes [rows, K/32]):
+// a byte permutation.  One thread per (expert, N tile, wave, step, lane), as the MXFP4
+// quantizer below: the lane's 8 codes of each of the 4 tiles; lanes 0..15 also move the
+// scale bytes of row `lane`.
+// ---------------------------------------------------------------------------------------
+template <bool UP>
+__global__ __launch_bounds__(256) void mx8_prepare_panels_kernel(
+    const uint8_t* __restrict__ codes, const uint8_t* __restrict__ scales, int E, int H, int I,
+    uint8_t* __restrict__ pcodes, uint8_t* __restrict__ pscales) {
+  const int K = UP ? H : I;
+  const int steps = K / 32;
+  const int nnt = UP ? I / 256 : (H + 511) / 512;
+  const size_t threads = (size_t)E * nnt * kFragWaves * steps * 64;
+  for (size_t g = (size_t)blockIdx.x * blockDim.x + threadIdx.x; g < threads;
+       g += (size_t)gridDim.x * blockDim.x) {
+    size_t r = g;
+    const int lane = (int)(r % 64); r /= 64;
+    const int st = (int)(r % steps); r /= steps;
+    const int wv = (int)(r % kFragWaves); r /= kFragWaves;
+    const int n = (int)(r % nnt); r /= nnt;
+    const int e = (int)r;
+    uint2 word[4];
+    uint32_t sbyte[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      int row;
+      bool on = true;
+      if (UP) {
+        const int col = n * 256 + 32 * wv + 16 * (j & 1) + (lane & 15);
+        row = j < 2 ? col : I + col;
+      } else {
+        row = n * 512 + 64 * wv + 16 * j + (lane & 15);
+        on = row < H;
+      }
+      word[j] = make_uint2(0u, 0u);
+      sbyte[j] = 0u;
+      if (!on) continue;
+      const size_t grow = (size_t)e * (UP ? 2 * I : H) + row;
+      word[j] = *reinterpret_cast<const uint2*>(codes + grow * K + 32 * st + 8 * (lane >> 4));
+      sbyte[j] = scales[grow * steps + st];
+    }
+    const size_t stepi = (((size_t)e * nnt + n) * kFragWaves + wv) * steps + st;
+    st16(pcodes + stepi * 2048 + lane * 16, u32x4{word[0].x, word[0].y, word[1].x, word[1].y});
+    st16(pcodes + stepi * 2048 + 1024 + lane * 16, u32x4{word[2].x, word[2].y, word[3].x, word[3].y});
+    if (lane < 16)
+      *reinterpret_cast<uint32_t*>(pscales + stepi * 64 + lane * 4) =
+          sbyte[0] | (sbyte[1] << 8) | (sbyte[2] << 16) | (sbyte[3] << 24);
+  }
+}
+
+size_t mx8_codes_bytes(int E, int H, int I, bool w13) {
+  return w13 ? (size_t)E * 2 * I * H : (size_t)E * ((H + 511) / 512) * 512 * I;
+}
+
+hipError_t launch_mx8_prepare(const uint8_t* codes, const uint8_t* scales, bool w13, int E, int H,
+                              int I, uint8_t* pcodes, uint8_t* pscales, hipStream_t s) {
+  if (H % 64 != 0 || I % 256 != 0) return hipErrorInvalidValue;
+  const size_t threads = mx8_codes_bytes(E, H, I, w13) / 32;
+  const long grid = std::min<long>((long)((threads + 255) / 256), 1L << 20);
+  if (w13)
+    hipLaunchKernelGGL(mx8_prepare_panels_kernel<true>, dim3((unsigned)grid), dim3(256), 0, s,
+                       codes, scales, E, H, I, pcodes, pscales);
+  else
+    hipLaunchKernelGGL(mx8_prepare_panels_kernel<false>, dim3((unsigned)grid), dim3(256), 0, s,
+                       codes, scales, E, H, I, pcodes, pscales);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------
 // MXFP4 panels: quantization (natural bf16 stacks -> panels) and dequantization back
 // ---------------------------------------------------------------------------------------
 // E2M1 code of x (the weight times 2^-s, |x| < 8 by the choice of s): the nearest of
@@ -154,6 +239,16 @@ __device__ __forceinline__ u32x4 mx4_dequant8(uint32_t codes, uint32_t scale_byt
   __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, b))
   return u32x4{MOE_CVT4(0), MOE_CVT4(1), MOE_CVT4(2), MOE_CVT4(3)};
 #undef MOE_CVT4
+}
+
+// 8 E4M3 codes (two words, value v in byte v) and their block's scale byte -> one bf16 MFMA
+// fragment (exact: a 4-bit significand times a power of two)
+__device__ __forceinline__ u32x4 mx8_dequant8(uint32_t c0, uint32_t c1, uint32_t scale_byte) {
+  const float scale = __uint_as_float(scale_byte ? scale_byte << 23 : 0x00400000u);
+#define MOE_CVT8(w, hi) \
+  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w, scale, hi))
+  return u32x4{MOE_CVT8(c0, false), MOE_CVT8(c0, true), MOE_CVT8(c1, false), MOE_CVT8(c1, true)};
+#undef MOE_CVT8
 }
 
 // One thread per (expert, N tile, wave, step, lane): for each of the 4 tiles, the row's
@@ -328,7 +423,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const void* base, 
 // compiler's own load waits exact).  The ring is a __restrict__ parameter so that the
 // compiler can tell the token copies in flight apart from the LDS reads (without it, it
 // drains every load before each fragment read).
-template <int BM, bool UP, int WPOL, int NA, bool FP4, int NWG>
+template <int BM, bool UP, int WPOL, int NA, int WF, int NWG>
 __device__ __forceinline__ void frag_item(
     unsigned char* __restrict__ tlds, const uint16_t* __restrict__ tok_src,
     const void* __restrict__ wp, const uint8_t* __restrict__ wsc,
@@ -339,9 +434,14 @@ __device__ __forceinline__ void frag_item(
   constexpr int MT = C::MT;
   constexpr int TS = kFragTS;
   // weight ring depth in K steps and loads per step: bf16 4 fragments (16 VGPRs a step);
-  // MXFP4 one 16-byte load of codes and one 4-byte load of scale bytes (5 VGPRs a step)
-  constexpr int RS = FP4 ? (BM == 64 ? kFragRS4Small : kFragRS4) : kFragRS;
-  constexpr int WPS = FP4 ? 2 : 4;
+  // MXFP8 two 16-byte loads of codes and one 4-byte load of scale bytes (9 VGPRs a step);
+  // MXFP4 one 16-byte load of codes and one of scale bytes (5 VGPRs a step)
+  constexpr int RS = WF == kWMx4   ? (BM == 64 ? kFragRS4Small : kFragRS4)
+                     : WF == kWMx8 ? (BM == 64 ? kFragRS8Small : kFragRS8)
+                                   : kFragRS;
+  constexpr int WPS = WF == kWMx4 ? 2 : WF == kWMx8 ? 3 : 4;
+  constexpr int WREGS = WF == kWMx4 ? 1 : WF == kWMx8 ? 2 : 4;   // 16-byte loads of codes
+  constexpr int SB = 1024 * WREGS;                                 // bytes per step and wave
   // token copies: copy f (0 .. TCOPIES-1) of a chunk covers rows 8h..8h+7 (h = f % 2) of
   // token tile f / 2; wave w of the NWG issues copies w, w + NWG, ...
   constexpr int TCPW = C::TCOPIES / NWG;
@@ -374,14 +474,13 @@ __device__ __forceinline__ void frag_item(
   // this wave's weight stream (nsteps x 4 KiB, contiguous): fragment (step s, tile j) at byte
   // s * 4096 + j * 1024, lane l's 16 bytes at + 16 l; loaded through a buffer resource (the
   // step offset in a scalar register, one vector register for all lanes' offsets)
-  // (MXFP4: codes nsteps x 1 KiB, scale bytes nsteps x 64 B, lane l's scale word -- row
-  // l % 16 of the 4 tiles -- at 4 (l % 16))
+  // (MXFP8 / MXFP4: codes nsteps x 2 / 1 KiB, scale bytes nsteps x 64 B, lane l's scale
+  // word -- row l % 16 of the 4 tiles -- at 4 (l % 16))
   const size_t stream = ((size_t)e * n_ntiles + ntile) * kFragWaves + pw;
   const __amdgpu_buffer_rsrc_t wrsrc =
-      FP4 ? stream_rsrc(static_cast<const uint8_t*>(wp) + stream * nsteps * 1024, nsteps * 1024)
-          : stream_rsrc(static_cast<const uint16_t*>(wp) + stream * nsteps * 2048, nsteps * 4096);
-  const __amdgpu_buffer_rsrc_t srsrc =
-      stream_rsrc(FP4 ? wsc + stream * nsteps * 64 : static_cast<const uint8_t*>(wp), nsteps * 64);
+      stream_rsrc(static_cast<const uint8_t*>(wp) + stream * nsteps * SB, nsteps * SB);
+  const __amdgpu_buffer_rsrc_t srsrc = stream_rsrc(
+      WF != kWBf16 ? wsc + stream * nsteps * 64 : static_cast<const uint8_t*>(wp), nsteps * 64);
   const int lane_off = lane * 16;
   const int scale_off = (lane & 15) * 4;
   // token copies of this wave; rows past the tile's real rows read its first row
@@ -414,22 +513,18 @@ __device__ __forceinline__ void frag_item(
     return *reinterpret_cast<const u32x4*>(tlds + (size_t)(c % TS) * C::TSTAGE + t * 2048 +
                                            frag_off + q * 16);
   };
-  // bf16: wr[slot][j] is fragment j; MXFP4: wr[slot][0] holds the 4 tiles' code words and
-  // wsr[slot] their scale bytes
-  u32x4 wr[RS][FP4 ? 1 : 4];
-  uint32_t wsr[FP4 ? RS : 1];
+  // bf16: wr[slot][j] is fragment j; MXFP8: wr[slot][h] holds the code words of tiles 2h
+  // and 2h + 1; MXFP4: wr[slot][0] holds the 4 tiles' code words; wsr[slot] the scale bytes
+  u32x4 wr[RS][WREGS];
+  uint32_t wsr[WF != kWBf16 ? RS : 1];
   auto issue_w = [&](int st, int slot) {  // st is clamped to the last step
     const int ss = st < nsteps ? st : nsteps - 1;
-    if constexpr (FP4) {
-      wr[slot][0] = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, lane_off, ss * 1024, WPOL));
-      wsr[slot] = __builtin_amdgcn_raw_buffer_load_b32(srsrc, scale_off, ss * 64, WPOL);
-    } else {
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        wr[slot][j] = __builtin_bit_cast(
-            u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, lane_off, ss * 4096 + j * 1024, WPOL));
-    }
+    for (int j = 0; j < WREGS; ++j)
+      wr[slot][j] = __builtin_bit_cast(
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(wrsrc, lane_off, ss * SB + j * 1024, WPOL));
+    if constexpr (WF != kWBf16)
+      wsr[slot] = __builtin_amdgcn_raw_buffer_load_b32(srsrc, scale_off, ss * 64, WPOL);
   };
 
   static_assert(NA >= 1 && NA <= MT, "computed token tiles");
@@ -457,18 +552,24 @@ __device__ __forceinline__ void frag_item(
       issue_t(c + TS - 1);
     }
     frag_wait_vmcnt<kWaitW>();   // this step's weights are in registers
-    if constexpr (FP4) {
-      // keep the dequantization of this step's codes below the wait: the empty asm takes the
-      // registers as inputs and outputs, so nothing computed from them moves above it (the
-      // compiler would otherwise hoist the scale arithmetic of later steps and drain every
-      // load to feed it)
-      asm volatile("" : "+v"(wr[u % RS][0]), "+v"(wsr[u % RS]));
-    }
+    // keep the dequantization of this step's codes below the wait: the empty asm takes the
+    // registers as inputs and outputs, so nothing computed from them moves above it (the
+    // compiler would otherwise hoist the scale arithmetic of later steps and drain every
+    // load to feed it)
+    if constexpr (WF == kWMx4) asm volatile("" : "+v"(wr[u % RS][0]), "+v"(wsr[u % RS]));
+    if constexpr (WF == kWMx8)
+      asm volatile("" : "+v"(wr[u % RS][0]), "+v"(wr[u % RS][1]), "+v"(wsr[u % RS]));
     u32x4 wa[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      if constexpr (FP4) wa[j] = mx4_dequant8(wr[u % RS][0][j], (wsr[u % RS] >> (8 * j)) & 0xFFu);
-      else wa[j] = wr[u % RS][j];
+      if constexpr (WF == kWMx4) {
+        wa[j] = mx4_dequant8(wr[u % RS][0][j], (wsr[u % RS] >> (8 * j)) & 0xFFu);
+      } else if constexpr (WF == kWMx8) {
+        const u32x4 h = wr[u % RS][j >> 1];
+        wa[j] = mx8_dequant8(h[2 * (j & 1)], h[2 * (j & 1) + 1], (wsr[u % RS] >> (8 * j)) & 0xFFu);
+      } else {
+        wa[j] = wr[u % RS][j];
+      }
     }
     issue_w(st + RS, u % RS);
 #pragma unroll
@@ -551,7 +652,7 @@ struct ExpertMajorWalk {
   }
 };
 
-template <int BM, bool UP, int WPOL, bool FP4, int NWG>
+template <int BM, bool UP, int WPOL, int WF, int NWG>
 __global__ __launch_bounds__(64 * NWG) void expert_frag_kernel(
     const uint16_t* __restrict__ tok_src, const void* __restrict__ wp,
     const uint8_t* __restrict__ wsc,
@@ -575,18 +676,18 @@ __global__ __launch_bounds__(64 * NWG) void expert_frag_kernel(
     constexpr int MT = FragCfg<BM>::MT;
     constexpr int NS = BM == 64 ? 1 : MT / 2;
     if (tile.y <= 16 * NS)
-      frag_item<BM, UP, WPOL, NS, FP4, NWG>(tlds, tok_src, wp, wsc, sorted_ids + tile.x, tile.x,
+      frag_item<BM, UP, WPOL, NS, WF, NWG>(tlds, tok_src, wp, wsc, sorted_ids + tile.x, tile.x,
                                             tile.y, block_expert[tile.x / block], ntile, part,
                                             n_ntiles, K, ncols, I, top_k, act, y);
     else
-      frag_item<BM, UP, WPOL, MT, FP4, NWG>(tlds, tok_src, wp, wsc, sorted_ids + tile.x, tile.x,
+      frag_item<BM, UP, WPOL, MT, WF, NWG>(tlds, tok_src, wp, wsc, sorted_ids + tile.x, tile.x,
                                             tile.y, block_expert[tile.x / block], ntile, part,
                                             n_ntiles, K, ncols, I, top_k, act, y);
     __syncthreads();  // the next item's first token copies reuse the ring
   }
 }
 
-template <int BM, bool UP, int WPOL, bool FP4 = false>
+template <int BM, bool UP, int WPOL, int WF = kWBf16>
 static hipError_t launch_frag(const uint16_t* src, const void* wp, const uint8_t* wsc,
                               const int32_t* sorted_ids,
                               const int32_t* block_expert, const int2* tiles,
@@ -603,7 +704,7 @@ static hipError_t launch_frag(const uint16_t* src, const void* wp, const uint8_t
   constexpr int NWG = BM == 64 ? 4 : 8;
   const long items = (long)max_tiles * n_ntiles * (kFragWaves / NWG);
   const long grid = BM == 64 ? walk_grid(items, 80 * 1024) : (items + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((expert_frag_kernel<BM, UP, WPOL, FP4, NWG>), dim3((unsigned)grid),
+  hipLaunchKernelGGL((expert_frag_kernel<BM, UP, WPOL, WF, NWG>), dim3((unsigned)grid),
                      dim3(64 * NWG), 0, s, src, wp, wsc, sorted_ids, block_expert, tiles,
                      tile_groups, num_tiles, n_ntiles, K, ncols, I, top_k, block, act, y);
   return hipGetLastError();
@@ -654,47 +755,61 @@ hipError_t launch_expert_down_frag(const uint16_t* act, const uint16_t* w2p,
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_expert_up_frag4(const uint16_t* x, const uint8_t* w13q, const uint8_t* w13s,
-                                  const int32_t* sorted_ids, const int32_t* block_expert,
-                                  const int2* tiles, const int2* tile_groups,
-                                  const int32_t* num_tiles, int max_tiles, int tile_rows,
-                                  bool stream_weights, int H, int I, int top_k, int block,
-                                  uint16_t* act, hipStream_t s) {
-#define MOE_FRAG4_UP(BM, POL)                                                                   \
-  return launch_frag<BM, true, POL, true>(x, w13q, w13s, sorted_ids, block_expert, tiles,     \
-                                          tile_groups, num_tiles, max_tiles, H, I, I, top_k,  \
-                                          block, act, nullptr, s)
-  if (tile_rows == 64) {
-    if (stream_weights) MOE_FRAG4_UP(64, kFragNT);
-    MOE_FRAG4_UP(64, 0);
+hipError_t launch_expert_up_frag_mx(const uint16_t* x, const uint8_t* w13c, const uint8_t* w13s,
+                                   bool fp4, const int32_t* sorted_ids,
+                                   const int32_t* block_expert, const int2* tiles,
+                                   const int2* tile_groups, const int32_t* num_tiles,
+                                   int max_tiles, int tile_rows, bool stream_weights, int H, int I,
+                                   int top_k, int block, uint16_t* act, hipStream_t s) {
+#define MOE_FRAGMX_UP(BM, POL, WF)                                                              \
+  return launch_frag<BM, true, POL, WF>(x, w13c, w13s, sorted_ids, block_expert, tiles,         \
+                                        tile_groups, num_tiles, max_tiles, H, I, I, top_k,      \
+                                        block, act, nullptr, s)
+#define MOE_FRAGMX_UP_FMT(WF)                   \
+  if (tile_rows == 64) {                        \
+    if (stream_weights) MOE_FRAGMX_UP(64, kFragNT, WF); \
+    MOE_FRAGMX_UP(64, 0, WF);                   \
+  }                                             \
+  if (tile_rows == 128) {                       \
+    if (stream_weights) MOE_FRAGMX_UP(128, kFragNT, WF); \
+    MOE_FRAGMX_UP(128, 0, WF);                  \
   }
-  if (tile_rows == 128) {
-    if (stream_weights) MOE_FRAG4_UP(128, kFragNT);
-    MOE_FRAG4_UP(128, 0);
+  if (fp4) {
+    MOE_FRAGMX_UP_FMT(kWMx4)
+  } else {
+    MOE_FRAGMX_UP_FMT(kWMx8)
   }
-#undef MOE_FRAG4_UP
+#undef MOE_FRAGMX_UP_FMT
+#undef MOE_FRAGMX_UP
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_expert_down_frag4(const uint16_t* act, const uint8_t* w2q, const uint8_t* w2s,
-                                    const int32_t* sorted_ids, const int32_t* block_expert,
-                                    const int2* tiles, const int2* tile_groups,
-                                    const int32_t* num_tiles, int max_tiles, int tile_rows,
-                                    bool stream_weights, int H, int I, int top_k, int block,
-                                    uint16_t* y, hipStream_t s) {
-#define MOE_FRAG4_DOWN(BM, POL)                                                                 \
-  return launch_frag<BM, false, POL, true>(act, w2q, w2s, sorted_ids, block_expert, tiles,    \
-                                           tile_groups, num_tiles, max_tiles, I, H, I, top_k, \
-                                           block, nullptr, y, s)
-  if (tile_rows == 64) {
-    if (stream_weights) MOE_FRAG4_DOWN(64, kFragNT);
-    MOE_FRAG4_DOWN(64, 0);
+hipError_t launch_expert_down_frag_mx(const uint16_t* act, const uint8_t* w2c, const uint8_t* w2s,
+                                     bool fp4, const int32_t* sorted_ids,
+                                     const int32_t* block_expert, const int2* tiles,
+                                     const int2* tile_groups, const int32_t* num_tiles,
+                                     int max_tiles, int tile_rows, bool stream_weights, int H,
+                                     int I, int top_k, int block, uint16_t* y, hipStream_t s) {
+#define MOE_FRAGMX_DOWN(BM, POL, WF)                                                            \
+  return launch_frag<BM, false, POL, WF>(act, w2c, w2s, sorted_ids, block_expert, tiles,        \
+                                         tile_groups, num_tiles, max_tiles, I, H, I, top_k,     \
+                                         block, nullptr, y, s)
+#define MOE_FRAGMX_DOWN_FMT(WF)                 \
+  if (tile_rows == 64) {                        \
+    if (stream_weights) MOE_FRAGMX_DOWN(64, kFragNT, WF); \
+    MOE_FRAGMX_DOWN(64, 0, WF);                 \
+  }                                             \
+  if (tile_rows == 128) {                       \
+    if (stream_weights) MOE_FRAGMX_DOWN(128, kFragNT, WF); \
+    MOE_FRAGMX_DOWN(128, 0, WF);                \
   }
-  if (tile_rows == 128) {
-    if (stream_weights) MOE_FRAG4_DOWN(128, kFragNT);
-    MOE_FRAG4_DOWN(128, 0);
+  if (fp4) {
+    MOE_FRAGMX_DOWN_FMT(kWMx4)
+  } else {
+    MOE_FRAGMX_DOWN_FMT(kWMx8)
   }
-#undef MOE_FRAG4_DOWN
+#undef MOE_FRAGMX_DOWN_FMT
+#undef MOE_FRAGMX_DOWN
   return hipErrorInvalidValue;
 }
 

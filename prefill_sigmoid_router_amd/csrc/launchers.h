@@ -138,18 +138,25 @@ hipError_t launch_mx4_quantize(const uint16_t* w, bool w13, int E, int H, int I,
                                uint8_t* scales, hipStream_t s);
 hipError_t launch_mx4_dequantize(const uint8_t* codes, const uint8_t* scales, bool w13, int E,
                                  int H, int I, uint16_t* w, hipStream_t s);
-hipError_t launch_expert_up_frag4(const uint16_t* x, const uint8_t* w13q, const uint8_t* w13s,
-                                  const int32_t* sorted_ids, const int32_t* block_expert,
-                                  const int2* tiles, const int2* tile_groups,
-                                  const int32_t* num_tiles, int max_tiles, int tile_rows,
-                                  bool stream_weights, int H, int I, int top_k, int block,
-                                  uint16_t* act, hipStream_t s);
-hipError_t launch_expert_down_frag4(const uint16_t* act, const uint8_t* w2q, const uint8_t* w2s,
-                                    const int32_t* sorted_ids, const int32_t* block_expert,
-                                    const int2* tiles, const int2* tile_groups,
-                                    const int32_t* num_tiles, int max_tiles, int tile_rows,
-                                    bool stream_weights, int H, int I, int top_k, int block,
-                                    uint16_t* y, hipStream_t s);
+// MXFP8 expert weights in the panel order (E4M3 codes, 8 bytes per lane and tile; scale
+// bytes as for MXFP4), re-laid-out from the natural MXFP8 stacks of launch_mx_quantize
+// (codes [rows, K], scale bytes [rows, K/32]); scale panels are mx4_scales_bytes long.
+size_t mx8_codes_bytes(int E, int H, int I, bool w13);
+hipError_t launch_mx8_prepare(const uint8_t* codes, const uint8_t* scales, bool w13, int E, int H,
+                              int I, uint8_t* pcodes, uint8_t* pscales, hipStream_t s);
+// The grouped GEMMs on MXFP4 (fp4) or MXFP8 panels.
+hipError_t launch_expert_up_frag_mx(const uint16_t* x, const uint8_t* w13c, const uint8_t* w13s,
+                                   bool fp4, const int32_t* sorted_ids,
+                                   const int32_t* block_expert, const int2* tiles,
+                                   const int2* tile_groups, const int32_t* num_tiles,
+                                   int max_tiles, int tile_rows, bool stream_weights, int H, int I,
+                                   int top_k, int block, uint16_t* act, hipStream_t s);
+hipError_t launch_expert_down_frag_mx(const uint16_t* act, const uint8_t* w2c, const uint8_t* w2s,
+                                     bool fp4, const int32_t* sorted_ids,
+                                     const int32_t* block_expert, const int2* tiles,
+                                     const int2* tile_groups, const int32_t* num_tiles,
+                                     int max_tiles, int tile_rows, bool stream_weights, int H,
+                                     int I, int top_k, int block, uint16_t* y, hipStream_t s);
 
 // Weighted top-k combine + residual add + RMSNorm over fp32 or bf16 rows of y.
 hipError_t launch_finalize(const float* y, const float* topk_w, const uint16_t* residual,

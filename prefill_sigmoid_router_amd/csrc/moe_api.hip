@@ -124,7 +124,7 @@ const char* moe_strerror(int status) {
   }
 }
 
-int moe_abi_version(void) { return 105; }
+int moe_abi_version(void) { return 106; }
 
 size_t moe_align_capacity(int32_t M, int32_t top_k, int32_t E, int32_t block) {
   if (M < 0 || top_k < 1 || E < 1 || block < 1) return 0;
@@ -277,7 +277,9 @@ struct ExpertWeights {
   const uint8_t* w2s = nullptr;
   bool prepared = false;  // w13 / w2 hold the fragment panels of moe_prepare_weights
   bool fp4 = false;       // w13c / w13s / w2c / w2s hold the MXFP4 panels of moe_mx4_quantize
-  bool mx() const { return w13c != nullptr && !fp4; }
+  bool fp8p = false;      // ... the MXFP8 panels of moe_mx_prepare_weights
+  bool mx() const { return w13c != nullptr && !fp4 && !fp8p; }     // natural MXFP8
+  bool panels() const { return prepared || fp4 || fp8p; }
 };
 
 int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
@@ -290,11 +292,12 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   if (!sizes_ok(M, H, E, I, top_k) || !(eps > 0.0f) || !isfinite(eps)) return MOE_ERR_INVALID_ARG;
   if (!gemm_block_ok(block)) return MOE_ERR_UNSUPPORTED;
   if (W.mx() && (H % 256 != 0 || I % 256 != 0)) return MOE_ERR_UNSUPPORTED;
-  if ((W.prepared || W.fp4) && (H % 64 != 0 || I % 256 != 0)) return MOE_ERR_UNSUPPORTED;
+  if (W.panels() && (H % 64 != 0 || I % 256 != 0)) return MOE_ERR_UNSUPPORTED;
   if (M == 0) return MOE_OK;
   const bool w_ok =
-      W.fp4  ? (W.w13c && W.w13s && W.w2c && W.w2s && aligned(W.w13c, 16) && aligned(W.w2c, 16) &&
-                aligned(W.w13s, 4) && aligned(W.w2s, 4))
+      (W.fp4 || W.fp8p)
+          ? (W.w13c && W.w13s && W.w2c && W.w2s && aligned(W.w13c, 16) && aligned(W.w2c, 16) &&
+             aligned(W.w13s, 4) && aligned(W.w2s, 4))
       : W.mx() ? (W.w13c && W.w13s && W.w2c && W.w2s && aligned(W.w13c, 16) &&
                   aligned(W.w2c, 16) && aligned(W.w13s, 8) && aligned(W.w2s, 8))
                : (W.w13 && W.w2 && aligned(W.w13, 16) && aligned(W.w2, 16));
@@ -340,16 +343,17 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   const bool stream_w = stream_weights(M, E, top_k, trows);
   const int max_tiles = moe::tile_capacity(M * top_k, E, trows);
   // few ids: the up GEMM builds the plan itself (no align launch)
-  const bool self_route = !W.mx() && !W.prepared && !W.fp4 && self_routes(M, E, top_k, I);
+  const bool self_route = !W.mx() && !W.panels() && self_routes(M, E, top_k, I);
   if (!self_route &&
       moe::launch_align(ids, M * top_k, E, block, sorted, bexp, npad, trows, tiles, ntiles, s,
-                        (W.prepared || W.fp4) ? groups : nullptr) != hipSuccess)
+                        W.panels() ? groups : nullptr) != hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(2)) return MOE_ERR_HIP;
   hipError_t up_err;
-  if (W.fp4)
-    up_err = moe::launch_expert_up_frag4(x, W.w13c, W.w13s, sorted, bexp, tiles, groups, ntiles,
-                                         max_tiles, trows, stream_w, H, I, top_k, block, act, s);
+  if (W.fp4 || W.fp8p)
+    up_err = moe::launch_expert_up_frag_mx(x, W.w13c, W.w13s, W.fp4, sorted, bexp, tiles, groups,
+                                           ntiles, max_tiles, trows, stream_w, H, I, top_k, block,
+                                           act, s);
   else if (W.prepared)
     up_err = moe::launch_expert_up_frag(x, W.w13, sorted, bexp, tiles, groups, ntiles, max_tiles,
                                         trows, stream_w, H, I, top_k, block, act, s);
@@ -371,10 +375,10 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   if (up_err != hipSuccess) return MOE_ERR_HIP;
   if (!mark(3)) return MOE_ERR_HIP;
   hipError_t down_err;
-  if (W.fp4)
-    down_err = moe::launch_expert_down_frag4(act, W.w2c, W.w2s, sorted, bexp, tiles, groups,
-                                             ntiles, max_tiles, trows, stream_w, H, I, top_k,
-                                             block, y, s);
+  if (W.fp4 || W.fp8p)
+    down_err = moe::launch_expert_down_frag_mx(act, W.w2c, W.w2s, W.fp4, sorted, bexp, tiles,
+                                               groups, ntiles, max_tiles, trows, stream_w, H, I,
+                                               top_k, block, y, s);
   else if (W.prepared)
     down_err = moe::launch_expert_down_frag(act, W.w2, sorted, bexp, tiles, groups, ntiles,
                                             max_tiles, trows, stream_w, H, I, top_k, block, y, s);
@@ -539,6 +543,64 @@ int moe_forward_mx4(const uint16_t* x, const uint16_t* router_w, const float* ro
   W.w2s = w2_scales;
   W.fp4 = true;
   if (!w13_codes) return MOE_ERR_INVALID_ARG;
+  return forward_impl(x, router_w, router_bias, W, residual, norm_w, eps, M, H, E, I, top_k, block,
+                      out, residual_out, topk_ids_out, topk_w_out, sorted_ids_out,
+                      block_expert_out, num_padded_out, workspace, workspace_bytes, stage_events,
+                      stream);
+}
+
+int moe_mx_prepared_bytes(int32_t E, int32_t H, int32_t I, size_t* w13_codes,
+                          size_t* w13_scales, size_t* w2_codes, size_t* w2_scales) {
+  if (E < 1 || E > kMaxE || H < 8 || H > kMaxH || H % 8 != 0 || I < 16 || I % 16 != 0)
+    return MOE_ERR_INVALID_ARG;
+  if (H % 64 != 0 || I % 256 != 0) return MOE_ERR_UNSUPPORTED;
+  if (w13_codes) *w13_codes = moe::mx8_codes_bytes(E, H, I, true);
+  if (w13_scales) *w13_scales = moe::mx4_scales_bytes(E, H, I, true);
+  if (w2_codes) *w2_codes = moe::mx8_codes_bytes(E, H, I, false);
+  if (w2_scales) *w2_scales = moe::mx4_scales_bytes(E, H, I, false);
+  return MOE_OK;
+}
+
+int moe_mx_prepare_weights(const uint8_t* w13_codes, const uint8_t* w13_scales,
+                           const uint8_t* w2_codes, const uint8_t* w2_scales, int32_t E,
+                           int32_t H, int32_t I, uint8_t* w13_codes_p, uint8_t* w13_scales_p,
+                           uint8_t* w2_codes_p, uint8_t* w2_scales_p, moe_stream_t stream) {
+  const int st = moe_mx_prepared_bytes(E, H, I, nullptr, nullptr, nullptr, nullptr);
+  if (st != MOE_OK) return st;
+  const bool a13 = w13_codes != nullptr, a2 = w2_codes != nullptr;
+  if (a13 != (w13_scales != nullptr) || a13 != (w13_codes_p != nullptr) ||
+      a13 != (w13_scales_p != nullptr) || a2 != (w2_scales != nullptr) ||
+      a2 != (w2_codes_p != nullptr) || a2 != (w2_scales_p != nullptr))
+    return MOE_ERR_INVALID_ARG;
+  if ((a13 && (!aligned(w13_codes, 16) || !aligned(w13_codes_p, 16) || !aligned(w13_scales_p, 4))) ||
+      (a2 && (!aligned(w2_codes, 16) || !aligned(w2_codes_p, 16) || !aligned(w2_scales_p, 4))))
+    return MOE_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (a13 && moe::launch_mx8_prepare(w13_codes, w13_scales, true, E, H, I, w13_codes_p,
+                                     w13_scales_p, s) != hipSuccess)
+    return MOE_ERR_HIP;
+  if (a2 && moe::launch_mx8_prepare(w2_codes, w2_scales, false, E, H, I, w2_codes_p, w2_scales_p,
+                                    s) != hipSuccess)
+    return MOE_ERR_HIP;
+  return MOE_OK;
+}
+
+int moe_forward_mx_prepared(const uint16_t* x, const uint16_t* router_w, const float* router_bias,
+                            const uint8_t* w13_codes_p, const uint8_t* w13_scales_p,
+                            const uint8_t* w2_codes_p, const uint8_t* w2_scales_p,
+                            const uint16_t* residual, const uint16_t* norm_w, float eps, int32_t M,
+                            int32_t H, int32_t E, int32_t I, int32_t top_k, int32_t block,
+                            uint16_t* out, uint16_t* residual_out, int32_t* topk_ids_out,
+                            float* topk_w_out, int32_t* sorted_ids_out, int32_t* block_expert_out,
+                            int32_t* num_padded_out, void* workspace, size_t workspace_bytes,
+                            const moe_event_t* stage_events, moe_stream_t stream) {
+  ExpertWeights W;
+  W.w13c = w13_codes_p;
+  W.w13s = w13_scales_p;
+  W.w2c = w2_codes_p;
+  W.w2s = w2_scales_p;
+  W.fp8p = true;
+  if (!w13_codes_p) return MOE_ERR_INVALID_ARG;
   return forward_impl(x, router_w, router_bias, W, residual, norm_w, eps, M, H, E, I, top_k, block,
                       out, residual_out, topk_ids_out, topk_w_out, sorted_ids_out,
                       block_expert_out, num_padded_out, workspace, workspace_bytes, stage_events,

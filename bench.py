@@ -490,6 +490,9 @@ def main():
             sweep[name] = run_workload(B, mi, torch, mi.CONFIGS[name], weights,
                                        max(3, args.steps // 2), max(1, args.warmup // 2), dev)
 
+    # (leg dict, workload, result, up kernel, weight format) of the fragment-panel legs, whose
+    # roofline objects are filled in once the read probes have run
+    leg_roofs = []
     mx_line = None
     if not args.no_mx:
         # the same layer with MXFP8 expert weights (quantized on the device)
@@ -549,8 +552,9 @@ def main():
                 mxp_line[name]["up_mfma_frac"] = round(r["up_tflops"] / BF16_PEAK_TFLOPS, 4)
                 mxp_line[name]["down_hbm_frac"] = round(r["down_gbs"] / HBM_PEAK_GBS, 4)
                 mxp_line[name]["up_kernel"] = (
-                    f"expert_frag_kernel<{B.moe_gemm_tile_rows(c.M, c.E, c.top_k, c.I)}, "
+                    f"expert_frag_kernel<{B.moe_gemm_tile_rows_panels(c.M, c.E, c.top_k, c.I, 8)}, "
                     "true, ..., MXFP8>")
+                leg_roofs.append((mxp_line, name, r, mxp_line[name]["up_kernel"], "mx8"))
             mxp_line["weights"] = ("MXFP8 (E4M3 + E8M0 per 32 values along K, fragment "
                                    "panels), activations bf16")
             mx_line["prepared_panels"] = mxp_line
@@ -584,7 +588,9 @@ def main():
             prep_line[name]["up_mfma_frac"] = round(r["up_tflops"] / BF16_PEAK_TFLOPS, 4)
             prep_line[name]["down_hbm_frac"] = round(r["down_gbs"] / HBM_PEAK_GBS, 4)
             prep_line[name]["up_kernel"] = (
-                f"expert_frag_kernel<{B.moe_gemm_tile_rows(c.M, c.E, c.top_k, c.I)}, true, ...>")
+                f"expert_frag_kernel<{B.moe_gemm_tile_rows_panels(c.M, c.E, c.top_k, c.I, 16)}, "
+                "true, ...>")
+            leg_roofs.append((prep_line, name, r, prep_line[name]["up_kernel"], "bf16"))
         del p13, p2
         torch.cuda.empty_cache()
 
@@ -610,7 +616,9 @@ def main():
             mx4_line[name]["up_hbm_frac"] = round(r["up_gbs"] / HBM_PEAK_GBS, 4)
             mx4_line[name]["down_hbm_frac"] = round(r["down_gbs"] / HBM_PEAK_GBS, 4)
             mx4_line[name]["up_kernel"] = (
-                f"expert_frag_kernel<{B.moe_gemm_tile_rows(c.M, c.E, c.top_k, c.I)}, true, ..., MXFP4>")
+                f"expert_frag_kernel<{B.moe_gemm_tile_rows_panels(c.M, c.E, c.top_k, c.I, 4)}, "
+                "true, ..., MXFP4>")
+            leg_roofs.append((mx4_line, name, r, mx4_line[name]["up_kernel"], "mx4"))
         mx4_line["weights"] = ("MXFP4 (E2M1 + E8M0 per 32 values along K, fragment panels), "
                                "activations bf16")
         del q
@@ -627,6 +635,9 @@ def main():
     roof["read_probes_gbs"] = {"plain_nontemporal_loads": round(plain_gbs, 1)}
     for stages, g in lds_rates.items():
         roof["read_probes_gbs"][f"global_load_lds_nt_ring_{stages}_stages"] = round(g, 1)
+    for line_d, name, r, kernel, fmt in leg_roofs:
+        line_d[name]["roofline"] = roofline(
+            r, kernel, read_gbs, load_profile(f"traffic_expert_frag_up_{fmt}_{name}.json", name))
     sweep_out = {}
     for name, r in sweep.items():
         c = mi.CONFIGS[name]

@@ -64,7 +64,7 @@ enum {
 /* Human-readable text of a status code.  Never NULL; static storage. */
 const char* moe_strerror(int status);
 
-/* ABI version of this header (major * 100 + minor): 106. */
+/* ABI version of this header (major * 100 + minor): 107. */
 int moe_abi_version(void);
 
 /*
@@ -102,6 +102,12 @@ int32_t moe_gemm_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I);
  * dequantize them into the MFMA operands, except the up GEMM at 128-row tiles, which
  * dequantizes them into the LDS tiles of the tiled kernel. */
 int32_t moe_gemm_tile_rows_mx(int32_t M, int32_t E, int32_t top_k, int32_t I);
+/* The same for the entry points on fragment panels: weight_bits 16 (moe_forward_prepared)
+ * follows moe_gemm_tile_rows; 8 (moe_forward_mx_prepared) gives 64 below 64 expected tokens
+ * per expert, then 128; 4 (moe_forward_mx4) 64 below 256, then 128.  Host-only; 0 for
+ * invalid sizes, I not a multiple of 256, or another weight_bits. */
+int32_t moe_gemm_tile_rows_panels(int32_t M, int32_t E, int32_t top_k, int32_t I,
+                                  int32_t weight_bits);
 /* 1 when moe_forward (bf16 weights) builds the plan inside its up-GEMM kernel for these
  * sizes -- the self-routing up kernels of the AlphaMoE page (FlashInfer PR #6511 analysis),
  * section 6: 64-row tiles, weights copied nontemporally, at most 256 flat ids M * top_k --

@@ -18,7 +18,8 @@ __all__ = [
     "moe_strerror", "moe_abi_version", "moe_align_capacity", "moe_route_workspace_bytes",
     "moe_workspace_bytes", "moe_route", "moe_align", "moe_expert_up", "moe_expert_down",
     "moe_finalize", "moe_forward", "moe_mx_quantize", "moe_mx_dequantize", "moe_forward_mx",
-    "moe_gemm_tile_rows", "moe_gemm_tile_rows_mx", "moe_forward_self_routes",
+    "moe_gemm_tile_rows", "moe_gemm_tile_rows_mx", "moe_gemm_tile_rows_panels",
+    "moe_forward_self_routes",
     "moe_forward_noalloc", "NOALLOC_SCRATCH_BYTES", "moe_prepared_w13_bytes",
     "moe_prepared_w2_bytes", "moe_prepare_weights", "moe_forward_prepared",
     "moe_mx4_weight_bytes", "moe_mx4_quantize", "moe_mx4_dequantize", "moe_forward_mx4",
@@ -44,6 +45,7 @@ _PROTOS = {
     "moe_workspace_bytes": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "moe_gemm_tile_rows": (_i32, [_i32, _i32, _i32, _i32]),
     "moe_gemm_tile_rows_mx": (_i32, [_i32, _i32, _i32, _i32]),
+    "moe_gemm_tile_rows_panels": (_i32, [_i32, _i32, _i32, _i32, _i32]),
     "moe_forward_self_routes": (_i32, [_i32, _i32, _i32, _i32]),
     "moe_route": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _p, _p, _p, _sz, _p]),
     "moe_align": (ctypes.c_int, [_p, _i32, _i32, _i32, _i32, _p, _p, _p, _p]),
@@ -176,6 +178,10 @@ def moe_gemm_tile_rows(M: int, E: int, top_k: int, I: int) -> int:
 
 def moe_gemm_tile_rows_mx(M: int, E: int, top_k: int, I: int) -> int:
     return int(load_library().moe_gemm_tile_rows_mx(M, E, top_k, I))
+
+
+def moe_gemm_tile_rows_panels(M: int, E: int, top_k: int, I: int, weight_bits: int) -> int:
+    return int(load_library().moe_gemm_tile_rows_panels(M, E, top_k, I, weight_bits))
 
 
 def moe_forward_self_routes(M: int, E: int, top_k: int, I: int) -> bool:

@@ -99,6 +99,18 @@ int gemm_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I, bool mx) {
 constexpr int kSelfRouteIds = 256;
 static_assert(kSelfRouteIds <= moe::kSelfRouteMaxIds, "self-routing id limit");
 
+// Token-tile height of the fragment GEMMs on panels, by weight format (16 bf16, 8 MXFP8,
+// 4 MXFP4).  The narrower the weights, the less a hot expert's extra tiles cost in weight
+// bytes against the token rows and MFMAs the taller tiles waste on padding (measured: MXFP4
+// 64-row tiles at M=512 / 2048 2,326 -> 1,800 / 3,701 -> 3,517 us per layer; MXFP8 at
+// M=512 2,775 -> 2,588 us, but 4,180 -> 4,428 us at M=2048; bf16 keeps gemm_tile_rows).
+int panel_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I, int bits) {
+  const int64_t per_expert = (int64_t)M * top_k / E;
+  if (bits == 4) return per_expert < 256 ? 64 : 128;
+  if (bits == 8) return per_expert < 64 ? 64 : 128;
+  return gemm_tile_rows(M, E, top_k, I, false);
+}
+
 bool stream_weights(int32_t M, int32_t E, int32_t top_k, int trows) {
   return (int64_t)M * top_k / E < trows / 2;
 }
@@ -124,7 +136,7 @@ const char* moe_strerror(int status) {
   }
 }
 
-int moe_abi_version(void) { return 106; }
+int moe_abi_version(void) { return 107; }
 
 size_t moe_align_capacity(int32_t M, int32_t top_k, int32_t E, int32_t block) {
   if (M < 0 || top_k < 1 || E < 1 || block < 1) return 0;
@@ -145,6 +157,13 @@ int32_t moe_gemm_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I) {
 int32_t moe_gemm_tile_rows_mx(int32_t M, int32_t E, int32_t top_k, int32_t I) {
   if (M < 0 || E < 1 || E > kMaxE || top_k < 1 || top_k > E || I < 256 || I % 256 != 0) return 0;
   return gemm_tile_rows(M, E, top_k, I, true);
+}
+
+int32_t moe_gemm_tile_rows_panels(int32_t M, int32_t E, int32_t top_k, int32_t I,
+                                  int32_t weight_bits) {
+  if (M < 0 || E < 1 || E > kMaxE || top_k < 1 || top_k > E || I < 256 || I % 256 != 0) return 0;
+  if (weight_bits != 16 && weight_bits != 8 && weight_bits != 4) return 0;
+  return panel_tile_rows(M, E, top_k, I, weight_bits);
 }
 
 int32_t moe_forward_self_routes(int32_t M, int32_t E, int32_t top_k, int32_t I) {
@@ -336,7 +355,8 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   if (moe::launch_route(x, router_w, router_bias, M, H, E, top_k, ids, w, keys, s) != hipSuccess)
     return MOE_ERR_HIP;
   if (!mark(1)) return MOE_ERR_HIP;
-  const int trows = gemm_tile_rows(M, E, top_k, I, W.mx());
+  const int trows = W.panels() ? panel_tile_rows(M, E, top_k, I, W.fp4 ? 4 : W.fp8p ? 8 : 16)
+                                : gemm_tile_rows(M, E, top_k, I, W.mx());
   // about one token tile per expert: each weight is read once, copied nontemporally
   // (measured: M=8/128/512 gain, M=2048 -- many tiles of a hot expert share its weights
   // through the L2 -- loses 3 %)

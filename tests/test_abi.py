@@ -56,7 +56,7 @@ def test_library_links_no_torch(B):
 
 
 def test_strerror_and_version(B):
-    assert B.moe_abi_version() == 106
+    assert B.moe_abi_version() == 107
     for s in (0, -1, -2, -3, -4, 17):
         assert isinstance(B.moe_strerror(s), str) and B.moe_strerror(s)
 
@@ -177,6 +177,18 @@ def test_gemm_tile_rows_follows_tokens_per_expert(B):
     assert B.moe_gemm_tile_rows_mx(1024, 256, 16, 2048) == 128
     assert B.moe_gemm_tile_rows_mx(2048, 256, 16, 2048) == 128
     assert B.moe_gemm_tile_rows_mx(2048, 256, 16, 384) == 0
+    # fragment panels: bf16 as moe_forward; MXFP8 64-row tiles below 64 tokens per expert;
+    # MXFP4 below 256
+    for M in (1, 8, 128, 512, 2048):
+        assert B.moe_gemm_tile_rows_panels(M, 256, 16, 2048, 16) == B.moe_gemm_tile_rows(M, 256, 16, 2048)
+    assert B.moe_gemm_tile_rows_panels(512, 256, 16, 2048, 8) == 64
+    assert B.moe_gemm_tile_rows_panels(1023, 256, 16, 2048, 8) == 64
+    assert B.moe_gemm_tile_rows_panels(1024, 256, 16, 2048, 8) == 128
+    assert B.moe_gemm_tile_rows_panels(2048, 256, 16, 2048, 4) == 64
+    assert B.moe_gemm_tile_rows_panels(4095, 256, 16, 2048, 4) == 64
+    assert B.moe_gemm_tile_rows_panels(4096, 256, 16, 2048, 4) == 128
+    assert B.moe_gemm_tile_rows_panels(2048, 256, 16, 2048, 6) == 0
+    assert B.moe_gemm_tile_rows_panels(2048, 256, 16, 384, 4) == 0
 
 
 def test_read_probe_library_is_built_apart_from_the_layer(B):

@@ -130,12 +130,14 @@ def test_prepare_rejects_unsupported_widths(B, dev):
 # ---------------------------------------------------------------------------------------
 # Whole layer
 # ---------------------------------------------------------------------------------------
+# MXFP8 panel tiles: 64 rows below 64 expected tokens per expert (nontemporal weights below
+# 32), 128 rows from there
 SMALL = {
     # 64-row tiles, nontemporal weights; 4-wave workgroups on half N tiles
     "mxp_tiles64": mi.LayerConfig("mxp_tiles64", M=64, H=320, E=16, top_k=4, I=256, block=16),
-    # 128-row tiles with streamed weights, Zipf routing
-    "mxp_tiles128_stream": mi.LayerConfig("mxp_tiles128_stream", M=100, H=448, E=8, top_k=4,
-                                          I=256, block=32, zipf_s=1.0),
+    # 64-row tiles, default cache policy, Zipf routing
+    "mxp_tiles64_zipf": mi.LayerConfig("mxp_tiles64_zipf", M=100, H=448, E=8, top_k=4,
+                                       I=256, block=32, zipf_s=1.0),
     # 128-row tiles of a hot expert sharing its weights, a partial W2 panel (H = 640)
     "mxp_tiles128_shared": mi.LayerConfig("mxp_tiles128_shared", M=300, H=640, E=8, top_k=4,
                                           I=512, block=64, zipf_s=1.0),

@@ -148,6 +148,14 @@ def run_workload(B, mi, torch, cfg, weights, steps, warmup, dev, mx=None, prepar
     torch.cuda.synchronize()
     stage_ms = {name: sum(B.HipEvent.elapsed_ms(ev[i], ev[i + 1]) for ev in events) / steps
                 for i, name in enumerate(STAGES)}
+    # per-layer distribution of that pass (first to last event of each layer)
+    per_layer = sorted(B.HipEvent.elapsed_ms(ev[0], ev[-1]) * 1e3 for ev in events)
+
+    def pct(q):
+        x = q * (len(per_layer) - 1)
+        lo = int(x)
+        hi = min(lo + 1, len(per_layer) - 1)
+        return per_layer[lo] + (per_layer[hi] - per_layer[lo]) * (x - lo)
     ms = max(wall_ms, span_ms)
     touched = int(torch.unique(ids).numel())
     counts = torch.bincount(ids.flatten().long(), minlength=E)
@@ -164,6 +172,7 @@ def run_workload(B, mi, torch, cfg, weights, steps, warmup, dev, mx=None, prepar
     return {
         "M": M, "ms_per_step": ms, "us_per_layer": ms * 1e3, "tokens_per_s": M / (ms / 1e3),
         "wall_ms": wall_ms, "event_span_ms": span_ms, "stages_us": stages,
+        "layer_us_p10_p50_p90": [round(pct(0.1), 2), round(pct(0.5), 2), round(pct(0.9), 2)],
         "align": "fused into the up GEMM (self-routing)" if self_routed else "align kernel",
         "touched_experts": touched, "max_expert_count": int(counts.max().item()),
         "plan_rows": int(sum(((c + blk - 1) // blk) * blk for c in counts.tolist())),

@@ -668,6 +668,7 @@ def main():
         "warmup": args.warmup,
         "ms_per_step": round(res["ms_per_step"], 4),
         "us_per_layer": round(res["us_per_layer"], 2),
+        "layer_us_p10_p50_p90": res["layer_us_p10_p50_p90"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,

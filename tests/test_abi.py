@@ -240,3 +240,68 @@ def test_size_contract_is_h_mod_8_and_i_mod_16(B):
         assert (B.moe_workspace_bytes(4, H, 8, I, 2, 16) > 0) == ok, (H, I)
     assert B.moe_gemm_tile_rows(64, 8, 2, 48) == 16
     assert B.moe_gemm_tile_rows(64, 8, 2, 256) == 64
+
+
+def test_panel_entry_points_validate_on_the_host(B):
+    """moe_prepare_weights / moe_forward_prepared, the MXFP4 and the MXFP8-panel entry points:
+    sizes outside H % 64 == 0 and I % 256 == 0 are MOE_ERR_UNSUPPORTED, null, unpaired or
+    misaligned pointers MOE_ERR_INVALID_ARG, before any launch."""
+    lib = B.load_library()
+    p = ctypes.c_void_p
+    sz = ctypes.c_size_t
+    # sizes of the panels
+    assert lib.moe_prepared_w13_bytes(256, 7168, 2048) == 256 * 4096 * 7168 * 2
+    assert lib.moe_prepared_w2_bytes(256, 7168, 2048) == 256 * 7168 * 2048 * 2
+    assert lib.moe_prepared_w2_bytes(2, 640, 512) == 2 * 1024 * 512 * 2     # whole 512-row N tiles
+    assert lib.moe_prepared_w13_bytes(4, 96, 256) == 0
+    assert lib.moe_prepared_w13_bytes(4, 128, 128) == 0
+    out = [sz(7) for _ in range(4)]
+    assert lib.moe_mx4_weight_bytes(256, 7168, 2048, *[ctypes.byref(o) for o in out]) == 0
+    assert [o.value for o in out] == [256 * 4096 * 7168 // 2, 256 * 4096 * 7168 // 32,
+                                      256 * 7168 * 2048 // 2, 256 * 7168 * 2048 // 32]
+    assert lib.moe_mx_prepared_bytes(256, 7168, 2048, *[ctypes.byref(o) for o in out]) == 0
+    assert [o.value for o in out] == [256 * 4096 * 7168, 256 * 4096 * 7168 // 32,
+                                      256 * 7168 * 2048, 256 * 7168 * 2048 // 32]
+    for fn in (lib.moe_mx4_weight_bytes, lib.moe_mx_prepared_bytes):
+        assert fn(4, 96, 256, None, None, None, None) == -2
+        assert fn(4, 128, 128, None, None, None, None) == -2
+        assert fn(4, 100, 256, None, None, None, None) == -1       # H % 8 != 0
+        assert fn(0, 128, 256, None, None, None, None) == -1
+    # re-layout and quantization: unpaired or misaligned pointers
+    assert lib.moe_prepare_weights(p(256), None, 2, 128, 256, None, None, None) == -1
+    assert lib.moe_prepare_weights(p(258), None, 2, 128, 256, p(256), None, None) == -1
+    assert lib.moe_prepare_weights(p(256), None, 2, 96, 256, p(256), None, None) == -2
+    assert lib.moe_mx4_quantize(p(256), None, 2, 128, 256, p(256), None, None, None, None) == -1
+    assert lib.moe_mx4_quantize(p(256), None, 2, 128, 256, p(256), p(258), None, None, None) == -1
+    assert lib.moe_mx4_dequantize(p(256), p(256), 7, 2, 128, 256, p(256), None) == -1
+    assert lib.moe_mx_prepare_weights(p(256), p(256), None, None, 2, 128, 256, p(256), None, None,
+                                      None, None) == -1
+    assert lib.moe_mx_prepare_weights(p(256), p(256), None, None, 2, 128, 256, p(256), p(258),
+                                      None, None, None) == -1
+    assert lib.moe_mx_prepare_weights(None, None, None, None, 2, 128, 128, None, None, None, None,
+                                      None) == -2
+
+    # the forward passes on panels: unsupported widths, null weights, misaligned scales
+    def fwd(fn, H=256, I=512, c13=256, s13=256, s2=256, M=4, eps=1e-5):
+        return fn(p(256), p(256), None, None if c13 is None else p(c13), p(s13), p(256), p(s2),
+                  p(256), p(256), eps, M, H, 8, I, 2, 16, p(256), None, None, None, None, None,
+                  None, p(256), 1 << 40, None, None)
+    for fn in (lib.moe_forward_mx4, lib.moe_forward_mx_prepared):
+        assert fwd(fn, H=96) == -2
+        assert fwd(fn, I=128) == -2
+        assert fwd(fn, H=100) == -1
+        assert fwd(fn, c13=None) == -1
+        assert fwd(fn, s13=258) == -1                # scale panels 4-byte aligned
+        assert fwd(fn, s2=254) == -1
+        assert fwd(fn, eps=0.0) == -1
+        assert fwd(fn, M=0) == 0                      # no tokens: nothing to do
+    def fwd_prep(H=256, I=512, w13=256, M=4):
+        return lib.moe_forward_prepared(p(256), p(256), None, None if w13 is None else p(w13),
+                                        p(256), p(256), p(256), 1e-5, M, H, 8, I, 2, 16, p(256),
+                                        None, None, None, None, None, None, p(256), 1 << 40, None,
+                                        None)
+    assert fwd_prep(H=96) == -2
+    assert fwd_prep(I=128) == -2
+    assert fwd_prep(w13=None) == -1
+    assert fwd_prep(w13=264) == -1                    # 16-byte aligned panels
+    assert fwd_prep(M=0) == 0

@@ -21,7 +21,8 @@
 //      search of b * block in the prefix.
 // Optionally (for the grouped GEMMs of moe_forward) the kernel also lists the row tiles
 // of height T that hold real entries: tile = {first plan row, real rows in it}, tiles
-// never straddle two experts, listed expert by expert.
+// never straddle two experts, listed expert by expert (in id order, or -- with tile groups
+// -- in a hot/cold-mixed order, step 5; the plan itself is always in id order).
 #include "device_common.h"
 #include "launchers.h"
 
@@ -155,16 +156,48 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
     block_expert[b] = l;
   }
 
-  // 5. optional list of row tiles holding real entries
+  // 5. optional list of row tiles holding real entries.  With tile groups (the panel GEMMs,
+  // which walk the list expert by expert in one contiguous share per XCD, so that the tiles
+  // of an expert share its weight lines in one L2) the experts are listed hot and cold
+  // mixed: ranked by count (descending, ties by id), dealt in a snake over 8 bins (ranks 0-7
+  // to bins 0-7, 8-15 to bins 7-0, ...) and listed bin after bin, so that every share reads
+  // about as many distinct weight bytes as the others (listed by id, the shares that hold
+  // the hot experts fetch a few streams many times over while the cold shares fetch ten
+  // times their bytes: measured M=2048 bf16 panels 5,383 -> 5,122 us per layer); without
+  // tile groups in id order.
   if (tiles != nullptr) {
-    const int ntile_e = (tid < E) ? (total + tile_rows - 1) / tile_rows : 0;
-    __syncthreads();  // wave_total is reused by the scan
+    __shared__ int32_t s_total[kAlignMaxE];
+    __shared__ int32_t s_pos[kAlignMaxE];
+    if (tid < E) s_total[tid] = total;
+    __syncthreads();  // totals complete; wave_total is reused by the scan
+    int ep = tid;     // expert at list position tid
+    if (tile_groups != nullptr) {
+      if (tid < E) {
+        const int mine = s_total[tid];
+        int rank = 0;
+        for (int e = 0; e < E; ++e) {
+          const int o = s_total[e];
+          rank += (o > mine) || (o == mine && e < tid);
+        }
+        const int round = rank / 8, r8 = rank % 8;
+        const int bin = (round & 1) ? 7 - r8 : r8;
+        // experts in bins 0 .. bin-1: two per whole block of 16 ranks, plus the partial block
+        int before = 0;
+        for (int b = 0; b < bin; ++b) before += E / 16 * 2 + (E % 16 > b) + (E % 16 > 15 - b);
+        s_pos[before + round] = tid;   // one expert per bin and round, in rank order
+      }
+      __syncthreads();
+      if (tid < E) ep = s_pos[tid];
+    }
+    const int tot_e = tid < E ? s_total[ep] : 0;
+    const int ntile_e = (tid < E) ? (tot_e + tile_rows - 1) / tile_rows : 0;
     int all_tiles;
     const int first = block_exclusive_scan(ntile_e, wave_total, lane, wave, &all_tiles);
     if (tid < E) {
+      const int base = prefix[ep];
       for (int j = 0; j < ntile_e; ++j) {
-        const int left = total - j * tile_rows;
-        tiles[first + j] = make_int2(excl + j * tile_rows, left < tile_rows ? left : tile_rows);
+        const int left = tot_e - j * tile_rows;
+        tiles[first + j] = make_int2(base + j * tile_rows, left < tile_rows ? left : tile_rows);
         // optional: each tile's expert as {its first tile, its tile count}
         if (tile_groups != nullptr) tile_groups[first + j] = make_int2(first, ntile_e);
       }

@@ -35,13 +35,14 @@
 //   W2c8  [E][ceil(H/512)][8][I/32][2][64][2][8],                   W2s8 as W2s
 // dequantized in registers with v_cvt_scalef32_pk_bf16_fp8 (exact).
 //
-// Workgroup = 8 waves; item = one token tile (BM = 64 or 128 plan rows of one expert) x one
-// N tile (up: 256 act columns = 512 weight rows; down: 512 output columns).  Wave w owns 4
-// weight row tiles (64 rows) x all BM/16 token tiles.  Per MFMA K step of 32 values a wave
-// loads its 4 weight fragments (4 KiB) into a register ring of RS steps (the weights of
-// RS - 1 steps, 16 KiB per wave and 128 KiB per CU, in flight while one step is computed),
-// and per K chunk of 64 values 2 (BM = 128) or 1 (BM = 64) 1 KiB token copies into an LDS
-// ring of TS stages.
+// Item = one token tile (BM = 64 or 128 plan rows of one expert) x one N tile (up: 256 act
+// columns = 512 weight rows; down: 512 output columns), 8 wave streams of 64 weight rows;
+// a 128-row tile's item runs on an 8-wave workgroup, a 64-row tile's on two 4-wave
+// workgroups taking 4 streams each.  Each wave owns 4 weight row tiles (64 rows) x all
+// BM/16 token tiles.  Per MFMA K step of 32 values a wave loads its 4 weight fragments
+// (4 KiB for bf16) into a register ring of RS steps (the weights of RS - 1 steps in flight
+// while one step is computed), and per K chunk of 64 values 2 KiB per 16 token rows, split
+// over the workgroup's waves, into an LDS ring of TS stages.
 #include <algorithm>
 
 #include "device_common.h"
@@ -398,7 +399,6 @@ struct FragCfg {
   static constexpr int MT = BM / 16;                  // token row tiles
   static constexpr int TSTAGE = MT * 2048;            // bytes of one token chunk
   static constexpr int TCOPIES = MT * 2;              // 1 KiB copies per token chunk
-  static constexpr int WPC = 8;                       // weight loads per wave per chunk
 };
 
 // s_waitcnt vmcnt(N) (expcnt and lgkmcnt left open) through the builtin, which the
@@ -412,7 +412,8 @@ __device__ __forceinline__ void frag_wait_vmcnt() {
 }
 
 // Buffer resource over one wave's weight stream (`bytes` long, 4-byte aligned base): raw,
-// untyped 32-bit data, so loads past `bytes` return zero instead of touching memory.
+// untyped 32-bit data.  Every load the GEMMs issue through it stays inside `bytes` (steps
+// past the last one are clamped to it).
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t stream_rsrc(const void* base, int bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
 }

@@ -166,18 +166,32 @@ __global__ __launch_bounds__(kAlignThreads) void align_kernel(
   // times their bytes: measured M=2048 bf16 panels 5,383 -> 5,122 us per layer); without
   // tile groups in id order.
   if (tiles != nullptr) {
-    __shared__ int32_t s_total[kAlignMaxE];
+    __shared__ __align__(16) int32_t s_total[kAlignMaxE];
     __shared__ int32_t s_pos[kAlignMaxE];
-    if (tid < E) s_total[tid] = total;
+    __shared__ int32_t s_multi;
+    if (tid == 0) s_multi = 0;
+    __syncthreads();
+    if (tid < E) {
+      s_total[tid] = total;
+      if (total > tile_rows) s_multi = 1;   // some expert has several tiles
+    } else if (tid < ((E + 3) & ~3)) {
+      s_total[tid] = -1;                    // pads the last group of four
+    }
     __syncthreads();  // totals complete; wave_total is reused by the scan
     int ep = tid;     // expert at list position tid
-    if (tile_groups != nullptr) {
+    // (with one tile per expert every share streams its experts' weights once: no reorder)
+    if (tile_groups != nullptr && s_multi) {
       if (tid < E) {
         const int mine = s_total[tid];
         int rank = 0;
-        for (int e = 0; e < E; ++e) {
-          const int o = s_total[e];
-          rank += (o > mine) || (o == mine && e < tid);
+        const int4* t4 = reinterpret_cast<const int4*>(s_total);
+        for (int q = 0; q < (E + 3) / 4; ++q) {
+          const int4 o = t4[q];
+          const int e = 4 * q;
+          rank += (o.x > mine) || (o.x == mine && e < tid);
+          rank += (o.y > mine) || (o.y == mine && e + 1 < tid);
+          rank += (o.z > mine) || (o.z == mine && e + 2 < tid);
+          rank += (o.w > mine) || (o.w == mine && e + 3 < tid);
         }
         const int round = rank / 8, r8 = rank % 8;
         const int bin = (round & 1) ? 7 - r8 : r8;

@@ -493,6 +493,54 @@ def test_forward_graph_replay_and_side_stream(B, dev, name):
         torch.randn(1 << 20, device=dev).sum().item()
 
 
+
+@pytest.mark.parametrize("name", ["mid", "tiled128_zipf", "tiled64_zipf"])
+def test_forward_concurrent_streams(B, dev, name):
+    """Two moe_forward calls in flight at once on two streams, each with its own inputs,
+    outputs and workspace, give bit for bit what each gives alone: the library keeps no
+    state between calls outside the caller's buffers."""
+    cfg = SMALL[name]
+    print(f"concurrent streams {name}", flush=True)
+    L = mi.make_layer(cfg, device=dev, seed=5)
+    M, H, E, I, k, blk = L["M"], cfg.H, cfg.E, cfg.I, cfg.top_k, cfg.block
+    nws = B.moe_workspace_bytes(M, H, E, I, k, blk)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(12)
+    xs = [torch.randn((M, H), generator=gen, device=dev).to(torch.bfloat16) for _ in range(2)]
+
+    def buffers():
+        return (torch.full((M, H), float("nan"), dtype=torch.bfloat16, device=dev),
+                torch.full((M, k), -7, dtype=torch.int32, device=dev),
+                torch.empty(nws, dtype=torch.uint8, device=dev))
+
+    def call(x, bufs):
+        out, ids, ws = bufs
+        B.moe_forward(x, L["router_w"], L["router_bias"], L["w13"], L["w2"], L["residual"],
+                      L["norm_w"], L["eps"], k, blk, out, ws, topk_ids_out=ids)
+
+    alone = []
+    for x in xs:
+        bufs = buffers()
+        call(x, bufs)
+        torch.cuda.synchronize()
+        alone.append(bufs)
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    together = [buffers(), buffers()]
+    for rep in range(3):
+        for st in streams:
+            st.wait_stream(torch.cuda.current_stream())
+        for x, bufs, st in zip(xs, together, streams):
+            with torch.cuda.stream(st):
+                call(x, bufs)
+        torch.cuda.synchronize()
+        for j in range(2):
+            assert torch.equal(together[j][1], alone[j][1]), (name, rep, j)
+            assert torch.equal(together[j][0].view(torch.int16), alone[j][0].view(torch.int16)), \
+                (name, rep, j)
+        for bufs in together:
+            bufs[0].fill_(float("nan"))
+            bufs[1].fill_(-7)
+
 def test_forward_zero_tokens(B, dev):
     cfg = SMALL["mid"]
     L = mi.make_layer(cfg, device=dev, seed=0, M=0)

@@ -107,6 +107,11 @@ SMALL = {
     "fin_topk12": mi.LayerConfig("fin_topk12", M=264, H=256, E=32, top_k=12, I=256, block=32),
 }
 FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048"]
+# A maximum-size case beyond the timed workloads: four times the prefill batch (131,072
+# flat ids, about 2,000 token tiles of 128 rows) on the same real-shape weights.
+LARGE = {"prefill_m8192": mi.LayerConfig("prefill_m8192", M=8192, H=7168, E=256, top_k=16,
+                                         I=2048, block=64, zipf_s=1.0)}
+FULL_RUNS = FULL + list(LARGE)
 
 
 def _poisoned(shape, dtype, dev):
@@ -561,11 +566,11 @@ def full_weights(dev):
 
 @pytest.fixture(scope="module")
 def full_runs(B, dev, full_weights):
-    """The four real-shape workloads through moe_forward (the kernels the benchmark times),
-    their results copied to the host."""
+    """The four real-shape workloads through moe_forward (the kernels the benchmark times)
+    and the larger M=8192 batch, their results copied to the host."""
     runs = {}
-    for name in FULL:
-        cfg = mi.CONFIGS[name]
+    for name in FULL_RUNS:
+        cfg = LARGE.get(name) or mi.CONFIGS[name]
         print(f"forward full-size {name} M={cfg.M}", flush=True)
         L = mi.make_layer(cfg, device=dev, seed=0, with_experts=False)
         L.update(full_weights)
@@ -585,7 +590,7 @@ def full_runs(B, dev, full_weights):
     return runs
 
 
-@pytest.mark.parametrize("name", FULL)
+@pytest.mark.parametrize("name", FULL_RUNS)
 def test_forward_full_size_routing_and_plan(full_runs, name):
     """Every token: routing ids bit-exact, weights within 1e-6, the plan bit-exact; every
     output row finite."""
@@ -603,8 +608,8 @@ def test_forward_full_size_routing_and_plan(full_runs, name):
 
 @pytest.fixture(scope="module")
 def full_oracle(full_runs, full_weights):
-    """The oracle on the sampled tokens of all four workloads, in one pass over the experts
-    (each expert copied to the host and decoded once)."""
+    """The oracle on the sampled tokens of all the real-shape workloads, in one pass over
+    the experts (each expert copied to the host and decoded once)."""
     jobs, meta = {}, {}
     for name, run in full_runs.items():
         cfg = run["cfg"]
@@ -626,10 +631,10 @@ def full_oracle(full_runs, full_weights):
 
 
 @pytest.mark.timeout(1200)
-@pytest.mark.parametrize("name", FULL)
+@pytest.mark.parametrize("name", FULL_RUNS)
 def test_forward_full_size_against_oracle(full_runs, full_oracle, name):
     """Sampled tokens of the real-shape layer against the oracle: every token at M=8 and
-    M=128; at M=512 and M=2048 at least 256 tokens including token M-1 and, for every
+    M=128; from M=512 (512, 2048, 8192) at least 256 tokens including token M-1 and, for every
     expert, the first and the last token that picked it, so every expert's first and last
     token tile of both grouped GEMMs (all K chunks, all N tiles) holds a checked row."""
     run = full_runs[name]

@@ -1,7 +1,7 @@
 """Seeded synthetic inputs for the routed-MoE layer (router -> align -> up -> down -> finalize).
 
 This module is plumbing shared by the tests, the benchmark and the smoke check.  It
-holds the five layer workloads and the generators that fill their tensors; it holds
+holds the layer workloads and the generators that fill their tensors; it holds
 none of the layer's arithmetic.  Both the HIP path and the CPU oracle receive the
 tensors produced here, so neither side ever sees inputs that the other made.
 
@@ -14,6 +14,8 @@ the AlphaMoE page names the GLM m8 / m128 / m512 / m2048 route workloads, sectio
   batch_m128     M=128,  H=7168, E=256, k=16, I=2048, block=64, no router bias
   batch_m512     M=512,  same layer, block=64, Zipf(1.0)-shaped router bias
   prefill_m2048  M=2048, same layer, block=64, Zipf(1.0)-shaped router bias
+  prefill_m8192  M=8192, same layer, block=64, Zipf(1.0)-shaped router bias (a parity
+                 case past the timed sizes: 131,072 flat ids)
 
 Value recipe (every tensor has its own seed so that any one of them, or any single
 expert's weights, can be regenerated on its own):
@@ -76,6 +78,8 @@ CONFIGS = {
     "batch_m512": LayerConfig("batch_m512", M=512, H=7168, E=256, top_k=16, I=2048, block=64,
                               zipf_s=1.0),
     "prefill_m2048": LayerConfig("prefill_m2048", M=2048, H=7168, E=256, top_k=16, I=2048,
+                                 block=64, zipf_s=1.0),
+    "prefill_m8192": LayerConfig("prefill_m8192", M=8192, H=7168, E=256, top_k=16, I=2048,
                                  block=64, zipf_s=1.0),
 }
 

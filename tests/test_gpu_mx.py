@@ -196,7 +196,7 @@ def test_forward_mx_rejects_unsupported_widths(B, dev):
     assert ei.value.status == -2
 
 
-MX_FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048"]
+MX_FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048", "prefill_m8192"]
 
 
 @pytest.fixture(scope="module")

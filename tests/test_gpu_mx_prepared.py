@@ -200,7 +200,7 @@ def test_forward_mx_prepared_small(B, dev, name):
     _check_close(r["rout"], ref["residual_out"], name + " residual_out")
 
 
-FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048"]
+FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048", "prefill_m8192"]
 
 
 @pytest.fixture(scope="module")

@@ -107,11 +107,9 @@ SMALL = {
     "fin_topk12": mi.LayerConfig("fin_topk12", M=264, H=256, E=32, top_k=12, I=256, block=32),
 }
 FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048"]
-# A maximum-size case beyond the timed workloads: four times the prefill batch (131,072
-# flat ids, about 2,000 token tiles of 128 rows) on the same real-shape weights.
-LARGE = {"prefill_m8192": mi.LayerConfig("prefill_m8192", M=8192, H=7168, E=256, top_k=16,
-                                         I=2048, block=64, zipf_s=1.0)}
-FULL_RUNS = FULL + list(LARGE)
+# with a maximum-size case past the timed workloads: four times the prefill batch (131,072
+# flat ids, about 2,000 token tiles of 128 rows) on the same real-shape weights
+FULL_RUNS = FULL + ["prefill_m8192"]
 
 
 def _poisoned(shape, dtype, dev):
@@ -570,7 +568,7 @@ def full_runs(B, dev, full_weights):
     and the larger M=8192 batch, their results copied to the host."""
     runs = {}
     for name in FULL_RUNS:
-        cfg = LARGE.get(name) or mi.CONFIGS[name]
+        cfg = mi.CONFIGS[name]
         print(f"forward full-size {name} M={cfg.M}", flush=True)
         L = mi.make_layer(cfg, device=dev, seed=0, with_experts=False)
         L.update(full_weights)

@@ -183,7 +183,7 @@ def test_prepared_rejects_unsupported_widths(B, dev):
 # Real shape: every workload, bit for bit against the natural path, sampled tokens against
 # the oracle
 # ---------------------------------------------------------------------------------------
-FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048"]
+FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048", "prefill_m8192"]
 
 
 @pytest.fixture(scope="module")

@@ -330,7 +330,7 @@ int moe_forward_mx_prepared(const uint16_t* x, const uint16_t* router_w, const f
  * ends.  It allocates nothing and takes no workspace or stage events.  Sizes whose
  * moe_workspace_bytes exceed MOE_NOALLOC_SCRATCH_BYTES return MOE_ERR_WORKSPACE before
  * anything is launched (the real-shape layer, H=7168, E=256, top_k=16, I=2048, fits up to
- * 154 tokens with block 16, 15 with block 64).  Every call on a GPU shares that GPU's array,
+ * 142 tokens with block 16, 14 with block 64).  Every call on a GPU shares that GPU's array,
  * which keeps the last call's contents (nothing in it needs to start at zero): calls that
  * overlap on one GPU -- on different streams, or from different host threads -- race and
  * must be ordered by the caller.  The first call on a device looks up that device's array

@@ -32,6 +32,33 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ float silu_f32(float z) { return z / (1.0f + __expf(-z)); }
 
+// Where moe_forward's down GEMMs put the row of flat index i = t * top_k + j: the first pick
+// of each token (j = 0, the largest routing weight, since picks are in key order) in fp32
+// at row t of y0 [M, H]; every other pick rounded to bf16 (nearest even) at row i of
+// y [M * top_k, H].  A token whose weight sits on one pick would otherwise carry that
+// pick's bf16 rounding into its output unaveraged.
+struct YRow {
+  size_t off;   // element offset of the row in y0 (first pick) or y
+  bool first;
+};
+__device__ __forceinline__ YRow y_row(int i, int top_k, int ncols) {
+  const int t = i / top_k;
+  const bool first = i == t * top_k;
+  return YRow{(size_t)(first ? t : i) * ncols, first};
+}
+// values n .. n + 3 of the row
+__device__ __forceinline__ void store_y4(uint16_t* __restrict__ y, float* __restrict__ y0,
+                                         YRow r, int n, float a, float b, float c, float d) {
+  if (r.first) {
+    *reinterpret_cast<float4*>(y0 + r.off + n) = make_float4(a, b, c, d);
+  } else {
+    uint2 v;
+    v.x = pack_bf16x2(a, b);
+    v.y = pack_bf16x2(c, d);
+    *reinterpret_cast<uint2*>(y + r.off + n) = v;
+  }
+}
+
 // 16-byte global load / store through the vector memory path.
 __device__ __forceinline__ u32x4 ld16(const void* p) {
   return *reinterpret_cast<const u32x4*>(p);

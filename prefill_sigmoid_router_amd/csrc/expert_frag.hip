@@ -430,7 +430,7 @@ __device__ __forceinline__ void frag_item(
     const void* __restrict__ wp, const uint8_t* __restrict__ wsc,
     const int32_t* __restrict__ row_ids, int start, int nlive, int e, int ntile, int part,
     int n_ntiles, int K, int ncols, int I, int top_k, uint16_t* __restrict__ act,
-    uint16_t* __restrict__ y) {
+    uint16_t* __restrict__ y, float* __restrict__ y0) {
   using C = FragCfg<BM>;
   constexpr int MT = C::MT;
   constexpr int TS = kFragTS;
@@ -613,17 +613,13 @@ __device__ __forceinline__ void frag_item(
         *reinterpret_cast<uint2*>(act + (size_t)(start + r) * I + n) = v;
       }
     } else {
-      const int dst = row_ids[r];
+      const YRow yr = y_row(row_ids[r], top_k, ncols);
       const int col0 = ntile * 512 + 64 * pw;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int n = col0 + 16 * j + 4 * lg;
-        if (n < ncols) {
-          uint2 v;
-          v.x = pack_bf16x2(acc[j][s][0], acc[j][s][1]);
-          v.y = pack_bf16x2(acc[j][s][2], acc[j][s][3]);
-          *reinterpret_cast<uint2*>(y + (size_t)dst * ncols + n) = v;
-        }
+        if (n < ncols)
+          store_y4(y, y0, yr, n, acc[j][s][0], acc[j][s][1], acc[j][s][2], acc[j][s][3]);
       }
     }
   }
@@ -660,7 +656,7 @@ __global__ __launch_bounds__(64 * NWG) void expert_frag_kernel(
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
     const int2* __restrict__ tiles, const int2* __restrict__ tile_groups,
     const int32_t* __restrict__ num_tiles, int n_ntiles, int K, int ncols, int I, int top_k,
-    int block, uint16_t* __restrict__ act, uint16_t* __restrict__ y) {
+    int block, uint16_t* __restrict__ act, uint16_t* __restrict__ y, float* __restrict__ y0) {
   __shared__ __align__(16) unsigned char tlds[kFragTS * FragCfg<BM>::TSTAGE];
   // items: (tile, N tile of the panels, part); a workgroup of NWG waves does 8 / NWG parts
   // of an N tile, the parts counted as N tiles of their own in the walk
@@ -679,11 +675,11 @@ __global__ __launch_bounds__(64 * NWG) void expert_frag_kernel(
     if (tile.y <= 16 * NS)
       frag_item<BM, UP, WPOL, NS, WF, NWG>(tlds, tok_src, wp, wsc, sorted_ids + tile.x, tile.x,
                                             tile.y, block_expert[tile.x / block], ntile, part,
-                                            n_ntiles, K, ncols, I, top_k, act, y);
+                                            n_ntiles, K, ncols, I, top_k, act, y, y0);
     else
       frag_item<BM, UP, WPOL, MT, WF, NWG>(tlds, tok_src, wp, wsc, sorted_ids + tile.x, tile.x,
                                             tile.y, block_expert[tile.x / block], ntile, part,
-                                            n_ntiles, K, ncols, I, top_k, act, y);
+                                            n_ntiles, K, ncols, I, top_k, act, y, y0);
     __syncthreads();  // the next item's first token copies reuse the ring
   }
 }
@@ -694,7 +690,7 @@ static hipError_t launch_frag(const uint16_t* src, const void* wp, const uint8_t
                               const int32_t* block_expert, const int2* tiles,
                               const int2* tile_groups, const int32_t* num_tiles, int max_tiles,
                               int K, int ncols, int I, int top_k, int block, uint16_t* act,
-                              uint16_t* y, hipStream_t s) {
+                              uint16_t* y, float* y0, hipStream_t s) {
   const int per_ntile = UP ? 256 : 512;
   if (K % kFragKC != 0 || (UP && I % per_ntile != 0)) return hipErrorInvalidValue;
   const int n_ntiles = (ncols + per_ntile - 1) / per_ntile;
@@ -707,7 +703,7 @@ static hipError_t launch_frag(const uint16_t* src, const void* wp, const uint8_t
   const long grid = BM == 64 ? walk_grid(items, 80 * 1024) : (items + kXcds - 1) / kXcds * kXcds;
   hipLaunchKernelGGL((expert_frag_kernel<BM, UP, WPOL, WF, NWG>), dim3((unsigned)grid),
                      dim3(64 * NWG), 0, s, src, wp, wsc, sorted_ids, block_expert, tiles,
-                     tile_groups, num_tiles, n_ntiles, K, ncols, I, top_k, block, act, y);
+                     tile_groups, num_tiles, n_ntiles, K, ncols, I, top_k, block, act, y, y0);
   return hipGetLastError();
 }
 
@@ -721,7 +717,8 @@ hipError_t launch_expert_up_frag(const uint16_t* x, const uint16_t* w13p, const 
 #define MOE_FRAG_UP(BM, POL)                                                                    \
   return launch_frag<BM, true, POL>(x, w13p, nullptr, sorted_ids, block_expert, tiles,        \
                                     tile_groups,                                              \
-                                    num_tiles, max_tiles, H, I, I, top_k, block, act, nullptr, s)
+                                    num_tiles, max_tiles, H, I, I, top_k, block, act, nullptr, \
+                                    nullptr, s)
   if (tile_rows == 64) {
     if (stream_weights) MOE_FRAG_UP(64, kFragNT);
     MOE_FRAG_UP(64, 0);
@@ -739,11 +736,11 @@ hipError_t launch_expert_down_frag(const uint16_t* act, const uint16_t* w2p,
                                    const int2* tiles, const int2* tile_groups,
                                    const int32_t* num_tiles, int max_tiles, int tile_rows,
                                    bool stream_weights, int H, int I, int top_k, int block,
-                                   uint16_t* y, hipStream_t s) {
+                                   uint16_t* y, float* y0, hipStream_t s) {
 #define MOE_FRAG_DOWN(BM, POL)                                                                  \
   return launch_frag<BM, false, POL>(act, w2p, nullptr, sorted_ids, block_expert, tiles,       \
-                                     tile_groups,                                             \
-                                     num_tiles, max_tiles, I, H, I, top_k, block, nullptr, y, s)
+                                     tile_groups, num_tiles, max_tiles, I, H, I, top_k, block, \
+                                     nullptr, y, y0, s)
   if (tile_rows == 64) {
     if (stream_weights) MOE_FRAG_DOWN(64, kFragNT);
     MOE_FRAG_DOWN(64, 0);
@@ -765,7 +762,7 @@ hipError_t launch_expert_up_frag_mx(const uint16_t* x, const uint8_t* w13c, cons
 #define MOE_FRAGMX_UP(BM, POL, WF)                                                              \
   return launch_frag<BM, true, POL, WF>(x, w13c, w13s, sorted_ids, block_expert, tiles,         \
                                         tile_groups, num_tiles, max_tiles, H, I, I, top_k,      \
-                                        block, act, nullptr, s)
+                                        block, act, nullptr, nullptr, s)
 #define MOE_FRAGMX_UP_FMT(WF)                   \
   if (tile_rows == 64) {                        \
     if (stream_weights) MOE_FRAGMX_UP(64, kFragNT, WF); \
@@ -790,11 +787,12 @@ hipError_t launch_expert_down_frag_mx(const uint16_t* act, const uint8_t* w2c, c
                                      const int32_t* block_expert, const int2* tiles,
                                      const int2* tile_groups, const int32_t* num_tiles,
                                      int max_tiles, int tile_rows, bool stream_weights, int H,
-                                     int I, int top_k, int block, uint16_t* y, hipStream_t s) {
+                                     int I, int top_k, int block, uint16_t* y, float* y0,
+                                     hipStream_t s) {
 #define MOE_FRAGMX_DOWN(BM, POL, WF)                                                            \
   return launch_frag<BM, false, POL, WF>(act, w2c, w2s, sorted_ids, block_expert, tiles,        \
                                          tile_groups, num_tiles, max_tiles, I, H, I, top_k,     \
-                                         block, nullptr, y, s)
+                                         block, nullptr, y, y0, s)
 #define MOE_FRAGMX_DOWN_FMT(WF)                 \
   if (tile_rows == 64) {                        \
     if (stream_weights) MOE_FRAGMX_DOWN(64, kFragNT, WF); \

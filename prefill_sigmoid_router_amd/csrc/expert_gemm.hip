@@ -158,8 +158,8 @@ __global__ __launch_bounds__(256) void expert_down_stream_kernel(
     const uint16_t* __restrict__ act, const uint16_t* __restrict__ w2,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
     const int32_t* __restrict__ num_padded, const int2* __restrict__ tiles,
-    const int32_t* __restrict__ num_tiles, int H, int I, int block, int sentinel,
-    Y* __restrict__ y) {
+    const int32_t* __restrict__ num_tiles, int H, int I, int top_k, int block, int sentinel,
+    Y* __restrict__ y, float* __restrict__ y0) {
   __shared__ f32x4 red[2][kWave];
   int start, nlive;
   if (!tile_of(tiles, num_tiles, sorted_ids, num_padded, sentinel, start, nlive)) return;
@@ -187,11 +187,9 @@ __global__ __launch_bounds__(256) void expert_down_stream_kernel(
   if constexpr (std::is_same<Y, float>::value) {
     *reinterpret_cast<float4*>(y + (size_t)dst * H + n0 + 4 * lg) =
         make_float4(acc[0][0], acc[0][1], acc[0][2], acc[0][3]);
-  } else {                                           // bf16 y, nearest even
-    uint2 v;
-    v.x = pack_bf16x2(acc[0][0], acc[0][1]);
-    v.y = pack_bf16x2(acc[0][2], acc[0][3]);
-    *reinterpret_cast<uint2*>(y + (size_t)dst * H + n0 + 4 * lg) = v;
+  } else {                                           // first picks fp32, the others bf16
+    store_y4(y, y0, y_row(dst, top_k, H), n0 + 4 * lg, acc[0][0], acc[0][1], acc[0][2],
+             acc[0][3]);
   }
 }
 
@@ -210,11 +208,12 @@ template <typename Y>
 static hipError_t launch_down_rows(const uint16_t* act, const uint16_t* w2, const int32_t* sorted_ids,
                               const int32_t* block_expert, const int32_t* num_padded,
                               const int2* tiles, const int32_t* num_tiles, int max_tiles, int M,
-                              int H, int I, int top_k, int block, Y* y, hipStream_t s) {
+                              int H, int I, int top_k, int block, Y* y, float* y0,
+                              hipStream_t s) {
   dim3 grid((H + 31) / 32, max_tiles);
   hipLaunchKernelGGL((expert_down_stream_kernel<kDownStreamU, Y>), grid, dim3(256), 0, s, act, w2,
-                     sorted_ids, block_expert, num_padded, tiles, num_tiles, H, I, block,
-                     M * top_k, y);
+                     sorted_ids, block_expert, num_padded, tiles, num_tiles, H, I, top_k, block,
+                     M * top_k, y, y0);
   return hipGetLastError();
 }
 
@@ -223,14 +222,15 @@ hipError_t launch_expert_down(const uint16_t* act, const uint16_t* w2, const int
                               const int2* tiles, const int32_t* num_tiles, int max_tiles, int M,
                               int H, int I, int top_k, int block, float* y, hipStream_t s) {
   return launch_down_rows(act, w2, sorted_ids, block_expert, num_padded, tiles, num_tiles,
-                          max_tiles, M, H, I, top_k, block, y, s);
+                          max_tiles, M, H, I, top_k, block, y, nullptr, s);
 }
 hipError_t launch_expert_down(const uint16_t* act, const uint16_t* w2, const int32_t* sorted_ids,
                               const int32_t* block_expert, const int32_t* num_padded,
                               const int2* tiles, const int32_t* num_tiles, int max_tiles, int M,
-                              int H, int I, int top_k, int block, uint16_t* y, hipStream_t s) {
+                              int H, int I, int top_k, int block, uint16_t* y, float* y0,
+                              hipStream_t s) {
   return launch_down_rows(act, w2, sorted_ids, block_expert, num_padded, tiles, num_tiles,
-                          max_tiles, M, H, I, top_k, block, y, s);
+                          max_tiles, M, H, I, top_k, block, y, y0, s);
 }
 
 }  // namespace moe

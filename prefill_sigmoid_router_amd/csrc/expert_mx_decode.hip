@@ -84,7 +84,8 @@ __device__ __forceinline__ void mx_decode_item(
     const uint16_t* __restrict__ tok_src, const uint8_t* __restrict__ wc,
     const uint8_t* __restrict__ ws, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int2* __restrict__ tiles, int K, int ncols,
-    int I, int top_k, int block, uint16_t* __restrict__ act, uint16_t* __restrict__ y) {
+    int I, int top_k, int block, uint16_t* __restrict__ act, uint16_t* __restrict__ y,
+    float* __restrict__ y0) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int li = lane & 15, lg = lane >> 4;
   const int nch = K / kKC;
@@ -248,14 +249,12 @@ __device__ __forceinline__ void mx_decode_item(
         *reinterpret_cast<uint2*>(act + (size_t)(start + r) * I + n) = v;
       }
     } else {
-      const int dst = sorted_ids[start + r];
+      const YRow yr = y_row(sorted_ids[start + r], top_k, ncols);
 #pragma unroll
       for (int j = 0; j < kTW; ++j) {
         const int n = ntile * kRows + 16 * (kTW * wave + j) + 4 * lg;
-        if (n < ncols)                                   // y in bf16 (nearest even)
-          *reinterpret_cast<uint64_t*>(y + (size_t)dst * ncols + n) =
-              pack_bf16x2(acc[j][s][0], acc[j][s][1]) |
-                  ((uint64_t)pack_bf16x2(acc[j][s][2], acc[j][s][3]) << 32);
+        if (n < ncols)
+          store_y4(y, y0, yr, n, acc[j][s][0], acc[j][s][1], acc[j][s][2], acc[j][s][3]);
       }
     }
   }
@@ -267,14 +266,14 @@ __global__ __launch_bounds__(64 * kWaves) void expert_mx_decode_kernel(
     const uint8_t* __restrict__ ws, const int32_t* __restrict__ sorted_ids,
     const int32_t* __restrict__ block_expert, const int2* __restrict__ tiles,
     const int32_t* __restrict__ num_tiles, int n_ntiles, int K, int ncols, int I, int top_k,
-    int block, uint16_t* __restrict__ act, uint16_t* __restrict__ y) {
+    int block, uint16_t* __restrict__ act, uint16_t* __restrict__ y, float* __restrict__ y0) {
   using C = MxdCfg<BM>;
   __shared__ __align__(16) unsigned char lds[C::LDS];
   TiledWalk walk(*num_tiles, n_ntiles);
   int ntile, ti;
   while (walk.next(ntile, ti)) {
     mx_decode_item<BM, WPOL, UP>(lds, lds + C::S * C::STAGE, ntile, ti, tok_src, wc, ws, sorted_ids,
-                       block_expert, tiles, K, ncols, I, top_k, block, act, y);
+                       block_expert, tiles, K, ncols, I, top_k, block, act, y, y0);
     __syncthreads();  // the next item's first copies reuse the rings
   }
 }
@@ -283,7 +282,8 @@ template <int BM, int WPOL, bool UP>
 hipError_t launch_mx_lds(const uint16_t* src, const uint8_t* wc, const uint8_t* ws,
                          const int32_t* sorted_ids, const int32_t* block_expert, const int2* tiles,
                          const int32_t* num_tiles, int max_tiles, int K, int ncols, int I,
-                         int top_k, int block, uint16_t* act, uint16_t* y, hipStream_t s) {
+                         int top_k, int block, uint16_t* act, uint16_t* y, float* y0,
+                         hipStream_t s) {
   if (K % kKC != 0 || (UP && I % 128 != 0) || (uintptr_t)ws % 4 != 0) return hipErrorInvalidValue;
   const int per_ntile = UP ? 128 : kRows;
   const int n_ntiles = (ncols + per_ntile - 1) / per_ntile;
@@ -291,7 +291,7 @@ hipError_t launch_mx_lds(const uint16_t* src, const uint8_t* wc, const uint8_t* 
   const long grid = walk_grid(items, MxdCfg<BM>::LDS);
   hipLaunchKernelGGL((expert_mx_decode_kernel<BM, WPOL, UP>), dim3((unsigned)grid),
                      dim3(64 * kWaves), 0, s, src, wc, ws, sorted_ids, block_expert, tiles,
-                     num_tiles, n_ntiles, K, ncols, I, top_k, block, act, y);
+                     num_tiles, n_ntiles, K, ncols, I, top_k, block, act, y, y0);
   return hipGetLastError();
 }
 
@@ -300,10 +300,11 @@ hipError_t launch_mx_lds_rows(const uint16_t* src, const uint8_t* wc, const uint
                               const int32_t* sorted_ids, const int32_t* block_expert,
                               const int2* tiles, const int32_t* num_tiles, int max_tiles,
                               int tile_rows, bool stream_weights, int K, int ncols, int I,
-                              int top_k, int block, uint16_t* act, uint16_t* y, hipStream_t s) {
+                              int top_k, int block, uint16_t* act, uint16_t* y, float* y0,
+                              hipStream_t s) {
 #define MOE_MXL(BM, POL)                                                                      \
   return launch_mx_lds<BM, POL, UP>(src, wc, ws, sorted_ids, block_expert, tiles, num_tiles, \
-                                    max_tiles, K, ncols, I, top_k, block, act, y, s)
+                                    max_tiles, K, ncols, I, top_k, block, act, y, y0, s)
   if (tile_rows == 32) {
     if (stream_weights) MOE_MXL(32, kNT);
     MOE_MXL(32, 0);
@@ -329,17 +330,17 @@ hipError_t launch_expert_up_mx_lds(const uint16_t* x, const uint8_t* w13c, const
                                    int block, uint16_t* act, hipStream_t s) {
   return launch_mx_lds_rows<true>(x, w13c, w13s, sorted_ids, block_expert, tiles, num_tiles,
                                   max_tiles, tile_rows, stream_weights, H, I, I, top_k, block,
-                                  act, nullptr, s);
+                                  act, nullptr, nullptr, s);
 }
 
 hipError_t launch_expert_down_mx_lds(const uint16_t* act, const uint8_t* w2c, const uint8_t* w2s,
                                      const int32_t* sorted_ids, const int32_t* block_expert,
                                      const int2* tiles, const int32_t* num_tiles, int max_tiles,
                                      int tile_rows, bool stream_weights, int H, int I, int top_k,
-                                     int block, uint16_t* y, hipStream_t s) {
+                                     int block, uint16_t* y, float* y0, hipStream_t s) {
   return launch_mx_lds_rows<false>(act, w2c, w2s, sorted_ids, block_expert, tiles, num_tiles,
                                    max_tiles, tile_rows, stream_weights, I, H, I, top_k, block,
-                                   nullptr, y, s);
+                                   nullptr, y, y0, s);
 }
 
 }  // namespace moe

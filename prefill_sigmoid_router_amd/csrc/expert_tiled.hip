@@ -78,7 +78,7 @@ __device__ __forceinline__ void tiled_gemm(
     unsigned char* __restrict__ lds, const uint16_t* __restrict__ tok_src,
     const uint16_t* __restrict__ w, const int32_t* row_ids, int start, int nlive, int e,
     int ntile, int K, int ncols, int I, int top_k, uint16_t* __restrict__ act,
-    uint16_t* __restrict__ y) {
+    uint16_t* __restrict__ y, float* __restrict__ y0) {
   using C = TiledCfg<BM, WN, WM>;
   const int mt_active = (nlive + 15) >> 4;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -219,18 +219,14 @@ __device__ __forceinline__ void tiled_gemm(
         *reinterpret_cast<uint2*>(act + (size_t)(start + r) * I + n) = v;
       }
     } else if (!UP && r < nlive) {
-      const int dst = row_ids[r];
+      const YRow yr = y_row(row_ids[r], top_k, ncols);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int n = col0 + wn * 64 + j * 16 + 4 * lg;
-        if (n < ncols) {
-          // y in bf16 (round to nearest even), plain stores: nontemporal stores of these
-          // 8-byte pieces drain slower (decode finalize 13 -> 15 us, MXFP8 M=2048 down
-          // 1,803 -> 1,879 us); with fp32 y nontemporal stores had been the faster ones
-          *reinterpret_cast<uint64_t*>(y + (size_t)dst * ncols + n) =
-              pack_bf16x2(acc[j][s][0], acc[j][s][1]) |
-              ((uint64_t)pack_bf16x2(acc[j][s][2], acc[j][s][3]) << 32);
-        }
+        // plain stores: nontemporal stores of the 8-byte bf16 pieces drain slower (decode
+        // finalize 13 -> 15 us, MXFP8 M=2048 down 1,803 -> 1,879 us)
+        if (n < ncols)
+          store_y4(y, y0, yr, n, acc[j][s][0], acc[j][s][1], acc[j][s][2], acc[j][s][3]);
       }
     }
   }
@@ -241,7 +237,8 @@ __global__ __launch_bounds__(64 * WN * WM) void expert_tiled_kernel(
     const uint16_t* __restrict__ tok_src, const uint16_t* __restrict__ w,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
     const int2* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int n_ntiles, int K,
-    int ncols, int I, int top_k, int block, uint16_t* __restrict__ act, uint16_t* __restrict__ y) {
+    int ncols, int I, int top_k, int block, uint16_t* __restrict__ act, uint16_t* __restrict__ y,
+    float* __restrict__ y0) {
   using C = TiledCfg<BM, WN, WM>;
   static_assert(S >= 2 && (S - 2) * C::FPW <= 63, "the copies in flight must fit the vmcnt counter");
   static_assert(S * C::FRAGS * 1024 <= 160 * 1024, "the ring must fit the LDS");
@@ -253,7 +250,7 @@ __global__ __launch_bounds__(64 * WN * WM) void expert_tiled_kernel(
     const int start = tile.x, nlive = tile.y;
     tiled_gemm<BM, WN, WM, S, UP, WPOL>(lds, tok_src, w, sorted_ids + start, start, nlive,
                                         block_expert[start / block], ntile, K, ncols, I, top_k,
-                                        act, y);
+                                        act, y, y0);
     __syncthreads();  // the next item's first copies reuse the ring
   }
 }
@@ -388,7 +385,7 @@ __global__ __launch_bounds__(64 * WN) void expert_up_selfroute_kernel(
       if (tid == 0) tiles[ti] = make_int2(start, nlive);
     }
     tiled_gemm<BM, WN, 1, S, true, WPOL>(lds, x, w13, s_rows, start, nlive, e, ntile, K, I, I,
-                                         top_k, act, nullptr);
+                                         top_k, act, nullptr, nullptr);
     __syncthreads();  // s_rows and the ring are reused by the next item
   }
 }
@@ -409,7 +406,8 @@ __global__ __launch_bounds__(512) void expert_tiled_reg_kernel(
     const uint16_t* __restrict__ tok_src, const uint16_t* __restrict__ w,
     const int32_t* __restrict__ sorted_ids, const int32_t* __restrict__ block_expert,
     const int2* __restrict__ tiles, const int32_t* __restrict__ num_tiles, int n_ntiles, int K,
-    int ncols, int I, int top_k, int block, uint16_t* __restrict__ act, uint16_t* __restrict__ y) {
+    int ncols, int I, int top_k, int block, uint16_t* __restrict__ act, uint16_t* __restrict__ y,
+    float* __restrict__ y0) {
   constexpr int NW = 8;                          // waves
   constexpr int WT = 32;                         // weight row tiles (512 rows)
   constexpr int MT = BM / 16;                    // token row tiles
@@ -559,16 +557,12 @@ __global__ __launch_bounds__(512) void expert_tiled_reg_kernel(
           *reinterpret_cast<uint2*>(act + (size_t)(start + r) * I + n) = v;
         }
       } else if (!UP && r < nlive) {
-        const int dst = sorted_ids[start + r];
+        const YRow yr = y_row(sorted_ids[start + r], top_k, ncols);
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int n = col0 + 64 * wave + 16 * j + 4 * lg;
-          if (n < ncols) {                               // y in bf16 (nearest even)
-            uint2 v;
-            v.x = pack_bf16x2(acc[j][s][0], acc[j][s][1]);
-            v.y = pack_bf16x2(acc[j][s][2], acc[j][s][3]);
-            *reinterpret_cast<uint2*>(y + (size_t)dst * ncols + n) = v;
-          }
+          if (n < ncols)
+            store_y4(y, y0, yr, n, acc[j][s][0], acc[j][s][1], acc[j][s][2], acc[j][s][3]);
         }
       }
     }
@@ -791,7 +785,8 @@ template <int BM, int WN, int WM, int S, bool UP, int WPOL>
 static hipError_t launch_tiled(const uint16_t* src, const uint16_t* w, const int32_t* sorted_ids,
                                const int32_t* block_expert, const int2* tiles,
                                const int32_t* num_tiles, int max_tiles, int K, int ncols, int I,
-                               int top_k, int block, uint16_t* act, uint16_t* y, hipStream_t s) {
+                               int top_k, int block, uint16_t* act, uint16_t* y, float* y0,
+                               hipStream_t s) {
   const int per_ntile = UP ? 32 * WN : 64 * WN;
   if (UP && I % per_ntile != 0) return hipErrorInvalidValue;
   const int n_ntiles = (ncols + per_ntile - 1) / per_ntile;
@@ -802,7 +797,7 @@ static hipError_t launch_tiled(const uint16_t* src, const uint16_t* w, const int
                              : (items + kXcds - 1) / kXcds * kXcds;
   hipLaunchKernelGGL((expert_tiled_kernel<BM, WN, WM, S, UP, WPOL>), dim3((unsigned)grid),
                      dim3(TiledCfg<BM, WN, WM>::THREADS), 0, s, src, w, sorted_ids, block_expert,
-                     tiles, num_tiles, n_ntiles, K, ncols, I, top_k, block, act, y);
+                     tiles, num_tiles, n_ntiles, K, ncols, I, top_k, block, act, y, y0);
   return hipGetLastError();
 }
 
@@ -811,7 +806,7 @@ static hipError_t launch_tiled_reg(const uint16_t* src, const uint16_t* w,
                                    const int32_t* sorted_ids, const int32_t* block_expert,
                                    const int2* tiles, const int32_t* num_tiles, int max_tiles,
                                    int K, int ncols, int I, int top_k, int block, uint16_t* act,
-                                   uint16_t* y, hipStream_t s) {
+                                   uint16_t* y, float* y0, hipStream_t s) {
   const int per_ntile = UP ? 256 : 512;
   if (K % kTileKC != 0 || (UP && I % per_ntile != 0)) return hipErrorInvalidValue;
   const int n_ntiles = (ncols + per_ntile - 1) / per_ntile;
@@ -819,7 +814,7 @@ static hipError_t launch_tiled_reg(const uint16_t* src, const uint16_t* w,
   const long grid = (items + kXcds - 1) / kXcds * kXcds;  // one item per workgroup
   hipLaunchKernelGGL((expert_tiled_reg_kernel<BM, UP, WPOL>), dim3((unsigned)grid), dim3(512), 0, s,
                      src, w, sorted_ids, block_expert, tiles, num_tiles, n_ntiles, K, ncols, I,
-                     top_k, block, act, y);
+                     top_k, block, act, y, y0);
   return hipGetLastError();
 }
 
@@ -869,7 +864,7 @@ hipError_t launch_expert_up_tiled(const uint16_t* x, const uint16_t* w13, const 
 #define MOE_UP(BM, WN, S, POL)                                                                   \
   return launch_tiled<BM, WN, 1, S, true, POL>(x, w13, sorted_ids, block_expert, tiles,         \
                                                num_tiles, max_tiles, H, I, I, top_k, block, act, \
-                                               nullptr, s)
+                                               nullptr, nullptr, s)
   if (tile_rows == 64) {
     if (stream_weights) MOE_UP(64, 4, 3, kNT);
     MOE_UP(64, kTileWN, kTileStages, 0);
@@ -877,7 +872,8 @@ hipError_t launch_expert_up_tiled(const uint16_t* x, const uint16_t* w13, const 
   if (tile_rows == 128) {
     if (stream_weights && H % kTileKC == 0)
       return launch_tiled_reg<128, true, kNT>(x, w13, sorted_ids, block_expert, tiles, num_tiles,
-                                              max_tiles, H, I, I, top_k, block, act, nullptr, s);
+                                              max_tiles, H, I, I, top_k, block, act, nullptr,
+                                              nullptr, s);
     if (stream_weights) MOE_UP(128, 4, 3, kNT);
     MOE_UP(128, kTileWN, kTileStages, 0);
   }
@@ -889,12 +885,13 @@ hipError_t launch_expert_down_tiled(const uint16_t* act, const uint16_t* w2,
                                     const int32_t* sorted_ids, const int32_t* block_expert,
                                     const int2* tiles, const int32_t* num_tiles, int max_tiles,
                                     int tile_rows, bool stream_weights, int M, int H, int I,
-                                    int top_k, int block, uint16_t* y, hipStream_t s) {
+                                    int top_k, int block, uint16_t* y, float* y0,
+                                    hipStream_t s) {
   (void)M;
 #define MOE_DOWN(BM, POL)                                                                       \
   return launch_tiled<BM, kTileWN, 1, kTileStages, false, POL>(act, w2, sorted_ids, block_expert, \
                                                                tiles, num_tiles, max_tiles, I, H, \
-                                                               I, top_k, block, nullptr, y, s)
+                                                               I, top_k, block, nullptr, y, y0, s)
   if (tile_rows == 64) {
     if (stream_weights) MOE_DOWN(64, kNT);
     MOE_DOWN(64, 0);
@@ -904,9 +901,9 @@ hipError_t launch_expert_down_tiled(const uint16_t* act, const uint16_t* w2,
       if (stream_weights)
         return launch_tiled_reg<128, false, kNT>(act, w2, sorted_ids, block_expert, tiles,
                                                  num_tiles, max_tiles, I, H, I, top_k, block,
-                                                 nullptr, y, s);
+                                                 nullptr, y, y0, s);
       return launch_tiled_reg<128, false, 0>(act, w2, sorted_ids, block_expert, tiles, num_tiles,
-                                             max_tiles, I, H, I, top_k, block, nullptr, y, s);
+                                             max_tiles, I, H, I, top_k, block, nullptr, y, y0, s);
     }
     if (stream_weights) MOE_DOWN(128, kNT);
     MOE_DOWN(128, 0);

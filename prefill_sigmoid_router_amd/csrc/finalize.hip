@@ -13,6 +13,8 @@
 // picks are requested together (all V groups), with the residual and norm weight in the
 // first batch, so a token costs about k/8 memory round trips rather than k + 2.  All arithmetic is fp32 with a single bf16 rounding (RNE) at the
 // store; the combine adds the picks in ascending j.
+#include <type_traits>
+
 #include "device_common.h"
 #include "launchers.h"
 
@@ -22,7 +24,7 @@ constexpr int kFinThreads = 1024;
 constexpr int kFinBatch = 8;
 
 // Values 4 c .. 4 c + 3 of a y row as fp32: fp32 rows (moe_finalize) or bf16 rows
-// (moe_forward, whose down GEMMs round y to bf16).
+// (moe_forward, whose down GEMMs round every pick but a token's first to bf16).
 __device__ __forceinline__ float4 y4(const float* row, int c) {
   return reinterpret_cast<const float4*>(row)[c];
 }
@@ -137,13 +139,15 @@ static hipError_t launch_fin(const Y* y, const float* w, const uint16_t* res, co
   return hipGetLastError();
 }
 
-// bf16 y (moe_forward) when H is a multiple of 8: each thread owns V groups of 8 hidden
-// values, so every y request is 16 bytes per lane -- twice the bytes in flight of the
+// moe_forward's y (each token's first pick in fp32 at row t of y0, the other picks in bf16
+// at their rows of y) when H is a multiple of 8: each thread owns V groups of 8 hidden
+// values, so every bf16 y request is 16 bytes per lane -- twice the bytes in flight of the
 // 4-value groups above for the same number of requests.  Same fp32 arithmetic and
 // combine order; the sum of squares is taken over 8-value groups.
 template <int V>
 __global__ __launch_bounds__(kFinThreads) void finalize_bf16_kernel(
-    const uint16_t* __restrict__ y, const float* __restrict__ topk_w,
+    const uint16_t* __restrict__ y, const float* __restrict__ y0,
+    const float* __restrict__ topk_w,
     const uint16_t* __restrict__ residual, const uint16_t* __restrict__ norm_w, float eps, int H,
     int top_k, uint16_t* __restrict__ out, uint16_t* __restrict__ residual_out) {
   __shared__ float part[kFinThreads / kWave];
@@ -156,19 +160,35 @@ __global__ __launch_bounds__(kFinThreads) void finalize_bf16_kernel(
 #pragma unroll
     for (int e = 0; e < 8; ++e) m[v][e] = 0.f;
 
+  // residual, norm weight and the first pick's fp32 row are requested with the first batch
+  // of bf16 rows
   const uint4* rr = reinterpret_cast<const uint4*>(residual + (size_t)t * H);
   const uint4* gw = reinterpret_cast<const uint4*>(norm_w);
+  const float4* f0 = reinterpret_cast<const float4*>(y0 + (size_t)t * H);
   uint4 res[V], gv[V];
+  float4 first[V][2];
 #pragma unroll
   for (int v = 0; v < V; ++v) {
     const int c = tid + kFinThreads * v;
     res[v] = c < ngroups ? rr[c] : uint4{0u, 0u, 0u, 0u};
     gv[v] = c < ngroups ? gw[c] : uint4{0u, 0u, 0u, 0u};
+    first[v][0] = c < ngroups ? f0[2 * c] : make_float4(0.f, 0.f, 0.f, 0.f);
+    first[v][1] = c < ngroups ? f0[2 * c + 1] : make_float4(0.f, 0.f, 0.f, 0.f);
   }
 
   const uint16_t* yt = y + (size_t)t * top_k * H;
   const float* wt = topk_w + (size_t)t * top_k;
-  for (int j0 = 0; j0 < top_k; j0 += kFinBatch) {
+  {
+    const float w = wt[0];
+#pragma unroll
+    for (int v = 0; v < V; ++v) {
+      const float f[8] = {first[v][0].x, first[v][0].y, first[v][0].z, first[v][0].w,
+                          first[v][1].x, first[v][1].y, first[v][1].z, first[v][1].w};
+#pragma unroll
+      for (int e = 0; e < 8; ++e) m[v][e] = fmaf(w, f[e], m[v][e]);
+    }
+  }
+  for (int j0 = 1; j0 < top_k; j0 += kFinBatch) {
     uint4 a[kFinBatch][V];
 #pragma unroll
     for (int u = 0; u < kFinBatch; ++u)
@@ -239,11 +259,11 @@ __global__ __launch_bounds__(kFinThreads) void finalize_bf16_kernel(
 }
 
 template <int V>
-static hipError_t launch_fin_bf16(const uint16_t* y, const float* w, const uint16_t* res,
-                                  const uint16_t* g, float eps, int M, int H, int k,
-                                  uint16_t* out, uint16_t* rout, hipStream_t s) {
-  hipLaunchKernelGGL((finalize_bf16_kernel<V>), dim3(M), dim3(kFinThreads), 0, s, y, w, res, g,
-                     eps, H, k, out, rout);
+static hipError_t launch_fin_bf16(const uint16_t* y, const float* y0, const float* w,
+                                  const uint16_t* res, const uint16_t* g, float eps, int M, int H,
+                                  int k, uint16_t* out, uint16_t* rout, hipStream_t s) {
+  hipLaunchKernelGGL((finalize_bf16_kernel<V>), dim3(M), dim3(kFinThreads), 0, s, y, y0, w, res,
+                     g, eps, H, k, out, rout);
   return hipGetLastError();
 }
 
@@ -262,14 +282,17 @@ hipError_t launch_finalize(const float* y, const float* topk_w, const uint16_t* 
                            uint16_t* out, uint16_t* residual_out, hipStream_t s) {
   return launch_fin_rows(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
 }
-hipError_t launch_finalize(const uint16_t* y, const float* topk_w, const uint16_t* residual,
-                           const uint16_t* norm_w, float eps, int M, int H, int top_k,
-                           uint16_t* out, uint16_t* residual_out, hipStream_t s) {
+hipError_t launch_finalize(const uint16_t* y, const float* y0, const float* topk_w,
+                           const uint16_t* residual, const uint16_t* norm_w, float eps, int M,
+                           int H, int top_k, uint16_t* out, uint16_t* residual_out,
+                           hipStream_t s) {
   // every H the API accepts (a multiple of 8, at most 16384) fits one of the two
   if (H % 8 != 0 || H / 8 > 2 * kFinThreads) return hipErrorInvalidValue;
   if (H / 8 <= kFinThreads)
-    return launch_fin_bf16<1>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
-  return launch_fin_bf16<2>(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
+    return launch_fin_bf16<1>(y, y0, topk_w, residual, norm_w, eps, M, H, top_k, out,
+                              residual_out, s);
+  return launch_fin_bf16<2>(y, y0, topk_w, residual, norm_w, eps, M, H, top_k, out,
+                            residual_out, s);
 }
 
 
@@ -281,9 +304,11 @@ hipError_t launch_finalize(const uint16_t* y, const float* topk_w, const uint16_
 constexpr int kFinSliceThreads = 256;
 constexpr int kFinSlice = 4 * kFinSliceThreads;     // hidden values per slice
 
+// Y = uint16_t: moe_forward's y, each token's first pick in fp32 at row t of y0, the others
+// in bf16; Y = float: every pick in fp32 in y (y0 unused).
 template <typename Y>
 __global__ __launch_bounds__(kFinSliceThreads) void finalize_slice_kernel(
-    const Y* __restrict__ y, const float* __restrict__ topk_w,
+    const Y* __restrict__ y, const float* __restrict__ y0, const float* __restrict__ topk_w,
     const uint16_t* __restrict__ residual, int H, int top_k, float* __restrict__ z,
     float* __restrict__ slice_ss) {
   __shared__ float part[kFinSliceThreads / kWave];
@@ -298,9 +323,12 @@ __global__ __launch_bounds__(kFinSliceThreads) void finalize_slice_kernel(
   for (int j0 = 0; j0 < top_k; j0 += 16) {
     float4 a[16];
 #pragma unroll
-    for (int u = 0; u < 16; ++u)
-      a[u] = (in && j0 + u < top_k) ? y4(yt + (size_t)(j0 + u) * H, c)
-                                    : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int u = 0; u < 16; ++u) {
+      const bool split_first = std::is_same<Y, uint16_t>::value && u == 0 && j0 == 0;
+      a[u] = !(in && j0 + u < top_k) ? make_float4(0.f, 0.f, 0.f, 0.f)
+             : split_first ? reinterpret_cast<const float4*>(y0 + (size_t)t * H)[c]
+                           : y4(yt + (size_t)(j0 + u) * H, c);
+    }
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       if (j0 + u < top_k) {
@@ -365,16 +393,16 @@ size_t finalize_slices_scratch_bytes(int M, int H) {
 }
 
 template <typename Y>
-static hipError_t launch_fin_slices(const Y* y, const float* topk_w, const uint16_t* residual,
-                                    const uint16_t* norm_w, float eps, int M, int H, int top_k,
-                                    uint16_t* out, uint16_t* residual_out, float* scratch,
-                                    hipStream_t s) {
+static hipError_t launch_fin_slices(const Y* y, const float* y0, const float* topk_w,
+                                    const uint16_t* residual, const uint16_t* norm_w, float eps,
+                                    int M, int H, int top_k, uint16_t* out, uint16_t* residual_out,
+                                    float* scratch, hipStream_t s) {
   if (M == 0) return hipSuccess;
   const int slices = (H / 4 + kFinSliceThreads - 1) / kFinSliceThreads;
   float* z = scratch;
   float* slice_ss = scratch + (size_t)M * H;
   hipLaunchKernelGGL((finalize_slice_kernel<Y>), dim3(slices, M), dim3(kFinSliceThreads), 0, s, y,
-                     topk_w, residual, H, top_k, z, slice_ss);
+                     y0, topk_w, residual, H, top_k, z, slice_ss);
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
   hipLaunchKernelGGL(finalize_scale_kernel, dim3(slices, M), dim3(kFinSliceThreads), 0, s, z,
@@ -386,14 +414,14 @@ hipError_t launch_finalize_slices(const float* y, const float* topk_w, const uin
                                   const uint16_t* norm_w, float eps, int M, int H, int top_k,
                                   uint16_t* out, uint16_t* residual_out, float* scratch,
                                   hipStream_t s) {
-  return launch_fin_slices(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out,
-                           scratch, s);
+  return launch_fin_slices(y, nullptr, topk_w, residual, norm_w, eps, M, H, top_k, out,
+                           residual_out, scratch, s);
 }
-hipError_t launch_finalize_slices(const uint16_t* y, const float* topk_w, const uint16_t* residual,
-                                  const uint16_t* norm_w, float eps, int M, int H, int top_k,
-                                  uint16_t* out, uint16_t* residual_out, float* scratch,
-                                  hipStream_t s) {
-  return launch_fin_slices(y, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out,
+hipError_t launch_finalize_slices(const uint16_t* y, const float* y0, const float* topk_w,
+                                  const uint16_t* residual, const uint16_t* norm_w, float eps,
+                                  int M, int H, int top_k, uint16_t* out, uint16_t* residual_out,
+                                  float* scratch, hipStream_t s) {
+  return launch_fin_slices(y, y0, topk_w, residual, norm_w, eps, M, H, top_k, out, residual_out,
                            scratch, s);
 }
 

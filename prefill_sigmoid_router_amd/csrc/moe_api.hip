@@ -40,7 +40,7 @@ size_t capacity_of(int32_t M, int32_t top_k, int32_t E, int32_t block) {
 
 // Workspace layout of moe_forward; every region starts on a 256-byte boundary.
 struct Layout {
-  size_t keys, ids, w, sorted, bexp, npad, tiles, groups, ntiles, act, y, fin, total;
+  size_t keys, ids, w, sorted, bexp, npad, tiles, groups, ntiles, act, y, y0, fin, total;
   int max_tiles;
 };
 
@@ -61,6 +61,7 @@ Layout layout_of(int32_t M, int32_t H, int32_t E, int32_t I, int32_t top_k, int3
   L.ntiles = off; off += kAlign;
   L.act = off;    off += round_up(cap * (size_t)I * sizeof(uint16_t), kAlign);
   L.y = off;      off += round_up(n * (size_t)H * sizeof(uint16_t), kAlign);  // bf16 y
+  L.y0 = off;     off += round_up((size_t)M * H * sizeof(float), kAlign);     // first picks
   L.fin = off;    // z and per-slice sums of the sliced finalize (few tokens only)
   if (M < moe::kFinSlicesMaxTokens) off += round_up(moe::finalize_slices_scratch_bytes(M, H), kAlign);
   L.total = off;
@@ -346,6 +347,7 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   int32_t* ntiles = reinterpret_cast<int32_t*>(ws + L.ntiles);
   uint16_t* act = reinterpret_cast<uint16_t*>(ws + L.act);
   uint16_t* y = reinterpret_cast<uint16_t*>(ws + L.y);
+  float* y0 = reinterpret_cast<float*>(ws + L.y0);
   hipStream_t s = (hipStream_t)stream;
 
   auto mark = [&](int i) -> bool {
@@ -398,26 +400,29 @@ int forward_impl(const uint16_t* x, const uint16_t* router_w, const float* route
   if (W.fp4 || W.fp8p)
     down_err = moe::launch_expert_down_frag_mx(act, W.w2c, W.w2s, W.fp4, sorted, bexp, tiles,
                                                groups, ntiles, max_tiles, trows, stream_w, H, I,
-                                               top_k, block, y, s);
+                                               top_k, block, y, y0, s);
   else if (W.prepared)
     down_err = moe::launch_expert_down_frag(act, W.w2, sorted, bexp, tiles, groups, ntiles,
-                                            max_tiles, trows, stream_w, H, I, top_k, block, y, s);
+                                            max_tiles, trows, stream_w, H, I, top_k, block, y, y0,
+                                            s);
   else if (W.mx())
     down_err = moe::launch_expert_down_mx_lds(act, W.w2c, W.w2s, sorted, bexp, tiles, ntiles,
-                                              max_tiles, trows, stream_w, H, I, top_k, block, y, s);
+                                              max_tiles, trows, stream_w, H, I, top_k, block, y,
+                                              y0, s);
   else if (trows == 16)
     down_err = moe::launch_expert_down(act, W.w2, sorted, bexp, npad, tiles, ntiles, max_tiles, M,
-                                       H, I, top_k, block, y, s);
+                                       H, I, top_k, block, y, y0, s);
   else
     down_err = moe::launch_expert_down_tiled(act, W.w2, sorted, bexp, tiles, ntiles, max_tiles,
-                                             trows, stream_w, M, H, I, top_k, block, y, s);
+                                             trows, stream_w, M, H, I, top_k, block, y, y0, s);
   if (down_err != hipSuccess) return MOE_ERR_HIP;
   if (!mark(4)) return MOE_ERR_HIP;
   const hipError_t fin_err =
       M < moe::kFinSlicesMaxTokens
-          ? moe::launch_finalize_slices(y, w, residual, norm_w, eps, M, H, top_k, out,
+          ? moe::launch_finalize_slices(y, y0, w, residual, norm_w, eps, M, H, top_k, out,
                                         residual_out, reinterpret_cast<float*>(ws + L.fin), s)
-          : moe::launch_finalize(y, w, residual, norm_w, eps, M, H, top_k, out, residual_out, s);
+          : moe::launch_finalize(y, y0, w, residual, norm_w, eps, M, H, top_k, out, residual_out,
+                                 s);
   if (fin_err != hipSuccess) return MOE_ERR_HIP;
   if (!mark(5)) return MOE_ERR_HIP;
   return MOE_OK;

@@ -72,8 +72,10 @@ def test_workspace_bytes_cover_the_buffers(B):
     M, H, E, I, k, blk = 2048, 7168, 256, 2048, 16, 64
     cap = B.moe_align_capacity(M, k, E, blk)
     tiles16 = (M * k + 15) // 16 + min(E, M * k)      # 16-row tiles of real entries, at most
+    # tiles and their expert groups: 2 x tiles16 int2; y: bf16 rows of every pick and the
+    # fp32 rows of each token's first pick
     need = (M * E * 32 + 2 * M * k * 4 + cap * 4 + cap // blk * 4 + 4 + 2 * tiles16 * 8 + 4
-            + cap * I * 2 + M * k * H * 2)   # tiles and their expert groups: 2 x tiles16 int2
+            + cap * I * 2 + M * k * H * 2 + M * H * 4)
     got = B.moe_workspace_bytes(M, H, E, I, k, blk)
     assert need <= got <= need + 10 * 256
     assert B.moe_workspace_bytes(M, H, E, I, k, 48) == 0          # no kernel for block 48

@@ -92,15 +92,15 @@ def test_noalloc_equals_workspace_call_twice_in_a_row(B, dev, seq):
 
 
 def test_noalloc_refuses_sizes_past_the_scratch(B, dev):
-    """The real-shape layer with block 64 fits the scratch up to 15 tokens; 16 do not: the
+    """The real-shape layer with block 64 fits the scratch up to 14 tokens; 15 do not: the
     call fails with MOE_ERR_WORKSPACE on the host, before any launch (pointers are never
     dereferenced)."""
     lib = B.load_library()
     p = ctypes.c_void_p
-    fits = B.moe_workspace_bytes(15, 7168, 256, 2048, 16, 64) <= B.NOALLOC_SCRATCH_BYTES
-    past = B.moe_workspace_bytes(16, 7168, 256, 2048, 16, 64) > B.NOALLOC_SCRATCH_BYTES
+    fits = B.moe_workspace_bytes(14, 7168, 256, 2048, 16, 64) <= B.NOALLOC_SCRATCH_BYTES
+    past = B.moe_workspace_bytes(15, 7168, 256, 2048, 16, 64) > B.NOALLOC_SCRATCH_BYTES
     assert fits and past
-    st = lib.moe_forward_noalloc(p(256), p(256), None, p(256), p(256), p(256), p(256), 1e-5, 16,
+    st = lib.moe_forward_noalloc(p(256), p(256), None, p(256), p(256), p(256), p(256), 1e-5, 15,
                                  7168, 256, 2048, 16, 64, p(256), None, None, None, None, None,
                                  None, None)
     assert st == -3

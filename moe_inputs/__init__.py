@@ -16,6 +16,8 @@ the AlphaMoE page names the GLM m8 / m128 / m512 / m2048 route workloads, sectio
   prefill_m2048  M=2048, same layer, block=64, Zipf(1.0)-shaped router bias
   prefill_m8192  M=8192, same layer, block=64, Zipf(1.0)-shaped router bias (a parity
                  case past the timed sizes: 131,072 flat ids)
+  skew_m512      M=512,  same layer, block=64, the bias with s = 50 (a parity case: the
+                 first dozen experts take every token, most experts none)
 
 Value recipe (every tensor has its own seed so that any one of them, or any single
 expert's weights, can be regenerated on its own):
@@ -81,6 +83,8 @@ CONFIGS = {
                                  block=64, zipf_s=1.0),
     "prefill_m8192": LayerConfig("prefill_m8192", M=8192, H=7168, E=256, top_k=16, I=2048,
                                  block=64, zipf_s=1.0),
+    "skew_m512": LayerConfig("skew_m512", M=512, H=7168, E=256, top_k=16, I=2048, block=64,
+                             zipf_s=50.0),
 }
 
 

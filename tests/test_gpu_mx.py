@@ -9,6 +9,7 @@ import numpy as np
 import pytest
 import torch
 
+import _bars as bars
 import _fullsize as fs
 import moe_inputs as mi
 from oracle import moe_oracle as orc
@@ -16,8 +17,6 @@ from oracle import mx_oracle as mxo
 
 pytestmark = pytest.mark.gpu
 
-MAX_ABS = 2e-2
-REL_L2 = 1e-2
 bits = mi.bf16_bits
 
 
@@ -117,13 +116,7 @@ def _run_forward_mx(B, L, dev, mx):
     return r
 
 
-def _check_close(got_bf16, ref, what):
-    g = got_bf16.float().cpu().numpy().astype(np.float64)
-    assert np.isfinite(g).all(), f"{what}: non-finite output"
-    err = np.abs(g - ref)
-    rel = np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-30)
-    assert err.max() <= MAX_ABS, f"{what}: max-abs {err.max():.3e}"
-    assert rel <= REL_L2, f"{what}: rel-L2 {rel:.3e}"
+_check_close = bars.check_close
 
 
 def _bias_np(L):
@@ -196,7 +189,8 @@ def test_forward_mx_rejects_unsupported_widths(B, dev):
     assert ei.value.status == -2
 
 
-MX_FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048", "prefill_m8192"]
+MX_FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048", "prefill_m8192",
+           "skew_m512"]
 
 
 @pytest.fixture(scope="module")
@@ -272,12 +266,13 @@ def mx_full_oracle(mx_full_runs, mx_full):
           "tokens", flush=True)
     w13 = lambda e: mxo.mx_roundtrip_bf16_bits_lut(bits(weights["w13"][int(e)]))  # noqa: E731
     w2 = lambda e: mxo.mx_roundtrip_bf16_bits_lut(bits(weights["w2"][int(e)]))    # noqa: E731
-    ys = fs.stream_expert_rows(jobs, w13, w2, mi.CONFIGS["decode_m8"].I)
+    ys, ys7 = fs.stream_expert_rows(jobs, w13, w2, mi.CONFIGS["decode_m8"].I, act_bf16=True)
     res = {}
     for name, run in mx_full_runs.items():
         sample, w = meta[name]
         out, z = orc.finalize(ys[name], w, run["residual"][sample], run["norm_w"], run["eps"])
-        res[name] = (sample, out, z)
+        z7 = orc.finalize(ys7[name], w, run["residual"][sample], run["norm_w"], run["eps"])[1]
+        res[name] = (sample, out, z, z7)
     return res
 
 
@@ -289,7 +284,7 @@ def test_forward_mx_full_size_against_oracle(mx_full_runs, mx_full_oracle, name)
     and, for every expert, the first and the last token that picked it."""
     run = mx_full_runs[name]
     cfg = run["cfg"]
-    sample, out, z = mx_full_oracle[name]
+    sample, out, z, z7 = mx_full_oracle[name]
     if cfg.M <= 128:
         assert len(sample) == cfg.M
     else:
@@ -300,7 +295,8 @@ def test_forward_mx_full_size_against_oracle(mx_full_runs, mx_full_oracle, name)
             assert rows[-1] in sample and rows[0] in sample
     print(f"{name}: {len(sample)} tokens against the oracle", flush=True)
     _check_close(torch.from_numpy(run["out"][sample]), out, f"{name} mx out")
-    _check_close(torch.from_numpy(run["rout"][sample]), z, f"{name} mx residual_out")
+    _check_close(torch.from_numpy(run["rout"][sample]), z, f"{name} mx residual_out",
+                 extra=z7 - z)
 
 
 @pytest.mark.parametrize("name", ["mx_tiny", "mx_many"])

@@ -11,6 +11,7 @@ import numpy as np
 import pytest
 import torch
 
+import _bars as bars
 import _fullsize as fs
 import moe_inputs as mi
 from oracle import moe_oracle as orc
@@ -18,8 +19,6 @@ from oracle import mx_oracle as mxo
 
 pytestmark = pytest.mark.gpu
 
-MAX_ABS = 2e-2
-REL_L2 = 1e-2
 bits = mi.bf16_bits
 
 
@@ -185,13 +184,7 @@ def _run(B, L, dev, q):
     return r
 
 
-def _check_close(got_bf16, ref, what):
-    g = got_bf16.float().cpu().numpy().astype(np.float64)
-    assert np.isfinite(g).all(), f"{what}: non-finite output"
-    err = np.abs(g - ref)
-    rel = np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-30)
-    assert err.max() <= MAX_ABS, f"{what}: max-abs {err.max():.4e}"
-    assert rel <= REL_L2, f"{what}: rel-L2 {rel:.4e}"
+_check_close = bars.check_close
 
 
 def _bias_np(L):
@@ -218,7 +211,8 @@ def test_forward_mx4_small(B, dev, name):
     _check_close(r["rout"], ref["residual_out"], name + " residual_out")
 
 
-FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048", "prefill_m8192"]
+FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048", "prefill_m8192",
+        "skew_m512"]
 
 
 @pytest.fixture(scope="module")
@@ -283,12 +277,13 @@ def mx4_full_oracle(mx4_full):
         meta[name] = (sample, ref_w[sample])
     w13 = lambda e: mxo.mx4_roundtrip_bf16_bits_lut(bits(weights["w13"][int(e)]))  # noqa: E731
     w2 = lambda e: mxo.mx4_roundtrip_bf16_bits_lut(bits(weights["w2"][int(e)]))    # noqa: E731
-    ys = fs.stream_expert_rows(jobs, w13, w2, mi.CONFIGS["decode_m8"].I)
+    ys, ys7 = fs.stream_expert_rows(jobs, w13, w2, mi.CONFIGS["decode_m8"].I, act_bf16=True)
     res = {}
     for name, run in runs.items():
         sample, w = meta[name]
-        res[name] = (sample,) + orc.finalize(ys[name], w, run["residual"][sample], run["norm_w"],
-                                             run["eps"])
+        out, z = orc.finalize(ys[name], w, run["residual"][sample], run["norm_w"], run["eps"])
+        z7 = orc.finalize(ys7[name], w, run["residual"][sample], run["norm_w"], run["eps"])[1]
+        res[name] = (sample, out, z, z7)
     return res
 
 
@@ -297,11 +292,12 @@ def mx4_full_oracle(mx4_full):
 def test_forward_mx4_full_size_against_oracle(mx4_full, mx4_full_oracle, name):
     _, runs = mx4_full
     run = runs[name]
-    sample, out, z = mx4_full_oracle[name]
+    sample, out, z, z7 = mx4_full_oracle[name]
     if run["cfg"].M <= 128:
         assert len(sample) == run["cfg"].M
     else:
         assert len(sample) >= 256 and sample[-1] == run["cfg"].M - 1
     print(f"{name}: {len(sample)} tokens against the oracle", flush=True)
     _check_close(torch.from_numpy(run["out"][sample]), out, f"{name} mx4 out")
-    _check_close(torch.from_numpy(run["rout"][sample]), z, f"{name} mx4 residual_out")
+    _check_close(torch.from_numpy(run["rout"][sample]), z, f"{name} mx4 residual_out",
+                 extra=z7 - z)

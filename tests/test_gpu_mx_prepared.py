@@ -14,6 +14,7 @@ import numpy as np
 import pytest
 import torch
 
+import _bars as bars
 import _fullsize as fs
 import moe_inputs as mi
 from oracle import moe_oracle as orc
@@ -21,8 +22,6 @@ from oracle import mx_oracle as mxo
 
 pytestmark = pytest.mark.gpu
 
-MAX_ABS = 2e-2
-REL_L2 = 1e-2
 bits = mi.bf16_bits
 
 
@@ -165,13 +164,7 @@ def _run(B, L, dev, p):
     return r
 
 
-def _check_close(got_bf16, ref, what):
-    g = got_bf16.float().cpu().numpy().astype(np.float64)
-    assert np.isfinite(g).all(), f"{what}: non-finite output"
-    err = np.abs(g - ref)
-    rel = np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-30)
-    assert err.max() <= MAX_ABS, f"{what}: max-abs {err.max():.4e}"
-    assert rel <= REL_L2, f"{what}: rel-L2 {rel:.4e}"
+_check_close = bars.check_close
 
 
 def _bias_np(L):
@@ -200,7 +193,8 @@ def test_forward_mx_prepared_small(B, dev, name):
     _check_close(r["rout"], ref["residual_out"], name + " residual_out")
 
 
-FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048", "prefill_m8192"]
+FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048", "prefill_m8192",
+        "skew_m512"]
 
 
 @pytest.fixture(scope="module")
@@ -282,12 +276,13 @@ def mxp_full_oracle(mxp_full):
         meta[name] = (sample, ref_w[sample])
     w13 = lambda e: mxo.mx_roundtrip_bf16_bits_lut(bits(weights["w13"][int(e)]))  # noqa: E731
     w2 = lambda e: mxo.mx_roundtrip_bf16_bits_lut(bits(weights["w2"][int(e)]))    # noqa: E731
-    ys = fs.stream_expert_rows(jobs, w13, w2, mi.CONFIGS["decode_m8"].I)
+    ys, ys7 = fs.stream_expert_rows(jobs, w13, w2, mi.CONFIGS["decode_m8"].I, act_bf16=True)
     res = {}
     for name, run in runs.items():
         sample, w = meta[name]
-        res[name] = (sample,) + orc.finalize(ys[name], w, run["residual"][sample], run["norm_w"],
-                                             run["eps"])
+        out, z = orc.finalize(ys[name], w, run["residual"][sample], run["norm_w"], run["eps"])
+        z7 = orc.finalize(ys7[name], w, run["residual"][sample], run["norm_w"], run["eps"])[1]
+        res[name] = (sample, out, z, z7)
     return res
 
 
@@ -296,11 +291,12 @@ def mxp_full_oracle(mxp_full):
 def test_forward_mx_prepared_full_size_against_oracle(mxp_full, mxp_full_oracle, name):
     _, runs = mxp_full
     run = runs[name]
-    sample, out, z = mxp_full_oracle[name]
+    sample, out, z, z7 = mxp_full_oracle[name]
     if run["cfg"].M <= 128:
         assert len(sample) == run["cfg"].M
     else:
         assert len(sample) >= 256 and sample[-1] == run["cfg"].M - 1
     print(f"{name}: {len(sample)} tokens against the oracle", flush=True)
     _check_close(torch.from_numpy(run["out"][sample]), out, f"{name} mxfp8 panels out")
-    _check_close(torch.from_numpy(run["rout"][sample]), z, f"{name} mxfp8 panels residual_out")
+    _check_close(torch.from_numpy(run["rout"][sample]), z, f"{name} mxfp8 panels residual_out",
+                 extra=z7 - z)

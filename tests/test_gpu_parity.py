@@ -11,14 +11,12 @@ import numpy as np
 import pytest
 import torch
 
+import _bars as bars
 import _fullsize as fs
 import moe_inputs as mi
 from oracle import moe_oracle as orc
 
 pytestmark = pytest.mark.gpu
-
-MAX_ABS = 2e-2
-REL_L2 = 1e-2
 
 
 @pytest.fixture(scope="module")
@@ -107,9 +105,11 @@ SMALL = {
     "fin_topk12": mi.LayerConfig("fin_topk12", M=264, H=256, E=32, top_k=12, I=256, block=32),
 }
 FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048"]
-# with a maximum-size case past the timed workloads: four times the prefill batch (131,072
-# flat ids, about 2,000 token tiles of 128 rows) on the same real-shape weights
-FULL_RUNS = FULL + ["prefill_m8192"]
+# with two cases past the timed workloads on the same real-shape weights: four times the
+# prefill batch (131,072 flat ids, about 2,000 token tiles of 128 rows), and a batch whose
+# router bias sends every token to the first dozen experts (hot experts of M rows, most
+# experts empty)
+FULL_RUNS = FULL + ["prefill_m8192", "skew_m512"]
 
 
 def _poisoned(shape, dtype, dev):
@@ -144,14 +144,7 @@ def _bias_np(L):
     return None if L["router_bias"] is None else L["router_bias"].cpu().numpy()
 
 
-def _check_close(got_bf16, ref, what):
-    g = got_bf16.float().cpu().numpy().astype(np.float64)
-    assert np.isfinite(g).all(), f"{what}: non-finite output"
-    err = np.abs(g - ref)
-    rel = np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-30)
-    assert err.max() <= MAX_ABS, f"{what}: max-abs {err.max():.4e} at {np.unravel_index(err.argmax(), err.shape)}"
-    assert rel <= REL_L2, f"{what}: rel-L2 {rel:.4e}"
-    return err.max(), rel
+_check_close = bars.check_close
 
 
 def _check_plan(r, ref, blk, what):
@@ -496,7 +489,6 @@ def test_forward_graph_replay_and_side_stream(B, dev, name):
         torch.randn(1 << 20, device=dev).sum().item()
 
 
-
 @pytest.mark.parametrize("name", ["mid", "tiled128_zipf", "tiled64_zipf"])
 def test_forward_concurrent_streams(B, dev, name):
     """Two moe_forward calls in flight at once on two streams, each with its own inputs,
@@ -619,12 +611,14 @@ def full_oracle(full_runs, full_weights):
           flush=True)
     w13 = mi.DeviceExpertsAsBits(full_weights["w13"])
     w2 = mi.DeviceExpertsAsBits(full_weights["w2"])
-    ys = fs.stream_expert_rows(jobs, w13.__getitem__, w2.__getitem__, mi.CONFIGS["decode_m8"].I)
+    ys, ys7 = fs.stream_expert_rows(jobs, w13.__getitem__, w2.__getitem__,
+                                    mi.CONFIGS["decode_m8"].I, act_bf16=True)
     res = {}
     for name, run in full_runs.items():
         sample, w = meta[name]
         out, z = orc.finalize(ys[name], w, run["residual"][sample], run["norm_w"], run["eps"])
-        res[name] = (sample, out, z)
+        z7 = orc.finalize(ys7[name], w, run["residual"][sample], run["norm_w"], run["eps"])[1]
+        res[name] = (sample, out, z, z7)
     return res
 
 
@@ -637,7 +631,7 @@ def test_forward_full_size_against_oracle(full_runs, full_oracle, name):
     token tile of both grouped GEMMs (all K chunks, all N tiles) holds a checked row."""
     run = full_runs[name]
     cfg = run["cfg"]
-    sample, out, z = full_oracle[name]
+    sample, out, z, z7 = full_oracle[name]
     M = cfg.M
     if M <= 128:
         assert len(sample) == M
@@ -649,4 +643,5 @@ def test_forward_full_size_against_oracle(full_runs, full_oracle, name):
             assert rows[-1] in sample and rows[0] in sample
     print(f"{name}: {len(sample)} tokens against the oracle", flush=True)
     _check_close(torch.from_numpy(run["out"][sample]), out, f"{name} out")
-    _check_close(torch.from_numpy(run["rout"][sample]), z, f"{name} residual_out")
+    _check_close(torch.from_numpy(run["rout"][sample]), z, f"{name} residual_out",
+                 extra=z7 - z)

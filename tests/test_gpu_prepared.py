@@ -11,14 +11,13 @@ import numpy as np
 import pytest
 import torch
 
+import _bars as bars
 import _fullsize as fs
 import moe_inputs as mi
 from oracle import moe_oracle as orc
 
 pytestmark = pytest.mark.gpu
 
-MAX_ABS = 2e-2
-REL_L2 = 1e-2
 bits = mi.bf16_bits
 
 
@@ -135,13 +134,7 @@ def _run(B, L, dev, prepared=None):
     return r
 
 
-def _check_close(got_bf16, ref, what):
-    g = got_bf16.float().cpu().numpy().astype(np.float64)
-    assert np.isfinite(g).all(), f"{what}: non-finite output"
-    err = np.abs(g - ref)
-    rel = np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-30)
-    assert err.max() <= MAX_ABS, f"{what}: max-abs {err.max():.4e}"
-    assert rel <= REL_L2, f"{what}: rel-L2 {rel:.4e}"
+_check_close = bars.check_close
 
 
 def _bias_np(L):
@@ -183,7 +176,8 @@ def test_prepared_rejects_unsupported_widths(B, dev):
 # Real shape: every workload, bit for bit against the natural path, sampled tokens against
 # the oracle
 # ---------------------------------------------------------------------------------------
-FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048", "prefill_m8192"]
+FULL = ["decode_m8", "batch_m128", "batch_m512", "prefill_m2048", "prefill_m8192",
+        "skew_m512"]
 
 
 @pytest.fixture(scope="module")
@@ -243,12 +237,14 @@ def prep_full_oracle(prep_full):
         meta[name] = (sample, ref_w[sample])
     w13 = mi.DeviceExpertsAsBits(weights["w13"])
     w2 = mi.DeviceExpertsAsBits(weights["w2"])
-    ys = fs.stream_expert_rows(jobs, w13.__getitem__, w2.__getitem__, mi.CONFIGS["decode_m8"].I)
+    ys, ys7 = fs.stream_expert_rows(jobs, w13.__getitem__, w2.__getitem__,
+                                    mi.CONFIGS["decode_m8"].I, act_bf16=True)
     res = {}
     for name, run in runs.items():
         sample, w = meta[name]
-        res[name] = (sample,) + orc.finalize(ys[name], w, run["residual"][sample], run["norm_w"],
-                                             run["eps"])
+        out, z = orc.finalize(ys[name], w, run["residual"][sample], run["norm_w"], run["eps"])
+        z7 = orc.finalize(ys7[name], w, run["residual"][sample], run["norm_w"], run["eps"])[1]
+        res[name] = (sample, out, z, z7)
     return res
 
 
@@ -257,7 +253,8 @@ def prep_full_oracle(prep_full):
 def test_forward_prepared_full_size_against_oracle(prep_full, prep_full_oracle, name):
     _, runs = prep_full
     run = runs[name]
-    sample, out, z = prep_full_oracle[name]
+    sample, out, z, z7 = prep_full_oracle[name]
     print(f"{name}: {len(sample)} tokens against the oracle", flush=True)
     _check_close(torch.from_numpy(run["out"][sample]), out, f"{name} prepared out")
-    _check_close(torch.from_numpy(run["rout"][sample]), z, f"{name} prepared residual_out")
+    _check_close(torch.from_numpy(run["rout"][sample]), z, f"{name} prepared residual_out",
+                 extra=z7 - z)

@@ -8,14 +8,13 @@ import numpy as np
 import pytest
 import torch
 
+import _bars as bars
 import moe_inputs as mi
 from oracle import moe_oracle as orc
 from oracle import mx_oracle as mxo
 
 pytestmark = pytest.mark.gpu
 
-MAX_ABS = 2e-2
-REL_L2 = 1e-2
 bits = mi.bf16_bits
 
 
@@ -101,11 +100,7 @@ def _check(r, ref, cfg, name):
     assert np.array_equal(r["sorted"].cpu().numpy()[:n_pad], ref["sorted_ids"]), name
     assert np.array_equal(r["bexp"].cpu().numpy()[:n_pad // cfg.block], ref["block_expert"]), name
     for key, want in (("out", ref["out"]), ("rout", ref["residual_out"])):
-        g = r[key].float().cpu().numpy().astype(np.float64)
-        assert np.isfinite(g).all(), (name, key)
-        err = np.abs(g - want)
-        rel = np.linalg.norm(g - want) / max(np.linalg.norm(want), 1e-30)
-        assert err.max() <= MAX_ABS and rel <= REL_L2, (name, key, err.max(), rel)
+        bars.check_close(r[key], want, f"{name} {key}")
 
 
 def _bias(L):

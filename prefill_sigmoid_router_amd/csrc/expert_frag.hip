@@ -593,8 +593,8 @@ __device__ __forceinline__ void frag_item(
   // and the ring are reused
   frag_wait_vmcnt<0>();
 
-  // epilogue (as in the tiled kernels): act rows in bf16 for the up GEMM, y rows in bf16
-  // for the down GEMM, real rows only
+  // epilogue (as in the tiled kernels): act rows in bf16 for the up GEMM, y rows for the
+  // down GEMM (bf16, a token's first pick fp32: store_y4), real rows only
 #pragma unroll
   for (int s = 0; s < NA; ++s) {
     const int r = 16 * s + li;

@@ -58,12 +58,15 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
     gv[v] = c < ngroups ? gw[c] : uint2{0u, 0u};
   }
 
+  // picks per batch: 8, or 4 with 4 groups per thread (1024 threads leave 128 registers each;
+  // 8 x 4 float4 rows in flight would spill)
+  constexpr int NB = V >= 4 ? kFinBatch / 2 : kFinBatch;
   const Y* yt = y + (size_t)t * top_k * H;
   const float* wt = topk_w + (size_t)t * top_k;
-  for (int j0 = 0; j0 < top_k; j0 += kFinBatch) {
-    float4 a[kFinBatch][V];
+  for (int j0 = 0; j0 < top_k; j0 += NB) {
+    float4 a[NB][V];
 #pragma unroll
-    for (int u = 0; u < kFinBatch; ++u)
+    for (int u = 0; u < NB; ++u)
 #pragma unroll
       for (int v = 0; v < V; ++v) {
         const int c = tid + kFinThreads * v;
@@ -71,7 +74,7 @@ __global__ __launch_bounds__(kFinThreads) void finalize_kernel(
                                                   : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
-    for (int u = 0; u < kFinBatch; ++u) {
+    for (int u = 0; u < NB; ++u) {
       if (j0 + u < top_k) {
         const float w = wt[j0 + u];
 #pragma unroll

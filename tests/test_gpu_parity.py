@@ -393,9 +393,18 @@ def test_expert_down(B, dev, name):
     assert seen.all()
 
 
-def test_finalize_closed_form_and_oracle(B, dev):
+@pytest.mark.parametrize("H", [7168, 8200, 16384])
+def test_finalize_closed_form_and_oracle(B, dev, H):
+    """moe_finalize (fp32 y) against the oracle at 2, 3 and 4 groups of 4 values per thread
+    (H = 7168, 8200, 16384), with 5 picks and with 12 (several batches of picks), plus a
+    closed form."""
     torch.manual_seed(3)
-    M, k, H, eps = 19, 5, 7168, 1e-5
+    for M, k in ((19, 5), (7, 12)):
+        _finalize_against_oracle(B, dev, M, k, H)
+
+
+def _finalize_against_oracle(B, dev, M, k, H):
+    eps = 1e-5
     y = torch.randn(M * k, H, device=dev)
     wt = torch.rand(M, k, device=dev)
     wt = wt / wt.sum(dim=1, keepdim=True)
@@ -407,8 +416,8 @@ def test_finalize_closed_form_and_oracle(B, dev):
     torch.cuda.synchronize()
     ref, z = orc.finalize(y.cpu().numpy().astype(np.float64), wt.cpu().numpy().astype(np.float64),
                           bits(res), bits(g), eps)
-    _check_close(out, ref, "finalize out")
-    _check_close(rout, z, "finalize residual_out")
+    _check_close(out, ref, f"finalize out H={H} k={k}")
+    _check_close(rout, z, f"finalize residual_out H={H} k={k}")
     # constant vector: z = 2 everywhere, g = 1 -> out = 2 / sqrt(4 + eps) -> bf16
     y0 = torch.zeros(2 * 1, 256, device=dev)
     w0 = torch.full((1, 2), 0.5, device=dev)

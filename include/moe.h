@@ -64,7 +64,7 @@ enum {
 /* Human-readable text of a status code.  Never NULL; static storage. */
 const char* moe_strerror(int status);
 
-/* ABI version of this header (major * 100 + minor): 107. */
+/* ABI version of this header (major * 100 + minor): 108. */
 int moe_abi_version(void);
 
 /*

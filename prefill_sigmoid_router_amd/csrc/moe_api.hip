@@ -137,7 +137,7 @@ const char* moe_strerror(int status) {
   }
 }
 
-int moe_abi_version(void) { return 107; }
+int moe_abi_version(void) { return 108; }
 
 size_t moe_align_capacity(int32_t M, int32_t top_k, int32_t E, int32_t block) {
   if (M < 0 || top_k < 1 || E < 1 || block < 1) return 0;

@@ -56,7 +56,7 @@ def test_library_links_no_torch(B):
 
 
 def test_strerror_and_version(B):
-    assert B.moe_abi_version() == 107
+    assert B.moe_abi_version() == 108
     for s in (0, -1, -2, -3, -4, 17):
         assert isinstance(B.moe_strerror(s), str) and B.moe_strerror(s)
 

@@ -60,6 +60,7 @@ constexpr int kFragRS4Small = 16;      // ... and 64-row tiles, whose accumulato
 constexpr int kFragRS8 = 4;            // the same for MXFP8 codes (128-row tiles)
 constexpr int kFragRS8Small = 8;       // ... and 64-row tiles
 constexpr int kFragTS = 4;             // token LDS ring stages
+constexpr int kFragNT = 2;             // cache policy bits of a nontemporal load (gfx950)
 
 // weight formats of the fragment GEMMs
 constexpr int kWBf16 = 0;   // bf16 panels (moe_prepare_weights)
@@ -636,6 +637,7 @@ struct ExpertMajorWalk {
   TiledWalk w;
   const int2* groups;
   int n_ntiles;
+  int expert_tiles = 0;   // token tiles of the expert of the last item
   __device__ ExpertMajorWalk(int ntl, int nnt, const int2* g) : w(ntl, nnt), groups(g), n_ntiles(nnt) {}
   __device__ bool next(int& ntile, int& ti) {
     int a, b;
@@ -645,6 +647,7 @@ struct ExpertMajorWalk {
     const int local = logical - g.x * n_ntiles;
     ntile = local / g.y;
     ti = g.x + local % g.y;
+    expert_tiles = g.y;
     return true;
   }
 };
@@ -672,14 +675,33 @@ __global__ __launch_bounds__(64 * NWG) void expert_frag_kernel(
     // waits exact
     constexpr int MT = FragCfg<BM>::MT;
     constexpr int NS = BM == 64 ? 1 : MT / 2;
-    if (tile.y <= 16 * NS)
+    // In the up GEMM of a launch that keeps weights cached (several tiles share the hot
+    // experts' weights), the weights of an expert with a single token tile are copied
+    // nontemporally: they are read by that one item per N tile, and cached they would evict
+    // the lines the hot experts' tiles share (M=2048, bf16 panels: up 3,021 -> 2,832 us,
+    // layer 5,156 -> 5,017 us; nontemporal for every tile costs 3 %).  Only the up GEMM (the
+    // down GEMM's added instantiations spill) and 128-row tiles (with 64-row MXFP4 tiles the
+    // added copies leave one wave per SIMD).
+    if (UP && WPOL == 0 && BM == 128 && walk.expert_tiles == 1) {
+      if (tile.y <= 16 * NS)
+        frag_item<BM, UP, kFragNT, NS, WF, NWG>(tlds, tok_src, wp, wsc, sorted_ids + tile.x,
+                                                tile.x, tile.y, block_expert[tile.x / block],
+                                                ntile, part, n_ntiles, K, ncols, I, top_k, act,
+                                                y, y0);
+      else
+        frag_item<BM, UP, kFragNT, MT, WF, NWG>(tlds, tok_src, wp, wsc, sorted_ids + tile.x,
+                                                tile.x, tile.y, block_expert[tile.x / block],
+                                                ntile, part, n_ntiles, K, ncols, I, top_k, act,
+                                                y, y0);
+    } else if (tile.y <= 16 * NS) {
       frag_item<BM, UP, WPOL, NS, WF, NWG>(tlds, tok_src, wp, wsc, sorted_ids + tile.x, tile.x,
                                             tile.y, block_expert[tile.x / block], ntile, part,
                                             n_ntiles, K, ncols, I, top_k, act, y, y0);
-    else
+    } else {
       frag_item<BM, UP, WPOL, MT, WF, NWG>(tlds, tok_src, wp, wsc, sorted_ids + tile.x, tile.x,
                                             tile.y, block_expert[tile.x / block], ntile, part,
                                             n_ntiles, K, ncols, I, top_k, act, y, y0);
+    }
     __syncthreads();  // the next item's first token copies reuse the ring
   }
 }
@@ -707,7 +729,6 @@ static hipError_t launch_frag(const uint16_t* src, const void* wp, const uint8_t
   return hipGetLastError();
 }
 
-constexpr int kFragNT = 2;  // cache policy bits of a nontemporal load (gfx950)
 
 hipError_t launch_expert_up_frag(const uint16_t* x, const uint16_t* w13p, const int32_t* sorted_ids,
                                  const int32_t* block_expert, const int2* tiles,

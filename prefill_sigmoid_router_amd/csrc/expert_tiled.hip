@@ -47,6 +47,8 @@ constexpr int kTileKS = kTileKC / 32;           // MFMA K steps per chunk
 // Workgroup of WN x WM waves.  Weight rows: 64 * WN (4 row tiles of 16 per wave along
 // WN); token rows: BM (BM / 16 / WM row tiles per wave along WM).  Each wave accumulates
 // 4 weight tiles x MTW token tiles.
+constexpr int kNT = 2;  // cache policy bits of a nontemporal load (gfx950)
+
 template <int BM, int WN, int WM>
 struct TiledCfg {
   static constexpr int THREADS = 64 * WN * WM;
@@ -248,9 +250,24 @@ __global__ __launch_bounds__(64 * WN * WM) void expert_tiled_kernel(
   while (walk.next(ntile, ti)) {
     const int2 tile = tiles[ti];
     const int start = tile.x, nlive = tile.y;
-    tiled_gemm<BM, WN, WM, S, UP, WPOL>(lds, tok_src, w, sorted_ids + start, start, nlive,
-                                        block_expert[start / block], ntile, K, ncols, I, top_k,
-                                        act, y, y0);
+    const int e = block_expert[start / block];
+    // In the up GEMM of a launch that keeps weights cached, an expert whose rows fit one
+    // 128-row tile (the tiles before and after it in the list belong to other experts) has
+    // its weights copied nontemporally: one item per N tile reads them, and cached they
+    // would evict the lines the hot experts' tiles share (M=2048: up 3,707 -> 3,635 us,
+    // layer 6,027 -> 5,962 us).
+    bool single = false;
+    if (UP && WPOL == 0 && BM == 128) {
+      const bool first = ti == 0 || block_expert[tiles[ti - 1].x / block] != e;
+      const bool last = ti + 1 >= walk.ntiles_live || block_expert[tiles[ti + 1].x / block] != e;
+      single = first && last;
+    }
+    if (single)
+      tiled_gemm<BM, WN, WM, S, UP, kNT>(lds, tok_src, w, sorted_ids + start, start, nlive, e,
+                                         ntile, K, ncols, I, top_k, act, y, y0);
+    else
+      tiled_gemm<BM, WN, WM, S, UP, WPOL>(lds, tok_src, w, sorted_ids + start, start, nlive, e,
+                                          ntile, K, ncols, I, top_k, act, y, y0);
     __syncthreads();  // the next item's first copies reuse the ring
   }
 }
@@ -830,7 +847,6 @@ static hipError_t launch_tiled_reg(const uint16_t* src, const uint16_t* w,
 // streaming kernels, M=128 2,458 -> 2,181 us; the down GEMM 8 waves x 512 rows (M=8:
 // 499 -> 459 us; the split ring loses 2 % there).  With 128-row tiles (M=512) both GEMMs
 // run the split-ring kernel: up 2,549 -> 2,428 us, down 1,455 -> 1,400 us.
-constexpr int kNT = 2;        // cache policy bits of a nontemporal load (gfx950)
 constexpr int kTileWN = 8;
 constexpr int kTileStages = 2;
 

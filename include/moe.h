@@ -104,8 +104,8 @@ int32_t moe_gemm_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I);
  * dequantizes them into the LDS tiles of the tiled kernel. */
 int32_t moe_gemm_tile_rows_mx(int32_t M, int32_t E, int32_t top_k, int32_t I);
 /* The same for the entry points on fragment panels: weight_bits 16 (moe_forward_prepared)
- * follows moe_gemm_tile_rows; 8 (moe_forward_mx_prepared) gives 64 below 64 expected tokens
- * per expert, then 128; 4 (moe_forward_mx4) 64 below 256, then 128.  Host-only; 0 for
+ * follows moe_gemm_tile_rows; 8 (moe_forward_mx_prepared) and 4 (moe_forward_mx4) give 64
+ * below 64 expected tokens per expert, then 128.  Host-only; 0 for
  * invalid sizes, I not a multiple of 256, or another weight_bits. */
 int32_t moe_gemm_tile_rows_panels(int32_t M, int32_t E, int32_t top_k, int32_t I,
                                   int32_t weight_bits);

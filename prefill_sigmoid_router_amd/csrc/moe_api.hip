@@ -107,8 +107,7 @@ static_assert(kSelfRouteIds <= moe::kSelfRouteMaxIds, "self-routing id limit");
 // M=512 2,775 -> 2,588 us, but 4,180 -> 4,428 us at M=2048; bf16 keeps gemm_tile_rows).
 int panel_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I, int bits) {
   const int64_t per_expert = (int64_t)M * top_k / E;
-  if (bits == 4) return per_expert < 256 ? 64 : 128;
-  if (bits == 8) return per_expert < 64 ? 64 : 128;
+  if (bits == 4 || bits == 8) return per_expert < 64 ? 64 : 128;
   return gemm_tile_rows(M, E, top_k, I, false);
 }
 

@@ -186,9 +186,10 @@ def test_gemm_tile_rows_follows_tokens_per_expert(B):
     assert B.moe_gemm_tile_rows_panels(512, 256, 16, 2048, 8) == 64
     assert B.moe_gemm_tile_rows_panels(1023, 256, 16, 2048, 8) == 64
     assert B.moe_gemm_tile_rows_panels(1024, 256, 16, 2048, 8) == 128
-    assert B.moe_gemm_tile_rows_panels(2048, 256, 16, 2048, 4) == 64
-    assert B.moe_gemm_tile_rows_panels(4095, 256, 16, 2048, 4) == 64
-    assert B.moe_gemm_tile_rows_panels(4096, 256, 16, 2048, 4) == 128
+    assert B.moe_gemm_tile_rows_panels(512, 256, 16, 2048, 4) == 64
+    assert B.moe_gemm_tile_rows_panels(1023, 256, 16, 2048, 4) == 64
+    assert B.moe_gemm_tile_rows_panels(1024, 256, 16, 2048, 4) == 128
+    assert B.moe_gemm_tile_rows_panels(2048, 256, 16, 2048, 4) == 128
     assert B.moe_gemm_tile_rows_panels(2048, 256, 16, 2048, 6) == 0
     assert B.moe_gemm_tile_rows_panels(2048, 256, 16, 384, 4) == 0
 

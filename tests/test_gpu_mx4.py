@@ -150,14 +150,14 @@ def test_quantize_bit_exact(B, dev, shape):
 # ---------------------------------------------------------------------------------------
 # Whole layer
 # ---------------------------------------------------------------------------------------
-# MXFP4 tiles: 64 rows below 256 expected tokens per expert (nontemporal weights below 32),
+# MXFP4 tiles: 64 rows below 64 expected tokens per expert (nontemporal weights below 32),
 # 128 rows from there
 MX4_SMALL = {
     "mx4_tiles64_stream": mi.LayerConfig("mx4_tiles64_stream", M=64, H=320, E=16, top_k=4,
                                          I=256, block=16),
     "mx4_tiles64_zipf": mi.LayerConfig("mx4_tiles64_zipf", M=100, H=448, E=8, top_k=4,
                                        I=256, block=32, zipf_s=1.0),
-    "mx4_tiles64_shared": mi.LayerConfig("mx4_tiles64_shared", M=300, H=640, E=8, top_k=4,
+    "mx4_tiles64_shared": mi.LayerConfig("mx4_tiles64_shared", M=120, H=640, E=8, top_k=4,
                                          I=512, block=64, zipf_s=1.0),
     "mx4_tiles128": mi.LayerConfig("mx4_tiles128", M=600, H=384, E=8, top_k=4, I=256,
                                    block=64, zipf_s=1.0),

@@ -30,6 +30,7 @@ import argparse
 import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -202,15 +203,22 @@ def up_kernel_name(B, cfg, mx=False):
     return f"expert_tiled ({rows}-row tiles, up)"
 
 
-def load_profile(name: str, workload: str):
+def _tile_rows(kernel: str):
+    """Token-tile height named in a kernel label ("...<128, ..." or "(64-row tiles"), or None."""
+    m = re.search(r"<(\d+),|\((\d+)-row", kernel)
+    return None if m is None else int(m.group(1) or m.group(2))
+
+
+def load_profile(name: str, workload: str, kernel: str):
     """A counter summary under profiles/ (FETCH_SIZE / WRITE_SIZE, MFMA busy), or None when
-    it is missing, was taken on another workload, or the kernel source changed since."""
+    it is missing, was taken on another workload or another tile height than `kernel` runs
+    with, or the kernel source changed since."""
     try:
         with open(os.path.join(PROFILES, name)) as f:
             t = json.load(f)
     except (OSError, ValueError):
         return None
-    if t.get("workload") != workload:
+    if t.get("workload") != workload or _tile_rows(t.get("kernel", "")) != _tile_rows(kernel):
         return None
     src = os.path.join(ROOT, "prefill_sigmoid_router_amd", "csrc", t.get("source_file", ""))
     if not os.path.isfile(src) or t.get("source_sha256_16") != source_hash(src):
@@ -639,20 +647,23 @@ def main():
     lds_rates = read_probe_lds_gbs(torch, dev, weights["w13"])
     read_gbs = max(plain_gbs, *lds_rates.values())
 
-    roof = roofline(res, up_kernel_name(B, head), read_gbs,
-                    load_profile(f"traffic_expert_up_{head.name}.json", head.name))
+    head_kernel = up_kernel_name(B, head)
+    roof = roofline(res, head_kernel, read_gbs,
+                    load_profile(f"traffic_expert_up_{head.name}.json", head.name, head_kernel))
     roof["read_probes_gbs"] = {"plain_nontemporal_loads": round(plain_gbs, 1)}
     for stages, g in lds_rates.items():
         roof["read_probes_gbs"][f"global_load_lds_nt_ring_{stages}_stages"] = round(g, 1)
     for line_d, name, r, kernel, fmt in leg_roofs:
         line_d[name]["roofline"] = roofline(
-            r, kernel, read_gbs, load_profile(f"traffic_expert_frag_up_{fmt}_{name}.json", name))
+            r, kernel, read_gbs,
+            load_profile(f"traffic_expert_frag_up_{fmt}_{name}.json", name, kernel))
     sweep_out = {}
     for name, r in sweep.items():
         c = mi.CONFIGS[name]
         sweep_out[name] = _rounded(r)
-        sweep_out[name]["roofline"] = roofline(r, up_kernel_name(B, c), read_gbs,
-                                               load_profile(f"traffic_expert_up_{name}.json", name))
+        kernel = up_kernel_name(B, c)
+        sweep_out[name]["roofline"] = roofline(
+            r, kernel, read_gbs, load_profile(f"traffic_expert_up_{name}.json", name, kernel))
 
     cpu = None
     if not args.no_cpu_baseline:

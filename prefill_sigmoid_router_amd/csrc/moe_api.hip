@@ -101,10 +101,11 @@ constexpr int kSelfRouteIds = 256;
 static_assert(kSelfRouteIds <= moe::kSelfRouteMaxIds, "self-routing id limit");
 
 // Token-tile height of the fragment GEMMs on panels, by weight format (16 bf16, 8 MXFP8,
-// 4 MXFP4).  The narrower the weights, the less a hot expert's extra tiles cost in weight
-// bytes against the token rows and MFMAs the taller tiles waste on padding (measured: MXFP4
-// 64-row tiles at M=512 / 2048 2,326 -> 1,800 / 3,701 -> 3,517 us per layer; MXFP8 at
-// M=512 2,775 -> 2,588 us, but 4,180 -> 4,428 us at M=2048; bf16 keeps gemm_tile_rows).
+// 4 MXFP4).  Narrow weights make a hot expert's extra tiles cheap in weight bytes, so the
+// MX formats take 64-row tiles (less padding) below 64 tokens per expert (measured: MXFP4
+// at M=512 2,326 -> 1,800 us per layer, MXFP8 2,775 -> 2,588 us) and 128-row tiles from 64,
+// where the up GEMM's per-expert cache policy favours them (M=2048: MXFP8 4,428 -> 4,180 us,
+// MXFP4 3,471 -> 3,268 us); bf16 keeps gemm_tile_rows.
 int panel_tile_rows(int32_t M, int32_t E, int32_t top_k, int32_t I, int bits) {
   const int64_t per_expert = (int64_t)M * top_k / E;
   if (bits == 4 || bits == 8) return per_expert < 64 ? 64 : 128;

@@ -50,10 +50,10 @@ def _random_configs(seed, n, mx, panels=False):
 BF16_CASES = _random_configs(2024, 8, mx=False)
 MX_CASES = _random_configs(2025, 5, mx=True)
 PANEL_CASES = _random_configs(2026, 6, mx=False, panels=True) + [
-    # many tokens per expert: 128-row tiles for every format (MXFP4 from 256 per expert)
+    # many tokens per expert: 128-row tiles for every format
     mi.LayerConfig("panel_many_M400_H320_E3_k2_I256_B64", M=400, H=320, E=3, top_k=2, I=256,
                    block=64),
-    # 128-row bf16 and MXFP8 tiles, 64-row MXFP4 tiles, a partial W2 N tile (H = 448)
+    # 128-row tiles for every format (150 tokens per expert), a partial W2 N tile (H = 448)
     mi.LayerConfig("panel_mid_M300_H448_E4_k2_I512_B32_zipf", M=300, H=448, E=4, top_k=2,
                    I=512, block=32, zipf_s=1.0),
 ]

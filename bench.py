@@ -17,9 +17,10 @@ algorithmic bytes per launch / its average duration from the HIP events, against
 8 TB/s HBM peak, with the MFMA rate of the same launch against the 2.5 PFLOP/s bf16 dense
 peak beside it; `traffic` is the HBM bytes that rocprofv3's FETCH_SIZE + WRITE_SIZE
 counters read for that kernel (profiles/traffic_*.json, null once the kernel source has
-changed since).  `measured_read_peak` is the larger of two read probes over the resident
+changed since).  `measured_read_peak` is the best of the read probes over the resident
 W13 (probe/read_bw.hip): a plain nontemporal vector-load pass, and the tiled GEMMs' own
-copy path (nontemporal global_load_lds whole-line copies into a 3-stage LDS ring).
+copy path (nontemporal global_load_lds whole-line copies into LDS rings, 256-row items on
+one workgroup per CU and 128-row items on two or three).
 `cpu_baseline` is the CPU oracle timed on the GPU run's own inputs (copied to the host).
 `mxfp8_decode` times the same layer with the expert weights quantized to MXFP8
 (moe_forward_mx); it is a separate measurement, not the headline, whose weights are bf16.
@@ -380,7 +381,8 @@ def _probe_lib():
     lib.moe_probe_read_grid.restype = ctypes.c_int
     lib.moe_probe_read_lds.restype = ctypes.c_int
     lib.moe_probe_read_lds.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int, ctypes.c_int,
-                                       ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+                                       ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p,
+                                       ctypes.c_void_p]
     return lib
 
 
@@ -417,27 +419,38 @@ def read_probe_gbs(torch, dev, buf, reps=5):
 
 
 def read_probe_lds_gbs(torch, dev, w13, reps=5):
-    """The tiled up GEMM's copy path over the W13 stack [E, 2I, H]: nontemporal
-    global_load_lds whole-line copies of items of 128 gate + 128 up rows in the kernel's
-    XCD-aware order, one 4-wave workgroup per CU, no arithmetic, through LDS rings of 3, 4
-    and 5 stages of 32 KiB; the best rate of each ring depth over reps passes."""
+    """The tiled up GEMMs' copy path over the W13 stack [E, 2I, H]: nontemporal
+    global_load_lds whole-line copies in the kernels' XCD-aware item order, no arithmetic:
+    items of 256 rows (128 gate + 128 up) on one 4-wave workgroup per CU through rings of
+    3, 4 and 5 chunks of 32 KiB, and items of 128 rows on two or three workgroups per CU
+    through rings of 3 or 4 chunks of 16 KiB; the best rate of each over reps passes."""
     import ctypes
     lib = _probe_lib()
     E, two_i, K = w13.shape
-    grid = torch.cuda.get_device_properties(dev).multi_processor_count // 8 * 8
-    sink = torch.empty(grid, dtype=torch.int32, device=dev)
+    cus = torch.cuda.get_device_properties(dev).multi_processor_count // 8 * 8
+    sink = torch.empty(3 * cus, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
     rates = {}
-    for stages in (3, 4, 5):
+    for rows, stages, per_cu in ((256, 3, 1), (256, 4, 1), (256, 5, 1), (128, 3, 2),
+                                 (128, 3, 3), (128, 4, 2)):
         def once():
             st = lib.moe_probe_read_lds(ctypes.c_void_p(w13.data_ptr()), E, two_i // 2, K, stages,
-                                        grid, ctypes.c_void_p(sink.data_ptr()),
+                                        rows, per_cu * cus, ctypes.c_void_p(sink.data_ptr()),
                                         ctypes.c_void_p(stream.cuda_stream))
             if st != 0:
                 raise RuntimeError(f"moe_probe_read_lds failed with status {st}")
 
-        rates[stages] = w13.numel() * 2 / (_best_ms(torch, stream, once, reps) * 1e-3) / 1e9
+        rates[(rows, stages, per_cu)] = (w13.numel() * 2 /
+                                         (_best_ms(torch, stream, once, reps) * 1e-3) / 1e9)
     return rates
+
+
+def read_probes(torch, dev, w13):
+    """Every read probe over `w13`, by name: GB/s."""
+    out = {"plain_nontemporal_loads": read_probe_gbs(torch, dev, w13)}
+    for (rows, stages, per_cu), g in read_probe_lds_gbs(torch, dev, w13).items():
+        out[f"global_load_lds_nt_{rows}_rows_{stages}_stages_{per_cu}_per_cu"] = g
+    return out
 
 
 def _rounded(r):
@@ -495,6 +508,12 @@ def main():
                "norm_w": full["norm_w"]}
     del full
     torch.cuda.synchronize()
+
+    # read probes over the resident W13 (the bytes the up GEMM streams), once before the
+    # legs and once after them (a box that has run for minutes can read at another rate);
+    # each probe keeps the better of its two passes
+    print("bench: timing the HBM read probes", file=sys.stderr, flush=True)
+    probes = read_probes(torch, dev, weights["w13"])
 
     print(f"bench: timing {args.workload}", file=sys.stderr, flush=True)
     res = run_workload(B, mi, torch, head, weights, args.steps, args.warmup, dev)
@@ -641,18 +660,14 @@ def main():
         del q
         torch.cuda.empty_cache()
 
-    # read probes over the resident W13 (the bytes the up GEMM streams)
-    print("bench: timing the HBM read probes", file=sys.stderr, flush=True)
-    plain_gbs = read_probe_gbs(torch, dev, weights["w13"])
-    lds_rates = read_probe_lds_gbs(torch, dev, weights["w13"])
-    read_gbs = max(plain_gbs, *lds_rates.values())
+    print("bench: timing the HBM read probes again", file=sys.stderr, flush=True)
+    probes = {k: max(v, probes[k]) for k, v in read_probes(torch, dev, weights["w13"]).items()}
+    read_gbs = max(probes.values())
 
     head_kernel = up_kernel_name(B, head)
     roof = roofline(res, head_kernel, read_gbs,
                     load_profile(f"traffic_expert_up_{head.name}.json", head.name, head_kernel))
-    roof["read_probes_gbs"] = {"plain_nontemporal_loads": round(plain_gbs, 1)}
-    for stages, g in lds_rates.items():
-        roof["read_probes_gbs"][f"global_load_lds_nt_ring_{stages}_stages"] = round(g, 1)
+    roof["read_probes_gbs"] = {k: round(g, 1) for k, g in probes.items()}
     for line_d, name, r, kernel, fmt in leg_roofs:
         line_d[name]["roofline"] = roofline(
             r, kernel, read_gbs,

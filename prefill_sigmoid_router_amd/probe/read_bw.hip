@@ -8,13 +8,14 @@
 // loaded words are folded with xor into one word per workgroup so the loads cannot be
 // dropped.
 //
-// A second pass reads the W13 stack [E, 2I, K] the way the decode up GEMM streams it:
+// A second pass reads the W13 stack [E, 2I, K] the way the tiled up GEMMs stream it:
 // whole 128-byte lines copied global -> LDS with nontemporal global_load_lds_dwordx4 (each
-// copy 8 rows x one line), items of 128 gate + 128 up rows x 64 K values per chunk (32 KiB),
-// a 3-stage LDS ring (two chunks in flight), one workgroup of 4 waves per CU walking its
-// XCD's share of the (expert, N tile) items.  Each wave waits for its own copies and a bare barrier publishes
-// the chunk; every lane then folds one 16-byte LDS word per copy into its xor.  It is the
-// ceiling of that copy path with no arithmetic behind it.
+// copy 8 rows x one line), items of 256 rows (128 gate + 128 up; 32 KiB per chunk of 64 K
+// values) or 128 rows (16 KiB per chunk), a ring of 3 to 5 chunks, 4-wave workgroups (one
+// per CU with 256-row items, two or three with 128-row items) walking their XCD's share of
+// the (expert, N tile) items.  Each wave waits for its own copies and a bare barrier
+// publishes the chunk; every lane then folds one 16-byte LDS word per copy into its xor.
+// It is the rate of that copy path with no arithmetic behind it.
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -52,20 +53,19 @@ __global__ __launch_bounds__(kThreads) void read_pass_kernel(const u32x4* __rest
 typedef __attribute__((address_space(1))) void global_void;
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int kLdsRows = 256;                  // rows per block
 constexpr int kLdsKC = 64;                     // K values per chunk: one line per row
 constexpr int kLdsWaves = 4;
-constexpr int kLdsCopies = kLdsRows / 8;       // 1 KiB copies per chunk
-constexpr int kLdsCPW = kLdsCopies / kLdsWaves;
 
 template <int N>
 __device__ __forceinline__ void probe_wait_vmcnt() {
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
 }
 
-template <int kLdsStages>
+template <int kLdsStages, int kLdsRows>
 __global__ __launch_bounds__(64 * kLdsWaves) void read_lds_ring_kernel(
     const uint16_t* __restrict__ m, int E, int I, int K, uint32_t* __restrict__ sink) {
+  constexpr int kLdsCopies = kLdsRows / 8;       // 1 KiB copies per chunk
+  constexpr int kLdsCPW = kLdsCopies / kLdsWaves;
   __shared__ __align__(16) unsigned char lds[kLdsStages * kLdsCopies * 1024];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   // items (expert e, N tile nt): rows nt*128 .. +127 of the first half of e's 2I rows and the
@@ -135,23 +135,33 @@ extern "C" {
 // Workgroups of one pass; the sink must hold this many uint32.
 int moe_probe_read_grid(void) { return 4096; }
 
-// Reads a [E, 2I, K] bf16 weight stack (the W13 layout; I a multiple of 128, K of 64,
+// Reads a [E, 2I, K] bf16 weight stack (the W13 layout; I a multiple of rows / 2, K of 64,
 // 16-byte aligned) once through the LDS ring on `stream`, in the item order of the tiled up
-// GEMM, with an LDS ring of `stages` (3..5) chunks of 32 KiB and `grid` workgroups (a
-// multiple of 8: the CU count); the sink must hold `grid` uint32.  Returns 0, -1 for invalid arguments, -4 for a launch failure.
-int moe_probe_read_lds(const void* m, int E, int I, int K, int stages, int grid, uint32_t* sink,
-                       hipStream_t stream) {
-  if (m == nullptr || sink == nullptr || E <= 0 || I <= 0 || I % (kLdsRows / 2) != 0 || K <= 0 ||
-      K % kLdsKC != 0 || grid <= 0 || grid % 8 != 0 || reinterpret_cast<uintptr_t>(m) % 16 != 0 ||
-      stages < 3 || stages > 5)
+// GEMM: items of `rows` (256 or 128) weight rows, half gate and half up, an LDS ring of
+// `stages` (3..5) chunks of rows x 128 bytes, and `grid` workgroups (a multiple of 8; with
+// 128-row items two or three workgroups fit on a CU, so that more copies are in flight per
+// CU); the sink must hold `grid` uint32.  Returns 0, -1 for invalid arguments, -4 for a
+// launch failure.
+int moe_probe_read_lds(const void* m, int E, int I, int K, int stages, int rows, int grid,
+                       uint32_t* sink, hipStream_t stream) {
+  if (m == nullptr || sink == nullptr || E <= 0 || I <= 0 || (rows != 256 && rows != 128) ||
+      I % (rows / 2) != 0 || K <= 0 || K % kLdsKC != 0 || grid <= 0 || grid % 8 != 0 ||
+      reinterpret_cast<uintptr_t>(m) % 16 != 0 || stages < 3 || stages > 5)
     return -1;
   const uint16_t* mm = static_cast<const uint16_t*>(m);
-  if (stages == 3)
-    hipLaunchKernelGGL(read_lds_ring_kernel<3>, dim3(grid), dim3(64 * kLdsWaves), 0, stream, mm, E, I, K, sink);
-  else if (stages == 4)
-    hipLaunchKernelGGL(read_lds_ring_kernel<4>, dim3(grid), dim3(64 * kLdsWaves), 0, stream, mm, E, I, K, sink);
-  else
-    hipLaunchKernelGGL(read_lds_ring_kernel<5>, dim3(grid), dim3(64 * kLdsWaves), 0, stream, mm, E, I, K, sink);
+#define MOE_PROBE_LDS(S, R)                                                                      \
+  hipLaunchKernelGGL((read_lds_ring_kernel<S, R>), dim3(grid), dim3(64 * kLdsWaves), 0, stream, \
+                     mm, E, I, K, sink)
+  if (rows == 256) {
+    if (stages == 3) MOE_PROBE_LDS(3, 256);
+    else if (stages == 4) MOE_PROBE_LDS(4, 256);
+    else MOE_PROBE_LDS(5, 256);
+  } else {
+    if (stages == 3) MOE_PROBE_LDS(3, 128);
+    else if (stages == 4) MOE_PROBE_LDS(4, 128);
+    else MOE_PROBE_LDS(5, 128);
+  }
+#undef MOE_PROBE_LDS
   return hipGetLastError() == hipSuccess ? 0 : -4;
 }
 
